@@ -1,0 +1,76 @@
+// Splitting a packed base-3 word into base-81 chunks (as LDS byte offsets).
+//
+// A word holds 20 ternary digits d_0..d_19 (d = t + 1), least significant
+// first: w = sum_i d_i 3^i < 3^20.  The kernels consume it four digits at a
+// time: chunk c_j = d_{4j} + 3 d_{4j+1} + 9 d_{4j+2} + 27 d_{4j+3} in [0, 81),
+// so w = sum_j c_j 81^j.  Because 4 divides both 20 and 128, a chunk never
+// straddles a scale group.  word_offsets() returns 4*c_j, the byte offset of
+// entry c_j in a table of 4-byte entries.
+//
+// Every step avoids the quarter-rate 32-bit integer multiply:
+//   a  = floor(w / 3^8):  one FP64 FMA, floor(w * (1/6561) + 0.5/6561).  For
+//        w < 3^20 the FMA is within 1.3e-10 of (w + 0.5)/6561, which lies at
+//        least 0.5/6561 = 7.6e-5 from an integer, so truncation is exact.
+//   e  = floor(a / 6561) = mulhi_u24(a, 654622): 654622 = ceil(2^32/6561),
+//        exact while a * (654622*6561 - 2^32) < 2^32, i.e. a < 561736, and
+//        a < 3^12 = 531441.
+//   4b = 4w - 26244 a (digits 0..7, times 4) and 4m = 4a - 26244 e (digits
+//        8..15, times 4) by 24-bit multiply-add, exact modulo 2^32.
+//   floor(b / 81) = mulhi_u24(4b, 13256072): 13256072 = ceil(2^30/81) and
+//        81 * 13256072 = 2^30 + 8, so the error stays below 6e-7 < 1/81.
+//   4 c_even = 4v - 324 floor(v/81), 4 c_odd = floor(v/81) << 2.
+// 15 VALU instructions per word for five offsets.  The host build of this
+// header emulates the same instructions (24-bit operands) so that a CPU test
+// can check every step exhaustively against plain division.
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define TQ_HD __host__ __device__ __forceinline__
+#else
+#define TQ_HD static inline
+#endif
+
+namespace tq {
+
+// Low 32 bits of sext24(a) * sext24(b) + c  (v_mad_i32_i24).
+TQ_HD uint32_t mad_i24(uint32_t a, int32_t b, uint32_t c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t r;
+  asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(b), "v"(c));
+  return r;
+#else
+  const int64_t sa = static_cast<int64_t>(static_cast<int32_t>(a << 8) >> 8);
+  const int64_t sb = static_cast<int64_t>(static_cast<int32_t>(static_cast<uint32_t>(b) << 8) >> 8);
+  return static_cast<uint32_t>(static_cast<uint64_t>(sa * sb) + c);
+#endif
+}
+
+// Bits 32..47 of (a & 0xffffff) * (b & 0xffffff)  (v_mul_hi_u32_u24).
+TQ_HD uint32_t mulhi_u24(uint32_t a, uint32_t b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t r;
+  asm("v_mul_hi_u32_u24 %0, %1, %2" : "=v"(r) : "s"(b), "v"(a));
+  return r;
+#else
+  return static_cast<uint32_t>((static_cast<uint64_t>(a & 0xffffffu) * (b & 0xffffffu)) >> 32);
+#endif
+}
+
+// o[j] = 4 * chunk j (digits 4j..4j+3) of the word.
+TQ_HD void word_offsets(uint32_t w, uint32_t o[5]) {
+  const double wd = static_cast<double>(w);
+  const uint32_t a = static_cast<uint32_t>(__builtin_fma(wd, 1.0 / 6561.0, 0.5 / 6561.0));
+  const uint32_t e = mulhi_u24(a, 654622u);
+  const uint32_t b4 = mad_i24(a, -26244, w << 2);
+  const uint32_t m4 = mad_i24(e, -26244, a << 2);
+  const uint32_t b1 = mulhi_u24(b4, 13256072u);
+  const uint32_t m1 = mulhi_u24(m4, 13256072u);
+  o[0] = mad_i24(b1, -324, b4);
+  o[1] = b1 << 2;
+  o[2] = mad_i24(m1, -324, m4);
+  o[3] = m1 << 2;
+  o[4] = e << 2;
+}
+
+}  // namespace tq

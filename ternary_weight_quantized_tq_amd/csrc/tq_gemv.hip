@@ -1,0 +1,428 @@
+// Decode GEMV on packed ternary weights: y = W_hat . (H_128 x), M = 1..8.
+//
+// Work split (TQ_LAYOUT_ROW64, slice-major): a workgroup owns one 640-trit K
+// slice (8 quads, 5 scale groups) of W consecutive 64-row blocks; lane r of
+// wavefront w owns row 64*(W*blockIdx.y + w) + r.  W is chosen on the host so
+// that (row groups) x (slices) fills the compute units in a single round;
+// partial sums of the slices of a row are then combined (see finish()).
+// All lanes of a wavefront sit at the same K position, so activations and
+// lookup tables are wavefront-uniform and scale-group boundaries fall at
+// compile-time chunk positions.
+//
+// Order of work inside a workgroup, chosen so that nothing waits on the
+// weight stream before it has to:
+//   1. load the scales and this wavefront's block of activations, then only
+//      kLookahead quads of weights (non-temporal: streamed once);
+//   2. block-128 transform of the activations in registers (wavefront
+//      shuffles), staged in LDS;
+//   3. table build (M == 1) or code table + fp16 activations (M >= 2);
+//   4. decode quad i while quad i + kLookahead is in flight.
+// The barriers in 2-3 wait for LDS only (a plain __syncthreads() would also
+// wait for every outstanding weight load).
+//
+// M == 1 (single-stream decode) uses a partial-sum table in LDS: for every
+// 4-trit position p of the slice and every chunk value c in [0, 81),
+// T[p][c] = sum_{i<4} (d_i(c) - 1) x'[4p + i] in FP32.  Each 4 trits then
+// cost one LDS read and one add: with weights in {-1, 0, 1} the product
+// reduces to sign tests and additions/subtractions ("Ternary-Bonsai2-27B vs
+// Qwen3.8-27B-GSQ-RCO" page, §1.1).  M >= 2 reads fp16 trit codes per chunk
+// and accumulates with v_dot2_f32_f16 against the fp16-rounded x'.
+#include "tq_internal.h"
+
+using namespace tq;
+
+namespace {
+
+constexpr int kSliceChunks = 160;
+constexpr int kLutEntries = 81;
+constexpr int kMaxWaves = 16;
+constexpr int kLookahead = 3;
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+struct GemvArgs {
+  const uint4* words;       // ROW64 words, as quads
+  const uint16_t* scales;   // ROW64 scales
+  const void* x;            // [m][k]
+  float* y;                 // [m][n]
+  float* partial;           // [nsl][m][npad] (mode kPartial)
+  int mode;                 // kDirect, kPartial or kAtomic (see finish())
+  int x_dtype;
+  int n, k, nq, groups, nb, npad, nsl;
+  int fused;
+};
+
+// s_barrier after this wavefront's LDS traffic has completed; outstanding
+// global loads are left in flight.
+#define TQ_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+// Keeps the compiler from hoisting later loads above this point.
+#define TQ_ORDER() asm volatile("" ::: "memory")
+
+__device__ __forceinline__ uint4 load_quad(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+struct Tile {
+  int slice, rg, tid, wave, lane, waves, rb, rbc, nq_here, k0;
+  bool active;
+};
+
+__device__ __forceinline__ Tile make_tile(const GemvArgs& a) {
+  Tile t;
+  t.slice = blockIdx.x;
+  t.rg = blockIdx.y;
+  t.tid = threadIdx.x;
+  t.wave = t.tid >> 6;
+  t.lane = t.tid & 63;
+  t.waves = blockDim.x >> 6;
+  t.rb = t.rg * t.waves + t.wave;
+  t.active = t.rb < a.nb;
+  t.rbc = t.active ? t.rb : a.nb - 1;
+  t.nq_here = min(kSliceQuads, a.nq - t.slice * kSliceQuads);
+  t.k0 = t.slice * kSliceTrits;
+  return t;
+}
+
+__device__ __forceinline__ void load_scales(const GemvArgs& a, const Tile& t, float (&sc)[kSliceGroups]) {
+  const uint16_t* sp = a.scales + row64_scale_base(t.slice, t.rbc, a.nb) + t.lane;
+#pragma unroll
+  for (int j = 0; j < kSliceGroups; ++j) {
+    const float v = f16_to_f32(sp[j * 64]);
+    sc[j] = t.active ? v : 0.0f;
+  }
+}
+
+// Activations of block `blk` (0..4) of the slice for row m; zero past K.
+__device__ __forceinline__ void load_block(const GemvArgs& a, const Tile& t, int m, int blk, float& v0, float& v1,
+                                           bool& valid) {
+  const int kb = t.k0 + blk * 128;
+  valid = kb < a.k;
+  load_act2(a.x, a.x_dtype, static_cast<size_t>(m) * a.k + (valid ? kb : 0) + 2 * t.lane, v0, v1);
+}
+
+__device__ __forceinline__ void transform(const GemvArgs& a, float& v0, float& v1, bool valid, int lane) {
+  if (a.fused) wave_fwht128<float>(v0, v1, lane, kInvSqrt128);
+  if (!valid) {
+    v0 = 0.0f;
+    v1 = 0.0f;
+  }
+}
+
+// How a workgroup delivers its per-row partial sums:
+//   kDirect  (one slice per row):  y = partial;
+//   kPartial (default):            partial[slice][m][row] = partial, summed in
+//                                  slice order by reduce_kernel (deterministic);
+//   kAtomic  (TQ_ACCUMULATE):      y += partial with device-scope float
+//                                  atomics (single launch; the order of the
+//                                  slice additions is not fixed).
+enum { kDirect = 0, kPartial = 1, kAtomic = 2 };
+
+template <int M>
+__device__ __forceinline__ void finish(const GemvArgs& a, const Tile& t, const float (&part)[M]) {
+  const int row = t.rb * 64 + t.lane;
+  if (!t.active || row >= a.n) return;
+  if (a.mode == kPartial) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) a.partial[(static_cast<size_t>(t.slice) * M + m) * a.npad + row] = part[m];
+  } else if (a.mode == kAtomic) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) atomicAdd(&a.y[static_cast<size_t>(m) * a.n + row], part[m]);
+  } else {
+#pragma unroll
+    for (int m = 0; m < M; ++m) a.y[static_cast<size_t>(m) * a.n + row] = part[m];
+  }
+}
+
+// y[m][row] = sum over slices, in slice order, of partial[slice][m][row].
+__global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ partial, float* __restrict__ y, int m,
+                                                     int n, int npad, int nsl) {
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  const int mm = blockIdx.y;
+  if (row >= n) return;
+  const float* p = partial + static_cast<size_t>(mm) * npad + row;
+  const size_t stride = static_cast<size_t>(m) * npad;
+  float v[8];
+  float sum = 0.0f;
+  for (int s0 = 0; s0 < nsl; s0 += 8) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = (s0 + q < nsl) ? p[(s0 + q) * stride] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) sum += v[q];
+  }
+  y[static_cast<size_t>(mm) * n + row] = sum;
+}
+
+// ------------------------------------------------------------ M == 1 ---
+__global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a) {
+  __shared__ float lut[kSliceChunks * kLutEntries];                   // 51840 B
+  __shared__ __attribute__((aligned(16))) float xs[kSliceTrits];      // 2560 B
+  const Tile t = make_tile(a);
+
+  float sc[kSliceGroups];
+  load_scales(a, t, sc);
+  float v0 = 0.0f, v1 = 0.0f;
+  bool valid = false;
+  if (t.wave < kSliceGroups) load_block(a, t, 0, t.wave, v0, v1, valid);
+  TQ_ORDER();
+  const uint4* wp = a.words + row64_quad_base(t.slice, t.rbc, a.nb) + t.lane;
+  uint4 wq[kSliceQuads];
+#pragma unroll
+  for (int i = 0; i < kLookahead; ++i) wq[i] = load_quad(wp + min(i, t.nq_here - 1) * 64);
+
+  for (int blk = t.wave; blk < kSliceGroups; blk += t.waves) {
+    if (blk != t.wave) load_block(a, t, 0, blk, v0, v1, valid);  // only when fewer than 5 wavefronts
+    transform(a, v0, v1, valid, t.lane);
+    xs[blk * 128 + 2 * t.lane] = v0;
+    xs[blk * 128 + 2 * t.lane + 1] = v1;
+  }
+  TQ_LDS_BARRIER();
+
+  // T[p][b + 27 d3] = t0 x0 + t1 x1 + t2 x2 + (d3 - 1) x3, b = d0 + 3 d1 + 9 d2.
+  const int stride = blockDim.x / 27;
+  if (t.tid < 27 * stride) {
+    const int b = t.tid % 27;
+    const float t0 = static_cast<float>(b % 3) - 1.0f;
+    const float t1 = static_cast<float>((b / 3) % 3) - 1.0f;
+    const float t2 = static_cast<float>(b / 9) - 1.0f;
+    for (int p = t.tid / 27; p < kSliceChunks; p += stride) {
+      const float4 x4 = *reinterpret_cast<const float4*>(&xs[4 * p]);
+      const float base = fmaf(t2, x4.z, fmaf(t1, x4.y, t0 * x4.x));
+      float* e = &lut[p * kLutEntries + b];
+      e[0] = base - x4.w;
+      e[27] = base;
+      e[54] = base + x4.w;
+    }
+  }
+  TQ_LDS_BARRIER();
+
+  float acc[kSliceGroups] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < kSliceQuads; ++i) {
+    if (i + kLookahead < kSliceQuads) wq[i + kLookahead] = load_quad(wp + min(i + kLookahead, t.nq_here - 1) * 64);
+    if (i < t.nq_here) {
+      const uint32_t wv[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
+      float v[20];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t o[5];
+        word_offsets(wv[j], o);
+#pragma unroll
+        for (int h = 0; h < 5; ++h) {
+          const int p = i * 20 + j * 5 + h;  // chunk position in the slice, compile-time
+          v[j * 5 + h] =
+              *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + p * kLutEntries * 4 + o[h]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 20; ++c) acc[(i * 20 + c) / 32] += v[c];
+    }
+    TQ_ORDER();
+  }
+  float part[1] = {0.0f};
+#pragma unroll
+  for (int g = 0; g < kSliceGroups; ++g) part[0] = fmaf(sc[g], acc[g], part[0]);
+  finish<1>(a, t, part);
+}
+
+// ------------------------------------------------------- 2 <= M <= 8 ---
+template <int M>
+__global__ __launch_bounds__(kMaxWaves * 64) void gemv_dot2_kernel(GemvArgs a) {
+  __shared__ uint32_t codes_lo[kLutEntries];  // fp16 trits 0, 1 of each chunk value
+  __shared__ uint32_t codes_hi[kLutEntries];  // fp16 trits 2, 3
+  __shared__ __attribute__((aligned(16))) _Float16 xh[M][kSliceTrits];
+  const Tile t = make_tile(a);
+  constexpr int kJobs = M * kSliceGroups;      // (row m, block) transforms per slice
+
+  float sc[kSliceGroups];
+  load_scales(a, t, sc);
+  // Activations of this wavefront's first transform job, before the weights.
+  float v0 = 0.0f, v1 = 0.0f;
+  bool valid = false;
+  if (t.wave < kJobs) load_block(a, t, t.wave / kSliceGroups, t.wave % kSliceGroups, v0, v1, valid);
+  TQ_ORDER();
+  const uint4* wp = a.words + row64_quad_base(t.slice, t.rbc, a.nb) + t.lane;
+  uint4 wq[kSliceQuads];
+#pragma unroll
+  for (int i = 0; i < kLookahead; ++i) wq[i] = load_quad(wp + min(i, t.nq_here - 1) * 64);
+
+  for (int e = t.tid; e < kLutEntries; e += blockDim.x) {
+    uint16_t h[4];
+    int c = e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(static_cast<float>(c % 3) - 1.0f));
+      c /= 3;
+    }
+    codes_lo[e] = h[0] | (static_cast<uint32_t>(h[1]) << 16);
+    codes_hi[e] = h[2] | (static_cast<uint32_t>(h[3]) << 16);
+  }
+  for (int job = t.wave; job < kJobs; job += t.waves) {
+    if (job != t.wave) load_block(a, t, job / kSliceGroups, job % kSliceGroups, v0, v1, valid);
+    transform(a, v0, v1, valid, t.lane);
+    _Float16* dst = &xh[job / kSliceGroups][(job % kSliceGroups) * 128 + 2 * t.lane];
+    dst[0] = static_cast<_Float16>(v0);
+    dst[1] = static_cast<_Float16>(v1);
+  }
+  TQ_LDS_BARRIER();
+
+  float acc[M][kSliceGroups];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int g = 0; g < kSliceGroups; ++g) acc[m][g] = 0.0f;
+
+#pragma unroll
+  for (int i = 0; i < kSliceQuads; ++i) {
+    if (i + kLookahead < kSliceQuads) wq[i + kLookahead] = load_quad(wp + min(i + kLookahead, t.nq_here - 1) * 64);
+    if (i < t.nq_here) {
+      const uint32_t wv[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t o[5];
+        word_offsets(wv[j], o);
+#pragma unroll
+        for (int h = 0; h < 5; ++h) {
+          const int p = i * 20 + j * 5 + h;
+          const half2_t lo = __builtin_bit_cast(
+              half2_t, *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(codes_lo) + o[h]));
+          const half2_t hi = __builtin_bit_cast(
+              half2_t, *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(codes_hi) + o[h]));
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            const uint2 xq = *reinterpret_cast<const uint2*>(&xh[m][4 * p]);
+            float s = acc[m][p / 32];
+            s = __builtin_amdgcn_fdot2(lo, __builtin_bit_cast(half2_t, xq.x), s, false);
+            s = __builtin_amdgcn_fdot2(hi, __builtin_bit_cast(half2_t, xq.y), s, false);
+            acc[m][p / 32] = s;
+          }
+        }
+      }
+    }
+    TQ_ORDER();
+  }
+  float part[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float s = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kSliceGroups; ++g) s = fmaf(sc[g], acc[m][g], s);
+    part[m] = s;
+  }
+  finish<M>(a, t, part);
+}
+
+inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+struct GemvPlan {
+  int nb, npad, nsl, waves, ngroups;
+  size_t partial_bytes;
+};
+
+// Workspace: the per-slice partial sums (only when K spans several slices).
+GemvPlan plan_sizes(int n, int k, int m) {
+  GemvPlan p;
+  p.nb = row_blocks(n);
+  p.npad = p.nb * 64;
+  p.nsl = slices_per_row(k);
+  p.waves = 0;
+  p.ngroups = 0;
+  p.partial_bytes = p.nsl > 1 ? static_cast<size_t>(p.nsl) * m * p.npad * sizeof(float) : 0;
+  return p;
+}
+
+// Wavefronts per workgroup: enough row blocks per workgroup that
+// (row groups) x (slices) fits the compute units in one round.
+void plan_waves(GemvPlan& p) {
+  const int cus = tq_device_cus();
+  const int per_slice = cus / p.nsl > 0 ? cus / p.nsl : 1;
+  int w = (p.nb + per_slice - 1) / per_slice;
+  if (w < 1) w = 1;
+  if (w > kMaxWaves) w = kMaxWaves;
+  p.waves = w;
+  p.ngroups = (p.nb + w - 1) / w;
+}
+
+}  // namespace
+
+// Compute units of the current device (queried once per device).
+int tq_device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+// Shared by the C entry points: validates a compute descriptor.
+int tq_check_weights(const tq_weights* w, int experts_expected) {
+  if (!w) return TQ_EINVAL;
+  if (w->magic != TQ_MAGIC || w->version != TQ_VERSION) return TQ_EFORMAT;
+  if (w->layout != TQ_LAYOUT_ROW64) return w->layout == TQ_LAYOUT_ROWMAJOR ? TQ_EUNSUPPORTED : TQ_EFORMAT;
+  if (experts_expected > 0 && w->num_experts != experts_expected) return TQ_EFORMAT;
+  if (w->num_experts < 1) return TQ_EFORMAT;
+  if (w->n <= 0 || w->k <= 0 || w->k % TQ_GROUP) return TQ_ESHAPE;
+  if (!w->words || !w->scales) return TQ_EINVAL;
+  return TQ_OK;
+}
+
+size_t tq_gemv_workspace(int n, int k, int m) { return plan_sizes(n, k, m).partial_bytes; }
+
+extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, float* y, unsigned flags,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  int st = tq_check_weights(w, 1);
+  if (st != TQ_OK) return st;
+  if (!x || !y) return TQ_EINVAL;
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16 && x_dtype != TQ_F16) return TQ_EINVAL;
+  if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED | TQ_ACCUMULATE)) return TQ_EINVAL;
+  if (m < 1 || m > 8) return TQ_ESHAPE;
+  GemvPlan p = plan_sizes(w->n, w->k, m);
+  const bool accumulate = (flags & TQ_ACCUMULATE) != 0;
+  const int mode = accumulate ? kAtomic : (p.nsl > 1 ? kPartial : kDirect);
+  if (mode == kPartial) {
+    if (!workspace) return TQ_EINVAL;
+    if (ws_bytes < p.partial_bytes) return TQ_ENOSPACE;
+  }
+  plan_waves(p);
+  GemvArgs a;
+  a.words = reinterpret_cast<const uint4*>(w->words);
+  a.scales = w->scales;
+  a.x = x;
+  a.y = y;
+  a.partial = static_cast<float*>(workspace);
+  a.mode = mode;
+  a.x_dtype = x_dtype;
+  a.n = w->n;
+  a.k = w->k;
+  a.nq = quads_per_row(w->k);
+  a.groups = w->k / TQ_GROUP;
+  a.nb = p.nb;
+  a.npad = p.npad;
+  a.nsl = p.nsl;
+  a.fused = (flags & TQ_FWHT_FUSED) ? 1 : 0;
+  const dim3 grid(p.nsl, p.ngroups);
+  const dim3 block(p.waves * 64);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (m) {
+    case 1: hipLaunchKernelGGL(gemv_lut_m1_kernel, grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL(gemv_dot2_kernel<2>, grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL(gemv_dot2_kernel<3>, grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL(gemv_dot2_kernel<4>, grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL(gemv_dot2_kernel<5>, grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL(gemv_dot2_kernel<6>, grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL(gemv_dot2_kernel<7>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(gemv_dot2_kernel<8>, grid, block, 0, s, a); break;
+  }
+  TQ_LAUNCH_CHECK();
+  if (mode == kPartial) {
+    hipLaunchKernelGGL(reduce_kernel, dim3((w->n + 255) / 256, m), dim3(256), 0, s, a.partial, y, m, w->n, p.npad,
+                       p.nsl);
+    TQ_LAUNCH_CHECK();
+  }
+  return TQ_OK;
+}

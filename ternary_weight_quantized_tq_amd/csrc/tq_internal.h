@@ -1,0 +1,159 @@
+// Internal helpers shared by the HIP kernels and the C-ABI host layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+#include "tq_decode.h"
+
+namespace tq {
+
+constexpr uint32_t kZeroWord = 1743392200u;  // every digit 1: twenty zero trits
+constexpr int kWave = 64;
+constexpr float kInvSqrt128 = 0.08838834764831845f;
+
+// ---------------------------------------------------------------- sizes ---
+// A slice is 640 trits = 32 words = 8 quads of 4 words = 5 scale groups;
+// 640 = lcm(20, 128), so slices start on word and group boundaries.
+constexpr int kSliceTrits = 640;
+constexpr int kSliceWords = 32;
+constexpr int kSliceQuads = 8;
+constexpr int kSliceGroups = 5;
+
+__host__ __device__ inline int words_per_row(int k) { return (k + TQ_TRITS_PER_WORD - 1) / TQ_TRITS_PER_WORD; }
+__host__ __device__ inline int quads_per_row(int k) { return (words_per_row(k) + 3) / 4; }
+__host__ __device__ inline int row_blocks(int n) { return (n + 63) / 64; }
+__host__ __device__ inline int slices_per_row(int k) { return (words_per_row(k) + kSliceWords - 1) / kSliceWords; }
+
+// TQ_LAYOUT_ROW64 addressing: slice s, row block b (64 rows), quad qi of
+// the slice, row r of the block, word j of the quad:
+//   word index  = (((s*nb + b)*8 + qi)*64 + r)*4 + j
+//   scale index = ((s*nb + b)*5 + gi)*64 + r        (group g = 5s + gi)
+// so the words of one slice of one row block are 8 KiB contiguous and a
+// wavefront reading quad qi of its 64 rows reads 1 KiB contiguously.
+__host__ __device__ inline size_t row64_word_index(int row, int w, int nb) {
+  const int s = w / kSliceWords, qi = (w % kSliceWords) >> 2, j = w & 3, b = row >> 6, r = row & 63;
+  return ((((static_cast<size_t>(s) * nb + b) * kSliceQuads + qi) * 64 + r) << 2) + j;
+}
+__host__ __device__ inline size_t row64_scale_index(int row, int g, int nb) {
+  const int s = g / kSliceGroups, gi = g % kSliceGroups, b = row >> 6, r = row & 63;
+  return ((static_cast<size_t>(s) * nb + b) * kSliceGroups + gi) * 64 + r;
+}
+// Quad / scale base of (slice, row block) in units of uint4 / uint16.
+__host__ __device__ inline size_t row64_quad_base(int s, int b, int nb) {
+  return (static_cast<size_t>(s) * nb + b) * kSliceQuads * 64;
+}
+__host__ __device__ inline size_t row64_scale_base(int s, int b, int nb) {
+  return (static_cast<size_t>(s) * nb + b) * kSliceGroups * 64;
+}
+
+// ------------------------------------------------------ element loads ---
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+__device__ __forceinline__ float load_act(const void* x, int dtype, size_t i) {
+  if (dtype == TQ_F32) return static_cast<const float*>(x)[i];
+  if (dtype == TQ_BF16) return bf16_to_f32(static_cast<const uint16_t*>(x)[i]);
+  return f16_to_f32(static_cast<const uint16_t*>(x)[i]);
+}
+// Two consecutive activations (i even).
+__device__ __forceinline__ void load_act2(const void* x, int dtype, size_t i, float& a, float& b) {
+  if (dtype == TQ_F32) {
+    const float2 v = *reinterpret_cast<const float2*>(static_cast<const float*>(x) + i);
+    a = v.x;
+    b = v.y;
+  } else {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(x) + i);
+    if (dtype == TQ_BF16) {
+      a = __uint_as_float(v << 16);
+      b = __uint_as_float(v & 0xffff0000u);
+    } else {
+      a = f16_to_f32(static_cast<uint16_t>(v & 0xffffu));
+      b = f16_to_f32(static_cast<uint16_t>(v >> 16));
+    }
+  }
+}
+
+// ----------------------------------------------- block-128 transform ---
+// Walsh-Hadamard transform of one block of 128 held by a wavefront, lane l
+// owning elements 2l and 2l+1.  Stage stride 1 is inside the lane; strides
+// 2..64 pair lane l with lane l ^ (stride/2).  Scaled by 1/sqrt(128).
+template <typename T>
+__device__ __forceinline__ void wave_fwht128(T& v0, T& v1, int lane, T scale) {
+  T a = v0 + v1, b = v0 - v1;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const T pa = __shfl_xor(a, s);
+    const T pb = __shfl_xor(b, s);
+    const bool upper = (lane & s) != 0;
+    a = upper ? (pa - a) : (a + pa);
+    b = upper ? (pb - b) : (b + pb);
+  }
+  v0 = a * scale;
+  v1 = b * scale;
+}
+
+// ------------------------------------------------- fp16 bit patterns ---
+// Round a double to the nearest fp16 (ties to even) in a single rounding.
+__host__ __device__ inline uint16_t f64_to_f16_rne(double d) {
+  uint64_t b;
+  __builtin_memcpy(&b, &d, 8);
+  const uint16_t sign = static_cast<uint16_t>((b >> 48) & 0x8000u);
+  const int exp = static_cast<int>((b >> 52) & 0x7ff);
+  const uint64_t mant = b & ((1ull << 52) - 1);
+  if (exp == 0x7ff) return sign | 0x7c00u | (mant ? 0x200u : 0u);
+  if (exp == 0) return sign;  // fp64 subnormals are far below fp16's range
+  const int e = exp - 1023;
+  const uint64_t m = mant | (1ull << 52);  // 53-bit significand, value m * 2^(e-52)
+  int shift;
+  int he;
+  if (e >= -14) {  // normal fp16 candidate: 11-bit significand
+    shift = 42;
+    he = e + 15;
+  } else {  // subnormal: units of 2^-24
+    shift = 42 + (-14 - e);
+    he = 0;
+    if (shift > 63) return sign;
+  }
+  uint64_t q = m >> shift;
+  const uint64_t r = m & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (r > half || (r == half && (q & 1))) ++q;
+  if (he == 0) {
+    // q <= 1024; q == 1024 is the smallest normal, which the encoding below
+    // produces naturally (exponent field 1, mantissa 0).
+    return sign | static_cast<uint16_t>(q);
+  }
+  if (q == (1ull << 11)) {  // significand overflow
+    q >>= 1;
+    ++he;
+  }
+  if (he >= 31) return sign | 0x7c00u;
+  return sign | static_cast<uint16_t>(he << 10) | static_cast<uint16_t>(q & 0x3ffu);
+}
+
+}  // namespace tq
+
+// Records a HIP failure for tq_last_error() (per host thread).
+void tq_set_hip_error(hipError_t e, const char* where);
+
+// Host-side launch check shared by all entry points.
+#define TQ_LAUNCH_CHECK()                      \
+  do {                                         \
+    const hipError_t tq_e_ = hipGetLastError(); \
+    if (tq_e_ != hipSuccess) {                 \
+      tq_set_hip_error(tq_e_, __func__);       \
+      return TQ_EHIP;                          \
+    }                                          \
+  } while (0)
+
+// Host-side helpers defined in the kernel sources.
+int tq_check_weights(const tq_weights* w, int experts_expected);
+int tq_device_cus();
+size_t tq_gemv_workspace(int n, int k, int m);
+size_t tq_moe_workspace(const tq_weights* gu, int t, int topk);
+size_t tq_gemm_workspace(int n, int k, int m);

@@ -1,0 +1,60 @@
+"""Host build of the kernels' word decoder (the same header, with each GPU
+instruction emulated bit-exactly) checked against plain division: every
+step over its full input range, the word boundaries of both FP64 divisions,
+and a large random sample of words."""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "ternary_weight_quantized_tq_amd", "csrc")
+
+PROG = r'''
+#include <stdio.h>
+#include <stdint.h>
+#include "tq_decode.h"
+using namespace tq;
+static int check(uint32_t w) {
+  uint32_t o[5];
+  word_offsets(w, o);
+  uint32_t v = w;
+  for (int j = 0; j < 5; ++j) {
+    if (o[j] != 4u * (v % 81u)) return 1;
+    v /= 81u;
+  }
+  return 0;
+}
+int main() {
+  const uint32_t N = 3486784401u;  /* 3^20 */
+  long bad = 0;
+  /* 24-bit steps over their whole ranges */
+  for (uint32_t a = 0; a < 531441u; ++a) bad += mulhi_u24(a, 654622u) != a / 6561u;
+  for (uint32_t b = 0; b < 6561u; ++b) bad += mulhi_u24(4u * b, 13256072u) != b / 81u;
+  /* both FP64 divisions at every multiple boundary */
+  for (uint32_t q = 0; q < 531441u; ++q) {
+    uint32_t lo = q * 6561u;
+    bad += check(lo) + check(lo + 6560u);
+    if (q) bad += check(lo - 1u);
+  }
+  for (uint32_t q = 0; q < 81u; ++q) bad += check(q * 43046721u) + check(q * 43046721u + 43046720u);
+  bad += check(0) + check(N - 1u) + check(1743392200u);
+  /* a dense sweep of words */
+  for (uint64_t w = 0; w < N; w += 1009u) bad += check((uint32_t)w);
+  printf("%ld\n", bad);
+  return bad != 0;
+}
+'''
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_word_decoder_exhaustive():
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.cpp")
+        exe = os.path.join(d, "t")
+        open(src, "w").write(PROG)
+        subprocess.run(["g++", "-O2", "-std=c++17", f"-I{CSRC}", src, "-o", exe], check=True)
+        p = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+        assert p.returncode == 0 and p.stdout.strip() == "0", p.stdout + p.stderr

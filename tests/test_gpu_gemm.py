@@ -1,0 +1,65 @@
+"""GPU parity of the prefill GEMM (matrix cores) against the oracle."""
+import numpy as np
+import pytest
+
+import synth
+import ternary_weight_quantized_tq_amd as tq
+from oracle import tq_oracle as O
+
+from tqgpu import act_tensor, dev, gpu_pack, gpu_quantize_pack, run_gemm, run_gemv
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand(seed, n, k):
+    t = synth.trits(seed, n, k)
+    s = synth.scales(seed + 1, n, k // 128)
+    return t, s, gpu_pack(t, s)
+
+
+@pytest.mark.parametrize("m,n,k", [(70, 256, 384), (64, 300, 1280), (3, 257, 640)])
+def test_gemm_one_hot_exact(m, n, k):
+    t, s, w = _rand(40 + n, n, k)
+    rng = np.random.default_rng(41)
+    cols = rng.integers(0, k, m)
+    x = np.zeros((m, k), np.float32)
+    x[np.arange(m), cols] = 1.0
+    y = run_gemm(w, dev(x), m, fused=False)
+    want = (s[:, cols // 128].astype(np.float64) * t[:, cols]).T
+    assert np.array_equal(y, want)
+
+
+@pytest.mark.parametrize("m,n,k,dtype", [(130, 300, 1280, "bf16"), (64, 512, 2048, "f32"), (1, 256, 640, "bf16"),
+                                         (200, 1024, 5120, "bf16"), (65, 320, 17408, "f16")])
+def test_gemm_random_vs_oracle(m, n, k, dtype):
+    t, s, w = _rand(60 + m + n, n, k)
+    act = synth.activations(61 + m, m, k, dtype)
+    y = run_gemm(w, act_tensor(act), m)
+    y_ref = O.gemv(O.pack(t), s, k, act.values, True)
+    err = O.rel_l2(y, y_ref)
+    assert err < 1e-5, err
+
+
+def test_gemm_row_equals_gemv():
+    t, s, w = _rand(80, 512, 1280)
+    act = synth.activations(81, 4, 1280, "bf16")
+    yg = run_gemm(w, act_tensor(act), 4)
+    yv = run_gemv(w, act_tensor(synth.Activations(act.values[:1], act.raw[:1], "bf16")), 1)
+    assert np.abs(yg[0] - yv[0]).max() <= 1e-5 * np.abs(yv[0]).max()
+
+
+def test_gemm_prefill_full_size_sampled():
+    """2048 x 5120 x 17408, weights quantised on the GPU; the oracle checks
+    8 rows x 192 columns."""
+    wl = synth.PREFILL_GEMM.linears[0]
+    w64 = synth.weights(wl.w_seed, wl.n, wl.k)
+    act = synth.activations(wl.x_seed, 2048, wl.k, "bf16")
+    w = gpu_quantize_pack(w64)
+    y = run_gemm(w, act_tensor(act), 2048)
+    rng = np.random.default_rng(5)
+    rows = np.concatenate([rng.choice(2048, 6, replace=False), [0, 2047]])
+    cols = np.concatenate([rng.choice(wl.n, 190, replace=False), [0, wl.n - 1]])
+    t, s, _ = O.quantize(w64[cols])
+    y_ref = O.gemv(O.pack(t), s, wl.k, act.values[rows], True)
+    err = O.rel_l2(y[np.ix_(rows, cols)], y_ref)
+    assert err < 1e-5, err

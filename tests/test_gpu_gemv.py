@@ -1,0 +1,122 @@
+"""GPU parity of tq_gemv against the FP64 oracle.
+
+Exact cases (transform off): x = e_k gives y = s[n][k/128] t[n][k], and a
+group of ones gives s times an integer; both are exact in FP32.  Otherwise
+relative L2 <= 1e-3 (the gate), on small shapes spanning several tiles with
+ragged tails, and on the full 27B decode shapes on sampled rows."""
+import numpy as np
+import pytest
+
+import synth
+import ternary_weight_quantized_tq_amd as tq
+from oracle import tq_oracle as O
+
+from tqgpu import act_tensor, dev, gpu_pack, gpu_quantize_pack, run_gemv, torch
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+
+
+def _rand_packed(seed, n, k):
+    t = synth.trits(seed, n, k)
+    s = synth.scales(seed + 1, n, k // 128)
+    return t, s, gpu_pack(t, s)
+
+
+@pytest.mark.parametrize("m", [1, 3, 8])
+@pytest.mark.parametrize("n,k", [(300, 1280), (65, 768), (64, 128), (130, 2048)])
+def test_gemv_one_hot_exact(m, n, k):
+    t, s, w = _rand_packed(100 + n, n, k)
+    cols = [c % k for c in (0, 19, 20, 127, 128, k - 1, k // 2 + 7, 639)][:m]
+    x = np.zeros((m, k), np.float32)
+    for r, c in enumerate(cols):
+        x[r, c] = 1.0
+    y = run_gemv(w, dev(x), m, fused=False)
+    for r, c in enumerate(cols):
+        want = s[:, c // 128].astype(np.float64) * t[:, c]
+        assert np.array_equal(y[r], want), f"row {r} col {c}"
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_gemv_group_ones_exact(m):
+    n, k = 200, 1280
+    t, s, w = _rand_packed(7, n, k)
+    x = np.zeros((m, k), np.float32)
+    groups = [0, 5, 9, 3][:m]
+    for r, g in enumerate(groups):
+        x[r, g * 128:(g + 1) * 128] = 1.0
+    y = run_gemv(w, dev(x), m, fused=False)
+    for r, g in enumerate(groups):
+        want = s[:, g].astype(np.float64) * t[:, g * 128:(g + 1) * 128].sum(axis=1)
+        assert np.array_equal(y[r], want)
+
+
+def test_gemv_single_linear_workload():
+    """512 x 1024, fp32 x, weights N(0, 0.02) with x20 outliers; quantised and
+    packed on the GPU, compared with the oracle's own quantisation."""
+    wl = synth.SINGLE_LINEAR.linears[0]
+    w64 = synth.weights(wl.w_seed, wl.n, wl.k)
+    act = synth.activations(wl.x_seed, 1, wl.k, "f32")
+    w = gpu_quantize_pack(w64)
+    y = run_gemv(w, act_tensor(act), 1)
+    t, s, _ = O.quantize(w64)
+    y_ref = O.gemv(O.pack(t), s, wl.k, act.values, True)
+    err = O.rel_l2(y, y_ref)
+    assert err < 1e-5, err
+    # context: distance to the unquantised product (not a parity gate)
+    assert O.rel_l2(y, O.unquantized(w64, act.values)) < 0.6
+
+
+@pytest.mark.parametrize("m", [1, 2, 5, 8])
+@pytest.mark.parametrize("n,k", [(1, 128), (63, 640), (65, 768), (300, 1920), (257, 2048)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gemv_random_shapes(m, n, k, dtype):
+    t, s, w = _rand_packed(1000 + 7 * n + k, n, k)
+    act = synth.activations(3000 + m, m, k, dtype)
+    y = run_gemv(w, act_tensor(act), m)
+    y_ref = O.gemv(O.pack(t), s, k, act.values, True)
+    err = O.rel_l2(y, y_ref)
+    assert err < TOL, err
+    if m == 1:
+        assert err < 1e-5, err     # FP32 table path
+
+
+def test_gemv_deterministic():
+    t, s, w = _rand_packed(5, 1000, 5120)
+    act = synth.activations(6, 1, 5120, "bf16")
+    x = act_tensor(act)
+    y1 = run_gemv(w, x, 1)
+    y2 = run_gemv(w, x, 1)
+    assert np.array_equal(y1, y2)
+
+
+@pytest.mark.parametrize("which", ["up", "down"])
+def test_gemv_27b_decode_full_size_sampled(which):
+    """Full 27B decode shapes, quantised and packed on the GPU; the oracle
+    recomputes 192 sampled rows from the same seeded weights."""
+    wl = {l.name: l for l in synth.DENSE_DECODE_27B.linears}[which]
+    w64 = synth.weights(wl.w_seed, wl.n, wl.k)
+    act = synth.activations(wl.x_seed, 1, wl.k, "bf16")
+    w = gpu_quantize_pack(w64)
+    y = run_gemv(w, act_tensor(act), 1)[0]
+    rows = np.random.default_rng(9).choice(wl.n, 192, replace=False)
+    rows = np.concatenate([rows, [0, wl.n - 1]])
+    t, s, _ = O.quantize(w64[rows])
+    y_ref = O.gemv(O.pack(t), s, wl.k, act.values, True)[0]
+    err = O.rel_l2(y[rows], y_ref)
+    assert err < 1e-5, err
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 300, 1920), (1, 5120, 17408), (4, 257, 2048)])
+def test_gemv_accumulate(m, n, k):
+    """TQ_ACCUMULATE adds W x' into y (single launch, atomics)."""
+    th = torch()
+    t, s, w = _rand_packed(70 + n, n, k)
+    act = synth.activations(71, m, k, "bf16")
+    base = np.random.default_rng(72).normal(size=(m, n)).astype(np.float32)
+    y = dev(base.copy())
+    tq.tq_gemv(w, act_tensor(act), m, y, tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE)
+    th.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64) - base
+    y_ref = O.gemv(O.pack(t), s, k, act.values, True)
+    assert O.rel_l2(got, y_ref) < (1e-5 if m == 1 else 1e-3)

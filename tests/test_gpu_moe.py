@@ -1,0 +1,107 @@
+"""GPU parity of the MoE path (router, grouped expert MLP) against the oracle."""
+import numpy as np
+import pytest
+
+import synth
+import ternary_weight_quantized_tq_amd as tq
+from oracle import tq_oracle as O
+
+from tqgpu import act_tensor, dev, gpu_pack_expert, run_moe, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("t,e,topk,seed", [(64, 256, 8, 4903), (1, 256, 8, 4901), (5, 40, 3, 7), (3, 1000, 32, 9)])
+def test_router_matches_oracle(t, e, topk, seed):
+    lg = synth.logits(seed, t, e)
+    ids_ref, w_ref = O.route(lg, topk)
+    th = torch()
+    ids = th.empty((t, topk), dtype=th.int32, device="cuda")
+    w = th.empty((t, topk), dtype=th.float32, device="cuda")
+    tq.tq_moe_route(dev(lg), t, e, topk, ids, w)
+    th.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.abs(w.cpu().numpy() - w_ref).max() < 1e-5
+
+
+def _random_experts(seed, E, hidden, inter):
+    w_gu = tq.empty_weights(2 * inter, hidden, num_experts=E)
+    w_dn = tq.empty_weights(hidden, inter, num_experts=E)
+    host = {"gu_w": [], "gu_s": [], "dn_w": [], "dn_s": []}
+    for e in range(E):
+        t = synth.trits(seed + 10 * e, 2 * inter, hidden)
+        s = synth.scales(seed + 10 * e + 1, 2 * inter, hidden // 128)
+        gpu_pack_expert(w_gu, e, trits=t, scales=s)
+        host["gu_w"].append(O.pack(t)), host["gu_s"].append(s)
+        t = synth.trits(seed + 10 * e + 2, hidden, inter)
+        s = synth.scales(seed + 10 * e + 3, hidden, inter // 128)
+        gpu_pack_expert(w_dn, e, trits=t, scales=s)
+        host["dn_w"].append(O.pack(t)), host["dn_s"].append(s)
+    return w_gu, w_dn, host
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_moe_small_random(dtype):
+    E, hidden, inter, T, topk = 6, 256, 128, 5, 2
+    w_gu, w_dn, h = _random_experts(300, E, hidden, inter)
+    act = synth.activations(31, T, hidden, dtype)
+    rng = np.random.default_rng(32)
+    ids = np.stack([rng.choice(E, topk, replace=False) for _ in range(T)]).astype(np.int32)
+    rw = rng.random((T, topk))
+    rw /= rw.sum(axis=1, keepdims=True)
+    y = run_moe(w_gu, w_dn, act_tensor(act), T, topk, ids, rw)
+    y_ref = O.moe(act.values, ids, rw, h["gu_w"], h["gu_s"], h["dn_w"], h["dn_s"], hidden, inter)
+    assert O.rel_l2(y, y_ref) < 1e-3
+
+
+def test_moe_many_tokens_per_expert_and_bad_ids():
+    """More than 8 tokens on one expert (several tiles), and ids outside
+    [0, E) that must contribute nothing."""
+    E, hidden, inter, T, topk = 3, 384, 192, 21, 2
+    w_gu, w_dn, h = _random_experts(500, E, hidden, inter)
+    act = synth.activations(51, T, hidden, "bf16")
+    ids = np.zeros((T, topk), np.int32)
+    ids[:, 1] = np.arange(T) % E
+    ids[3, 1] = -1
+    ids[7, 0] = E + 4
+    rw = np.full((T, topk), 0.5)
+    y = run_moe(w_gu, w_dn, act_tensor(act), T, topk, ids, rw)
+    ok = (ids >= 0) & (ids < E)
+    y_ref = np.zeros_like(y)
+    for t in range(T):
+        for j in range(topk):
+            if ok[t, j]:
+                y_ref[t] += O.moe(act.values[t:t + 1], ids[t:t + 1, j:j + 1], rw[t:t + 1, j:j + 1], h["gu_w"],
+                                  h["gu_s"], h["dn_w"], h["dn_s"], hidden, inter)[0]
+    assert O.rel_l2(y, y_ref) < 1e-3
+
+
+@pytest.mark.parametrize("wl", [synth.MOE_T1, synth.MOE_T64], ids=["t1", "t64"])
+def test_moe_expert_layer_workload(wl):
+    """256 experts (hidden 2048, intermediate 512), top-8 from seeded logits,
+    experts quantised on the GPU; the oracle recomputes sampled tokens."""
+    lg = synth.logits(wl.logit_seed, wl.tokens, wl.experts)
+    ids, rw = O.route(lg, wl.topk)
+    act = synth.activations(wl.x_seed, wl.tokens, wl.hidden, "bf16")
+    w_gu = tq.empty_weights(2 * wl.inter, wl.hidden, num_experts=wl.experts)
+    w_dn = tq.empty_weights(wl.hidden, wl.inter, num_experts=wl.experts)
+    tokens = list(range(wl.tokens)) if wl.tokens <= 4 else [0, 17, 42, wl.tokens - 1]
+    need = sorted(set(ids.ravel().tolist()))
+    check = sorted(set(ids[tokens].ravel().tolist()))
+    host = {}
+    for e in need:
+        gu64, dn64 = synth.expert_weights(e, wl.hidden, wl.inter)
+        gpu_pack_expert(w_gu, e, weights64=gu64)
+        gpu_pack_expert(w_dn, e, weights64=dn64)
+        if e in check:
+            t, s, _ = O.quantize(gu64)
+            t2, s2, _ = O.quantize(dn64)
+            host[e] = (O.pack(t), s, O.pack(t2), s2)
+    y = run_moe(w_gu, w_dn, act_tensor(act), wl.tokens, wl.topk, ids, rw)
+    gu_w = {e: v[0] for e, v in host.items()}
+    gu_s = {e: v[1] for e, v in host.items()}
+    dn_w = {e: v[2] for e, v in host.items()}
+    dn_s = {e: v[3] for e, v in host.items()}
+    y_ref = O.moe(act.values, ids, rw, gu_w, gu_s, dn_w, dn_s, wl.hidden, wl.inter, tokens=tokens)
+    err = O.rel_l2(y[tokens], y_ref[tokens])
+    assert err < 1e-3, err
