@@ -9,24 +9,27 @@
 // lookup tables are wavefront-uniform and scale-group boundaries fall at
 // compile-time chunk positions.
 //
-// Order of work inside a workgroup, chosen so that nothing waits on the
-// weight stream before it has to:
-//   1. load the scales and this wavefront's block of activations, then only
-//      kLookahead quads of weights (non-temporal: streamed once);
-//   2. block-128 transform of the activations in registers (wavefront
-//      shuffles), staged in LDS;
-//   3. table build (M == 1) or code table + fp16 activations (M >= 2);
-//   4. decode quad i while quad i + kLookahead is in flight.
-// The barriers in 2-3 wait for LDS only (a plain __syncthreads() would also
-// wait for every outstanding weight load).
-//
 // M == 1 (single-stream decode) uses a partial-sum table in LDS: for every
 // 4-trit position p of the slice and every chunk value c in [0, 81),
 // T[p][c] = sum_{i<4} (d_i(c) - 1) x'[4p + i] in FP32.  Each 4 trits then
 // cost one LDS read and one add: with weights in {-1, 0, 1} the product
 // reduces to sign tests and additions/subtractions ("Ternary-Bonsai2-27B vs
-// Qwen3.8-27B-GSQ-RCO" page, §1.1).  M >= 2 reads fp16 trit codes per chunk
-// and accumulates with v_dot2_f32_f16 against the fp16-rounded x'.
+// Qwen3.8-27B-GSQ-RCO" page, section 1.1).  Order of work, chosen so that
+// nothing waits on the weight stream before it has to:
+//   1. load this wavefront's block of activations (the dtype is a template
+//      parameter, so the load is branch-free and the transform waits for it
+//      alone), then kLookahead quads of weights (non-temporal: streamed
+//      once), then the scales (needed last; loads complete in order);
+//   2. block-128 transform in registers (wavefront shuffles), and the table
+//      rows of the block built straight from those registers;
+//   3. decode, software-pipelined: the table reads of word w + 2 are in
+//      flight while the sums of word w are formed, and quad i + kLookahead
+//      is loaded while quad i is decoded.
+// The one barrier waits for LDS only (a plain __syncthreads() would also
+// wait for every outstanding weight load).
+//
+// M >= 2 reads fp16 trit codes per chunk and accumulates with
+// v_dot2_f32_f16 against the fp16-rounded x' staged in LDS.
 #include "tq_internal.h"
 
 using namespace tq;
@@ -102,6 +105,16 @@ __device__ __forceinline__ void load_block(const GemvArgs& a, const Tile& t, int
   load_act2(a.x, a.x_dtype, static_cast<size_t>(m) * a.k + (valid ? kb : 0) + 2 * t.lane, v0, v1);
 }
 
+// Same with the activation dtype fixed at compile time (no branch around
+// the load, so later loads need not wait for it).
+template <int XT>
+__device__ __forceinline__ void load_block_t(const GemvArgs& a, const Tile& t, int m, int blk, float& v0, float& v1,
+                                             bool& valid) {
+  const int kb = t.k0 + blk * 128;
+  valid = kb < a.k;
+  load_act2(a.x, XT, static_cast<size_t>(m) * a.k + (valid ? kb : 0) + 2 * t.lane, v0, v1);
+}
+
 __device__ __forceinline__ void transform(const GemvArgs& a, float& v0, float& v1, bool valid, int lane) {
   if (a.fused) wave_fwht128<float>(v0, v1, lane, kInvSqrt128);
   if (!valid) {
@@ -155,70 +168,116 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
 }
 
 // ------------------------------------------------------------ M == 1 ---
+// Table values of the five chunks of word w (0..31) of the slice.
+__device__ __forceinline__ void word_lookups(const float* lut, uint32_t word, int w, float (&v)[5]) {
+  uint32_t o[5];
+  word_offsets(word, o);
+#pragma unroll
+  for (int h = 0; h < 5; ++h) {
+    const int p = w * 5 + h;  // chunk position in the slice, compile-time after unrolling
+    v[h] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + p * kLutEntries * 4 + o[h]);
+  }
+}
+
+// Value of the neighbouring lane (lane ^ 1), through DPP.
+__device__ __forceinline__ float lane_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+
+// Table rows of the 32 chunk positions of transform block `blk`, built from
+// the registers of the wavefront that transformed it: lane 2j holds x'[4j],
+// x'[4j+1] and lane 2j+1 holds x'[4j+2], x'[4j+3] of position p = 32 blk + j.
+// With A[d0 + 3 d1] = (d0-1) x0 + (d1-1) x1 and B[d2 + 3 d3] likewise for
+// x2, x3, entry c = A[c % 9] + B[c / 9]; the even lane writes c / 9 in
+// 0..4, the odd lane 5..8.
+__device__ __forceinline__ void build_rows(float* lut, int blk, int lane, float v0, float v1) {
+  const float p0 = lane_xor1(v0), p1 = lane_xor1(v1);
+  const bool odd = (lane & 1) != 0;
+  const float x0 = odd ? p0 : v0, x1 = odd ? p1 : v1;
+  const float x2 = odd ? v0 : p0, x3 = odd ? v1 : p1;
+  const float A[9] = {-x0 - x1, -x1, x0 - x1, -x0, 0.0f, x0, x1 - x0, x1, x0 + x1};
+  const float B[9] = {-x2 - x3, -x3, x2 - x3, -x2, 0.0f, x2, x3 - x2, x3, x2 + x3};
+  float* row = lut + (blk * 32 + (lane >> 1)) * kLutEntries + (odd ? 45 : 0);
+#pragma unroll
+  for (int r = 0; r < 5; ++r) {
+    if (r < 4 || !odd) {
+      const float h = odd ? B[r < 4 ? r + 5 : 8] : B[r];
+#pragma unroll
+      for (int s = 0; s < 9; ++s) row[9 * r + s] = A[s] + h;
+    }
+  }
+}
+
+template <int XT>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a) {
   __shared__ float lut[kSliceChunks * kLutEntries];                   // 51840 B
-  __shared__ __attribute__((aligned(16))) float xs[kSliceTrits];      // 2560 B
   const Tile t = make_tile(a);
 
-  float sc[kSliceGroups];
-  load_scales(a, t, sc);
+  // Activations first (every wavefront loads a block, branch-free, so that
+  // the transform below waits for this load only), then the first weights,
+  // then the scales, which are needed last.
   float v0 = 0.0f, v1 = 0.0f;
   bool valid = false;
-  if (t.wave < kSliceGroups) load_block(a, t, 0, t.wave, v0, v1, valid);
+  load_block_t<XT>(a, t, 0, min(t.wave, kSliceGroups - 1), v0, v1, valid);
   TQ_ORDER();
   const uint4* wp = a.words + row64_quad_base(t.slice, t.rbc, a.nb) + t.lane;
   uint4 wq[kSliceQuads];
 #pragma unroll
   for (int i = 0; i < kLookahead; ++i) wq[i] = load_quad(wp + min(i, t.nq_here - 1) * 64);
+  TQ_ORDER();
+  float sc[kSliceGroups];
+  load_scales(a, t, sc);
+  TQ_ORDER();
 
-  for (int blk = t.wave; blk < kSliceGroups; blk += t.waves) {
-    if (blk != t.wave) load_block(a, t, 0, blk, v0, v1, valid);  // only when fewer than 5 wavefronts
-    transform(a, v0, v1, valid, t.lane);
-    xs[blk * 128 + 2 * t.lane] = v0;
-    xs[blk * 128 + 2 * t.lane + 1] = v1;
-  }
-  TQ_LDS_BARRIER();
-
-  // T[p][b + 27 d3] = t0 x0 + t1 x1 + t2 x2 + (d3 - 1) x3, b = d0 + 3 d1 + 9 d2.
-  const int stride = blockDim.x / 27;
-  if (t.tid < 27 * stride) {
-    const int b = t.tid % 27;
-    const float t0 = static_cast<float>(b % 3) - 1.0f;
-    const float t1 = static_cast<float>((b / 3) % 3) - 1.0f;
-    const float t2 = static_cast<float>(b / 9) - 1.0f;
-    for (int p = t.tid / 27; p < kSliceChunks; p += stride) {
-      const float4 x4 = *reinterpret_cast<const float4*>(&xs[4 * p]);
-      const float base = fmaf(t2, x4.z, fmaf(t1, x4.y, t0 * x4.x));
-      float* e = &lut[p * kLutEntries + b];
-      e[0] = base - x4.w;
-      e[27] = base;
-      e[54] = base + x4.w;
+  if (t.waves >= kSliceGroups) {
+    if (t.wave < kSliceGroups) {
+      transform(a, v0, v1, valid, t.lane);
+      build_rows(lut, t.wave, t.lane, v0, v1);
+    }
+  } else {  // fewer than 5 wavefronts: some transform several blocks
+    for (int blk = t.wave; blk < kSliceGroups; blk += t.waves) {
+      if (blk != t.wave) load_block_t<XT>(a, t, 0, blk, v0, v1, valid);
+      transform(a, v0, v1, valid, t.lane);
+      build_rows(lut, blk, t.lane, v0, v1);
     }
   }
   TQ_LDS_BARRIER();
 
   float acc[kSliceGroups] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  if (t.nq_here == kSliceQuads) {
+    // Software-pipelined: the table reads of word w + 2 are in flight while
+    // the sums of word w are formed, so the LDS and VALU pipes overlap
+    // within the wavefront.
+    float v[3][5];
+    word_lookups(lut, wq[0].x, 0, v[0]);
+    word_lookups(lut, wq[0].y, 1, v[1]);
 #pragma unroll
-  for (int i = 0; i < kSliceQuads; ++i) {
-    if (i + kLookahead < kSliceQuads) wq[i + kLookahead] = load_quad(wp + min(i + kLookahead, t.nq_here - 1) * 64);
-    if (i < t.nq_here) {
-      const uint32_t wv[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
-      float v[20];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t o[5];
-        word_offsets(wv[j], o);
-#pragma unroll
-        for (int h = 0; h < 5; ++h) {
-          const int p = i * 20 + j * 5 + h;  // chunk position in the slice, compile-time
-          v[j * 5 + h] =
-              *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + p * kLutEntries * 4 + o[h]);
-        }
+    for (int w = 0; w < kSliceWords; ++w) {
+      const int i = w >> 2;
+      if ((w & 3) == 0 && i + kLookahead < kSliceQuads) wq[i + kLookahead] = load_quad(wp + (i + kLookahead) * 64);
+      if (w + 2 < kSliceWords) {
+        const uint4 q = wq[(w + 2) >> 2];
+        const uint32_t wn = ((w + 2) & 3) == 0 ? q.x : ((w + 2) & 3) == 1 ? q.y : ((w + 2) & 3) == 2 ? q.z : q.w;
+        word_lookups(lut, wn, w + 2, v[(w + 2) % 3]);
       }
 #pragma unroll
-      for (int c = 0; c < 20; ++c) acc[(i * 20 + c) / 32] += v[c];
+      for (int h = 0; h < 5; ++h) acc[(w * 5 + h) / 32] += v[w % 3][h];
+      if ((w & 3) == 3) TQ_ORDER();
     }
-    TQ_ORDER();
+  } else {
+#pragma unroll
+    for (int i = 0; i < kSliceQuads; ++i) {
+      if (i + kLookahead < kSliceQuads) wq[i + kLookahead] = load_quad(wp + min(i + kLookahead, t.nq_here - 1) * 64);
+      if (i < t.nq_here) {
+        const uint32_t wv[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
+        float v[20];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) word_lookups(lut, wv[j], i * 4 + j, *reinterpret_cast<float(*)[5]>(&v[j * 5]));
+#pragma unroll
+        for (int c = 0; c < 20; ++c) acc[(i * 20 + c) / 32] += v[c];
+      }
+      TQ_ORDER();
+    }
   }
   float part[1] = {0.0f};
 #pragma unroll
@@ -409,7 +468,11 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
   const dim3 block(p.waves * 64);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (m) {
-    case 1: hipLaunchKernelGGL(gemv_lut_m1_kernel, grid, block, 0, s, a); break;
+    case 1:
+      if (x_dtype == TQ_F32) hipLaunchKernelGGL(gemv_lut_m1_kernel<TQ_F32>, grid, block, 0, s, a);
+      else if (x_dtype == TQ_BF16) hipLaunchKernelGGL(gemv_lut_m1_kernel<TQ_BF16>, grid, block, 0, s, a);
+      else hipLaunchKernelGGL(gemv_lut_m1_kernel<TQ_F16>, grid, block, 0, s, a);
+      break;
     case 2: hipLaunchKernelGGL(gemv_dot2_kernel<2>, grid, block, 0, s, a); break;
     case 3: hipLaunchKernelGGL(gemv_dot2_kernel<3>, grid, block, 0, s, a); break;
     case 4: hipLaunchKernelGGL(gemv_dot2_kernel<4>, grid, block, 0, s, a); break;

@@ -57,7 +57,7 @@ def test_moe_small_random(dtype):
 def test_moe_many_tokens_per_expert_and_bad_ids():
     """More than 8 tokens on one expert (several tiles), and ids outside
     [0, E) that must contribute nothing."""
-    E, hidden, inter, T, topk = 3, 384, 192, 21, 2
+    E, hidden, inter, T, topk = 3, 384, 256, 21, 2
     w_gu, w_dn, h = _random_experts(500, E, hidden, inter)
     act = synth.activations(51, T, hidden, "bf16")
     ids = np.zeros((T, topk), np.int32)
