@@ -180,10 +180,22 @@ def extra_block_m8(tq, torch, synth, np):
         for j, (lin, w) in enumerate(zip(wl.linears, sets[i % copies])):
             tq.tq_gemv(w, xs[lin.x_seed], 8, ys[j], tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE)
     ms = timed(torch, 32, 4, step)
+    per = {}
+    for j, lin in enumerate(wl.linears):
+        g = capture(torch, copies, lambda i: tq.tq_gemv(sets[i][j], xs[lin.x_seed], 8, ys[j],
+                                                         tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE))
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        per[lin.name] = round(1e3 * a.elapsed_time(b) / copies, 3)
     return {"workload": wl.name, "m": 8, "packed_bytes_per_step": nbytes, "weight_copies_rotated": copies,
             "ms_per_step": round(ms, 4), "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "layer_tok_s": round(8 / (ms * 1e-3), 1), "compute": "VALU v_dot2_f32_f16 (fp16 x', FP32 accumulate)"}
+            "layer_tok_s": round(8 / (ms * 1e-3), 1), "kernel_us": per,
+            "compute": "v_mfma_f32_16x16x32_f16 (fp16 x', fp16 trit codes, FP32 accumulate)"}
 
 
 def extra_moe(tq, torch, synth, np):

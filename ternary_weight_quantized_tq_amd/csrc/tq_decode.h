@@ -34,11 +34,21 @@
 namespace tq {
 
 // Low 32 bits of sext24(a) * sext24(b) + c  (v_mad_i32_i24).
+// kAsm: emit the instruction as inline asm (the compiler otherwise falls
+// back to quarter-rate 32-bit multiplies here).  Inline asm is hidden from
+// the compiler's hazard tracking, so kernels that issue matrix-core (MFMA)
+// instructions must use kAsm = false: an asm write can land on a register
+// an MFMA is still reading.
+template <bool kAsm = true>
 TQ_HD uint32_t mad_i24(uint32_t a, int32_t b, uint32_t c) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  uint32_t r;
-  asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(b), "v"(c));
-  return r;
+  if constexpr (kAsm) {
+    uint32_t r;
+    asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(b), "v"(c));
+    return r;
+  } else {
+    return static_cast<uint32_t>(static_cast<int32_t>(a) * b) + c;  // operands fit 24 bits at every call
+  }
 #else
   const int64_t sa = static_cast<int64_t>(static_cast<int32_t>(a << 8) >> 8);
   const int64_t sb = static_cast<int64_t>(static_cast<int32_t>(static_cast<uint32_t>(b) << 8) >> 8);
@@ -46,31 +56,39 @@ TQ_HD uint32_t mad_i24(uint32_t a, int32_t b, uint32_t c) {
 #endif
 }
 
-// Bits 32..47 of (a & 0xffffff) * (b & 0xffffff)  (v_mul_hi_u32_u24).
+// Bits 32..47 of (a & 0xffffff) * (b & 0xffffff)  (v_mul_hi_u32_u24; the
+// compiler selects it from this form).
 TQ_HD uint32_t mulhi_u24(uint32_t a, uint32_t b) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  uint32_t r;
-  asm("v_mul_hi_u32_u24 %0, %1, %2" : "=v"(r) : "s"(b), "v"(a));
-  return r;
-#else
   return static_cast<uint32_t>((static_cast<uint64_t>(a & 0xffffffu) * (b & 0xffffffu)) >> 32);
-#endif
 }
 
-// o[j] = 4 * chunk j (digits 4j..4j+3) of the word.
-TQ_HD void word_offsets(uint32_t w, uint32_t o[5]) {
+// o[j] = 2^S * chunk j (digits 4j..4j+3) of the word: the byte offset of
+// entry c_j in a table of 2^S-byte entries (S = 2: 4-byte entries, S = 3:
+// 8-byte entries).  The constants scale with 2^S: 4b = 4w - 26244 a becomes
+// 2^S b = 2^S w - 6561 * 2^S a, and floor(b / 81) = mulhi_u24(2^S b,
+// ceil(2^(32-S) / 81)), exact for b < 6561 (the multiplier exceeds
+// 2^(32-S)/81 by less than 1, so the error stays below 6561 * 2^S / 2^32).
+template <int S, bool kAsm = true>
+TQ_HD void word_offsets_s(uint32_t w, uint32_t o[5]) {
+  constexpr int32_t k6561 = -6561 * (1 << S);
+  constexpr int32_t k81 = -81 * (1 << S);
+  constexpr uint32_t kInv81 = S == 2 ? 13256072u : 6628036u;  // ceil(2^(32-S) / 81)
+  static_assert(S == 2 || S == 3, "table entries of 4 or 8 bytes");
   const double wd = static_cast<double>(w);
   const uint32_t a = static_cast<uint32_t>(__builtin_fma(wd, 1.0 / 6561.0, 0.5 / 6561.0));
   const uint32_t e = mulhi_u24(a, 654622u);
-  const uint32_t b4 = mad_i24(a, -26244, w << 2);
-  const uint32_t m4 = mad_i24(e, -26244, a << 2);
-  const uint32_t b1 = mulhi_u24(b4, 13256072u);
-  const uint32_t m1 = mulhi_u24(m4, 13256072u);
-  o[0] = mad_i24(b1, -324, b4);
-  o[1] = b1 << 2;
-  o[2] = mad_i24(m1, -324, m4);
-  o[3] = m1 << 2;
-  o[4] = e << 2;
+  const uint32_t bs = mad_i24<kAsm>(a, k6561, w << S);
+  const uint32_t ms = mad_i24<kAsm>(e, k6561, a << S);
+  const uint32_t b1 = mulhi_u24(bs, kInv81);
+  const uint32_t m1 = mulhi_u24(ms, kInv81);
+  o[0] = mad_i24<kAsm>(b1, k81, bs);
+  o[1] = b1 << S;
+  o[2] = mad_i24<kAsm>(m1, k81, ms);
+  o[3] = m1 << S;
+  o[4] = e << S;
 }
+
+// o[j] = 4 * chunk j (digits 4j..4j+3) of the word.
+TQ_HD void word_offsets(uint32_t w, uint32_t o[5]) { word_offsets_s<2>(w, o); }
 
 }  // namespace tq

@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           uint32_t o[5];
-          word_offsets(wv[j], o);
+          word_offsets_s<2, false>(wv[j], o);  // no inline asm next to MFMAs
 #pragma unroll
           for (int h = 0; h < 5; ++h) {
             const int kk = q * 80 + j * 20 + h * 4;

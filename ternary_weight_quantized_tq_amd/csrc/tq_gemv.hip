@@ -28,8 +28,9 @@
 // The one barrier waits for LDS only (a plain __syncthreads() would also
 // wait for every outstanding weight load).
 //
-// M >= 2 reads fp16 trit codes per chunk and accumulates with
-// v_dot2_f32_f16 against the fp16-rounded x' staged in LDS.
+// M >= 2 runs on the matrix cores (v_mfma_f32_16x16x32_f16): x' rounded to
+// fp16 in LDS is the A operand, fp16 trit codes read from an 81-entry LDS
+// table are the B operand (see gemv_mfma_kernel).
 #include "tq_internal.h"
 
 using namespace tq;
@@ -41,7 +42,8 @@ constexpr int kLutEntries = 81;
 constexpr int kMaxWaves = 16;
 constexpr int kLookahead = 3;
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 struct GemvArgs {
@@ -285,40 +287,110 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a)
   finish<1>(a, t, part);
 }
 
-// ------------------------------------------------------- 2 <= M <= 8 ---
-template <int M>
-__global__ __launch_bounds__(kMaxWaves * 64) void gemv_dot2_kernel(GemvArgs a) {
-  __shared__ uint32_t codes_lo[kLutEntries];  // fp16 trits 0, 1 of each chunk value
-  __shared__ uint32_t codes_hi[kLutEntries];  // fp16 trits 2, 3
-  __shared__ __attribute__((aligned(16))) _Float16 xh[M][kSliceTrits];
-  const Tile t = make_tile(a);
-  constexpr int kJobs = M * kSliceGroups;      // (row m, block) transforms per slice
+// ------------------------------------------- 2 <= M <= 8 on the matrix cores ---
+// v_mfma_f32_16x16x32_f16 with A = x' (16 rows = activation rows, M used,
+// the rest read as zero) and B = trit codes (16 columns = output rows), K
+// permuted so that every lane decodes whole words of its own row:
+//   lane l, j = l % 16, kb = l / 16 (0..3), row quarter h (0..3): output
+//   row 64 rb + 16 h + j; in unit u (0..3) = quads 2u, 2u + 1 of the slice
+//   the lane owns words 2 kb, 2 kb + 1 of the unit's eight, and step s
+//   (0..4) covers trits 160 u + 40 kb + 8 s .. + 7.
+// A word gives five 4-trit chunks; an 81-entry LDS table maps a chunk to
+// its four fp16 codes (d - 1), so B costs one 8-byte table read per chunk.
+// An MFMA sums over the four lane groups, whose trits may lie in two scale
+// groups: such steps are issued twice, each time with the activations of
+// the lanes in the other scale group read as zero.  Sums are kept per scale
+// group (two in flight) and scaled by the row's FP32 scale when complete.
+__host__ __device__ constexpr int mfma_group(int u, int s, int kb) { return (160 * u + 40 * kb + 8 * s) / 128; }
+__host__ __device__ constexpr int mfma_gmin(int u, int s) { return mfma_group(u, s, 0); }
+__host__ __device__ constexpr int mfma_gmax(int u, int s) { return mfma_group(u, s, 3); }
+// Lane groups kb whose trits of step (u, s) lie in the lower scale group.
+__host__ __device__ constexpr int mfma_lo_mask(int u, int s) {
+  return (mfma_group(u, s, 0) == mfma_gmin(u, s) ? 1 : 0) | (mfma_group(u, s, 1) == mfma_gmin(u, s) ? 2 : 0) |
+         (mfma_group(u, s, 2) == mfma_gmin(u, s) ? 4 : 0) | (mfma_group(u, s, 3) == mfma_gmin(u, s) ? 8 : 0);
+}
 
-  float sc[kSliceGroups];
-  load_scales(a, t, sc);
-  // Activations of this wavefront's first transform job, before the weights.
-  float v0 = 0.0f, v1 = 0.0f;
-  bool valid = false;
-  if (t.wave < kJobs) load_block(a, t, t.wave / kSliceGroups, t.wave % kSliceGroups, v0, v1, valid);
-  TQ_ORDER();
-  const uint4* wp = a.words + row64_quad_base(t.slice, t.rbc, a.nb) + t.lane;
-  uint4 wq[kSliceQuads];
+__device__ __forceinline__ uint2 load_pair(const uint32_t* p) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+constexpr int kMfmaMaxWaves = 9;  // 3 per SIMD at most: ~168 registers per lane
+
+template <int M, int XT>
+__global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 xh[M][kSliceTrits];
+  __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
+  __shared__ __attribute__((aligned(16))) uint2 codes[kLutEntries];
+  const Tile t = make_tile(a);
+  constexpr int kJobs = M * kSliceGroups;         // (activation row, block) transforms per slice
+  constexpr int kBatch = 8;                       // transform jobs per wavefront loaded at once
+  constexpr int kUnits = 4;                       // 8-word units per slice
+  constexpr int kIters = 4 * kUnits;              // (unit, row quarter)
+  const int j = t.lane & 15, kb = t.lane >> 4;
+
+  // Activations of this wavefront's transform jobs (job = wave + r * waves),
+  // all loads in flight together and before the weights.
+  float xv[kBatch][2];
+  bool xok[kBatch];
 #pragma unroll
-  for (int i = 0; i < kLookahead; ++i) wq[i] = load_quad(wp + min(i, t.nq_here - 1) * 64);
+  for (int r = 0; r < kBatch; ++r) {
+    const int job = min(t.wave + r * t.waves, kJobs - 1);
+    load_block_t<XT>(a, t, job / kSliceGroups, job % kSliceGroups, xv[r][0], xv[r][1], xok[r]);
+  }
+  TQ_ORDER();
+  // Word pair of (row quarter h, unit u): quad 2u + kb / 2, words 2 (kb % 2)
+  // and + 1.  Slices are stored whole (quads past the row's end hold
+  // all-zero words), so every unit is read and no clamp is needed.
+  const uint32_t* wbase = reinterpret_cast<const uint32_t*>(a.words) +
+                          (row64_quad_base(t.slice, t.rbc, a.nb) + (kb >> 1) * 64 + j) * 4 + 2 * (kb & 1);
+  auto pair_at = [&](int it) { return wbase + ((2 * (it / 4)) * 64 + 16 * (it % 4)) * 4; };  // it = 4 u + h
+  uint2 wq[kIters];
+#pragma unroll
+  for (int i = 0; i < kLookahead; ++i) wq[i] = load_pair(pair_at(i));
+  TQ_ORDER();
+  float sc[4][kSliceGroups];
+  {
+    const uint16_t* sp = a.scales + row64_scale_base(t.slice, t.rbc, a.nb) + j;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int g = 0; g < kSliceGroups; ++g) {
+        // Unconditional load (the row block index is clamped), select after:
+        // a load under the condition would be waited for on its own.
+        const float v = f16_to_f32(sp[g * 64 + 16 * h]);
+        sc[h][g] = t.active ? v : 0.0f;
+      }
+  }
+  TQ_ORDER();
 
   for (int e = t.tid; e < kLutEntries; e += blockDim.x) {
-    uint16_t h[4];
+    uint16_t hv[4];
     int c = e;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      h[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(static_cast<float>(c % 3) - 1.0f));
+      hv[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(static_cast<float>(c % 3) - 1.0f));
       c /= 3;
     }
-    codes_lo[e] = h[0] | (static_cast<uint32_t>(h[1]) << 16);
-    codes_hi[e] = h[2] | (static_cast<uint32_t>(h[3]) << 16);
+    codes[e] = make_uint2(hv[0] | (static_cast<uint32_t>(hv[1]) << 16), hv[2] | (static_cast<uint32_t>(hv[3]) << 16));
   }
-  for (int job = t.wave; job < kJobs; job += t.waves) {
-    if (job != t.wave) load_block(a, t, job / kSliceGroups, job % kSliceGroups, v0, v1, valid);
+  for (int i = t.tid; i < kSliceTrits; i += blockDim.x) zeros[i] = static_cast<_Float16>(0.0f);
+  if (a.fused) wave_fwht128_batch<kBatch>(xv, t.lane, kInvSqrt128);
+#pragma unroll
+  for (int r = 0; r < kBatch; ++r) {
+    const int job = t.wave + r * t.waves;
+    if (job < kJobs) {
+      _Float16* dst = &xh[job / kSliceGroups][(job % kSliceGroups) * 128 + 2 * t.lane];
+      dst[0] = static_cast<_Float16>(xok[r] ? xv[r][0] : 0.0f);
+      dst[1] = static_cast<_Float16>(xok[r] ? xv[r][1] : 0.0f);
+    }
+  }
+  // Fewer than kJobs / kBatch wavefronts: the remaining jobs one at a time.
+  for (int job = t.wave + kBatch * t.waves; job < kJobs; job += t.waves) {
+    float v0, v1;
+    bool valid;
+    load_block_t<XT>(a, t, job / kSliceGroups, job % kSliceGroups, v0, v1, valid);
     transform(a, v0, v1, valid, t.lane);
     _Float16* dst = &xh[job / kSliceGroups][(job % kSliceGroups) * 128 + 2 * t.lane];
     dst[0] = static_cast<_Float16>(v0);
@@ -326,50 +398,89 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_dot2_kernel(GemvArgs a) {
   }
   TQ_LDS_BARRIER();
 
-  float acc[M][kSliceGroups];
-#pragma unroll
-  for (int m = 0; m < M; ++m)
-#pragma unroll
-    for (int g = 0; g < kSliceGroups; ++g) acc[m][g] = 0.0f;
+  // This lane's activation row (activation row j, its 40-trit part of each
+  // unit), or the zero row for rows past M.
+  const _Float16* xrow = (j < M ? &xh[j < M ? j : 0][0] : &zeros[0]) + 40 * kb;
+  const _Float16* zrow = &zeros[0] + 40 * kb;
+  const char* cbase = reinterpret_cast<const char*>(codes);
 
+  float4_t acc[4][2];
+  float tot[4][4];
 #pragma unroll
-  for (int i = 0; i < kSliceQuads; ++i) {
-    if (i + kLookahead < kSliceQuads) wq[i + kLookahead] = load_quad(wp + min(i + kLookahead, t.nq_here - 1) * 64);
-    if (i < t.nq_here) {
-      const uint32_t wv[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
+  for (int h = 0; h < 4; ++h) {
+    acc[h][0] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    acc[h][1] = acc[h][0];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t o[5];
-        word_offsets(wv[j], o);
+    for (int v = 0; v < 4; ++v) tot[h][v] = 0.0f;
+  }
+  // Units outer, row quarters inner: each activation operand read serves the
+  // four quarters' independent accumulation chains.
 #pragma unroll
-        for (int h = 0; h < 5; ++h) {
-          const int p = i * 20 + j * 5 + h;
-          const half2_t lo = __builtin_bit_cast(
-              half2_t, *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(codes_lo) + o[h]));
-          const half2_t hi = __builtin_bit_cast(
-              half2_t, *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(codes_hi) + o[h]));
+  for (int u = 0; u < kUnits; ++u) {
+    half8_t af[5], al[5], ah[5];
 #pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const uint2 xq = *reinterpret_cast<const uint2*>(&xh[m][4 * p]);
-            float s = acc[m][p / 32];
-            s = __builtin_amdgcn_fdot2(lo, __builtin_bit_cast(half2_t, xq.x), s, false);
-            s = __builtin_amdgcn_fdot2(hi, __builtin_bit_cast(half2_t, xq.y), s, false);
-            acc[m][p / 32] = s;
+    for (int s = 0; s < 5; ++s) {
+      const int koff = 160 * u + 8 * s;
+      if (mfma_gmin(u, s) == mfma_gmax(u, s)) {
+        af[s] = *reinterpret_cast<const half8_t*>(xrow + koff);
+      } else {
+        const bool lo = ((mfma_lo_mask(u, s) >> kb) & 1) != 0;
+        al[s] = *reinterpret_cast<const half8_t*>((lo ? xrow : zrow) + koff);
+        ah[s] = *reinterpret_cast<const half8_t*>((lo ? zrow : xrow) + koff);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int it = u * 4 + h;
+      if (it + kLookahead < kIters) wq[it + kLookahead] = load_pair(pair_at(it + kLookahead));
+      uint32_t o[10];
+      word_offsets_s<3, false>(wq[it].x, o);
+      word_offsets_s<3, false>(wq[it].y, o + 5);
+      uint2 cv[10];
+#pragma unroll
+      for (int c = 0; c < 10; ++c) cv[c] = *reinterpret_cast<const uint2*>(cbase + o[c]);
+#pragma unroll
+      for (int s = 0; s < 5; ++s) {
+        const int gl = mfma_gmin(u, s), gh = mfma_gmax(u, s);
+        if (u > 0 || s > 0) {
+          const int pgl = s > 0 ? mfma_gmin(u, s - 1) : mfma_gmin(u - 1, 4);
+          if (gl > pgl) {  // every lane group has left scale group pgl: it is complete
+#pragma unroll
+            for (int v = 0; v < 4; ++v) tot[h][v] = fmaf(sc[h][pgl], acc[h][pgl & 1][v], tot[h][v]);
+            acc[h][pgl & 1] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
           }
+        }
+        const uint4 bq = make_uint4(cv[2 * s].x, cv[2 * s].y, cv[2 * s + 1].x, cv[2 * s + 1].y);
+        const half8_t bf = __builtin_bit_cast(half8_t, bq);
+        if (gl == gh) {
+          acc[h][gl & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s], bf, acc[h][gl & 1], 0, 0, 0);
+        } else {
+          acc[h][gl & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[s], bf, acc[h][gl & 1], 0, 0, 0);
+          acc[h][gh & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[s], bf, acc[h][gh & 1], 0, 0, 0);
         }
       }
     }
     TQ_ORDER();
   }
-  float part[M];
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    float s = 0.0f;
+  for (int h = 0; h < 4; ++h) {
+    constexpr int glast = mfma_gmin(kUnits - 1, 4);
 #pragma unroll
-    for (int g = 0; g < kSliceGroups; ++g) s = fmaf(sc[g], acc[m][g], s);
-    part[m] = s;
+    for (int v = 0; v < 4; ++v) tot[h][v] = fmaf(sc[h][glast], acc[h][glast & 1][v], tot[h][v]);
+    // D[i][j] for activation row i = 4 kb + v sits in acc[.][v] of lane l.
+    const int row = t.rb * 64 + 16 * h + j;
+    if (t.active && row < a.n) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * kb + v;
+        if (m < M) {
+          if (a.mode == kPartial) a.partial[(static_cast<size_t>(t.slice) * M + m) * a.npad + row] = tot[h][v];
+          else if (a.mode == kAtomic) atomicAdd(&a.y[static_cast<size_t>(m) * a.n + row], tot[h][v]);
+          else a.y[static_cast<size_t>(m) * a.n + row] = tot[h][v];
+        }
+      }
+    }
   }
-  finish<M>(a, t, part);
 }
 
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -393,14 +504,22 @@ GemvPlan plan_sizes(int n, int k, int m) {
 
 // Wavefronts per workgroup: enough row blocks per workgroup that
 // (row groups) x (slices) fits the compute units in one round.
-void plan_waves(GemvPlan& p) {
+void plan_waves(GemvPlan& p, int min_waves, int max_waves) {
   const int cus = tq_device_cus();
   const int per_slice = cus / p.nsl > 0 ? cus / p.nsl : 1;
   int w = (p.nb + per_slice - 1) / per_slice;
+  if (w < min(min_waves, p.nb)) w = min(min_waves, p.nb);
   if (w < 1) w = 1;
-  if (w > kMaxWaves) w = kMaxWaves;
+  if (w > max_waves) w = max_waves;
   p.waves = w;
   p.ngroups = (p.nb + w - 1) / w;
+}
+
+template <int M>
+void launch_mfma(int x_dtype, dim3 grid, dim3 block, hipStream_t s, const GemvArgs& a) {
+  if (x_dtype == TQ_F32) hipLaunchKernelGGL((gemv_mfma_kernel<M, TQ_F32>), grid, block, 0, s, a);
+  else if (x_dtype == TQ_BF16) hipLaunchKernelGGL((gemv_mfma_kernel<M, TQ_BF16>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((gemv_mfma_kernel<M, TQ_F16>), grid, block, 0, s, a);
 }
 
 }  // namespace
@@ -447,7 +566,10 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
     if (!workspace) return TQ_EINVAL;
     if (ws_bytes < p.partial_bytes) return TQ_ENOSPACE;
   }
-  plan_waves(p);
+  // M >= 2: every workgroup transforms M x 5 activation blocks, so it gets
+  // at least 8 wavefronts to share them.
+  if (m == 1) plan_waves(p, 1, kMaxWaves);
+  else plan_waves(p, 8, kMfmaMaxWaves);
   GemvArgs a;
   a.words = reinterpret_cast<const uint4*>(w->words);
   a.scales = w->scales;
@@ -473,13 +595,13 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
       else if (x_dtype == TQ_BF16) hipLaunchKernelGGL(gemv_lut_m1_kernel<TQ_BF16>, grid, block, 0, s, a);
       else hipLaunchKernelGGL(gemv_lut_m1_kernel<TQ_F16>, grid, block, 0, s, a);
       break;
-    case 2: hipLaunchKernelGGL(gemv_dot2_kernel<2>, grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL(gemv_dot2_kernel<3>, grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL(gemv_dot2_kernel<4>, grid, block, 0, s, a); break;
-    case 5: hipLaunchKernelGGL(gemv_dot2_kernel<5>, grid, block, 0, s, a); break;
-    case 6: hipLaunchKernelGGL(gemv_dot2_kernel<6>, grid, block, 0, s, a); break;
-    case 7: hipLaunchKernelGGL(gemv_dot2_kernel<7>, grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL(gemv_dot2_kernel<8>, grid, block, 0, s, a); break;
+    case 2: launch_mfma<2>(x_dtype, grid, block, s, a); break;
+    case 3: launch_mfma<3>(x_dtype, grid, block, s, a); break;
+    case 4: launch_mfma<4>(x_dtype, grid, block, s, a); break;
+    case 5: launch_mfma<5>(x_dtype, grid, block, s, a); break;
+    case 6: launch_mfma<6>(x_dtype, grid, block, s, a); break;
+    case 7: launch_mfma<7>(x_dtype, grid, block, s, a); break;
+    default: launch_mfma<8>(x_dtype, grid, block, s, a); break;
   }
   TQ_LAUNCH_CHECK();
   if (mode == kPartial) {

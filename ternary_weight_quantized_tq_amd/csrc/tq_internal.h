@@ -89,12 +89,72 @@ __device__ __forceinline__ void wave_fwht128(T& v0, T& v1, int lane, T scale) {
   for (int s = 1; s < 64; s <<= 1) {
     const T pa = __shfl_xor(a, s);
     const T pb = __shfl_xor(b, s);
-    const bool upper = (lane & s) != 0;
-    a = upper ? (pa - a) : (a + pa);
-    b = upper ? (pb - b) : (b + pb);
+    const T sgn = (lane & s) ? T(-1) : T(1);  // lower lane a + p, upper lane p - a
+    a = sgn * a + pa;
+    b = sgn * b + pb;
   }
   v0 = a * scale;
   v1 = b * scale;
+}
+
+// Value of lane (lane ^ S) for S = 1..32: DPP inside 16-lane rows for
+// S <= 8 (quad_perm for 1 and 2, row shifts for 4, row rotate for 8; plain
+// VALU, no LDS traffic), ds_swizzle for 16, ds_bpermute for 32.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int S>
+__device__ __forceinline__ float lane_xor_f32(float v, int lane) {
+  if constexpr (S == 1) return dpp_f32<0xB1>(v);         // quad_perm(1,0,3,2)
+  else if constexpr (S == 2) return dpp_f32<0x4E>(v);    // quad_perm(2,3,0,1)
+  else if constexpr (S == 4) {
+    const float up = dpp_f32<0x104>(v);                  // row_shl:4, lane i <- i + 4
+    const float dn = dpp_f32<0x114>(v);                  // row_shr:4, lane i <- i - 4
+    return (lane & 4) ? dn : up;
+  } else if constexpr (S == 8) return dpp_f32<0x128>(v);  // row_ror:8
+  else if constexpr (S == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+  else return __shfl_xor(v, S);
+}
+
+// B independent blocks at once (one per v[r]), stage by stage, so that the
+// lane exchanges of all blocks are in flight together; the four narrow
+// strides run on DPP, so only two stages go through the LDS crossbar.
+template <int S, int B>
+__device__ __forceinline__ void fwht_batch_stage(float (&a)[B], float (&b)[B], int lane) {
+  float pa[B], pb[B];
+#pragma unroll
+  for (int r = 0; r < B; ++r) {
+    pa[r] = lane_xor_f32<S>(a[r], lane);
+    pb[r] = lane_xor_f32<S>(b[r], lane);
+  }
+  // Lower lane of a pair: a + p; upper lane: p - a.  Both are p + sgn * a.
+  const float sgn = (lane & S) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int r = 0; r < B; ++r) {
+    a[r] = fmaf(sgn, a[r], pa[r]);
+    b[r] = fmaf(sgn, b[r], pb[r]);
+  }
+}
+template <int B>
+__device__ __forceinline__ void wave_fwht128_batch(float (&v)[B][2], int lane, float scale) {
+  float a[B], b[B];
+#pragma unroll
+  for (int r = 0; r < B; ++r) {
+    a[r] = v[r][0] + v[r][1];
+    b[r] = v[r][0] - v[r][1];
+  }
+  fwht_batch_stage<1>(a, b, lane);
+  fwht_batch_stage<2>(a, b, lane);
+  fwht_batch_stage<4>(a, b, lane);
+  fwht_batch_stage<8>(a, b, lane);
+  fwht_batch_stage<16>(a, b, lane);
+  fwht_batch_stage<32>(a, b, lane);
+#pragma unroll
+  for (int r = 0; r < B; ++r) {
+    v[r][0] = a[r] * scale;
+    v[r][1] = b[r] * scale;
+  }
 }
 
 // ------------------------------------------------- fp16 bit patterns ---

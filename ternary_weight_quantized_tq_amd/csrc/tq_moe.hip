@@ -63,9 +63,9 @@ __device__ __forceinline__ uint4 zero_quad() { return make_uint4(kZeroWord, kZer
 __global__ __launch_bounds__(1024) void moe_bucket_kernel(MoeArgs a) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int fill[kMaxExperts];
-  __shared__ int start[kMaxExperts + 1];
-  __shared__ int slot_of[kMaxExperts];
-  const int tid = threadIdx.x;
+  __shared__ int start[kMaxExperts];
+  __shared__ int wsum_c[kMaxExperts / 64], wsum_f[kMaxExperts / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = a.t * a.topk;
   for (int e = tid; e < a.experts; e += blockDim.x) {
     cnt[e] = 0;
@@ -77,26 +77,48 @@ __global__ __launch_bounds__(1024) void moe_bucket_kernel(MoeArgs a) {
     if (e >= 0 && e < a.experts) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
-  if (tid == 0) {
-    int off = 0, na = 0;
-    for (int e = 0; e < a.experts; ++e) {
-      start[e] = off;
-      slot_of[e] = -1;
-      if (cnt[e] > 0) {
-        slot_of[e] = na;
-        a.active[na] = e;
-        a.seg[na] = off;
-        ++na;
-      }
-      off += cnt[e];
+  // Exclusive prefix sums over experts (one per thread, blockDim >= experts)
+  // of the pair counts (segment starts) and of "has pairs" (active slots).
+  const int e = tid;
+  const int ce = e < a.experts ? cnt[e] : 0;
+  const int fe = ce > 0 ? 1 : 0;
+  int c = ce, f = fe;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int tc = __shfl_up(c, d);
+    const int tf = __shfl_up(f, d);
+    if (lane >= d) {
+      c += tc;
+      f += tf;
     }
-    a.seg[na] = off;
-    a.num_active[0] = na;
+  }
+  if (lane == 63) {
+    wsum_c[wave] = c;
+    wsum_f[wave] = f;
+  }
+  __syncthreads();
+  int oc = 0, of = 0;
+  for (int w = 0; w < wave; ++w) {
+    oc += wsum_c[w];
+    of += wsum_f[w];
+  }
+  const int off = oc + c - ce;   // pairs of the experts before e
+  const int slot = of + f - fe;  // active experts before e
+  if (e < a.experts) {
+    start[e] = off;
+    if (fe) {
+      a.active[slot] = e;
+      a.seg[slot] = off;
+    }
+    if (e == a.experts - 1) {
+      a.seg[slot + fe] = off + ce;
+      a.num_active[0] = slot + fe;
+    }
   }
   __syncthreads();
   for (int p = tid; p < P; p += blockDim.x) {
-    const int e = a.ids[p];
-    if (e >= 0 && e < a.experts) a.pairs[start[e] + atomicAdd(&fill[e], 1)] = p;
+    const int ep = a.ids[p];
+    if (ep >= 0 && ep < a.experts) a.pairs[start[ep] + atomicAdd(&fill[ep], 1)] = p;
   }
 }
 

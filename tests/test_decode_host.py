@@ -18,11 +18,12 @@ PROG = r'''
 #include "tq_decode.h"
 using namespace tq;
 static int check(uint32_t w) {
-  uint32_t o[5];
+  uint32_t o[5], o8[5];
   word_offsets(w, o);
+  word_offsets_s<3>(w, o8);
   uint32_t v = w;
   for (int j = 0; j < 5; ++j) {
-    if (o[j] != 4u * (v % 81u)) return 1;
+    if (o[j] != 4u * (v % 81u) || o8[j] != 8u * (v % 81u)) return 1;
     v /= 81u;
   }
   return 0;
@@ -33,6 +34,7 @@ int main() {
   /* 24-bit steps over their whole ranges */
   for (uint32_t a = 0; a < 531441u; ++a) bad += mulhi_u24(a, 654622u) != a / 6561u;
   for (uint32_t b = 0; b < 6561u; ++b) bad += mulhi_u24(4u * b, 13256072u) != b / 81u;
+  for (uint32_t b = 0; b < 6561u; ++b) bad += mulhi_u24(8u * b, 6628036u) != b / 81u;
   /* both FP64 divisions at every multiple boundary */
   for (uint32_t q = 0; q < 531441u; ++q) {
     uint32_t lo = q * 6561u;
