@@ -195,7 +195,7 @@ def extra_block_m8(tq, torch, synth, np):
             "ms_per_step": round(ms, 4), "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "layer_tok_s": round(8 / (ms * 1e-3), 1), "kernel_us": per,
-            "compute": "v_mfma_f32_16x16x32_f16 (fp16 x', fp16 trit codes, FP32 accumulate)"}
+            "compute": "v_mfma_f32_16x16x32_f16 (x' as two fp16 parts in the A rows, fp16 trit codes, FP32 accumulate)"}
 
 
 def extra_moe(tq, torch, synth, np):

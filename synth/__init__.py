@@ -72,9 +72,10 @@ class Activations:
     dtype: str
 
 
-def activations(seed, m: int, k: int, dtype: str = "bf16") -> Activations:
+def activations(seed, m: int, k: int, dtype: str = "bf16", scale: float = 1.0) -> Activations:
+    """N(0, scale^2) activations, rounded to `dtype`."""
     g = _gen(seed)
-    x = g.standard_normal((m, k)).astype(np.float32)
+    x = (g.standard_normal((m, k)) * scale).astype(np.float32)
     if dtype == "f32":
         return Activations(x.astype(np.float64), x, "f32")
     if dtype == "bf16":

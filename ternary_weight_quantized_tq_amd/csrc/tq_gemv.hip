@@ -28,9 +28,9 @@
 // The one barrier waits for LDS only (a plain __syncthreads() would also
 // wait for every outstanding weight load).
 //
-// M >= 2 runs on the matrix cores (v_mfma_f32_16x16x32_f16): x' rounded to
-// fp16 in LDS is the A operand, fp16 trit codes read from an 81-entry LDS
-// table are the B operand (see gemv_mfma_kernel).
+// M >= 2 runs on the matrix cores (v_mfma_f32_16x16x32_f16): x' split into
+// two fp16 parts in LDS is the A operand, fp16 trit codes read from an
+// 81-entry LDS table are the B operand (see gemv_mfma_kernel).
 #include "tq_internal.h"
 
 using namespace tq;
@@ -43,6 +43,7 @@ constexpr int kMaxWaves = 16;
 constexpr int kLookahead = 3;
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -288,9 +289,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a)
 }
 
 // ------------------------------------------- 2 <= M <= 8 on the matrix cores ---
-// v_mfma_f32_16x16x32_f16 with A = x' (16 rows = activation rows, M used,
-// the rest read as zero) and B = trit codes (16 columns = output rows), K
-// permuted so that every lane decodes whole words of its own row:
+// v_mfma_f32_16x16x32_f16 with A = x' and B = trit codes (16 columns =
+// output rows).  A row i = 2 m + p holds part p of activation row m: x'
+// scaled by 2^e_m (a power of two per row and slice that puts max |x'| in
+// [2^13, 2^14)) is split into p = 0: its fp16 rounding and p = 1: the fp16
+// rounding of the remainder, so the 16 A rows carry all eight activation
+// rows at about 22 significant bits and no fp16 overflow or underflow.
+// K is permuted so that every lane decodes whole words of its own row:
 //   lane l, j = l % 16, kb = l / 16 (0..3), row quarter h (0..3): output
 //   row 64 rb + 16 h + j; in unit u (0..3) = quads 2u, 2u + 1 of the slice
 //   the lane owns words 2 kb, 2 kb + 1 of the unit's eight, and step s
@@ -301,6 +306,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a)
 // groups: such steps are issued twice, each time with the activations of
 // the lanes in the other scale group read as zero.  Sums are kept per scale
 // group (two in flight) and scaled by the row's FP32 scale when complete.
+// Lane l ends with D rows 4 kb .. 4 kb + 3: both parts of activation rows
+// 2 kb and 2 kb + 1.
 __host__ __device__ constexpr int mfma_group(int u, int s, int kb) { return (160 * u + 40 * kb + 8 * s) / 128; }
 __host__ __device__ constexpr int mfma_gmin(int u, int s) { return mfma_group(u, s, 0); }
 __host__ __device__ constexpr int mfma_gmax(int u, int s) { return mfma_group(u, s, 3); }
@@ -316,28 +323,42 @@ __device__ __forceinline__ uint2 load_pair(const uint32_t* p) {
   return make_uint2(v.x, v.y);
 }
 
+// Maximum of v over the wavefront (every lane gets it).
+__device__ __forceinline__ float wave_max(float v, int lane) {
+  v = fmaxf(v, lane_xor_f32<1>(v, lane));
+  v = fmaxf(v, lane_xor_f32<2>(v, lane));
+  v = fmaxf(v, lane_xor_f32<4>(v, lane));
+  v = fmaxf(v, lane_xor_f32<8>(v, lane));
+  v = fmaxf(v, lane_xor_f32<16>(v, lane));
+  return fmaxf(v, lane_xor_f32<32>(v, lane));
+}
+
 constexpr int kMfmaMaxWaves = 9;  // 3 per SIMD at most: ~168 registers per lane
+constexpr int kXStride = kSliceTrits + 8;
 
 template <int M, int XT>
 __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 xh[M][kSliceTrits];
+  // A rows padded by 16 bytes: the 16 lanes of a lane group read 16 rows at
+  // one offset, which then fall on 16 different 4-bank groups.
+  __shared__ __attribute__((aligned(16))) _Float16 xh[2 * M][kXStride];
   __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
   __shared__ __attribute__((aligned(16))) uint2 codes[kLutEntries];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[kMfmaMaxWaves][kSliceGroups * 64];
+  __shared__ int xexp[M];
   const Tile t = make_tile(a);
-  constexpr int kJobs = M * kSliceGroups;         // (activation row, block) transforms per slice
-  constexpr int kBatch = 8;                       // transform jobs per wavefront loaded at once
   constexpr int kUnits = 4;                       // 8-word units per slice
   constexpr int kIters = 4 * kUnits;              // (unit, row quarter)
   const int j = t.lane & 15, kb = t.lane >> 4;
 
-  // Activations of this wavefront's transform jobs (job = wave + r * waves),
-  // all loads in flight together and before the weights.
-  float xv[kBatch][2];
-  bool xok[kBatch];
+  // Wavefront w transforms activation row w (and w + waves, ... when there
+  // are fewer wavefronts than rows): the slice's five blocks at once, loaded
+  // before the weights.
+  float xv[kSliceGroups][2];
+  bool xok[kSliceGroups];
+  {
+    const int m = t.wave < M ? t.wave : 0;
 #pragma unroll
-  for (int r = 0; r < kBatch; ++r) {
-    const int job = min(t.wave + r * t.waves, kJobs - 1);
-    load_block_t<XT>(a, t, job / kSliceGroups, job % kSliceGroups, xv[r][0], xv[r][1], xok[r]);
+    for (int r = 0; r < kSliceGroups; ++r) load_block_t<XT>(a, t, m, r, xv[r][0], xv[r][1], xok[r]);
   }
   TQ_ORDER();
   // Word pair of (row quarter h, unit u): quad 2u + kb / 2, words 2 (kb % 2)
@@ -350,19 +371,11 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
 #pragma unroll
   for (int i = 0; i < kLookahead; ++i) wq[i] = load_pair(pair_at(i));
   TQ_ORDER();
-  float sc[4][kSliceGroups];
-  {
-    const uint16_t* sp = a.scales + row64_scale_base(t.slice, t.rbc, a.nb) + j;
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-#pragma unroll
-      for (int g = 0; g < kSliceGroups; ++g) {
-        // Unconditional load (the row block index is clamped), select after:
-        // a load under the condition would be waited for on its own.
-        const float v = f16_to_f32(sp[g * 64 + 16 * h]);
-        sc[h][g] = t.active ? v : 0.0f;
-      }
-  }
+  // The block's 5 x 64 scales (640 contiguous bytes) in one 16-byte load by
+  // lanes 0..39, staged in LDS; each lane needs 20 of them at stride 32 B.
+  uint4 scq = make_uint4(0, 0, 0, 0);
+  if (t.lane < kSliceGroups * 8)
+    scq = *reinterpret_cast<const uint4*>(a.scales + row64_scale_base(t.slice, t.rbc, a.nb) + 8 * t.lane);
   TQ_ORDER();
 
   for (int e = t.tid; e < kLutEntries; e += blockDim.x) {
@@ -376,31 +389,51 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
     codes[e] = make_uint2(hv[0] | (static_cast<uint32_t>(hv[1]) << 16), hv[2] | (static_cast<uint32_t>(hv[3]) << 16));
   }
   for (int i = t.tid; i < kSliceTrits; i += blockDim.x) zeros[i] = static_cast<_Float16>(0.0f);
-  if (a.fused) wave_fwht128_batch<kBatch>(xv, t.lane, kInvSqrt128);
+  if (t.lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[t.wave][8 * t.lane]) = scq;
+  for (int m = t.wave; m < M; m += t.waves) {
+    if (m != t.wave) {
 #pragma unroll
-  for (int r = 0; r < kBatch; ++r) {
-    const int job = t.wave + r * t.waves;
-    if (job < kJobs) {
-      _Float16* dst = &xh[job / kSliceGroups][(job % kSliceGroups) * 128 + 2 * t.lane];
-      dst[0] = static_cast<_Float16>(xok[r] ? xv[r][0] : 0.0f);
-      dst[1] = static_cast<_Float16>(xok[r] ? xv[r][1] : 0.0f);
+      for (int r = 0; r < kSliceGroups; ++r) load_block_t<XT>(a, t, m, r, xv[r][0], xv[r][1], xok[r]);
     }
-  }
-  // Fewer than kJobs / kBatch wavefronts: the remaining jobs one at a time.
-  for (int job = t.wave + kBatch * t.waves; job < kJobs; job += t.waves) {
-    float v0, v1;
-    bool valid;
-    load_block_t<XT>(a, t, job / kSliceGroups, job % kSliceGroups, v0, v1, valid);
-    transform(a, v0, v1, valid, t.lane);
-    _Float16* dst = &xh[job / kSliceGroups][(job % kSliceGroups) * 128 + 2 * t.lane];
-    dst[0] = static_cast<_Float16>(v0);
-    dst[1] = static_cast<_Float16>(v1);
+    if (a.fused) wave_fwht128_batch<kSliceGroups>(xv, t.lane, kInvSqrt128);
+    float mx = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kSliceGroups; ++r) {
+      if (!xok[r]) {
+        xv[r][0] = 0.0f;
+        xv[r][1] = 0.0f;
+      }
+      mx = fmaxf(mx, fmaxf(fabsf(xv[r][0]), fabsf(xv[r][1])));
+    }
+    mx = wave_max(mx, t.lane);
+    // max |x'| 2^e in [2^13, 2^14): both fp16 parts stay normal and finite.
+    const int e = mx > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mx) : 0;
+#pragma unroll
+    for (int r = 0; r < kSliceGroups; ++r) {
+      const float s0 = ldexpf(xv[r][0], e), s1 = ldexpf(xv[r][1], e);
+      const _Float16 h0 = static_cast<_Float16>(s0), h1 = static_cast<_Float16>(s1);
+      const half2_t hv = {h0, h1};
+      const half2_t lv = {static_cast<_Float16>(s0 - static_cast<float>(h0)),
+                          static_cast<_Float16>(s1 - static_cast<float>(h1))};
+      *reinterpret_cast<half2_t*>(&xh[2 * m][r * 128 + 2 * t.lane]) = hv;
+      *reinterpret_cast<half2_t*>(&xh[2 * m + 1][r * 128 + 2 * t.lane]) = lv;
+    }
+    if (t.lane == 0) xexp[m] = e;
   }
   TQ_LDS_BARRIER();
 
-  // This lane's activation row (activation row j, its 40-trit part of each
-  // unit), or the zero row for rows past M.
-  const _Float16* xrow = (j < M ? &xh[j < M ? j : 0][0] : &zeros[0]) + 40 * kb;
+  float sc[4][kSliceGroups];
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int g = 0; g < kSliceGroups; ++g) {
+      const float v = f16_to_f32(ssc[t.wave][g * 64 + 16 * h + j]);
+      sc[h][g] = t.active ? v : 0.0f;
+    }
+
+  // This lane's A row (part j % 2 of activation row j / 2, its 40-trit part
+  // of each unit), or the zero row past the M activation rows.
+  const _Float16* xrow = (j < 2 * M ? &xh[j < 2 * M ? j : 0][0] : &zeros[0]) + 40 * kb;
   const _Float16* zrow = &zeros[0] + 40 * kb;
   const char* cbase = reinterpret_cast<const char*>(codes);
 
@@ -462,21 +495,27 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
     }
     TQ_ORDER();
   }
+  // D rows 4 kb + v: v = 0, 1 are the two parts of activation row 2 kb,
+  // v = 2, 3 those of row 2 kb + 1.
+  const int mrow[2] = {2 * kb, 2 * kb + 1};
+  int mexp[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) mexp[q] = mrow[q] < M ? -xexp[mrow[q] < M ? mrow[q] : 0] : 0;
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     constexpr int glast = mfma_gmin(kUnits - 1, 4);
 #pragma unroll
     for (int v = 0; v < 4; ++v) tot[h][v] = fmaf(sc[h][glast], acc[h][glast & 1][v], tot[h][v]);
-    // D[i][j] for activation row i = 4 kb + v sits in acc[.][v] of lane l.
     const int row = t.rb * 64 + 16 * h + j;
     if (t.active && row < a.n) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = 4 * kb + v;
+      for (int q = 0; q < 2; ++q) {
+        const int m = mrow[q];
         if (m < M) {
-          if (a.mode == kPartial) a.partial[(static_cast<size_t>(t.slice) * M + m) * a.npad + row] = tot[h][v];
-          else if (a.mode == kAtomic) atomicAdd(&a.y[static_cast<size_t>(m) * a.n + row], tot[h][v]);
-          else a.y[static_cast<size_t>(m) * a.n + row] = tot[h][v];
+          const float val = ldexpf(tot[h][2 * q] + tot[h][2 * q + 1], mexp[q]);
+          if (a.mode == kPartial) a.partial[(static_cast<size_t>(t.slice) * M + m) * a.npad + row] = val;
+          else if (a.mode == kAtomic) atomicAdd(&a.y[static_cast<size_t>(m) * a.n + row], val);
+          else a.y[static_cast<size_t>(m) * a.n + row] = val;
         }
       }
     }
