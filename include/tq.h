@@ -79,12 +79,21 @@ enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2, TQ_F64 = 3 };
  *   words = 5 scale groups; 640 is the least common multiple of 20 and 128),
  *   rows into blocks of 64.  Word 32s + 4q + j of row 64b + r is stored at
  *   words[(((s*nb + b)*8 + q)*64 + r)*4 + j], nb = ceil(n/64), and the scale
- *   of group 5s + g of that row at scales[((s*nb + b)*5 + g)*64 + r].  Rows
- *   past n, words past ceil(K/20) and groups past K/128 are padding (the
- *   all-zero word 1743392200, scale 0).  One 16-byte load per lane reads a
- *   quad of its row, a 64-lane wavefront reads 1 KiB contiguously, and the
- *   8 KiB of one slice of one row block are contiguous.  Word values are
- *   identical in both layouts. */
+ *   of group 5s + g of that row at scales[((s*nb + b)*5 + g)*64 + r].  One
+ *   16-byte load per lane reads a quad of its row, a 64-lane wavefront reads
+ *   1 KiB contiguously, and the 8 KiB of one slice of one row block are
+ *   contiguous.
+ *   Each word is a base-3 number of 20 trits as in ROWMAJOR, but within
+ *   each unit of 160 trits (quads 2u and 2u + 1 of a slice: unit words
+ *   wl = 0..7) the trits are grouped into 40 chunks of 4 and reordered:
+ *   digits 4j .. 4j + 3 of unit word wl are unit trits 4c .. 4c + 3 with
+ *     q = 5 (wl % 2) + j,   c = 8 (q / 2) + 2 (wl / 2) + q % 2,
+ *   so that words 2kb and 2kb + 1 hold, in digit order, the trit runs
+ *   32i + 8kb .. 32i + 8kb + 7 for i = 0..4 (a 32-trit run of the unit is
+ *   spread over the four word pairs and never crosses a scale group).
+ *   Rows past n, trits past K and groups past K/128 are padding (zero
+ *   trits, so a word of padding only is the all-zero word 1743392200;
+ *   scale 0).  tq_unpack inverts the layout exactly. */
 enum { TQ_LAYOUT_ROWMAJOR = 0, TQ_LAYOUT_ROW64 = 1 };
 
 /* Flags.

@@ -91,4 +91,20 @@ TQ_HD void word_offsets_s(uint32_t w, uint32_t o[5]) {
 // o[j] = 4 * chunk j (digits 4j..4j+3) of the word.
 TQ_HD void word_offsets(uint32_t w, uint32_t o[5]) { word_offsets_s<2>(w, o); }
 
+// Chunk order of the ROW64 layout.  A unit is 160 trits of a row = 8 words
+// = 40 chunks of 4 trits; its words hold its own trits only, but chunk j of
+// unit word wl (0..7) is unit chunk row64_chunk(wl, j), i.e. unit trits
+// 4c .. 4c + 3.  With kb = wl / 2 and q = 5 (wl % 2) + j (0..9):
+//   c = 8 (q / 2) + 2 kb + q % 2,
+// so the word pair 2kb, 2kb + 1 holds, in digit order, the chunk pairs
+// (8s + 2kb, 8s + 2kb + 1) for s = 0..4: a 32-trit step 32s .. 32s + 31 takes
+// two consecutive chunks from each of the four pairs and lies in a single
+// scale group (128 is a multiple of 32).
+constexpr int row64_chunk(int wl, int j) {
+  return 8 * ((5 * (wl & 1) + j) >> 1) + 2 * (wl >> 1) + ((5 * (wl & 1) + j) & 1);
+}
+// Inverse: unit word and chunk-in-word of unit chunk c (0..39).
+constexpr int row64_chunk_word(int c) { return 2 * ((c & 7) >> 1) + (2 * (c >> 3) + (c & 1)) / 5; }
+constexpr int row64_chunk_index(int c) { return (2 * (c >> 3) + (c & 1)) % 5; }
+
 }  // namespace tq

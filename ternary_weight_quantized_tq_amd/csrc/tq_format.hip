@@ -64,11 +64,27 @@ __global__ __launch_bounds__(256) void pack_rowmajor_kernel(const int8_t* __rest
   words[idx] = pack_word(trits + static_cast<size_t>(row) * k, k, w);
 }
 
-// ROW64 (slice-major, see row64_word_index): one thread per destination
-// word, padding included (padded rows and words hold the all-zero word).
-__global__ __launch_bounds__(256) void pack_row64_kernel(const int8_t* __restrict__ trits, int n, int k,
-                                                         int wpr, int nsl, int nb,
-                                                         uint32_t* __restrict__ words) {
+// ROW64 (slice-major, see row64_word_index; chunk order row64_chunk): one
+// thread per destination word, padding included (padded rows and trits
+// past k are zero trits, so a word of padding only is the all-zero word).
+__device__ __forceinline__ uint32_t pack_word_row64(const int8_t* __restrict__ row, int k, int s, int qi, int j) {
+  const int wl = 4 * (qi & 1) + j;
+  const int k0 = s * kSliceTrits + (qi >> 1) * 160;
+  uint32_t acc = 0;
+#pragma unroll
+  for (int c = 4; c >= 0; --c) {
+    const int kc = k0 + 4 * row64_chunk(wl, c);
+#pragma unroll
+    for (int d = 3; d >= 0; --d) {
+      const int kk = kc + d;
+      acc = acc * 3u + (kk < k ? static_cast<uint32_t>(row[kk] + 1) : 1u);
+    }
+  }
+  return acc;
+}
+
+__global__ __launch_bounds__(256) void pack_row64_kernel(const int8_t* __restrict__ trits, int n, int k, int nsl,
+                                                         int nb, uint32_t* __restrict__ words) {
   const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const size_t total = static_cast<size_t>(nsl) * nb * kSliceQuads * 256;
   if (idx >= total) return;
@@ -79,8 +95,7 @@ __global__ __launch_bounds__(256) void pack_row64_kernel(const int8_t* __restric
   const int b = static_cast<int>(sb % nb);
   const int s = static_cast<int>(sb / nb);
   const int row = b * 64 + r;
-  const int w = s * kSliceWords + qi * 4 + j;
-  words[idx] = (row < n && w < wpr) ? pack_word(trits + static_cast<size_t>(row) * k, k, w) : kZeroWord;
+  words[idx] = row < n ? pack_word_row64(trits + static_cast<size_t>(row) * k, k, s, qi, j) : kZeroWord;
 }
 
 __global__ __launch_bounds__(256) void scales_row64_kernel(const uint16_t* __restrict__ s, int n, int groups,
@@ -100,6 +115,8 @@ __global__ __launch_bounds__(256) void scales_row64_kernel(const uint16_t* __res
 
 // -------------------------------------------------------------- unpack ---
 // t = ((word / 3^i) mod 3) - 1 for digit i, peeled by repeated division.
+// One thread per word: wpr words per row (ROWMAJOR), or the nsl * 32 words
+// of a ROW64 row, each digit written to the column its chunk maps to.
 __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict__ words, int n, int k,
                                                      int layout, int wpr, int nb,
                                                      int8_t* __restrict__ trits) {
@@ -107,16 +124,13 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict_
   if (idx >= static_cast<size_t>(n) * wpr) return;
   const int row = static_cast<int>(idx / wpr);
   const int w = static_cast<int>(idx % wpr);
-  size_t src;
-  if (layout == TQ_LAYOUT_ROWMAJOR) {
-    src = idx;
-  } else {
-    src = row64_word_index(row, w, nb);
-  }
-  uint32_t v = words[src];
+  const bool r64 = layout == TQ_LAYOUT_ROW64;
+  uint32_t v = r64 ? words[row64_word_index(row, w, nb)] : words[idx];
+  const int wl = w & 7;
+  const int k0 = (w >> 3) * 160;  // ROW64: first column of the word's unit
   int8_t* out = trits + static_cast<size_t>(row) * k;
   for (int i = 0; i < TQ_TRITS_PER_WORD; ++i) {
-    const int kk = w * TQ_TRITS_PER_WORD + i;
+    const int kk = r64 ? k0 + 4 * row64_chunk(wl, i >> 2) + (i & 3) : w * TQ_TRITS_PER_WORD + i;
     const uint32_t q3 = v / 3u;
     if (kk < k) out[kk] = static_cast<int8_t>(static_cast<int>(v - 3u * q3) - 1);
     v = q3;
@@ -210,7 +224,7 @@ int tq_pack(const int8_t* trits, int n, int k, int layout, uint32_t* words, void
   } else {
     const int nsl = slices_per_row(k), nb = row_blocks(n);
     hipLaunchKernelGGL(pack_row64_kernel, dim3(grid_for(static_cast<size_t>(nsl) * nb * kSliceQuads * 256)),
-                       dim3(256), 0, s, trits, n, k, wpr, nsl, nb, words);
+                       dim3(256), 0, s, trits, n, k, nsl, nb, words);
   }
   TQ_LAUNCH_CHECK();
   return TQ_OK;
@@ -240,7 +254,7 @@ int tq_unpack(const uint32_t* words, int n, int k, int layout, int8_t* trits, vo
   if (layout != TQ_LAYOUT_ROWMAJOR && layout != TQ_LAYOUT_ROW64) return TQ_EINVAL;
   if (n <= 0 || k <= 0) return TQ_ESHAPE;
   if (layout == TQ_LAYOUT_ROW64 && k % TQ_GROUP) return TQ_ESHAPE;
-  const int wpr = words_per_row(k);
+  const int wpr = layout == TQ_LAYOUT_ROW64 ? slices_per_row(k) * kSliceWords : words_per_row(k);
   hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(static_cast<size_t>(n) * wpr)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), words, n, k, layout, wpr, row_blocks(n), trits);
   TQ_LAUNCH_CHECK();

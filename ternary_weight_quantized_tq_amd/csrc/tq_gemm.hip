@@ -68,7 +68,7 @@ struct GemmArgs {
   const _Float16* xh;
   const _Float16* xl;
   float* y;
-  int m, n, k, kpad, nb, nq, groups, mtiles, ntiles, steps, xcd_map;
+  int m, n, k, kpad, nb, groups, mtiles, ntiles, steps, xcd_map;
 };
 
 // Tile of this workgroup: all N tiles of an M tile on one XCD (workgroups
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
           word_offsets_s<2, false>(wv[j], o);  // no inline asm next to MFMAs
 #pragma unroll
           for (int h = 0; h < 5; ++h) {
-            const int kk = q * 80 + j * 20 + h * 4;
+            const int kk = 4 * row64_chunk(4 * q + j, h);  // trit offset in the 160-trit unit
             const _Float16 sc = kk < gsplit ? sa : sb;
             const half2_t s2 = {sc, sc};
             const half2_t lo = __builtin_bit_cast(
@@ -278,7 +278,6 @@ extern "C" int tq_gemm(const tq_weights* w, const void* x, int x_dtype, int m, f
   a.k = w->k;
   a.kpad = p.kpad;
   a.nb = row_blocks(w->n);
-  a.nq = quads_per_row(w->k);
   a.groups = w->k / TQ_GROUP;
   a.mtiles = p.mtiles;
   a.ntiles = p.ntiles;

@@ -55,7 +55,7 @@ struct GemvArgs {
   float* partial;           // [nsl][m][npad] (mode kPartial)
   int mode;                 // kDirect, kPartial or kAtomic (see finish())
   int x_dtype;
-  int n, k, nq, groups, nb, npad, nsl;
+  int n, k, groups, nb, npad, nsl;
   int fused;
 };
 
@@ -86,7 +86,7 @@ __device__ __forceinline__ Tile make_tile(const GemvArgs& a) {
   t.rb = t.rg * t.waves + t.wave;
   t.active = t.rb < a.nb;
   t.rbc = t.active ? t.rb : a.nb - 1;
-  t.nq_here = min(kSliceQuads, a.nq - t.slice * kSliceQuads);
+  t.nq_here = row64_slice_quads(a.k, t.slice);
   t.k0 = t.slice * kSliceTrits;
   return t;
 }
@@ -171,13 +171,17 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
 }
 
 // ------------------------------------------------------------ M == 1 ---
+// Slice chunk (0..159, trits 4p .. 4p + 3 of the slice) held by chunk h of
+// slice word w in the ROW64 layout.
+__host__ __device__ constexpr int slice_chunk(int w, int h) { return 40 * (w >> 3) + row64_chunk(w & 7, h); }
+
 // Table values of the five chunks of word w (0..31) of the slice.
 __device__ __forceinline__ void word_lookups(const float* lut, uint32_t word, int w, float (&v)[5]) {
   uint32_t o[5];
   word_offsets(word, o);
 #pragma unroll
   for (int h = 0; h < 5; ++h) {
-    const int p = w * 5 + h;  // chunk position in the slice, compile-time after unrolling
+    const int p = slice_chunk(w, h);  // compile-time after unrolling
     v[h] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + p * kLutEntries * 4 + o[h]);
   }
 }
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a)
         word_lookups(lut, wn, w + 2, v[(w + 2) % 3]);
       }
 #pragma unroll
-      for (int h = 0; h < 5; ++h) acc[(w * 5 + h) / 32] += v[w % 3][h];
+      for (int h = 0; h < 5; ++h) acc[slice_chunk(w, h) / 32] += v[w % 3][h];
       if ((w & 3) == 3) TQ_ORDER();
     }
   } else {
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a)
 #pragma unroll
         for (int j = 0; j < 4; ++j) word_lookups(lut, wv[j], i * 4 + j, *reinterpret_cast<float(*)[5]>(&v[j * 5]));
 #pragma unroll
-        for (int c = 0; c < 20; ++c) acc[(i * 20 + c) / 32] += v[c];
+        for (int c = 0; c < 20; ++c) acc[slice_chunk(4 * i + c / 5, c % 5) / 32] += v[c];
       }
       TQ_ORDER();
     }
@@ -295,28 +299,17 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a)
 // [2^13, 2^14)) is split into p = 0: its fp16 rounding and p = 1: the fp16
 // rounding of the remainder, so the 16 A rows carry all eight activation
 // rows at about 22 significant bits and no fp16 overflow or underflow.
-// K is permuted so that every lane decodes whole words of its own row:
-//   lane l, j = l % 16, kb = l / 16 (0..3), row quarter h (0..3): output
-//   row 64 rb + 16 h + j; in unit u (0..3) = quads 2u, 2u + 1 of the slice
-//   the lane owns words 2 kb, 2 kb + 1 of the unit's eight, and step s
-//   (0..4) covers trits 160 u + 40 kb + 8 s .. + 7.
-// A word gives five 4-trit chunks; an 81-entry LDS table maps a chunk to
+// Lane l, j = l % 16, kb = l / 16 (0..3), row quarter h (0..3) of the
+// wavefront's 64-row block: output row 64 rb + 16 h + j.  In unit u (0..3,
+// quads 2u and 2u + 1 of the slice) the lane decodes the unit's words 2 kb,
+// 2 kb + 1 of its row; by the ROW64 chunk order (row64_chunk) their ten
+// chunks are, in digit order, the chunk pairs that step s (0..4) needs:
+// trits 160 u + 32 s + 8 kb .. + 7.  An 81-entry LDS table maps a chunk to
 // its four fp16 codes (d - 1), so B costs one 8-byte table read per chunk.
-// An MFMA sums over the four lane groups, whose trits may lie in two scale
-// groups: such steps are issued twice, each time with the activations of
-// the lanes in the other scale group read as zero.  Sums are kept per scale
-// group (two in flight) and scaled by the row's FP32 scale when complete.
+// A step covers 32 consecutive trits and never crosses a scale group: sums
+// are scaled by the row's FP32 scale every four steps.
 // Lane l ends with D rows 4 kb .. 4 kb + 3: both parts of activation rows
 // 2 kb and 2 kb + 1.
-__host__ __device__ constexpr int mfma_group(int u, int s, int kb) { return (160 * u + 40 * kb + 8 * s) / 128; }
-__host__ __device__ constexpr int mfma_gmin(int u, int s) { return mfma_group(u, s, 0); }
-__host__ __device__ constexpr int mfma_gmax(int u, int s) { return mfma_group(u, s, 3); }
-// Lane groups kb whose trits of step (u, s) lie in the lower scale group.
-__host__ __device__ constexpr int mfma_lo_mask(int u, int s) {
-  return (mfma_group(u, s, 0) == mfma_gmin(u, s) ? 1 : 0) | (mfma_group(u, s, 1) == mfma_gmin(u, s) ? 2 : 0) |
-         (mfma_group(u, s, 2) == mfma_gmin(u, s) ? 4 : 0) | (mfma_group(u, s, 3) == mfma_gmin(u, s) ? 8 : 0);
-}
-
 __device__ __forceinline__ uint2 load_pair(const uint32_t* p) {
   typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
   const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
@@ -335,6 +328,7 @@ __device__ __forceinline__ float wave_max(float v, int lane) {
 
 constexpr int kMfmaMaxWaves = 9;  // 3 per SIMD at most: ~168 registers per lane
 constexpr int kXStride = kSliceTrits + 8;
+constexpr int kMfmaLookahead = 10;  // of 16 word pairs per lane: weights in flight during the prologue
 
 template <int M, int XT>
 __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs a) {
@@ -369,13 +363,13 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
   auto pair_at = [&](int it) { return wbase + ((2 * (it / 4)) * 64 + 16 * (it % 4)) * 4; };  // it = 4 u + h
   uint2 wq[kIters];
 #pragma unroll
-  for (int i = 0; i < kLookahead; ++i) wq[i] = load_pair(pair_at(i));
+  for (int i = 0; i < kMfmaLookahead; ++i) wq[i] = load_pair(pair_at(i));
   TQ_ORDER();
   // The block's 5 x 64 scales (640 contiguous bytes) in one 16-byte load by
   // lanes 0..39, staged in LDS; each lane needs 20 of them at stride 32 B.
-  uint4 scq = make_uint4(0, 0, 0, 0);
-  if (t.lane < kSliceGroups * 8)
-    scq = *reinterpret_cast<const uint4*>(a.scales + row64_scale_base(t.slice, t.rbc, a.nb) + 8 * t.lane);
+  // (Every lane loads: a load under a lane condition is waited for at once.)
+  const int sl = t.lane < kSliceGroups * 8 ? t.lane : 0;
+  const uint4 scq = *reinterpret_cast<const uint4*>(a.scales + row64_scale_base(t.slice, t.rbc, a.nb) + 8 * sl);
   TQ_ORDER();
 
   for (int e = t.tid; e < kLutEntries; e += blockDim.x) {
@@ -389,7 +383,6 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
     codes[e] = make_uint2(hv[0] | (static_cast<uint32_t>(hv[1]) << 16), hv[2] | (static_cast<uint32_t>(hv[3]) << 16));
   }
   for (int i = t.tid; i < kSliceTrits; i += blockDim.x) zeros[i] = static_cast<_Float16>(0.0f);
-  if (t.lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[t.wave][8 * t.lane]) = scq;
   for (int m = t.wave; m < M; m += t.waves) {
     if (m != t.wave) {
 #pragma unroll
@@ -420,6 +413,8 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
     }
     if (t.lane == 0) xexp[m] = e;
   }
+  // Stored after the transform, which then waits for the activations only.
+  if (t.lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[t.wave][8 * t.lane]) = scq;
   TQ_LDS_BARRIER();
 
   float sc[4][kSliceGroups];
@@ -431,18 +426,16 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
       sc[h][g] = t.active ? v : 0.0f;
     }
 
-  // This lane's A row (part j % 2 of activation row j / 2, its 40-trit part
-  // of each unit), or the zero row past the M activation rows.
-  const _Float16* xrow = (j < 2 * M ? &xh[j < 2 * M ? j : 0][0] : &zeros[0]) + 40 * kb;
-  const _Float16* zrow = &zeros[0] + 40 * kb;
+  // This lane's A row (part j % 2 of activation row j / 2, at its 8-trit
+  // offset of each step), or the zero row past the M activation rows.
+  const _Float16* xrow = (j < 2 * M ? &xh[j < 2 * M ? j : 0][0] : &zeros[0]) + 8 * kb;
   const char* cbase = reinterpret_cast<const char*>(codes);
 
-  float4_t acc[4][2];
+  float4_t acc[4];
   float tot[4][4];
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    acc[h][0] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    acc[h][1] = acc[h][0];
+    acc[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int v = 0; v < 4; ++v) tot[h][v] = 0.0f;
   }
@@ -450,22 +443,13 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
   // four quarters' independent accumulation chains.
 #pragma unroll
   for (int u = 0; u < kUnits; ++u) {
-    half8_t af[5], al[5], ah[5];
+    half8_t af[5];
 #pragma unroll
-    for (int s = 0; s < 5; ++s) {
-      const int koff = 160 * u + 8 * s;
-      if (mfma_gmin(u, s) == mfma_gmax(u, s)) {
-        af[s] = *reinterpret_cast<const half8_t*>(xrow + koff);
-      } else {
-        const bool lo = ((mfma_lo_mask(u, s) >> kb) & 1) != 0;
-        al[s] = *reinterpret_cast<const half8_t*>((lo ? xrow : zrow) + koff);
-        ah[s] = *reinterpret_cast<const half8_t*>((lo ? zrow : xrow) + koff);
-      }
-    }
+    for (int s = 0; s < 5; ++s) af[s] = *reinterpret_cast<const half8_t*>(xrow + 160 * u + 32 * s);
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const int it = u * 4 + h;
-      if (it + kLookahead < kIters) wq[it + kLookahead] = load_pair(pair_at(it + kLookahead));
+      if (it + kMfmaLookahead < kIters) wq[it + kMfmaLookahead] = load_pair(pair_at(it + kMfmaLookahead));
       uint32_t o[10];
       word_offsets_s<3, false>(wq[it].x, o);
       word_offsets_s<3, false>(wq[it].y, o + 5);
@@ -474,22 +458,13 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
       for (int c = 0; c < 10; ++c) cv[c] = *reinterpret_cast<const uint2*>(cbase + o[c]);
 #pragma unroll
       for (int s = 0; s < 5; ++s) {
-        const int gl = mfma_gmin(u, s), gh = mfma_gmax(u, s);
-        if (u > 0 || s > 0) {
-          const int pgl = s > 0 ? mfma_gmin(u, s - 1) : mfma_gmin(u - 1, 4);
-          if (gl > pgl) {  // every lane group has left scale group pgl: it is complete
-#pragma unroll
-            for (int v = 0; v < 4; ++v) tot[h][v] = fmaf(sc[h][pgl], acc[h][pgl & 1][v], tot[h][v]);
-            acc[h][pgl & 1] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-          }
-        }
+        const int step = 5 * u + s;  // scale group step / 4
         const uint4 bq = make_uint4(cv[2 * s].x, cv[2 * s].y, cv[2 * s + 1].x, cv[2 * s + 1].y);
-        const half8_t bf = __builtin_bit_cast(half8_t, bq);
-        if (gl == gh) {
-          acc[h][gl & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s], bf, acc[h][gl & 1], 0, 0, 0);
-        } else {
-          acc[h][gl & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[s], bf, acc[h][gl & 1], 0, 0, 0);
-          acc[h][gh & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[s], bf, acc[h][gh & 1], 0, 0, 0);
+        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s], __builtin_bit_cast(half8_t, bq), acc[h], 0, 0, 0);
+        if ((step & 3) == 3) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) tot[h][v] = fmaf(sc[h][step >> 2], acc[h][v], tot[h][v]);
+          acc[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
         }
       }
     }
@@ -503,9 +478,6 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
   for (int q = 0; q < 2; ++q) mexp[q] = mrow[q] < M ? -xexp[mrow[q] < M ? mrow[q] : 0] : 0;
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    constexpr int glast = mfma_gmin(kUnits - 1, 4);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) tot[h][v] = fmaf(sc[h][glast], acc[h][glast & 1][v], tot[h][v]);
     const int row = t.rb * 64 + 16 * h + j;
     if (t.active && row < a.n) {
 #pragma unroll
@@ -619,7 +591,6 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
   a.x_dtype = x_dtype;
   a.n = w->n;
   a.k = w->k;
-  a.nq = quads_per_row(w->k);
   a.groups = w->k / TQ_GROUP;
   a.nb = p.nb;
   a.npad = p.npad;

@@ -22,7 +22,6 @@ constexpr int kSliceQuads = 8;
 constexpr int kSliceGroups = 5;
 
 __host__ __device__ inline int words_per_row(int k) { return (k + TQ_TRITS_PER_WORD - 1) / TQ_TRITS_PER_WORD; }
-__host__ __device__ inline int quads_per_row(int k) { return (words_per_row(k) + 3) / 4; }
 __host__ __device__ inline int row_blocks(int n) { return (n + 63) / 64; }
 __host__ __device__ inline int slices_per_row(int k) { return (words_per_row(k) + kSliceWords - 1) / kSliceWords; }
 
@@ -46,6 +45,12 @@ __host__ __device__ inline size_t row64_quad_base(int s, int b, int nb) {
 }
 __host__ __device__ inline size_t row64_scale_base(int s, int b, int nb) {
   return (static_cast<size_t>(s) * nb + b) * kSliceGroups * 64;
+}
+// Quads of slice s that hold trits below k: whole 160-trit units (a unit's
+// chunks are reordered within it, see row64_chunk), 2 quads each.
+__host__ __device__ inline int row64_slice_quads(int k, int s) {
+  const int rem = k - s * kSliceTrits;
+  return rem >= kSliceTrits ? kSliceQuads : 2 * ((rem + 159) / 160);
 }
 
 // ------------------------------------------------------ element loads ---

@@ -139,30 +139,50 @@ __device__ __forceinline__ void transform_row_f16(_Float16* dst, int len, int dl
 }
 
 // Accumulate one 640-trit slice of R rows per lane against M activation rows.
-// words[r][i]: quad i of row r for this lane; sc[r][g]: scales; xs: LDS fp16
-// activations of the slice, row stride xstride (elements).
+// wp[r]: this lane's quad 0 of the slice for row r (quads 64 apart); nq_here:
+// quads holding trits below K (whole units); sc[r][g]: scales; xs: LDS fp16
+// activations of the slice, row stride xstride (elements).  A 160-trit unit
+// (quads 2u, 2u + 1, loaded one unit ahead) spans scale groups g0 = 5u / 4
+// and g0 + 1; its chunks come in ROW64 order, so each is summed into the
+// accumulator of its group and both are scaled at the end of the unit.
 template <int M, int R>
-__device__ __forceinline__ void slice_dot2(const uint4 (&wq)[R][kSliceQuads], const float (&sc)[R][kSliceGroups],
+__device__ __forceinline__ void slice_dot2(const uint4* const (&wp)[R], const float (&sc)[R][kSliceGroups],
                                            int nq_here, const _Float16* xs, int xstride, const uint32_t* codes_lo,
                                            const uint32_t* codes_hi, float (&tot)[R][M]) {
-  float acc[R][M];
+  uint4 cur[R][2];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+    for (int q = 0; q < 2; ++q) cur[r][q] = wp[r][q * 64];
 #pragma unroll
-  for (int i = 0; i < kSliceQuads; ++i) {
-    if (i < nq_here) {
+  for (int u = 0; u < kSliceQuads / 2; ++u) {
+    if (2 * u < nq_here) {
+      uint4 nxt[R][2];
+      if (u + 1 < kSliceQuads / 2) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) nxt[r][q] = wp[r][min(2 * u + 2 + q, nq_here - 1) * 64];
+      }
+      float acc[R][M][2];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m][0] = acc[r][m][1] = 0.0f;
+      const int g0 = (5 * u) / 4;
+#pragma unroll
+      for (int wl = 0; wl < 8; ++wl) {
+        const int j = wl & 3;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const uint32_t wv = j == 0 ? wq[r][i].x : j == 1 ? wq[r][i].y : j == 2 ? wq[r][i].z : wq[r][i].w;
+          const uint4 qv = cur[r][wl >> 2];
+          const uint32_t wv = j == 0 ? qv.x : j == 1 ? qv.y : j == 2 ? qv.z : qv.w;
           uint32_t o[5];
           word_offsets(wv, o);
 #pragma unroll
           for (int hh = 0; hh < 5; ++hh) {
-            const int p = i * 20 + j * 5 + hh;
+            const int p = 40 * u + row64_chunk(wl, hh);  // chunk of the slice
+            const int gi = p / 32 - g0;
             const half2_t lo = __builtin_bit_cast(
                 half2_t, *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(codes_lo) + o[hh]));
             const half2_t hi = __builtin_bit_cast(
@@ -170,20 +190,24 @@ __device__ __forceinline__ void slice_dot2(const uint4 (&wq)[R][kSliceQuads], co
 #pragma unroll
             for (int m = 0; m < M; ++m) {
               const uint2 xv = *reinterpret_cast<const uint2*>(xs + m * xstride + 4 * p);
-              float t = acc[r][m];
+              float t = acc[r][m][gi];
               t = __builtin_amdgcn_fdot2(lo, __builtin_bit_cast(half2_t, xv.x), t, false);
               t = __builtin_amdgcn_fdot2(hi, __builtin_bit_cast(half2_t, xv.y), t, false);
-              acc[r][m] = t;
-            }
-            if ((p + 1) % 32 == 0) {  // end of a scale group
-#pragma unroll
-              for (int m = 0; m < M; ++m) {
-                tot[r][m] = fmaf(sc[r][p / 32], acc[r][m], tot[r][m]);
-                acc[r][m] = 0.0f;
-              }
+              acc[r][m][gi] = t;
             }
           }
         }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+          tot[r][m] = fmaf(sc[r][g0], acc[r][m][0], fmaf(sc[r][g0 + 1], acc[r][m][1], tot[r][m]));
+      if (u + 1 < kSliceQuads / 2) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) cur[r][q] = nxt[r][q];
       }
     }
   }
@@ -204,15 +228,6 @@ __device__ __forceinline__ void build_codes(uint32_t* codes_lo, uint32_t* codes_
   }
 }
 
-// Loads the 8 quads of slice s of one ROW64 row block of one expert
-// (clamped to the last valid quad of the row).
-__device__ __forceinline__ void load_quads(const uint4* w, int nq, int nb, int rb, int lane, int s,
-                                           uint4 (&dst)[kSliceQuads]) {
-  const int nh = min(kSliceQuads, nq - s * kSliceQuads);
-  const uint4* wp = w + row64_quad_base(s, rb, nb) + lane;
-#pragma unroll
-  for (int i = 0; i < kSliceQuads; ++i) dst[i] = wp[min(i, nh - 1) * 64];
-}
 __device__ __forceinline__ void load_scales(const uint16_t* sbase, int nb, int rb, int lane, int s,
                                             float (&dst)[kSliceGroups]) {
   const uint16_t* sp = sbase + row64_scale_base(s, rb, nb) + lane;
@@ -226,7 +241,7 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs& a, int e, int b, con
                                              float* red, const uint32_t* codes_lo, const uint32_t* codes_hi) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int K = a.hidden;
-  const int nq = quads_per_row(K), nslices = slices_per_row(K), nb = row_blocks(2 * a.inter);
+  const int nslices = slices_per_row(K), nb = row_blocks(2 * a.inter);
   const int xstride = nslices * kSliceTrits;
   const uint4* wbase = a.gu_words + static_cast<size_t>(e) * a.gu_wstride;
   const uint16_t* sbase = a.gu_scales + static_cast<size_t>(e) * a.gu_sstride;
@@ -237,14 +252,24 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs& a, int e, int b, con
 #pragma unroll
     for (int m = 0; m < M; ++m) tot[r][m] = 0.0f;
   for (int s = wave; s < nslices; s += 4) {
-    uint4 wq[2][kSliceQuads];
-    float sc[2][kSliceGroups];
-    load_quads(wbase, nq, nb, rb_gate, lane, s, wq[0]);
-    load_quads(wbase, nq, nb, rb_up, lane, s, wq[1]);
-    load_scales(sbase, nb, rb_gate, lane, s, sc[0]);
-    load_scales(sbase, nb, rb_up, lane, s, sc[1]);
-    slice_dot2<M, 2>(wq, sc, min(kSliceQuads, nq - s * kSliceQuads), xh + s * kSliceTrits, xstride, codes_lo,
-                     codes_hi, tot);
+    // Gate row, then up row (two accumulators per activation row and unit
+    // leave no room for both rows at once).
+    const int nh = row64_slice_quads(K, s);
+    {
+      float sc[1][kSliceGroups];
+      const uint4* const wp[1] = {wbase + row64_quad_base(s, rb_gate, nb) + lane};
+      load_scales(sbase, nb, rb_gate, lane, s, sc[0]);
+      slice_dot2<M, 1>(wp, sc, nh, xh + s * kSliceTrits, xstride, codes_lo, codes_hi,
+                       *reinterpret_cast<float(*)[1][M]>(&tot[0][0]));
+    }
+    asm volatile("" ::: "memory");
+    {
+      float sc[1][kSliceGroups];
+      const uint4* const wp[1] = {wbase + row64_quad_base(s, rb_up, nb) + lane};
+      load_scales(sbase, nb, rb_up, lane, s, sc[0]);
+      slice_dot2<M, 1>(wp, sc, nh, xh + s * kSliceTrits, xstride, codes_lo, codes_hi,
+                       *reinterpret_cast<float(*)[1][M]>(&tot[1][0]));
+    }
   }
   // red[w][r][m][lane]; slices summed in wavefront order.
 #pragma unroll
@@ -308,7 +333,7 @@ __device__ __forceinline__ void down_tile(const MoeArgs& a, int e, int rb, const
                                           const uint32_t* codes_lo, const uint32_t* codes_hi) {
   const int lane = threadIdx.x & 63;
   const int K = a.inter;
-  const int nq = quads_per_row(K), nslices = slices_per_row(K);
+  const int nslices = slices_per_row(K);
   const int xstride = nslices * kSliceTrits;
   const int nb = row_blocks(a.hidden);
   if (rb >= nb) return;
@@ -318,11 +343,11 @@ __device__ __forceinline__ void down_tile(const MoeArgs& a, int e, int rb, const
 #pragma unroll
   for (int m = 0; m < M; ++m) tot[0][m] = 0.0f;
   for (int s = 0; s < nslices; ++s) {
-    uint4 wq[1][kSliceQuads];
     float sc[1][kSliceGroups];
-    load_quads(wbase, nq, nb, rb, lane, s, wq[0]);
+    const int nh = row64_slice_quads(K, s);
+    const uint4* const wp[1] = {wbase + row64_quad_base(s, rb, nb) + lane};
     load_scales(sbase, nb, rb, lane, s, sc[0]);
-    slice_dot2<M, 1>(wq, sc, min(kSliceQuads, nq - s * kSliceQuads), xh + s * kSliceTrits, xstride, codes_lo,
+    slice_dot2<M, 1>(wp, sc, nh, xh + s * kSliceTrits, xstride, codes_lo,
                      codes_hi, tot);
   }
   const int row = rb * 64 + lane;

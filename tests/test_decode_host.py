@@ -60,3 +60,43 @@ def test_word_decoder_exhaustive():
         subprocess.run(["g++", "-O2", "-std=c++17", f"-I{CSRC}", src, "-o", exe], check=True)
         p = subprocess.run([exe], capture_output=True, text=True, timeout=600)
         assert p.returncode == 0 and p.stdout.strip() == "0", p.stdout + p.stderr
+
+
+CHUNK_PROG = r'''
+#include <stdio.h>
+#include "tq_decode.h"
+using namespace tq;
+int main() {
+  for (int wl = 0; wl < 8; ++wl)
+    for (int j = 0; j < 5; ++j) {
+      const int c = row64_chunk(wl, j);
+      printf("%d %d %d %d\n", c, row64_chunk_word(c), row64_chunk_index(c), wl * 5 + j);
+    }
+  return 0;
+}
+'''
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_row64_chunk_order():
+    """The kernels' ROW64 chunk order is a permutation of a unit's 40 chunks,
+    its inverse is exact, it equals the test-side definition, and every
+    32-trit step 32s .. 32s + 31 is made of chunk pairs (8s + 2kb, +1) that
+    sit in digit order in words 2kb, 2kb + 1 (one scale group per step)."""
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from tqgpu import row64_chunk
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "c.cpp")
+        exe = os.path.join(d, "c")
+        open(src, "w").write(CHUNK_PROG)
+        subprocess.run(["g++", "-O2", "-std=c++17", f"-I{CSRC}", src, "-o", exe], check=True)
+        rows = [list(map(int, l.split())) for l in subprocess.run([exe], capture_output=True, text=True,
+                                                                    check=True).stdout.split("\n") if l]
+    assert sorted(r[0] for r in rows) == list(range(40))
+    for c, wl, j, idx in rows:
+        assert (wl, j) == divmod(idx, 5)
+        assert c == row64_chunk(wl, j)
+    for kb in range(4):
+        digits = [row64_chunk(2 * kb + h, j) for h in range(2) for j in range(5)]
+        assert digits == [8 * s + 2 * kb + e for s in range(5) for e in range(2)]

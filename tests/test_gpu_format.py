@@ -9,7 +9,7 @@ import ternary_weight_quantized_tq_amd as tq
 from oracle import tq_oracle as O
 
 from tqgpu import (ZERO_WORD, act_tensor, dev, gpu_pack, gpu_quantize, host_f16, host_u32, row64_scales_to_rowmajor,
-                   row64_to_rowmajor, torch)
+                   row64_to_rowmajor, row64_word_order, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,12 +36,9 @@ def test_pack_row64_layout(n, k):
     t = synth.trits(20 + n + k, n, k)
     s = synth.scales(21 + n, n, k // 128)
     w = gpu_pack(t, s, tq.TQ_LAYOUT_ROW64)
-    words = host_u32(w.words)
-    canon, full = row64_to_rowmajor(words, n, k)
-    assert np.array_equal(canon, O.pack(t))
-    pad = np.ones(full.shape, bool)
-    pad[:n, :canon.shape[1]] = False
-    assert np.all(full[pad] == ZERO_WORD)
+    full = row64_to_rowmajor(host_u32(w.words), n, k)
+    assert np.array_equal(full[:n], O.pack(row64_word_order(t)))
+    assert np.all(full[n:] == ZERO_WORD)
     sc = host_f16(w.scales)
     sc_canon, sc_full = row64_scales_to_rowmajor(sc, n, k)
     assert np.array_equal(sc_canon.view(np.uint16), s.view(np.uint16))

@@ -80,15 +80,38 @@ def run_gemv(w: tq.Weights, x, m: int, fused=True) -> np.ndarray:
     return y.cpu().numpy().astype(np.float64)
 
 
-def row64_to_rowmajor(words: np.ndarray, n: int, k: int):
-    """Re-index ROW64 words into [n][ceil(k/20)] per the layout definition in
-    tq.h: word (((s*nb + b)*8 + qi)*64 + r)*4 + j is word 32s + 4qi + j of
-    row 64b + r.  Returns (canonical view, full padded [nb*64][nsl*32])."""
-    wpr = -(-k // 20)
-    nsl = -(-wpr // 32)
+def row64_to_rowmajor(words: np.ndarray, n: int, k: int) -> np.ndarray:
+    """Re-index ROW64 words per the layout definition in tq.h: word
+    (((s*nb + b)*8 + qi)*64 + r)*4 + j is word 32s + 4qi + j of row 64b + r.
+    Returns [nb*64][nsl*32] (padding included)."""
+    nsl = -(-k // 640)
     nb = -(-n // 64)
-    a = words.reshape(nsl, nb, 8, 64, 4).transpose(1, 3, 0, 2, 4).reshape(nb * 64, nsl * 32)
-    return a[:n, :wpr], a
+    return words.reshape(nsl, nb, 8, 64, 4).transpose(1, 3, 0, 2, 4).reshape(nb * 64, nsl * 32)
+
+
+def row64_chunk(wl: int, j: int) -> int:
+    """Unit chunk held by chunk j (digits 4j..4j+3) of unit word wl, per the
+    ROW64 chunk order in tq.h: q = 5 (wl % 2) + j, c = 8 (q // 2) + 2 (wl // 2) + q % 2."""
+    q = 5 * (wl % 2) + j
+    return 8 * (q // 2) + 2 * (wl // 2) + q % 2
+
+
+def row64_word_order(t: np.ndarray) -> np.ndarray:
+    """Trits [n][k] rearranged so that trits 20w .. 20w + 19 are the digits of
+    ROW64 word w of the row (w = 32s + 8u + wl, unit u of slice s), zero trits
+    past k: packing this array row by row gives the ROW64 word values.  Index
+    bookkeeping only."""
+    n, k = t.shape
+    nsl = -(-k // 640)
+    src = np.empty(nsl * 640, np.int64)
+    for w in range(nsl * 32):
+        base = 640 * (w // 32) + 160 * ((w % 32) // 8)
+        for j in range(5):
+            c = row64_chunk(w % 8, j)
+            src[20 * w + 4 * j: 20 * w + 4 * j + 4] = base + 4 * c + np.arange(4)
+    padded = np.zeros((n, nsl * 640), np.int8)
+    padded[:, :k] = t
+    return padded[:, src]
 
 
 def row64_scales_to_rowmajor(s: np.ndarray, n: int, k: int) -> np.ndarray:
