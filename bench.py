@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-extras", action="store_true", help="only the main metric")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--only-extra", choices=["block_m8", "moe", "prefill_gemm"],
+                   help="run one extra workload alone and print its JSON (for profiling)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy (for scaling rocprofv3 byte counters)")
     return p.parse_args()
@@ -266,6 +268,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
+    if args.only_extra:
+        fn = {"block_m8": extra_block_m8, "moe": extra_moe, "prefill_gemm": extra_gemm}[args.only_extra]
+        print(json.dumps({args.only_extra: fn(tq, torch, synth, np)}), flush=True)
+        return
+
     if args.copy_calibration:
         src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -342,6 +349,19 @@ def main():
             b.record()
             torch.cuda.synchronize()
             mean_us.append(1e3 * a.elapsed_time(b) / copies)
+    # Context for the roofline: a plain device copy moving the same bytes per
+    # launch (half read, half written), timed the same way, sources rotated.
+    half = lin_bytes[0] // 8
+    srcs = [sets[i][0].words.view(-1)[:half] for i in range(copies)]
+    dst = torch.empty(half, dtype=srcs[0].dtype, device="cuda")
+    cg = capture(torch, copies, lambda i: dst.copy_(srcs[i]))
+    cg.replay()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    cg.replay()
+    b.record()
+    torch.cuda.synchronize()
+    copy_us = 1e3 * a.elapsed_time(b) / copies
     gbs = step_bytes / (ms * 1e-3) / 1e9
     kern_gbs = sum(lin_bytes) / (sum(mean_us) * 1e-6) / 1e9
     traffic = measured_traffic()
@@ -367,6 +387,9 @@ def main():
         "frac_hbm_peak_step": round(gbs / HBM_PEAK_GBS, 4),
         "kernel_us": {l.name: round(u, 3) for l, u in zip(lins, mean_us)},
         "kernel_timing": kernel_timing,
+        "plain_copy_same_bytes": {"bytes_moved": 8 * half, "us": round(copy_us, 3),
+                                  "gb_s": round(8 * half / (copy_us * 1e-6) / 1e9, 1),
+                                  "frac_hbm_peak": round(8 * half / (copy_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic)},
