@@ -175,7 +175,9 @@ int tq_fwht(const void *x, int x_dtype, int m, int k, float *x_rot,
  * has TQ_FWHT_FUSED else x (with TQ_ACCUMULATE: y += ...).  w: ROW64
  * layout, num_experts == 1.  x: [m][k] of x_dtype (F32/BF16/F16); y: FP32
  * [m][n].  m == 1 accumulates in FP32 throughout; m >= 2 multiplies fp16
- * trit codes by the fp16-rounded x' with FP32 accumulation.  Unless
+ * trit codes by x' split into two fp16 parts (about 22 significant bits,
+ * after a power-of-two scaling per activation row and 640-trit slice) with
+ * FP32 accumulation.  Unless
  * TQ_ACCUMULATE is set, needs a workspace of tq_workspace_bytes(TQ_OP_GEMV,
  * w, m, 0) bytes (0 when K <= 640).  One launch, plus a short reduction
  * launch when K > 640 and TQ_ACCUMULATE is not set. */
@@ -196,7 +198,10 @@ int tq_moe_route(const float *logits, int t, int e, int topk, int32_t *ids,
  *     o    = W_dn[e] . H h
  *   y[i] = sum_j route_w[i][j] * o.
  * w_gate_up: E experts of n = 2I, k = Hd; w_down: E experts of n = Hd,
- * k = I; both ROW64.  x: [t][Hd] of x_dtype; y FP32 [t][Hd].  Only the
+ * k = I; both ROW64 (I % 64 == 0, Hd and I multiples of 128).  x: [t][Hd]
+ * of x_dtype; y FP32 [t][Hd].  The expert products use the m >= 2 decode
+ * GEMV arithmetic (fp16 codes, x' and H h as two fp16 parts, FP32
+ * accumulation), up to 8 tokens of an expert at a time.  Only the
  * experts that receive tokens are read.  Ids outside [0, E) are an error
  * detected on the device: such slots contribute nothing.  Needs
  * tq_workspace_bytes(TQ_OP_MOE, w_gate_up, t, topk) bytes of workspace. */

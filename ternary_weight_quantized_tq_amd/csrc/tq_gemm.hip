@@ -31,8 +31,6 @@ constexpr int BK = 160;         // trits per K step = 2 quads = 8 words
 constexpr int LDA = BK + 8;     // padded LDS row stride (halves) against bank conflicts
 constexpr int kThreads = 256;
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
 #define TQ_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")

@@ -42,9 +42,6 @@ constexpr int kLutEntries = 81;
 constexpr int kMaxWaves = 16;
 constexpr int kLookahead = 3;
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 struct GemvArgs {
@@ -310,22 +307,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a)
 // are scaled by the row's FP32 scale every four steps.
 // Lane l ends with D rows 4 kb .. 4 kb + 3: both parts of activation rows
 // 2 kb and 2 kb + 1.
-__device__ __forceinline__ uint2 load_pair(const uint32_t* p) {
-  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
-  return make_uint2(v.x, v.y);
-}
-
-// Maximum of v over the wavefront (every lane gets it).
-__device__ __forceinline__ float wave_max(float v, int lane) {
-  v = fmaxf(v, lane_xor_f32<1>(v, lane));
-  v = fmaxf(v, lane_xor_f32<2>(v, lane));
-  v = fmaxf(v, lane_xor_f32<4>(v, lane));
-  v = fmaxf(v, lane_xor_f32<8>(v, lane));
-  v = fmaxf(v, lane_xor_f32<16>(v, lane));
-  return fmaxf(v, lane_xor_f32<32>(v, lane));
-}
-
 constexpr int kMfmaMaxWaves = 9;  // 3 per SIMD at most: ~168 registers per lane
 constexpr int kXStride = kSliceTrits + 8;
 constexpr int kMfmaLookahead = 10;  // of 16 word pairs per lane: weights in flight during the prologue
@@ -372,16 +353,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
   const uint4 scq = *reinterpret_cast<const uint4*>(a.scales + row64_scale_base(t.slice, t.rbc, a.nb) + 8 * sl);
   TQ_ORDER();
 
-  for (int e = t.tid; e < kLutEntries; e += blockDim.x) {
-    uint16_t hv[4];
-    int c = e;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      hv[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(static_cast<float>(c % 3) - 1.0f));
-      c /= 3;
-    }
-    codes[e] = make_uint2(hv[0] | (static_cast<uint32_t>(hv[1]) << 16), hv[2] | (static_cast<uint32_t>(hv[3]) << 16));
-  }
+  build_code_table(codes, t.tid, blockDim.x);
   for (int i = t.tid; i < kSliceTrits; i += blockDim.x) zeros[i] = static_cast<_Float16>(0.0f);
   for (int m = t.wave; m < M; m += t.waves) {
     if (m != t.wave) {
@@ -389,28 +361,14 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
       for (int r = 0; r < kSliceGroups; ++r) load_block_t<XT>(a, t, m, r, xv[r][0], xv[r][1], xok[r]);
     }
     if (a.fused) wave_fwht128_batch<kSliceGroups>(xv, t.lane, kInvSqrt128);
-    float mx = 0.0f;
 #pragma unroll
     for (int r = 0; r < kSliceGroups; ++r) {
       if (!xok[r]) {
         xv[r][0] = 0.0f;
         xv[r][1] = 0.0f;
       }
-      mx = fmaxf(mx, fmaxf(fabsf(xv[r][0]), fabsf(xv[r][1])));
     }
-    mx = wave_max(mx, t.lane);
-    // max |x'| 2^e in [2^13, 2^14): both fp16 parts stay normal and finite.
-    const int e = mx > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mx) : 0;
-#pragma unroll
-    for (int r = 0; r < kSliceGroups; ++r) {
-      const float s0 = ldexpf(xv[r][0], e), s1 = ldexpf(xv[r][1], e);
-      const _Float16 h0 = static_cast<_Float16>(s0), h1 = static_cast<_Float16>(s1);
-      const half2_t hv = {h0, h1};
-      const half2_t lv = {static_cast<_Float16>(s0 - static_cast<float>(h0)),
-                          static_cast<_Float16>(s1 - static_cast<float>(h1))};
-      *reinterpret_cast<half2_t*>(&xh[2 * m][r * 128 + 2 * t.lane]) = hv;
-      *reinterpret_cast<half2_t*>(&xh[2 * m + 1][r * 128 + 2 * t.lane]) = lv;
-    }
+    const int e = split_two_fp16<kSliceGroups>(xv, t.lane, &xh[2 * m][0], &xh[2 * m + 1][0]);
     if (t.lane == 0) xexp[m] = e;
   }
   // Stored after the transform, which then waits for the activations only.

@@ -162,6 +162,69 @@ __device__ __forceinline__ void wave_fwht128_batch(float (&v)[B][2], int lane, f
   }
 }
 
+// ------------------------------------------- matrix-core decode helpers ---
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// Two consecutive words, streamed once (non-temporal).
+__device__ __forceinline__ uint2 load_pair(const uint32_t* p) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+// Maximum of v over the wavefront (every lane gets it).
+__device__ __forceinline__ float wave_max(float v, int lane) {
+  v = fmaxf(v, lane_xor_f32<1>(v, lane));
+  v = fmaxf(v, lane_xor_f32<2>(v, lane));
+  v = fmaxf(v, lane_xor_f32<4>(v, lane));
+  v = fmaxf(v, lane_xor_f32<8>(v, lane));
+  v = fmaxf(v, lane_xor_f32<16>(v, lane));
+  return fmaxf(v, lane_xor_f32<32>(v, lane));
+}
+
+// Entry c of the 81-entry table of a 4-trit chunk: its four fp16 codes
+// (d_i - 1), digits 0, 1 in .x and 2, 3 in .y.
+__device__ __forceinline__ void build_code_table(uint2* codes, int tid, int nthreads) {
+  for (int e = tid; e < 81; e += nthreads) {
+    uint16_t hv[4];
+    int c = e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hv[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(static_cast<float>(c % 3) - 1.0f));
+      c /= 3;
+    }
+    codes[e] = make_uint2(hv[0] | (static_cast<uint32_t>(hv[1]) << 16), hv[2] | (static_cast<uint32_t>(hv[3]) << 16));
+  }
+}
+
+// A wavefront's NB transformed blocks of one activation row (lane l holds
+// elements 2l, 2l+1 of each) as the two fp16 parts of the matrix-core A
+// operand: with e from the wavefront maximum so that max |x'| 2^e lies in
+// [2^13, 2^14), hi = fp16(x' 2^e) and lo = fp16(x' 2^e - hi), both finite
+// and normal down to |x'| 2^e ~ 2^-3; together about 22 significant bits.
+// Writes hi[128 b + 2l], lo[128 b + 2l] (and + 1); returns e.
+template <int NB>
+__device__ __forceinline__ int split_two_fp16(const float (&xv)[NB][2], int lane, _Float16* hi, _Float16* lo) {
+  float mx = 0.0f;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) mx = fmaxf(mx, fmaxf(fabsf(xv[b][0]), fabsf(xv[b][1])));
+  mx = wave_max(mx, lane);
+  const int e = mx > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mx) : 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const float s0 = ldexpf(xv[b][0], e), s1 = ldexpf(xv[b][1], e);
+    const _Float16 h0 = static_cast<_Float16>(s0), h1 = static_cast<_Float16>(s1);
+    const half2_t hv = {h0, h1};
+    const half2_t lv = {static_cast<_Float16>(s0 - static_cast<float>(h0)),
+                        static_cast<_Float16>(s1 - static_cast<float>(h1))};
+    *reinterpret_cast<half2_t*>(hi + b * 128 + 2 * lane) = hv;
+    *reinterpret_cast<half2_t*>(lo + b * 128 + 2 * lane) = lv;
+  }
+  return e;
+}
+
 // ------------------------------------------------- fp16 bit patterns ---
 // Round a double to the nearest fp16 (ties to even) in a single rounding.
 __host__ __device__ inline uint16_t f64_to_f16_rne(double d) {

@@ -7,16 +7,20 @@
 //   1. bucket:   one workgroup groups the (token, slot) pairs by expert and
 //                lists the experts that received tokens (ascending id).
 //   2. gate/up:  grid (active expert slot, 64-row block of the intermediate
-//                dimension).  Lane r of every wavefront owns gate row 64b+r
-//                and up row I+64b+r of its expert; the four wavefronts split
-//                K (the hidden size) into 640-trit slices.  Tokens of the
-//                expert are processed 1..8 at a time against the block-128
-//                transformed activations (fp16, in LDS), accumulated with
-//                v_dot2_f32_f16 on fp16 trit codes; the slices are summed in
-//                LDS in a fixed order and h = silu(gate) * up is stored.
-//   3. down:     grid (active expert slot, 256-row group of the hidden
-//                size); the block-128 transform of h is fused in, and each
-//                (token, slot) pair's output row is stored.
+//                dimension, 640-trit slice of K = the hidden size).
+//                Wavefronts 0, 1 own the gate rows 64b..64b+63, 2, 3 the up
+//                rows I+64b.., each half of the slice's 160-trit units.
+//                Tokens of the expert go 1..8 at a time through the matrix
+//                cores as in the M >= 2 decode GEMV: the block-128
+//                transformed activations as two fp16 parts in the A rows (a
+//                power of two per token and slice keeps them in range),
+//                fp16 trit codes from an 81-entry table as B.  Each slice's
+//                partial sums are stored.
+//   3. down:     grid (active expert slot, 4 row blocks of the hidden size),
+//                one row block per wavefront, the same contraction; its
+//                prologue adds the gate/up slices in order, forms
+//                h = silu(gate) * up and applies the block-128 transform;
+//                each (token, slot) pair's output row is stored.
 //   4. combine:  y[t] = sum_j route_w[t][j] * o[t][j] in slot order.
 // Only experts that received tokens are read; every pair's arithmetic is
 // independent of which other pairs share its tile, so results do not depend
@@ -30,10 +34,8 @@ using namespace tq;
 namespace {
 
 constexpr int kTile = 8;          // tokens per pass
-constexpr int kMaxK = 4096;       // largest hidden / intermediate size held in LDS
 constexpr int kMaxExperts = 1024;
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 struct MoeArgs {
   const uint4* gu_words;
@@ -53,11 +55,12 @@ struct MoeArgs {
   int* active;       // [experts]   expert id of active slot a
   int* seg;          // [experts+1] pair range of slot a
   int* pairs;        // [t*topk]    pair indices grouped by expert
-  float* h;          // [t*topk][inter]
+  float* gu;         // gu_split: [gu_slices][t*topk][2*inter] gate/up partial sums per
+                     // hidden slice; otherwise [t*topk][inter] h = silu(gate) * up
+  int gu_slices, gu_split;
   float* o;          // [t*topk][hidden]
 };
 
-__device__ __forceinline__ uint4 zero_quad() { return make_uint4(kZeroWord, kZeroWord, kZeroWord, kZeroWord); }
 
 // ----------------------------------------------------------- bucket ---
 __global__ __launch_bounds__(1024) void moe_bucket_kernel(MoeArgs a) {
@@ -122,275 +125,289 @@ __global__ __launch_bounds__(1024) void moe_bucket_kernel(MoeArgs a) {
   }
 }
 
-// Transform `len` (multiple of 128) values of one row into fp16 LDS, by
-// wavefront-sized blocks; `load(i)` gives element i, dst row padded to dlen.
-template <typename Load>
-__device__ __forceinline__ void transform_row_f16(_Float16* dst, int len, int dlen, int wave, int nwaves, int lane,
-                                                  bool fused, Load load) {
-  for (int b = wave; b * 128 < dlen; b += nwaves) {
-    float v0 = 0.0f, v1 = 0.0f;
-    if (b * 128 < len) {
-      load(b * 128 + 2 * lane, v0, v1);
-      if (fused) wave_fwht128<float>(v0, v1, lane, kInvSqrt128);
-    }
-    dst[b * 128 + 2 * lane] = static_cast<_Float16>(v0);
-    dst[b * 128 + 2 * lane + 1] = static_cast<_Float16>(v1);
-  }
-}
+constexpr int kXStride = kSliceTrits + 8;  // A rows padded by 16 bytes (LDS banks)
 
-// Accumulate one 640-trit slice of R rows per lane against M activation rows.
-// wp[r]: this lane's quad 0 of the slice for row r (quads 64 apart); nq_here:
-// quads holding trits below K (whole units); sc[r][g]: scales; xs: LDS fp16
-// activations of the slice, row stride xstride (elements).  A 160-trit unit
-// (quads 2u, 2u + 1, loaded one unit ahead) spans scale groups g0 = 5u / 4
-// and g0 + 1; its chunks come in ROW64 order, so each is summed into the
-// accumulator of its group and both are scaled at the end of the unit.
-template <int M, int R>
-__device__ __forceinline__ void slice_dot2(const uint4* const (&wp)[R], const float (&sc)[R][kSliceGroups],
-                                           int nq_here, const _Float16* xs, int xstride, const uint32_t* codes_lo,
-                                           const uint32_t* codes_hi, float (&tot)[R][M]) {
-  uint4 cur[R][2];
+// Units u0 .. u1-1 of one 640-trit slice of one 64-row block on the matrix
+// cores (see gemv_mfma_kernel; u0, u1 are wavefront-uniform).  wb: this
+// lane's word-pair pointer of unit 0, row quarter 0 (quad kb / 2, words
+// 2 (kb % 2), +1 of row j); the pairs are loaded ahead by mfma_load.
+__device__ __forceinline__ void mfma_load(const uint32_t* wb, int u0, int u1, uint2 (&wq)[4][4]) {
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int u = 0; u < 4; ++u)
+    if (u >= u0 && u < u1)
 #pragma unroll
-    for (int q = 0; q < 2; ++q) cur[r][q] = wp[r][q * 64];
+      for (int h = 0; h < 4; ++h) wq[u][h] = load_pair(wb + ((2 * u) * 64 + 16 * h) * 4);
+}
+// ssc: the block's scales of the slice in LDS ([group][64 rows], fp16 bits);
+// xrow: this lane's A row at offset 8 kb; tot[h][v] += the group-scaled D
+// rows 4 kb + v of row quarter h.
+__device__ __forceinline__ void mfma_units(const uint2 (&wq)[4][4], const uint16_t* ssc, const _Float16* xrow,
+                                           const char* cbase, int j, int u0, int u1, float (&tot)[4][4]) {
+  float4_t acc[4];
 #pragma unroll
-  for (int u = 0; u < kSliceQuads / 2; ++u) {
-    if (2 * u < nq_here) {
-      uint4 nxt[R][2];
-      if (u + 1 < kSliceQuads / 2) {
+  for (int h = 0; h < 4; ++h) acc[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+  for (int u = 0; u < 4; ++u) {
+    if (u >= u0 && u < u1) {
+      half8_t af[5];
 #pragma unroll
-          for (int q = 0; q < 2; ++q) nxt[r][q] = wp[r][min(2 * u + 2 + q, nq_here - 1) * 64];
-      }
-      float acc[R][M][2];
+      for (int s = 0; s < 5; ++s) af[s] = *reinterpret_cast<const half8_t*>(xrow + 160 * u + 32 * s);
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+      for (int h = 0; h < 4; ++h) {
+        uint32_t o[10];
+        word_offsets_s<3, false>(wq[u][h].x, o);  // no inline asm next to MFMAs
+        word_offsets_s<3, false>(wq[u][h].y, o + 5);
+        uint2 cv[10];
 #pragma unroll
-        for (int m = 0; m < M; ++m) acc[r][m][0] = acc[r][m][1] = 0.0f;
-      const int g0 = (5 * u) / 4;
+        for (int c = 0; c < 10; ++c) cv[c] = *reinterpret_cast<const uint2*>(cbase + o[c]);
 #pragma unroll
-      for (int wl = 0; wl < 8; ++wl) {
-        const int j = wl & 3;
+        for (int s = 0; s < 5; ++s) {
+          const int step = 5 * u + s;  // scale group step / 4
+          const uint4 bq = make_uint4(cv[2 * s].x, cv[2 * s].y, cv[2 * s + 1].x, cv[2 * s + 1].y);
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s], __builtin_bit_cast(half8_t, bq), acc[h], 0, 0, 0);
+          if ((step & 3) == 3 || (s == 4 && u == u1 - 1)) {
+            const float sc = f16_to_f32(ssc[(step >> 2) * 64 + 16 * h + j]);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const uint4 qv = cur[r][wl >> 2];
-          const uint32_t wv = j == 0 ? qv.x : j == 1 ? qv.y : j == 2 ? qv.z : qv.w;
-          uint32_t o[5];
-          word_offsets(wv, o);
-#pragma unroll
-          for (int hh = 0; hh < 5; ++hh) {
-            const int p = 40 * u + row64_chunk(wl, hh);  // chunk of the slice
-            const int gi = p / 32 - g0;
-            const half2_t lo = __builtin_bit_cast(
-                half2_t, *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(codes_lo) + o[hh]));
-            const half2_t hi = __builtin_bit_cast(
-                half2_t, *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(codes_hi) + o[hh]));
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-              const uint2 xv = *reinterpret_cast<const uint2*>(xs + m * xstride + 4 * p);
-              float t = acc[r][m][gi];
-              t = __builtin_amdgcn_fdot2(lo, __builtin_bit_cast(half2_t, xv.x), t, false);
-              t = __builtin_amdgcn_fdot2(hi, __builtin_bit_cast(half2_t, xv.y), t, false);
-              acc[r][m][gi] = t;
-            }
+            for (int v = 0; v < 4; ++v) tot[h][v] = fmaf(sc, acc[h][v], tot[h][v]);
+            acc[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
           }
         }
       }
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-          tot[r][m] = fmaf(sc[r][g0], acc[r][m][0], fmaf(sc[r][g0 + 1], acc[r][m][1], tot[r][m]));
-      if (u + 1 < kSliceQuads / 2) {
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int q = 0; q < 2; ++q) cur[r][q] = nxt[r][q];
-      }
     }
   }
 }
 
-__device__ __forceinline__ void build_codes(uint32_t* codes_lo, uint32_t* codes_hi) {
-  const int tid = threadIdx.x;
-  if (tid < 81) {
-    uint16_t hv[4];
-    int c = tid;
+// Activation row m of the tile, slice s: the five blocks of 128 (lane l
+// holds elements 2l, 2l + 1 of each; zero past K).  load(i, v0, v1) reads
+// elements i, i + 1 of the row.  Split into a load and a transform so that
+// the weight loads can be issued in between: loads complete in order, and
+// the transform should wait for the activations only.
+struct SliceAct {
+  float v[kSliceGroups][2];
+  bool ok[kSliceGroups];
+};
+template <typename Load>
+__device__ __forceinline__ void load_slice(SliceAct& x, int s, int K, int lane, Load load) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      hv[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(static_cast<float>(c % 3) - 1.0f));
-      c /= 3;
-    }
-    codes_lo[tid] = hv[0] | (static_cast<uint32_t>(hv[1]) << 16);
-    codes_hi[tid] = hv[2] | (static_cast<uint32_t>(hv[3]) << 16);
+  for (int b = 0; b < kSliceGroups; ++b) {
+    const int k0 = s * kSliceTrits + b * 128;
+    x.ok[b] = k0 < K;
+    load((x.ok[b] ? k0 : 0) + 2 * lane, x.v[b][0], x.v[b][1]);
   }
 }
-
-__device__ __forceinline__ void load_scales(const uint16_t* sbase, int nb, int rb, int lane, int s,
-                                            float (&dst)[kSliceGroups]) {
-  const uint16_t* sp = sbase + row64_scale_base(s, rb, nb) + lane;
+// Transforms a loaded slice and splits it into A rows 2m, 2m + 1 of xh.
+__device__ __forceinline__ void transform_slice(SliceAct& x, _Float16 (*xh)[kXStride], int* xexp, int m, bool fused,
+                                                int lane) {
+  if (fused) wave_fwht128_batch<kSliceGroups>(x.v, lane, kInvSqrt128);
 #pragma unroll
-  for (int j = 0; j < kSliceGroups; ++j) dst[j] = f16_to_f32(sp[j * 64]);
+  for (int b = 0; b < kSliceGroups; ++b) {
+    if (!x.ok[b]) {
+      x.v[b][0] = 0.0f;
+      x.v[b][1] = 0.0f;
+    }
+  }
+  const int e = split_two_fp16<kSliceGroups>(x.v, lane, &xh[2 * m][0], &xh[2 * m + 1][0]);
+  if (lane == 0) xexp[m] = e;
+}
+
+// tot[h][q] += the slice sums of activation row 2 kb + q, scaled back by its
+// power of two.
+__device__ __forceinline__ void add_slice(const float (&ts)[4][4], const int* xexp, int kb, int M, float (&tot)[4][2]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int m = 2 * kb + q;
+    const int e = m < M ? xexp[m] : 0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) tot[h][q] += ldexpf(ts[h][2 * q] + ts[h][2 * q + 1], -e);
+  }
 }
 
 // ---------------------------------------------------------- gate/up ---
-template <int M>
-__device__ __forceinline__ void gate_up_tile(const MoeArgs& a, int e, int b, const int* tile_pairs, _Float16* xh,
-                                             float* red, const uint32_t* codes_lo, const uint32_t* codes_hi) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int K = a.hidden;
-  const int nslices = slices_per_row(K), nb = row_blocks(2 * a.inter);
-  const int xstride = nslices * kSliceTrits;
-  const uint4* wbase = a.gu_words + static_cast<size_t>(e) * a.gu_wstride;
-  const uint16_t* sbase = a.gu_scales + static_cast<size_t>(e) * a.gu_sstride;
-  const int rb_gate = b, rb_up = b + a.inter / 64;
-  float tot[2][M];
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int m = 0; m < M; ++m) tot[r][m] = 0.0f;
-  for (int s = wave; s < nslices; s += 4) {
-    // Gate row, then up row (two accumulators per activation row and unit
-    // leave no room for both rows at once).
-    const int nh = row64_slice_quads(K, s);
-    {
-      float sc[1][kSliceGroups];
-      const uint4* const wp[1] = {wbase + row64_quad_base(s, rb_gate, nb) + lane};
-      load_scales(sbase, nb, rb_gate, lane, s, sc[0]);
-      slice_dot2<M, 1>(wp, sc, nh, xh + s * kSliceTrits, xstride, codes_lo, codes_hi,
-                       *reinterpret_cast<float(*)[1][M]>(&tot[0][0]));
-    }
-    asm volatile("" ::: "memory");
-    {
-      float sc[1][kSliceGroups];
-      const uint4* const wp[1] = {wbase + row64_quad_base(s, rb_up, nb) + lane};
-      load_scales(sbase, nb, rb_up, lane, s, sc[0]);
-      slice_dot2<M, 1>(wp, sc, nh, xh + s * kSliceTrits, xstride, codes_lo, codes_hi,
-                       *reinterpret_cast<float(*)[1][M]>(&tot[1][0]));
-    }
-  }
-  // red[w][r][m][lane]; slices summed in wavefront order.
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int m = 0; m < M; ++m) red[((wave * 2 + r) * kTile + m) * 64 + lane] = tot[r][m];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < M * 64; idx += blockDim.x) {
-    const int m = idx >> 6, l = idx & 63;
-    float g = 0.0f, u = 0.0f;
-    for (int w = 0; w < 4; ++w) {
-      g += red[((w * 2 + 0) * kTile + m) * 64 + l];
-      u += red[((w * 2 + 1) * kTile + m) * 64 + l];
-    }
-    const float hv = g / (1.0f + __expf(-g)) * u;
-    a.h[static_cast<size_t>(tile_pairs[m]) * a.inter + b * 64 + l] = hv;
-  }
-}
-
+// Workgroup (active slot, 64-row block b of I[, 640-trit slice s of the
+// hidden size]): wavefronts 0, 1 take the gate rows 64b.., units 0-1 and 2-3
+// of each slice, wavefronts 2, 3 the up rows I + 64b...
+//   kSplit (few tokens, latency-bound): the workgroup takes slice
+//     blockIdx.z only and stores its partial sums to gu[s][pair][.] (gate in
+//     [0, I), up in [I, 2I)); the down launch adds the slices in order and
+//     applies silu(g) * u.  Four times the workgroups.
+//   otherwise: the workgroup runs all slices and stores h = silu(g) * u to
+//     gu[pair][0, I).
+template <bool kSplit>
 __global__ __launch_bounds__(256) void moe_gate_up_kernel(MoeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ uint32_t codes_lo[81], codes_hi[81];
+  __shared__ __attribute__((aligned(16))) _Float16 xh[2 * kTile][kXStride];
+  __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
+  __shared__ __attribute__((aligned(16))) uint2 codes[81];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[2][kSliceGroups * 64];  // gate, up block
+  __shared__ int xexp[kTile];
+  __shared__ float red[4][kTile][64];
   const int slot = blockIdx.x;
   if (slot >= a.num_active[0]) return;
   const int e = a.active[slot];
   const int p0 = a.seg[slot], p1 = a.seg[slot + 1];
   const int b = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int xstride = slices_per_row(a.hidden) * kSliceTrits;
-  _Float16* xh = reinterpret_cast<_Float16*>(smem);                        // [kTile][xstride]
-  float* red = reinterpret_cast<float*>(smem + kTile * xstride * 2);       // [4][2][kTile][64]
-  build_codes(codes_lo, codes_hi);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 15, kb = lane >> 4;
+  const int K = a.hidden, nb = row_blocks(2 * a.inter), I2 = 2 * a.inter;
+  const int s_begin = kSplit ? blockIdx.z : 0, s_end = kSplit ? blockIdx.z + 1 : slices_per_row(K);
+  const uint32_t* wexp = reinterpret_cast<const uint32_t*>(a.gu_words + static_cast<size_t>(e) * a.gu_wstride);
+  const uint16_t* sexp = a.gu_scales + static_cast<size_t>(e) * a.gu_sstride;
+  const int rb = wave < 2 ? b : b + a.inter / 64;  // this wavefront's gate or up block
+  const int u0 = 2 * (wave & 1);
+  build_code_table(codes, tid, blockDim.x);
+  for (int i = tid; i < kSliceTrits; i += blockDim.x) zeros[i] = static_cast<_Float16>(0.0f);
+  const char* cbase = reinterpret_cast<const char*>(codes);
   for (int q = p0; q < p1; q += kTile) {
     const int M = min(kTile, p1 - q);
-    __syncthreads();  // previous tile's readers are done
-    for (int m = 0; m < M; ++m) {
-      const int tok = a.pairs[q + m] / a.topk;
-      transform_row_f16(xh + m * xstride, a.hidden, xstride, wave, 4, lane, a.fused != 0,
-                        [&](int i, float& v0, float& v1) {
-                          load_act2(a.x, a.x_dtype, static_cast<size_t>(tok) * a.hidden + i, v0, v1);
-                        });
+    const _Float16* xrow = (j < 2 * M ? &xh[j < 2 * M ? j : 0][0] : &zeros[0]) + 8 * kb;
+    float tot[4][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}};
+    for (int s = s_begin; s < s_end; ++s) {
+      __syncthreads();  // the previous slice's readers are done
+      const int u1 = __builtin_amdgcn_readfirstlane(min(u0 + 2, row64_slice_quads(K, s) / 2));
+      const uint32_t* wb = wexp + (row64_quad_base(s, rb, nb) + (kb >> 1) * 64 + j) * 4 + 2 * (kb & 1);
+      uint2 wq[4][4];
+      if (kSplit) {
+        // Few tokens: this wavefront's activations (m = wave), then the
+        // weights, then the transform (loads complete in order, so the
+        // transform waits for the activations only).
+        SliceAct xa;
+        const size_t base = static_cast<size_t>(a.pairs[q + min(wave, M - 1)] / a.topk) * K;
+        load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) { load_act2(a.x, a.x_dtype, base + i, v0, v1); });
+        mfma_load(wb, u0, u1, wq);
+        if (wave < M) transform_slice(xa, xh, xexp, wave, a.fused != 0, lane);
+        for (int m = wave + 4; m < M; m += 4) {
+          const size_t bm = static_cast<size_t>(a.pairs[q + m] / a.topk) * K;
+          load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) { load_act2(a.x, a.x_dtype, bm + i, v0, v1); });
+          transform_slice(xa, xh, xexp, m, a.fused != 0, lane);
+        }
+      } else {
+        for (int m = wave; m < M; m += 4) {
+          SliceAct xa;
+          const size_t base = static_cast<size_t>(a.pairs[q + m] / a.topk) * K;
+          load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) { load_act2(a.x, a.x_dtype, base + i, v0, v1); });
+          transform_slice(xa, xh, xexp, m, a.fused != 0, lane);
+        }
+      }
+      if ((wave & 1) == 0 && lane < kSliceGroups * 8)
+        *reinterpret_cast<uint4*>(&ssc[wave >> 1][8 * lane]) =
+            *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rb, nb) + 8 * lane);
+      __syncthreads();
+      // Many workgroups in flight: the weights are requested here, after the
+      // barrier, which measured faster than requesting them early.
+      if (!kSplit) mfma_load(wb, u0, u1, wq);
+      float ts[4][4] = {};
+      mfma_units(wq, ssc[wave >> 1], xrow, cbase, j, u0, u1, ts);
+      add_slice(ts, xexp, kb, M, tot);
+    }
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const int m = 2 * kb + qq;
+      if (m < M)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) red[wave][m][16 * h + j] = tot[h][qq];
     }
     __syncthreads();
-    const int* tp = a.pairs + q;
-    switch (M) {
-      case 1: gate_up_tile<1>(a, e, b, tp, xh, red, codes_lo, codes_hi); break;
-      case 2: gate_up_tile<2>(a, e, b, tp, xh, red, codes_lo, codes_hi); break;
-      case 3: gate_up_tile<3>(a, e, b, tp, xh, red, codes_lo, codes_hi); break;
-      case 4: gate_up_tile<4>(a, e, b, tp, xh, red, codes_lo, codes_hi); break;
-      case 5: gate_up_tile<5>(a, e, b, tp, xh, red, codes_lo, codes_hi); break;
-      case 6: gate_up_tile<6>(a, e, b, tp, xh, red, codes_lo, codes_hi); break;
-      case 7: gate_up_tile<7>(a, e, b, tp, xh, red, codes_lo, codes_hi); break;
-      default: gate_up_tile<8>(a, e, b, tp, xh, red, codes_lo, codes_hi); break;
+    if (kSplit) {
+      // Units 0-1 + 2-3 of the gate block, then of the up block.
+      for (int idx = tid; idx < 2 * M * 64; idx += blockDim.x) {
+        const int up = idx >= M * 64 ? 1 : 0;
+        const int m = (idx >> 6) - up * M, l = idx & 63;
+        const float v = red[2 * up][m][l] + red[2 * up + 1][m][l];
+        a.gu[(static_cast<size_t>(s_begin) * a.t * a.topk + a.pairs[q + m]) * I2 + up * a.inter + b * 64 + l] = v;
+      }
+    } else {
+      for (int idx = tid; idx < M * 64; idx += blockDim.x) {
+        const int m = idx >> 6, l = idx & 63;
+        const float g = red[0][m][l] + red[1][m][l];
+        const float u = red[2][m][l] + red[3][m][l];
+        a.gu[static_cast<size_t>(a.pairs[q + m]) * a.inter + b * 64 + l] = g / (1.0f + __expf(-g)) * u;
+      }
     }
   }
 }
 
 // ------------------------------------------------------------- down ---
-template <int M>
-__device__ __forceinline__ void down_tile(const MoeArgs& a, int e, int rb, const int* tile_pairs, const _Float16* xh,
-                                          const uint32_t* codes_lo, const uint32_t* codes_hi) {
-  const int lane = threadIdx.x & 63;
-  const int K = a.inter;
-  const int nslices = slices_per_row(K);
-  const int xstride = nslices * kSliceTrits;
-  const int nb = row_blocks(a.hidden);
-  if (rb >= nb) return;
-  const uint4* wbase = a.dn_words + static_cast<size_t>(e) * a.dn_wstride;
-  const uint16_t* sbase = a.dn_scales + static_cast<size_t>(e) * a.dn_sstride;
-  float tot[1][M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) tot[0][m] = 0.0f;
-  for (int s = 0; s < nslices; ++s) {
-    float sc[1][kSliceGroups];
-    const int nh = row64_slice_quads(K, s);
-    const uint4* const wp[1] = {wbase + row64_quad_base(s, rb, nb) + lane};
-    load_scales(sbase, nb, rb, lane, s, sc[0]);
-    slice_dot2<M, 1>(wp, sc, nh, xh + s * kSliceTrits, xstride, codes_lo,
-                     codes_hi, tot);
-  }
-  const int row = rb * 64 + lane;
-  if (row < a.hidden) {
-#pragma unroll
-    for (int m = 0; m < M; ++m) a.o[static_cast<size_t>(tile_pairs[m]) * a.hidden + row] = tot[0][m];
-  }
-}
-
+template <bool kSplit>
 __global__ __launch_bounds__(256) void moe_down_kernel(MoeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ uint32_t codes_lo[81], codes_hi[81];
+  __shared__ __attribute__((aligned(16))) _Float16 xh[2 * kTile][kXStride];
+  __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
+  __shared__ __attribute__((aligned(16))) uint2 codes[81];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[4][kSliceGroups * 64];
+  __shared__ int xexp[kTile];
   const int slot = blockIdx.x;
   if (slot >= a.num_active[0]) return;
   const int e = a.active[slot];
   const int p0 = a.seg[slot], p1 = a.seg[slot + 1];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 15, kb = lane >> 4;
+  const int K = a.inter, nsl = slices_per_row(K), nb = row_blocks(a.hidden);
   const int rb = blockIdx.y * 4 + wave;
-  const int xstride = slices_per_row(a.inter) * kSliceTrits;
-  _Float16* xh = reinterpret_cast<_Float16*>(smem);  // [kTile][xstride]
-  build_codes(codes_lo, codes_hi);
+  const int rbc = min(rb, nb - 1);
+  const uint32_t* wexp = reinterpret_cast<const uint32_t*>(a.dn_words + static_cast<size_t>(e) * a.dn_wstride);
+  const uint16_t* sexp = a.dn_scales + static_cast<size_t>(e) * a.dn_sstride;
+  build_code_table(codes, tid, blockDim.x);
+  for (int i = tid; i < kSliceTrits; i += blockDim.x) zeros[i] = static_cast<_Float16>(0.0f);
+  const char* cbase = reinterpret_cast<const char*>(codes);
   for (int q = p0; q < p1; q += kTile) {
     const int M = min(kTile, p1 - q);
-    __syncthreads();
-    for (int m = 0; m < M; ++m) {
-      const float* hrow = a.h + static_cast<size_t>(a.pairs[q + m]) * a.inter;
-      transform_row_f16(xh + m * xstride, a.inter, xstride, wave, 4, lane, true, [&](int i, float& v0, float& v1) {
-        const float2 v = *reinterpret_cast<const float2*>(hrow + i);
-        v0 = v.x;
-        v1 = v.y;
-      });
+    const _Float16* xrow = (j < 2 * M ? &xh[j < 2 * M ? j : 0][0] : &zeros[0]) + 8 * kb;
+    float tot[4][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}};
+    for (int s = 0; s < nsl; ++s) {
+      __syncthreads();
+      const uint32_t* wb = wexp + (row64_quad_base(s, rbc, nb) + (kb >> 1) * 64 + j) * 4 + 2 * (kb & 1);
+      const int u1 = __builtin_amdgcn_readfirstlane(row64_slice_quads(K, s) / 2);
+      uint2 wq[4][4];
+      for (int m = wave; m < M; m += 4) {
+        const int pair = a.pairs[q + m];
+        SliceAct xa;
+        if (kSplit) {
+          // h = silu(g) * u, g and u summed over the gate/up slices in order.
+          const float* grow = a.gu + static_cast<size_t>(pair) * 2 * K;
+          const size_t sstride = static_cast<size_t>(a.t) * a.topk * 2 * K;
+          load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) {
+            float2 g = make_float2(0.0f, 0.0f), u = g;
+            for (int z = 0; z < a.gu_slices; ++z) {
+              const float2 gz = *reinterpret_cast<const float2*>(grow + z * sstride + i);
+              const float2 uz = *reinterpret_cast<const float2*>(grow + z * sstride + K + i);
+              g.x += gz.x;
+              g.y += gz.y;
+              u.x += uz.x;
+              u.y += uz.y;
+            }
+            v0 = g.x / (1.0f + __expf(-g.x)) * u.x;
+            v1 = g.y / (1.0f + __expf(-g.y)) * u.y;
+          });
+          if (m == wave) mfma_load(wb, 0, u1, wq);  // few tokens: weights in flight during the transform
+        } else {
+          const float* hrow = a.gu + static_cast<size_t>(pair) * K;
+          load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) {
+            const float2 v = *reinterpret_cast<const float2*>(hrow + i);
+            v0 = v.x;
+            v1 = v.y;
+          });
+        }
+        transform_slice(xa, xh, xexp, m, true, lane);
+      }
+      if (kSplit && wave >= M) mfma_load(wb, 0, u1, wq);
+      if (lane < kSliceGroups * 8)
+        *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) =
+            *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rbc, nb) + 8 * lane);
+      __syncthreads();
+      if (!kSplit) mfma_load(wb, 0, u1, wq);
+      if (rb < nb) {
+        float ts[4][4] = {};
+        mfma_units(wq, ssc[wave], xrow, cbase, j, 0, u1, ts);
+        add_slice(ts, xexp, kb, M, tot);
+      }
     }
-    __syncthreads();
-    const int* tp = a.pairs + q;
-    switch (M) {
-      case 1: down_tile<1>(a, e, rb, tp, xh, codes_lo, codes_hi); break;
-      case 2: down_tile<2>(a, e, rb, tp, xh, codes_lo, codes_hi); break;
-      case 3: down_tile<3>(a, e, rb, tp, xh, codes_lo, codes_hi); break;
-      case 4: down_tile<4>(a, e, rb, tp, xh, codes_lo, codes_hi); break;
-      case 5: down_tile<5>(a, e, rb, tp, xh, codes_lo, codes_hi); break;
-      case 6: down_tile<6>(a, e, rb, tp, xh, codes_lo, codes_hi); break;
-      case 7: down_tile<7>(a, e, rb, tp, xh, codes_lo, codes_hi); break;
-      default: down_tile<8>(a, e, rb, tp, xh, codes_lo, codes_hi); break;
+    if (rb < nb) {
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const int m = 2 * kb + qq;
+        if (m < M)
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const int row = rb * 64 + 16 * h + j;
+            if (row < a.hidden) a.o[static_cast<size_t>(a.pairs[q + m]) * a.hidden + row] = tot[h][qq];
+          }
+      }
     }
   }
 }
@@ -477,8 +494,11 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 struct MoeLayout {
-  size_t num_active, active, seg, pairs, h, o, total;
+  size_t num_active, active, seg, pairs, gu, o, total;
 };
+
+// Few tokens: one gate/up workgroup per hidden slice (latency-bound case).
+bool moe_split(int t) { return t <= 8; }
 
 MoeLayout moe_layout(int experts, int t, int topk, int hidden, int inter) {
   MoeLayout l;
@@ -492,22 +512,14 @@ MoeLayout moe_layout(int experts, int t, int topk, int hidden, int inter) {
   off += align256(sizeof(int) * (experts + 1));
   l.pairs = off;
   off += align256(sizeof(int) * P);
-  l.h = off;
-  off += align256(sizeof(float) * P * inter);
+  l.gu = off;
+  off += align256(sizeof(float) * (moe_split(t) ? slices_per_row(hidden) * P * 2 * inter : P * inter));
   l.o = off;
   off += align256(sizeof(float) * P * hidden);
   l.total = off;
   return l;
 }
 
-size_t moe_smem_gate_up(int hidden) {
-  const int xstride = slices_per_row(hidden) * kSliceTrits;
-  return static_cast<size_t>(kTile) * xstride * 2 + 4 * 2 * kTile * 64 * sizeof(float);
-}
-size_t moe_smem_down(int inter) {
-  const int xstride = slices_per_row(inter) * kSliceTrits;
-  return static_cast<size_t>(kTile) * xstride * 2;
-}
 
 }  // namespace
 
@@ -538,7 +550,7 @@ extern "C" int tq_moe_gemv(const tq_weights* w_gate_up, const tq_weights* w_down
   if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED)) return TQ_EINVAL;
   const int E = w_gate_up->num_experts, hidden = w_gate_up->k, inter = w_gate_up->n / 2;
   if (w_gate_up->n % 2 || inter % 64 || w_down->n != hidden || w_down->k != inter) return TQ_ESHAPE;
-  if (hidden > kMaxK || inter > kMaxK || E > kMaxExperts) return TQ_EUNSUPPORTED;
+  if (E > kMaxExperts) return TQ_EUNSUPPORTED;
   if (t < 1 || topk < 1 || topk > 32 || static_cast<long long>(t) * topk > INT_MAX / 4) return TQ_ESHAPE;
   const MoeLayout l = moe_layout(E, t, topk, hidden, inter);
   if (ws_bytes < l.total) return TQ_ENOSPACE;
@@ -567,7 +579,9 @@ extern "C" int tq_moe_gemv(const tq_weights* w_gate_up, const tq_weights* w_down
   a.active = reinterpret_cast<int*>(ws + l.active);
   a.seg = reinterpret_cast<int*>(ws + l.seg);
   a.pairs = reinterpret_cast<int*>(ws + l.pairs);
-  a.h = reinterpret_cast<float*>(ws + l.h);
+  a.gu = reinterpret_cast<float*>(ws + l.gu);
+  a.gu_slices = slices_per_row(hidden);
+  a.gu_split = moe_split(t) ? 1 : 0;
   a.o = reinterpret_cast<float*>(ws + l.o);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int P = t * topk;
@@ -575,26 +589,15 @@ extern "C" int tq_moe_gemv(const tq_weights* w_gate_up, const tq_weights* w_down
   hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(1024), 0, s, a);
   TQ_LAUNCH_CHECK();
   // Dynamic LDS above the default 64 KiB needs an explicit per-kernel limit.
-  const size_t smem_gu = moe_smem_gate_up(hidden), smem_dn = moe_smem_down(inter);
-  if (smem_gu > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_gate_up_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem_gu));
-    if (e != hipSuccess) {
-      tq_set_hip_error(e, "tq_moe_gemv (gate/up LDS limit)");
-      return TQ_EHIP;
-    }
-  }
-  if (smem_dn > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_down_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem_dn));
-    if (e != hipSuccess) {
-      tq_set_hip_error(e, "tq_moe_gemv (down LDS limit)");
-      return TQ_EHIP;
-    }
-  }
-  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(slots, inter / 64), dim3(256), smem_gu, s, a);
+  if (a.gu_split)
+    hipLaunchKernelGGL(moe_gate_up_kernel<true>, dim3(slots, inter / 64, a.gu_slices), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(moe_gate_up_kernel<false>, dim3(slots, inter / 64), dim3(256), 0, s, a);
   TQ_LAUNCH_CHECK();
-  hipLaunchKernelGGL(moe_down_kernel, dim3(slots, (row_blocks(hidden) + 3) / 4), dim3(256), smem_dn, s, a);
+  if (a.gu_split)
+    hipLaunchKernelGGL(moe_down_kernel<true>, dim3(slots, (row_blocks(hidden) + 3) / 4), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(moe_down_kernel<false>, dim3(slots, (row_blocks(hidden) + 3) / 4), dim3(256), 0, s, a);
   TQ_LAUNCH_CHECK();
   const size_t outs = static_cast<size_t>(t) * hidden;
   hipLaunchKernelGGL(moe_combine_kernel, dim3(static_cast<unsigned>((outs + 255) / 256)), dim3(256), 0, s, a);
