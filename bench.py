@@ -163,41 +163,58 @@ def cpu_baseline(O, synth, lins, w64s, seconds):
 
 # --------------------------------------------------------------- extras ---
 def extra_block_m8(tq, torch, synth, np):
+    """One dense block's seven linears at 8 activation rows.  Linears that
+    share an input (q, k, v; gate, up) are also packed as one matrix of
+    concatenated rows (the usual fused projections, same bytes and the same
+    per-row quantisation): one launch per input instead of seven."""
     wl = synth.DENSE_BLOCK_M8
-    base, nbytes = [], 0
+    nbytes = sum(tq.tq_packed_bytes(l.n, l.k) for l in wl.linears)
+    groups = {}
     for lin in wl.linears:
-        base.append(quantize_pack(tq, torch, synth.weights(lin.w_seed, lin.n, lin.k), lin.n, lin.k))
-        nbytes += tq.tq_packed_bytes(lin.n, lin.k)
-    torch.cuda.synchronize()
-    copies = max(1, -(-ROTATE_BYTES // nbytes))
-    sets = [base] + [[clone_w(tq, w) for w in base] for _ in range(copies - 1)]
-    xs = {s: bf16(torch, synth.activations(s, 8, 5120 if s != 3013 else 17408, "bf16")) for s in (3010, 3011, 3012, 3013)}
-    total_n = sum(l.n for l in wl.linears)
-    y_all = torch.empty(8 * total_n, dtype=torch.float32, device="cuda")
-    offs = np.cumsum([0] + [8 * l.n for l in wl.linears])
-    ys = [y_all[offs[i]:offs[i + 1]].view(8, l.n) for i, l in enumerate(wl.linears)]
+        groups.setdefault(lin.x_seed, []).append(lin)
+    xs = {s: bf16(torch, synth.activations(s, 8, g[0].k, "bf16")) for s, g in groups.items()}
 
-    def step(i):
-        y_all.zero_()
-        for j, (lin, w) in enumerate(zip(wl.linears, sets[i % copies])):
-            tq.tq_gemv(w, xs[lin.x_seed], 8, ys[j], tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE)
-    ms = timed(torch, 32, 4, step)
-    per = {}
-    for j, lin in enumerate(wl.linears):
-        g = capture(torch, copies, lambda i: tq.tq_gemv(sets[i][j], xs[lin.x_seed], 8, ys[j],
-                                                         tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE))
-        g.replay()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        g.replay()
-        b.record()
+    def run(mats, label):
+        """mats: [(name, n, k, x_seed, w64)]; timed step and per-matrix kernel time."""
+        base = [quantize_pack(tq, torch, w64, n, k) for _, n, k, _, w64 in mats]
         torch.cuda.synchronize()
-        per[lin.name] = round(1e3 * a.elapsed_time(b) / copies, 3)
-    return {"workload": wl.name, "m": 8, "packed_bytes_per_step": nbytes, "weight_copies_rotated": copies,
-            "ms_per_step": round(ms, 4), "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "layer_tok_s": round(8 / (ms * 1e-3), 1), "kernel_us": per,
-            "compute": "v_mfma_f32_16x16x32_f16 (x' as two fp16 parts in the A rows, fp16 trit codes, FP32 accumulate)"}
+        copies = max(1, -(-ROTATE_BYTES // nbytes))
+        sets = [base] + [[clone_w(tq, w) for w in base] for _ in range(copies - 1)]
+        y_all = torch.empty(8 * sum(m[1] for m in mats), dtype=torch.float32, device="cuda")
+        offs = np.cumsum([0] + [8 * m[1] for m in mats])
+        ys = [y_all[offs[i]:offs[i + 1]].view(8, m[1]) for i, m in enumerate(mats)]
+
+        def step(i):
+            y_all.zero_()
+            for j, (m, w) in enumerate(zip(mats, sets[i % copies])):
+                tq.tq_gemv(w, xs[m[3]], 8, ys[j], tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE)
+        ms = timed(torch, 32, 4, step)
+        per = {}
+        for j, m in enumerate(mats):
+            g = capture(torch, copies, lambda i: tq.tq_gemv(sets[i][j], xs[m[3]], 8, ys[j],
+                                                             tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE))
+            g.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            per[m[0]] = round(1e3 * a.elapsed_time(b) / copies, 3)
+        del sets
+        torch.cuda.empty_cache()
+        return {"launches": len(mats), "ms_per_step": round(ms, 4), "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "layer_tok_s": round(8 / (ms * 1e-3), 1), "kernel_us": per, "weight_copies_rotated": copies}
+
+    w64 = {l.name: synth.weights(l.w_seed, l.n, l.k) for l in wl.linears}
+    fused = run([("|".join(l.name for l in g), sum(l.n for l in g), g[0].k, s,
+                  np.concatenate([w64[l.name] for l in g], axis=0)) for s, g in groups.items()], "fused")
+    separate = run([(l.name, l.n, l.k, l.x_seed, w64[l.name]) for l in wl.linears], "separate")
+    out = {"workload": wl.name, "m": 8, "packed_bytes_per_step": nbytes}
+    out.update(fused)
+    out["separate_linears"] = separate
+    out["compute"] = "v_mfma_f32_16x16x32_f16 (x' as two fp16 parts in the A rows, fp16 trit codes, FP32 accumulate)"
+    return out
 
 
 def extra_moe(tq, torch, synth, np):

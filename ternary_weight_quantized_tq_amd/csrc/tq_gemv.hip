@@ -53,6 +53,7 @@ struct GemvArgs {
   int mode;                 // kDirect, kPartial or kAtomic (see finish())
   int x_dtype;
   int n, k, groups, nb, npad, nsl;
+  int bpg;                  // row blocks per workgroup (wavefronts past bpg only help with the prologue)
   int fused;
 };
 
@@ -80,8 +81,8 @@ __device__ __forceinline__ Tile make_tile(const GemvArgs& a) {
   t.wave = t.tid >> 6;
   t.lane = t.tid & 63;
   t.waves = blockDim.x >> 6;
-  t.rb = t.rg * t.waves + t.wave;
-  t.active = t.rb < a.nb;
+  t.rb = t.rg * a.bpg + t.wave;
+  t.active = t.wave < a.bpg && t.rb < a.nb;
   t.rbc = t.active ? t.rb : a.nb - 1;
   t.nq_here = row64_slice_quads(a.k, t.slice);
   t.k0 = t.slice * kSliceTrits;
@@ -339,9 +340,14 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
   // Word pair of (row quarter h, unit u): quad 2u + kb / 2, words 2 (kb % 2)
   // and + 1.  Slices are stored whole (quads past the row's end hold
   // all-zero words), so every unit is read and no clamp is needed.
+  // Wavefronts past the workgroup's row blocks (small matrices: more
+  // wavefronts than blocks, for the prologue) read one cached line instead.
+  const bool decodes = __builtin_amdgcn_readfirstlane(t.wave < a.bpg ? 1 : 0) != 0;
   const uint32_t* wbase = reinterpret_cast<const uint32_t*>(a.words) +
-                          (row64_quad_base(t.slice, t.rbc, a.nb) + (kb >> 1) * 64 + j) * 4 + 2 * (kb & 1);
-  auto pair_at = [&](int it) { return wbase + ((2 * (it / 4)) * 64 + 16 * (it % 4)) * 4; };  // it = 4 u + h
+                          (decodes ? (row64_quad_base(t.slice, t.rbc, a.nb) + (kb >> 1) * 64 + j) * 4 + 2 * (kb & 1)
+                                   : 0);
+  const int pstride = decodes ? 1 : 0;
+  auto pair_at = [&](int it) { return wbase + pstride * ((2 * (it / 4)) * 64 + 16 * (it % 4)) * 4; };  // it = 4 u + h
   uint2 wq[kIters];
 #pragma unroll
   for (int i = 0; i < kMfmaLookahead; ++i) wq[i] = load_pair(pair_at(i));
@@ -389,6 +395,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
   const _Float16* xrow = (j < 2 * M ? &xh[j < 2 * M ? j : 0][0] : &zeros[0]) + 8 * kb;
   const char* cbase = reinterpret_cast<const char*>(codes);
 
+  if (!decodes) return;
   float4_t acc[4];
   float tot[4][4];
 #pragma unroll
@@ -455,7 +462,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 struct GemvPlan {
-  int nb, npad, nsl, waves, ngroups;
+  int nb, npad, nsl, waves, bpg, ngroups;
   size_t partial_bytes;
 };
 
@@ -481,6 +488,7 @@ void plan_waves(GemvPlan& p, int min_waves, int max_waves) {
   if (w < 1) w = 1;
   if (w > max_waves) w = max_waves;
   p.waves = w;
+  p.bpg = w;
   p.ngroups = (p.nb + w - 1) / w;
 }
 
@@ -535,10 +543,15 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
     if (!workspace) return TQ_EINVAL;
     if (ws_bytes < p.partial_bytes) return TQ_ENOSPACE;
   }
-  // M >= 2: every workgroup transforms M x 5 activation blocks, so it gets
-  // at least 8 wavefronts to share them.
-  if (m == 1) plan_waves(p, 1, kMaxWaves);
-  else plan_waves(p, 8, kMfmaMaxWaves);
+  if (m == 1) {
+    plan_waves(p, 1, kMaxWaves);
+  } else {
+    // Row blocks per workgroup so that the grid fills the compute units in
+    // one round; every activation row gets a wavefront for the prologue
+    // (one transform per row), so small matrices have idle decoders.
+    plan_waves(p, 1, kMfmaMaxWaves);
+    p.waves = max(p.waves, m);
+  }
   GemvArgs a;
   a.words = reinterpret_cast<const uint4*>(w->words);
   a.scales = w->scales;
@@ -554,6 +567,7 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
   a.npad = p.npad;
   a.nsl = p.nsl;
   a.fused = (flags & TQ_FWHT_FUSED) ? 1 : 0;
+  a.bpg = p.bpg;
   const dim3 grid(p.nsl, p.ngroups);
   const dim3 block(p.waves * 64);
   hipStream_t s = static_cast<hipStream_t>(stream);
