@@ -250,7 +250,7 @@ def extra_moe(tq, torch, synth, np):
         out.append({"workload": wl.name, "tokens": T, "active_experts": active, "expert_bytes_read": bytes_,
                     "weight_copies_rotated": copies, "us_per_layer": round(ms * 1e3, 2),
                     "gb_s": round(bytes_ / (ms * 1e-3) / 1e9, 1), "tok_s": round(T / (ms * 1e-3), 1),
-                    "launches": 4})
+                    "launches": 2 if T * wl.topk <= 64 else 4})  # per-pair launches up to 64 pairs
     return out
 
 

@@ -3,7 +3,16 @@
 // only the experts ternary, the router gate at full precision).
 //
 // tq_moe_route: softmax over the expert logits, top-k, renormalised weights.
-// tq_moe_gemv, four launches on the caller's stream:
+// tq_moe_gemv with at most 64 (token, slot) pairs, two launches:
+//   1. gate/up:  grid (pair, 64-row block of the intermediate dimension,
+//                640-trit slice of the hidden size), no bucketing; the
+//                slice's partial sums are stored.
+//   2. down:     grid (pair, 64-row block of the hidden size), one wavefront:
+//                adds the gate/up partials in order, h = silu(gate) * up, the
+//                block-128 transform, the down rows, the route weight; the
+//                last slot of a token to finish adds the slots' rows in slot
+//                order and stores y.
+// Otherwise four launches on the caller's stream:
 //   1. bucket:   one workgroup groups the (token, slot) pairs by expert and
 //                lists the experts that received tokens (ascending id).
 //   2. gate/up:  grid (active expert slot, 64-row block of the intermediate
@@ -14,13 +23,12 @@
 //                cores as in the M >= 2 decode GEMV: the block-128
 //                transformed activations as two fp16 parts in the A rows (a
 //                power of two per token and slice keeps them in range),
-//                fp16 trit codes from an 81-entry table as B.  Each slice's
-//                partial sums are stored.
+//                fp16 trit codes from an 81-entry table as B; stores
+//                h = silu(gate) * up.
 //   3. down:     grid (active expert slot, 4 row blocks of the hidden size),
-//                one row block per wavefront, the same contraction; its
-//                prologue adds the gate/up slices in order, forms
-//                h = silu(gate) * up and applies the block-128 transform;
-//                each (token, slot) pair's output row is stored.
+//                one row block per wavefront, the same contraction after
+//                the block-128 transform of h; each (token, slot) pair's
+//                output row is stored.
 //   4. combine:  y[t] = sum_j route_w[t][j] * o[t][j] in slot order.
 // Only experts that received tokens are read; every pair's arithmetic is
 // independent of which other pairs share its tile, so results do not depend
@@ -55,10 +63,11 @@ struct MoeArgs {
   int* active;       // [experts]   expert id of active slot a
   int* seg;          // [experts+1] pair range of slot a
   int* pairs;        // [t*topk]    pair indices grouped by expert
-  float* gu;         // gu_split: [gu_slices][t*topk][2*inter] gate/up partial sums per
+  float* gu;         // few pairs: [gu_parts][t*topk][2*inter] gate/up partial sums per
                      // hidden slice; otherwise [t*topk][inter] h = silu(gate) * up
-  int gu_slices, gu_split;
+  int gu_parts;
   float* o;          // [t*topk][hidden]
+  int* cnt;          // few pairs: [t][row_blocks(hidden)] arrival counters
 };
 
 
@@ -223,16 +232,10 @@ __device__ __forceinline__ void add_slice(const float (&ts)[4][4], const int* xe
 }
 
 // ---------------------------------------------------------- gate/up ---
-// Workgroup (active slot, 64-row block b of I[, 640-trit slice s of the
-// hidden size]): wavefronts 0, 1 take the gate rows 64b.., units 0-1 and 2-3
-// of each slice, wavefronts 2, 3 the up rows I + 64b...
-//   kSplit (few tokens, latency-bound): the workgroup takes slice
-//     blockIdx.z only and stores its partial sums to gu[s][pair][.] (gate in
-//     [0, I), up in [I, 2I)); the down launch adds the slices in order and
-//     applies silu(g) * u.  Four times the workgroups.
-//   otherwise: the workgroup runs all slices and stores h = silu(g) * u to
-//     gu[pair][0, I).
-template <bool kSplit>
+// Workgroup (active expert slot, 64-row block b of I): wavefronts 0, 1 take
+// the gate rows 64b.., units 0-1 and 2-3 of each slice, wavefronts 2, 3 the
+// up rows I + 64b..; the expert's tokens 8 at a time, all slices;
+// h = silu(g) * u is stored to gu[pair][0, I).
 __global__ __launch_bounds__(256) void moe_gate_up_kernel(MoeArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 xh[2 * kTile][kXStride];
   __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
@@ -244,10 +247,10 @@ __global__ __launch_bounds__(256) void moe_gate_up_kernel(MoeArgs a) {
   if (slot >= a.num_active[0]) return;
   const int e = a.active[slot];
   const int p0 = a.seg[slot], p1 = a.seg[slot + 1];
+  auto pair_of = [&](int i) { return a.pairs[i]; };
   const int b = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 15, kb = lane >> 4;
   const int K = a.hidden, nb = row_blocks(2 * a.inter), I2 = 2 * a.inter;
-  const int s_begin = kSplit ? blockIdx.z : 0, s_end = kSplit ? blockIdx.z + 1 : slices_per_row(K);
   const uint32_t* wexp = reinterpret_cast<const uint32_t*>(a.gu_words + static_cast<size_t>(e) * a.gu_wstride);
   const uint16_t* sexp = a.gu_scales + static_cast<size_t>(e) * a.gu_sstride;
   const int rb = wave < 2 ? b : b + a.inter / 64;  // this wavefront's gate or up block
@@ -259,32 +262,16 @@ __global__ __launch_bounds__(256) void moe_gate_up_kernel(MoeArgs a) {
     const int M = min(kTile, p1 - q);
     const _Float16* xrow = (j < 2 * M ? &xh[j < 2 * M ? j : 0][0] : &zeros[0]) + 8 * kb;
     float tot[4][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}};
-    for (int s = s_begin; s < s_end; ++s) {
+    for (int s = 0; s < slices_per_row(K); ++s) {
       __syncthreads();  // the previous slice's readers are done
       const int u1 = __builtin_amdgcn_readfirstlane(min(u0 + 2, row64_slice_quads(K, s) / 2));
       const uint32_t* wb = wexp + (row64_quad_base(s, rb, nb) + (kb >> 1) * 64 + j) * 4 + 2 * (kb & 1);
       uint2 wq[4][4];
-      if (kSplit) {
-        // Few tokens: this wavefront's activations (m = wave), then the
-        // weights, then the transform (loads complete in order, so the
-        // transform waits for the activations only).
+      for (int m = wave; m < M; m += 4) {
         SliceAct xa;
-        const size_t base = static_cast<size_t>(a.pairs[q + min(wave, M - 1)] / a.topk) * K;
+        const size_t base = static_cast<size_t>(pair_of(q + m) / a.topk) * K;
         load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) { load_act2(a.x, a.x_dtype, base + i, v0, v1); });
-        mfma_load(wb, u0, u1, wq);
-        if (wave < M) transform_slice(xa, xh, xexp, wave, a.fused != 0, lane);
-        for (int m = wave + 4; m < M; m += 4) {
-          const size_t bm = static_cast<size_t>(a.pairs[q + m] / a.topk) * K;
-          load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) { load_act2(a.x, a.x_dtype, bm + i, v0, v1); });
-          transform_slice(xa, xh, xexp, m, a.fused != 0, lane);
-        }
-      } else {
-        for (int m = wave; m < M; m += 4) {
-          SliceAct xa;
-          const size_t base = static_cast<size_t>(a.pairs[q + m] / a.topk) * K;
-          load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) { load_act2(a.x, a.x_dtype, base + i, v0, v1); });
-          transform_slice(xa, xh, xexp, m, a.fused != 0, lane);
-        }
+        transform_slice(xa, xh, xexp, m, a.fused != 0, lane);
       }
       if ((wave & 1) == 0 && lane < kSliceGroups * 8)
         *reinterpret_cast<uint4*>(&ssc[wave >> 1][8 * lane]) =
@@ -292,7 +279,7 @@ __global__ __launch_bounds__(256) void moe_gate_up_kernel(MoeArgs a) {
       __syncthreads();
       // Many workgroups in flight: the weights are requested here, after the
       // barrier, which measured faster than requesting them early.
-      if (!kSplit) mfma_load(wb, u0, u1, wq);
+      mfma_load(wb, u0, u1, wq);
       float ts[4][4] = {};
       mfma_units(wq, ssc[wave >> 1], xrow, cbase, j, u0, u1, ts);
       add_slice(ts, xexp, kb, M, tot);
@@ -305,27 +292,18 @@ __global__ __launch_bounds__(256) void moe_gate_up_kernel(MoeArgs a) {
         for (int h = 0; h < 4; ++h) red[wave][m][16 * h + j] = tot[h][qq];
     }
     __syncthreads();
-    if (kSplit) {
-      // Units 0-1 + 2-3 of the gate block, then of the up block.
-      for (int idx = tid; idx < 2 * M * 64; idx += blockDim.x) {
-        const int up = idx >= M * 64 ? 1 : 0;
-        const int m = (idx >> 6) - up * M, l = idx & 63;
-        const float v = red[2 * up][m][l] + red[2 * up + 1][m][l];
-        a.gu[(static_cast<size_t>(s_begin) * a.t * a.topk + a.pairs[q + m]) * I2 + up * a.inter + b * 64 + l] = v;
-      }
-    } else {
+    {
       for (int idx = tid; idx < M * 64; idx += blockDim.x) {
         const int m = idx >> 6, l = idx & 63;
         const float g = red[0][m][l] + red[1][m][l];
         const float u = red[2][m][l] + red[3][m][l];
-        a.gu[static_cast<size_t>(a.pairs[q + m]) * a.inter + b * 64 + l] = g / (1.0f + __expf(-g)) * u;
+        a.gu[static_cast<size_t>(pair_of(q + m)) * a.inter + b * 64 + l] = g / (1.0f + __expf(-g)) * u;
       }
     }
   }
 }
 
 // ------------------------------------------------------------- down ---
-template <bool kSplit>
 __global__ __launch_bounds__(256) void moe_down_kernel(MoeArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 xh[2 * kTile][kXStride];
   __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
@@ -355,42 +333,20 @@ __global__ __launch_bounds__(256) void moe_down_kernel(MoeArgs a) {
       const int u1 = __builtin_amdgcn_readfirstlane(row64_slice_quads(K, s) / 2);
       uint2 wq[4][4];
       for (int m = wave; m < M; m += 4) {
-        const int pair = a.pairs[q + m];
+        const float* hrow = a.gu + static_cast<size_t>(a.pairs[q + m]) * K;
         SliceAct xa;
-        if (kSplit) {
-          // h = silu(g) * u, g and u summed over the gate/up slices in order.
-          const float* grow = a.gu + static_cast<size_t>(pair) * 2 * K;
-          const size_t sstride = static_cast<size_t>(a.t) * a.topk * 2 * K;
-          load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) {
-            float2 g = make_float2(0.0f, 0.0f), u = g;
-            for (int z = 0; z < a.gu_slices; ++z) {
-              const float2 gz = *reinterpret_cast<const float2*>(grow + z * sstride + i);
-              const float2 uz = *reinterpret_cast<const float2*>(grow + z * sstride + K + i);
-              g.x += gz.x;
-              g.y += gz.y;
-              u.x += uz.x;
-              u.y += uz.y;
-            }
-            v0 = g.x / (1.0f + __expf(-g.x)) * u.x;
-            v1 = g.y / (1.0f + __expf(-g.y)) * u.y;
-          });
-          if (m == wave) mfma_load(wb, 0, u1, wq);  // few tokens: weights in flight during the transform
-        } else {
-          const float* hrow = a.gu + static_cast<size_t>(pair) * K;
-          load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) {
-            const float2 v = *reinterpret_cast<const float2*>(hrow + i);
-            v0 = v.x;
-            v1 = v.y;
-          });
-        }
+        load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) {
+          const float2 v = *reinterpret_cast<const float2*>(hrow + i);
+          v0 = v.x;
+          v1 = v.y;
+        });
         transform_slice(xa, xh, xexp, m, true, lane);
       }
-      if (kSplit && wave >= M) mfma_load(wb, 0, u1, wq);
       if (lane < kSliceGroups * 8)
         *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) =
             *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rbc, nb) + 8 * lane);
       __syncthreads();
-      if (!kSplit) mfma_load(wb, 0, u1, wq);
+      mfma_load(wb, 0, u1, wq);
       if (rb < nb) {
         float ts[4][4] = {};
         mfma_units(wq, ssc[wave], xrow, cbase, j, 0, u1, ts);
@@ -410,6 +366,188 @@ __global__ __launch_bounds__(256) void moe_down_kernel(MoeArgs a) {
       }
     }
   }
+}
+
+// -------------------------------------------------------- few pairs ---
+// Gate/up: workgroup (pair, 64-row block b of I, 640-trit slice s of the
+// hidden size), 8 wavefronts: wavefront w decodes unit w % 4 of the gate
+// (w < 4) or up (w >= 4) block; wavefront 0 transforms the activations,
+// wavefronts 3 and 7 stage the scales.  The four units' sums are added
+// in order and stored to gu[s][pair][.] (gate in [0, I), up in [I, 2I)).
+// Workgroup (0, 0, 0) also clears the arrival counters of the down launch.
+constexpr int kPairGuWaves = 8;
+__global__ __launch_bounds__(kPairGuWaves * 64) void moe_gate_up_pairs_kernel(MoeArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 xh[2][kXStride];
+  __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
+  __shared__ __attribute__((aligned(16))) uint2 codes[81];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[2][kSliceGroups * 64];
+  __shared__ int xexp[1];
+  __shared__ float red[kPairGuWaves][64];
+  const int pair = blockIdx.x, b = blockIdx.y, s = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, kb = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int up = wave >> 2, unit = wave & 3;
+  const int K = a.hidden, I = a.inter, nb = row_blocks(2 * I);
+  const size_t P = static_cast<size_t>(a.t) * a.topk;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int i = tid; i < a.t * row_blocks(a.hidden); i += blockDim.x) a.cnt[i] = 0;
+  const int e = a.ids[pair];
+  if (e < 0 || e >= a.experts) return;  // contributes nothing; its partials are never read
+  SliceAct xa;
+  if (wave == 0) {
+    const size_t base = static_cast<size_t>(pair / a.topk) * K;
+    load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) { load_act2(a.x, a.x_dtype, base + i, v0, v1); });
+  }
+  const int rb = up ? b + I / 64 : b;
+  const int u1 = __builtin_amdgcn_readfirstlane(min(unit + 1, row64_slice_quads(K, s) / 2));
+  const uint32_t* wexp = reinterpret_cast<const uint32_t*>(a.gu_words + static_cast<size_t>(e) * a.gu_wstride);
+  const uint16_t* sexp = a.gu_scales + static_cast<size_t>(e) * a.gu_sstride;
+  const uint32_t* wb = wexp + (row64_quad_base(s, rb, nb) + (kb >> 1) * 64 + j) * 4 + 2 * (kb & 1);
+  uint2 wq[4][4];
+  mfma_load(wb, unit, u1, wq);
+  build_code_table(codes, tid, blockDim.x);
+  for (int i = tid; i < kSliceTrits; i += blockDim.x) zeros[i] = static_cast<_Float16>(0.0f);
+  if (unit == 3 && lane < kSliceGroups * 8)  // not wavefront 0: its transform waits for nothing else
+    *reinterpret_cast<uint4*>(&ssc[up][8 * lane]) =
+        *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rb, nb) + 8 * lane);
+  if (wave == 0) transform_slice(xa, xh, xexp, 0, a.fused != 0, lane);
+  __syncthreads();
+  const _Float16* xrow = (j < 2 ? &xh[j < 2 ? j : 0][0] : &zeros[0]) + 8 * kb;
+  float ts[4][4] = {};
+  mfma_units(wq, ssc[up], xrow, reinterpret_cast<const char*>(codes), j, unit, u1, ts);
+  float tot[4][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}};
+  add_slice(ts, xexp, kb, 1, tot);
+  if (kb == 0)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) red[wave][16 * h + j] = tot[h][0];
+  __syncthreads();
+  if (tid < 128) {
+    const int g = tid >> 6, l = tid & 63;  // g = 0: gate, 1: up
+    const float v = ((red[4 * g][l] + red[4 * g + 1][l]) + red[4 * g + 2][l]) + red[4 * g + 3][l];
+    a.gu[(static_cast<size_t>(s) * P + pair) * 2 * I + g * I + b * 64 + l] = v;
+  }
+}
+
+// Down + combine: workgroup (pair, 64-row block rb of the hidden size), 4
+// wavefronts: wavefront w decodes unit w of each slice of the intermediate
+// dimension; wavefront 0 assembles h = silu(g) * u from the gate/up partials
+// (added in order) and transforms it.  The units' sums are added in order,
+// scaled by the route weight and stored to o[pair][.]; the arrival is
+// counted, and the last of the token's slots to arrive adds the slots' rows
+// in slot order and stores y.  The o rows are written and read with
+// device-scope atomic accesses (they bypass the per-die caches), so waiting
+// for the stores before counting is enough: no cache-wide write-back.
+constexpr int kPairDnWaves = 4;
+__global__ __launch_bounds__(kPairDnWaves * 64) void moe_down_pairs_kernel(MoeArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 xh[2][kXStride];
+  __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
+  __shared__ __attribute__((aligned(16))) uint2 codes[81];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[kSliceGroups * 64];
+  __shared__ int xexp[1];
+  __shared__ float red[kPairDnWaves][64];
+  const int pair = blockIdx.x, rb = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, kb = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = a.inter, nsl = slices_per_row(K), nb = row_blocks(a.hidden);
+  const int tok = pair / a.topk;
+  const size_t P = static_cast<size_t>(a.t) * a.topk;
+  const int e = a.ids[pair];
+  const float wgt = a.route_w[pair];
+  const bool valid = e >= 0 && e < a.experts;
+  build_code_table(codes, tid, blockDim.x);
+  for (int i = tid; i < kSliceTrits; i += blockDim.x) zeros[i] = static_cast<_Float16>(0.0f);
+  float tot[4][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}};
+  if (valid) {
+    const uint32_t* wexp = reinterpret_cast<const uint32_t*>(a.dn_words + static_cast<size_t>(e) * a.dn_wstride);
+    const uint16_t* sexp = a.dn_scales + static_cast<size_t>(e) * a.dn_sstride;
+    const float* grow = a.gu + static_cast<size_t>(pair) * 2 * K;
+    const _Float16* xrow = (j < 2 ? &xh[j < 2 ? j : 0][0] : &zeros[0]) + 8 * kb;
+    for (int s = 0; s < nsl; ++s) {
+      if (s > 0) __syncthreads();  // the previous slice's readers are done
+      // This wavefront's weights first, then (wavefront 0) h of this slice:
+      // the gate/up partials added in order, four partials' loads in
+      // flight at a time.
+      const uint32_t* wb = wexp + (row64_quad_base(s, rb, nb) + (kb >> 1) * 64 + j) * 4 + 2 * (kb & 1);
+      const int u1 = __builtin_amdgcn_readfirstlane(min(wave + 1, row64_slice_quads(K, s) / 2));
+      uint2 wq[4][4];
+      mfma_load(wb, wave, u1, wq);
+      if (wave == 0) {
+        const uint4 scq = *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rb, nb) +
+                                                         8 * (lane < kSliceGroups * 8 ? lane : 0));
+        float g[kSliceGroups][2] = {}, u[kSliceGroups][2] = {};
+        for (int z0 = 0; z0 < a.gu_parts; z0 += 4) {
+          float2 gv[4][kSliceGroups], uv[4][kSliceGroups];
+#pragma unroll
+          for (int dz = 0; dz < 4; ++dz) {
+            const float* src = grow + static_cast<size_t>(min(z0 + dz, a.gu_parts - 1)) * P * 2 * K;
+#pragma unroll
+            for (int bb = 0; bb < kSliceGroups; ++bb) {
+              const int k0 = s * kSliceTrits + bb * 128;
+              const int i = (k0 < K ? k0 : 0) + 2 * lane;
+              gv[dz][bb] = *reinterpret_cast<const float2*>(src + i);
+              uv[dz][bb] = *reinterpret_cast<const float2*>(src + K + i);
+            }
+          }
+#pragma unroll
+          for (int dz = 0; dz < 4; ++dz)
+            if (z0 + dz < a.gu_parts)
+#pragma unroll
+              for (int bb = 0; bb < kSliceGroups; ++bb) {
+                g[bb][0] += gv[dz][bb].x;
+                g[bb][1] += gv[dz][bb].y;
+                u[bb][0] += uv[dz][bb].x;
+                u[bb][1] += uv[dz][bb].y;
+              }
+        }
+        SliceAct xa;
+#pragma unroll
+        for (int bb = 0; bb < kSliceGroups; ++bb) {
+          xa.ok[bb] = s * kSliceTrits + bb * 128 < K;
+#pragma unroll
+          for (int c = 0; c < 2; ++c) xa.v[bb][c] = g[bb][c] / (1.0f + __expf(-g[bb][c])) * u[bb][c];
+        }
+        transform_slice(xa, xh, xexp, 0, true, lane);
+        if (lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[8 * lane]) = scq;
+      }
+      __syncthreads();
+      float ts[4][4] = {};
+      mfma_units(wq, ssc, xrow, reinterpret_cast<const char*>(codes), j, wave, u1, ts);
+      add_slice(ts, xexp, kb, 1, tot);
+    }
+  }
+  if (kb == 0)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) red[wave][16 * h + j] = tot[h][0];
+  __syncthreads();
+  if (wave != 0) return;
+  const int row = rb * 64 + lane;
+  const int rowc = row < a.hidden ? row : 0;
+  if (valid && row < a.hidden) {
+    const float v = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    __hip_atomic_store(a.o + static_cast<size_t>(pair) * a.hidden + row, wgt * v, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this slot's row is stored before its arrival is counted
+  int prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(&a.cnt[tok * nb + rb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0);
+  if (prev != a.topk - 1) return;
+  const int32_t* tok_ids = a.ids + static_cast<size_t>(tok) * a.topk;
+  float* orow = a.o + static_cast<size_t>(tok) * a.topk * a.hidden + rowc;
+  float v = 0.0f;
+  for (int j0 = 0; j0 < a.topk; j0 += 8) {
+    float ov[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+      ov[d] = __hip_atomic_load(orow + static_cast<size_t>(min(j0 + d, a.topk - 1)) * a.hidden, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const int ej = tok_ids[min(j0 + d, a.topk - 1)];
+      if (j0 + d < a.topk && ej >= 0 && ej < a.experts) v += ov[d];
+    }
+  }
+  if (row < a.hidden) a.y[static_cast<size_t>(tok) * a.hidden + row] = v;
 }
 
 // ---------------------------------------------------------- combine ---
@@ -494,13 +632,15 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 struct MoeLayout {
-  size_t num_active, active, seg, pairs, gu, o, total;
+  size_t num_active, active, seg, pairs, gu, o, cnt, total;
 };
 
-// Few tokens: one gate/up workgroup per hidden slice (latency-bound case).
-bool moe_split(int t) { return t <= 8; }
+// Few (token, slot) pairs: no bucketing, one workgroup per pair for gate/up
+// (split over hidden slices), down and combine in one launch.
+bool moe_pairs(int t, int topk) { return static_cast<long long>(t) * topk <= 64; }
 
 MoeLayout moe_layout(int experts, int t, int topk, int hidden, int inter) {
+  const bool pairs = moe_pairs(t, topk);
   MoeLayout l;
   const size_t P = static_cast<size_t>(t) * topk;
   size_t off = 0;
@@ -513,9 +653,11 @@ MoeLayout moe_layout(int experts, int t, int topk, int hidden, int inter) {
   l.pairs = off;
   off += align256(sizeof(int) * P);
   l.gu = off;
-  off += align256(sizeof(float) * (moe_split(t) ? slices_per_row(hidden) * P * 2 * inter : P * inter));
+  off += align256(sizeof(float) * (pairs ? slices_per_row(hidden) * P * 2 * inter : P * inter));
   l.o = off;
   off += align256(sizeof(float) * P * hidden);
+  l.cnt = off;
+  off += align256(sizeof(int) * t * row_blocks(hidden));
   l.total = off;
   return l;
 }
@@ -580,24 +722,25 @@ extern "C" int tq_moe_gemv(const tq_weights* w_gate_up, const tq_weights* w_down
   a.seg = reinterpret_cast<int*>(ws + l.seg);
   a.pairs = reinterpret_cast<int*>(ws + l.pairs);
   a.gu = reinterpret_cast<float*>(ws + l.gu);
-  a.gu_slices = slices_per_row(hidden);
-  a.gu_split = moe_split(t) ? 1 : 0;
+  a.gu_parts = slices_per_row(hidden);
+  a.cnt = reinterpret_cast<int*>(ws + l.cnt);
   a.o = reinterpret_cast<float*>(ws + l.o);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int P = t * topk;
+  if (moe_pairs(t, topk)) {
+    hipLaunchKernelGGL(moe_gate_up_pairs_kernel, dim3(P, inter / 64, slices_per_row(hidden)), dim3(kPairGuWaves * 64), 0,
+                       s, a);
+    TQ_LAUNCH_CHECK();
+    hipLaunchKernelGGL(moe_down_pairs_kernel, dim3(P, row_blocks(hidden)), dim3(kPairDnWaves * 64), 0, s, a);
+    TQ_LAUNCH_CHECK();
+    return TQ_OK;
+  }
   const int slots = P < E ? P : E;
   hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(1024), 0, s, a);
   TQ_LAUNCH_CHECK();
-  // Dynamic LDS above the default 64 KiB needs an explicit per-kernel limit.
-  if (a.gu_split)
-    hipLaunchKernelGGL(moe_gate_up_kernel<true>, dim3(slots, inter / 64, a.gu_slices), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(moe_gate_up_kernel<false>, dim3(slots, inter / 64), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(slots, inter / 64), dim3(256), 0, s, a);
   TQ_LAUNCH_CHECK();
-  if (a.gu_split)
-    hipLaunchKernelGGL(moe_down_kernel<true>, dim3(slots, (row_blocks(hidden) + 3) / 4), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(moe_down_kernel<false>, dim3(slots, (row_blocks(hidden) + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(moe_down_kernel, dim3(slots, (row_blocks(hidden) + 3) / 4), dim3(256), 0, s, a);
   TQ_LAUNCH_CHECK();
   const size_t outs = static_cast<size_t>(t) * hidden;
   hipLaunchKernelGGL(moe_combine_kernel, dim3(static_cast<unsigned>((outs + 255) / 256)), dim3(256), 0, s, a);

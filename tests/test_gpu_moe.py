@@ -54,12 +54,12 @@ def test_moe_small_random(dtype):
     assert O.rel_l2(y, y_ref) < 1e-5
 
 
-@pytest.mark.parametrize("T", [2, 12])
+@pytest.mark.parametrize("T", [2, 40])
 @pytest.mark.parametrize("scale", [3e-6, 2e4])
 def test_moe_activation_range(T, scale):
-    """Activations of scale 2e4 and 3e-6 through both launch shapes (T <= 8:
-    one workgroup per hidden slice; T = 12: all slices per workgroup), with a
-    hidden size of 3.2 slices."""
+    """Activations of scale 2e4 and 3e-6 through both launch shapes (4 pairs:
+    per-pair launches; 80 pairs: bucketed by expert), with a hidden size of
+    3.2 slices."""
     E, hidden, inter, topk = 4, 2048, 256, 2
     w_gu, w_dn, h = _random_experts(700, E, hidden, inter)
     act = synth.activations(71, T, hidden, "bf16", scale=scale)
@@ -74,10 +74,12 @@ def test_moe_activation_range(T, scale):
     assert O.rel_l2(y, y_ref) < 1e-5
 
 
-def test_moe_many_tokens_per_expert_and_bad_ids():
-    """More than 8 tokens on one expert (several tiles), and ids outside
-    [0, E) that must contribute nothing."""
-    E, hidden, inter, T, topk = 3, 384, 256, 21, 2
+@pytest.mark.parametrize("T", [21, 40])
+def test_moe_many_tokens_per_expert_and_bad_ids(T):
+    """More than 8 tokens on one expert (several tiles when bucketed: 80
+    pairs; 42 pairs take the per-pair launches), and ids outside [0, E) that
+    must contribute nothing."""
+    E, hidden, inter, topk = 3, 384, 256, 2
     w_gu, w_dn, h = _random_experts(500, E, hidden, inter)
     act = synth.activations(51, T, hidden, "bf16")
     ids = np.zeros((T, topk), np.int32)
@@ -93,6 +95,27 @@ def test_moe_many_tokens_per_expert_and_bad_ids():
             if ok[t, j]:
                 y_ref[t] += O.moe(act.values[t:t + 1], ids[t:t + 1, j:j + 1], rw[t:t + 1, j:j + 1], h["gu_w"],
                                   h["gu_s"], h["dn_w"], h["dn_s"], hidden, inter)[0]
+    assert O.rel_l2(y, y_ref) < 1e-5
+
+
+@pytest.mark.parametrize("T,topk", [(2, 12), (2, 32), (3, 22)])
+def test_moe_wide_topk(T, topk):
+    """12 and 32 slots per token, combined by whichever of a token's slots
+    finishes last (64 pairs is the largest per-pair launch, 66 pairs are
+    bucketed), with two invalid ids."""
+    E, hidden, inter = 40, 640, 384
+    w_gu, w_dn, h = _random_experts(900, E, hidden, inter)
+    act = synth.activations(91, T, hidden, "f32")
+    rng = np.random.default_rng(92)
+    ids = np.stack([rng.choice(E, topk, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[0, topk - 1] = -3
+    ids[T - 1, 1] = E
+    rw = rng.random((T, topk))
+    rw /= rw.sum(axis=1, keepdims=True)
+    y = run_moe(w_gu, w_dn, act_tensor(act), T, topk, ids, rw)
+    ok = (ids >= 0) & (ids < E)
+    y_ref = O.moe(act.values, np.where(ok, ids, 0), np.where(ok, rw, 0.0), h["gu_w"], h["gu_s"], h["dn_w"], h["dn_s"],
+                  hidden, inter)
     assert O.rel_l2(y, y_ref) < 1e-5
 
 
