@@ -201,10 +201,14 @@ int tq_moe_route(const float *logits, int t, int e, int topk, int32_t *ids,
  * k = I; both ROW64 (I % 64 == 0, Hd and I multiples of 128).  x: [t][Hd]
  * of x_dtype; y FP32 [t][Hd].  The expert products use the m >= 2 decode
  * GEMV arithmetic (fp16 codes, x' and H h as two fp16 parts, FP32
- * accumulation), up to 8 tokens of an expert at a time.  Only the
- * experts that receive tokens are read.  Ids outside [0, E) are an error
- * detected on the device: such slots contribute nothing.  Needs
- * tq_workspace_bytes(TQ_OP_MOE, w_gate_up, t, topk) bytes of workspace. */
+ * accumulation).  With t * topk <= 64 every (token, slot) pair is its own
+ * one-row product (two launches; the last slot of a token to finish adds
+ * the slots in slot order); otherwise the pairs are grouped by expert and
+ * an expert's tokens go 8 at a time (four launches).  y is deterministic
+ * either way.  Only the experts that receive tokens are read.  Ids outside
+ * [0, E) are an error detected on the device: such slots contribute
+ * nothing.  Needs tq_workspace_bytes(TQ_OP_MOE, w_gate_up, t, topk) bytes of
+ * workspace, which calls that overlap in time must not share. */
 int tq_moe_gemv(const tq_weights *w_gate_up, const tq_weights *w_down,
                 const void *x, int x_dtype, int t, int topk,
                 const int32_t *expert_ids, const float *route_w, float *y,
