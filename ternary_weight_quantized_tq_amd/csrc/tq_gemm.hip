@@ -83,146 +83,156 @@ __device__ __forceinline__ void tile_of(const GemmArgs& a, int& mt, int& nt) {
   }
 }
 
-struct Prefetch {
-  uint4 w[2];       // two quads of this thread's weight row
-  float s[2];       // scales of the (at most two) groups the step touches
-  uint4 ah[5];      // activation hi: 64 rows x 160 halves = 1280 uint4 / 256 threads
-  uint4 al[5];
-};
+// Main kernel.  Workgroup (M tile of 64 tokens, N tile of 256 weight rows);
+// wavefront w owns weight rows 64 (4 nt + w) .. + 63 and all 64 tokens.
+// Per 160-trit unit (K step) and row quarter h, a lane decodes its row's
+// word pair exactly as the M >= 2 decode GEMV does (lane j = l % 16 takes
+// row 16 h + j, lane group kb = l / 16 words 2 kb, 2 kb + 1 of the unit),
+// giving the B operands of the unit's five 32-trit steps of
+// v_mfma_f32_16x16x32_f16 straight in registers: fp16 codes from the
+// 81-entry table, times the row's fp16 group scale (s*t is exact in fp16).
+// Each B operand then serves eight A tiles (8 tokens x {hi, lo} each), so
+// one table read feeds eight MFMAs.  The activation tile of the unit (64
+// tokens x 160 trits, hi and lo rows) is double-buffered in LDS; the next
+// unit's activations, word pairs and (at a slice boundary) scales are
+// loaded while the current unit's MFMAs run.  One barrier per unit.
+constexpr int kATiles = BM / 8;           // A tiles of 8 tokens (16 A rows)
+constexpr int kAStride = BK + 8;          // halves per A row in LDS (16-byte pad)
+constexpr int kARows = 2 * BM;            // A row 2 t + p: part p (hi, lo) of token t
+constexpr int kAVecs = kARows * BK / 8 / kThreads;  // uint4 per thread per unit (10)
 
-__device__ __forceinline__ void prefetch(const GemmArgs& a, int mt, int nt, int step, Prefetch& p) {
-  const int tid = threadIdx.x;
-  // weights: row n of the tile = tid
-  int row = nt * BN + tid;
-  if (row > a.nb * 64 - 1) row = a.nb * 64 - 1;
-  const int k0 = step * BK;
-  const int slice = k0 / kSliceTrits;
-  const int q0 = (k0 % kSliceTrits) / 80;  // 0, 2, 4, 6
-  const uint4* wp = a.words + row64_quad_base(slice, row >> 6, a.nb) + (row & 63);
-  p.w[0] = wp[q0 * 64];
-  p.w[1] = wp[(q0 + 1) * 64];
-  const int g0 = k0 / TQ_GROUP;
-  const int g1 = min(g0 + 1, (a.groups + kSliceGroups - 1) / kSliceGroups * kSliceGroups - 1);
-  p.s[0] = f16_to_f32(a.scales[row64_scale_index(row, g0, a.nb)]);
-  p.s[1] = f16_to_f32(a.scales[row64_scale_index(row, g1, a.nb)]);
-  // activations: 64 rows x 160 halves = 64 x 20 uint4; thread covers 5 of them
-#pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int idx = tid + i * kThreads;  // 0..1279
-    const int r = idx / 20, c = idx % 20;
-    const size_t off = static_cast<size_t>(mt * BM + r) * a.kpad + k0 + c * 8;
-    p.ah[i] = *reinterpret_cast<const uint4*>(a.xh + off);
-    p.al[i] = *reinterpret_cast<const uint4*>(a.xl + off);
-  }
-}
+__device__ __forceinline__ uint2 load_pair_cached(const uint32_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 As_h[BM * LDA];
-  __shared__ __attribute__((aligned(16))) _Float16 As_l[BM * LDA];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[BN * LDA];
-  __shared__ uint32_t codes_lo[81], codes_hi[81];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][kARows * kAStride];   // 86,016 B
+  __shared__ __attribute__((aligned(16))) uint2 codes[81];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[kThreads / 64][kSliceGroups * 64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 15, kb = lane >> 4;
   int mt, nt;
   tile_of(a, mt, nt);
-  if (tid < 81) {
-    uint16_t h[4];
-    int c = tid;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(static_cast<float>(c % 3) - 1.0f));
-      c /= 3;
-    }
-    codes_lo[tid] = h[0] | (static_cast<uint32_t>(h[1]) << 16);
-    codes_hi[tid] = h[2] | (static_cast<uint32_t>(h[3]) << 16);
-  }
-  float16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  const int rb = nt * (BN / 64) + wave;
+  const bool active = rb < a.nb;
+  const int rbc = active ? rb : a.nb - 1;
+  const int nsl = slices_per_row(a.k);
+  build_code_table(codes, tid, kThreads);
 
-  Prefetch p;
-  prefetch(a, mt, nt, 0, p);
-  for (int step = 0; step < a.steps; ++step) {
-    TQ_LDS_BARRIER();  // previous step's fragments have been read
-    // activations -> LDS
+  // Loaders.  Unit u: slice u / 4, unit u % 4 of the slice.
+  auto a_src = [&](int u, int i) {  // i-th uint4 of this thread in unit u
+    const int idx = tid + i * kThreads;               // 0 .. 2559
+    const int part = idx / (BM * BK / 8), rem = idx % (BM * BK / 8);
+    const int t = rem / (BK / 8), c = rem % (BK / 8);
+    const _Float16* src = part ? a.xl : a.xh;
+    return reinterpret_cast<const uint4*>(src + static_cast<size_t>(mt * BM + t) * a.kpad + u * BK + 8 * c);
+  };
+  auto a_dst = [&](int buf, int i) {
+    const int idx = tid + i * kThreads;
+    const int part = idx / (BM * BK / 8), rem = idx % (BM * BK / 8);
+    const int t = rem / (BK / 8), c = rem % (BK / 8);
+    return reinterpret_cast<uint4*>(&As[buf][(2 * t + part) * kAStride + 8 * c]);
+  };
+  auto pair_ptr = [&](int u, int h) {
+    const int s = u >> 2, uu = u & 3;
+    return reinterpret_cast<const uint32_t*>(a.words) +
+           (row64_quad_base(s, rbc, a.nb) + (2 * uu + (kb >> 1)) * 64 + 16 * h + j) * 4 + 2 * (kb & 1);
+  };
+  const int sl = lane < kSliceGroups * 8 ? lane : 0;
+  auto scale_ptr = [&](int s) {
+    return reinterpret_cast<const uint4*>(a.scales + row64_scale_base(s, rbc, a.nb) + 8 * sl);
+  };
+
+  // Unit 0 into buffer 0, slice 0's scales.
+  uint4 av[kAVecs];
+  uint2 wq[4], wn[4];
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const int idx = tid + i * kThreads;
-      const int r = idx / 20, c = idx % 20;
-      *reinterpret_cast<uint4*>(&As_h[r * LDA + c * 8]) = p.ah[i];
-      *reinterpret_cast<uint4*>(&As_l[r * LDA + c * 8]) = p.al[i];
+  for (int i = 0; i < kAVecs; ++i) av[i] = *a_src(0, i);
+#pragma unroll
+  for (int h = 0; h < 4; ++h) wq[h] = load_pair_cached(pair_ptr(0, h));
+  uint4 scq = *scale_ptr(0);
+#pragma unroll
+  for (int i = 0; i < kAVecs; ++i) *a_dst(0, i) = av[i];
+  if (lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
+  TQ_LDS_BARRIER();
+
+  float4_t acc[4][kATiles];
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int t = 0; t < kATiles; ++t) acc[h][t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const char* cbase = reinterpret_cast<const char*>(codes);
+
+  for (int s = 0; s < nsl; ++s) {
+    _Float16 sc[4][kSliceGroups];  // this lane's rows 16 h + j, the slice's five groups
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int g = 0; g < kSliceGroups; ++g)
+        sc[h][g] = __builtin_bit_cast(_Float16, ssc[wave][g * 64 + 16 * h + j]);
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu) {
+      const int u = 4 * s + uu;
+      if (u >= a.steps) break;
+      const int buf = u & 1;
+      const bool more = u + 1 < a.steps;
+      // Next unit's loads (clamped to this unit on the last one).
+      const int un = more ? u + 1 : u;
+#pragma unroll
+      for (int i = 0; i < kAVecs; ++i) av[i] = *a_src(un, i);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) wn[h] = load_pair_cached(pair_ptr(un, h));
+      if (uu == 3) scq = *scale_ptr(min(s + 1, nsl - 1));
+      // B operands of the unit: offsets and table reads for the four row quarters.
+      uint2 cv[4][10];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        uint32_t o[10];
+        word_offsets_s<3, false>(wq[h].x, o);  // no inline asm next to MFMAs
+        word_offsets_s<3, false>(wq[h].y, o + 5);
+#pragma unroll
+        for (int c = 0; c < 10; ++c) cv[h][c] = *reinterpret_cast<const uint2*>(cbase + o[c]);
+      }
+      const _Float16* abase = &As[buf][j * kAStride + 8 * kb];
+#pragma unroll
+      for (int st = 0; st < 5; ++st) {
+        const int g = (160 * uu + 32 * st) / 128;  // compile-time: one scale group per step
+        half8_t af[kATiles];
+#pragma unroll
+        for (int t = 0; t < kATiles; ++t)
+          af[t] = *reinterpret_cast<const half8_t*>(abase + 16 * t * kAStride + 32 * st);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint4 bq = make_uint4(cv[h][2 * st].x, cv[h][2 * st].y, cv[h][2 * st + 1].x, cv[h][2 * st + 1].y);
+          const half8_t b = __builtin_bit_cast(half8_t, bq) * sc[h][g];
+#pragma unroll
+          for (int t = 0; t < kATiles; ++t)
+            acc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t], b, acc[h][t], 0, 0, 0);
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int i = 0; i < kAVecs; ++i) *a_dst(buf ^ 1, i) = av[i];
+      }
+      if (uu == 3 && lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) wq[h] = wn[h];
+      TQ_LDS_BARRIER();
     }
-    // weights -> fp16 s*t in LDS (row tid, 160 trits)
-    {
-      const int k0 = step * BK;
-      const int gsplit = (k0 / TQ_GROUP + 1) * TQ_GROUP - k0;  // first K offset in the second group
-      const _Float16 sa = static_cast<_Float16>(p.s[0]), sb = static_cast<_Float16>(p.s[1]);
-      _Float16* brow = &Bs[tid * LDA];
+  }
+
+  // D rows 4 kb + v of A tile t: v = 0, 1 the parts of token 8 t + 2 kb,
+  // v = 2, 3 those of token 8 t + 2 kb + 1; column j = row 16 h + j.
+  if (!active) return;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int col = rb * 64 + 16 * h + j;
+    if (col >= a.n) continue;
+#pragma unroll
+    for (int t = 0; t < kATiles; ++t)
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const uint32_t wv[4] = {p.w[q].x, p.w[q].y, p.w[q].z, p.w[q].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t o[5];
-          word_offsets_s<2, false>(wv[j], o);  // no inline asm next to MFMAs
-#pragma unroll
-          for (int h = 0; h < 5; ++h) {
-            const int kk = 4 * row64_chunk(4 * q + j, h);  // trit offset in the 160-trit unit
-            const _Float16 sc = kk < gsplit ? sa : sb;
-            const half2_t s2 = {sc, sc};
-            const half2_t lo = __builtin_bit_cast(
-                half2_t, *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(codes_lo) + o[h]));
-            const half2_t hi = __builtin_bit_cast(
-                half2_t, *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(codes_hi) + o[h]));
-            const half2_t vlo = lo * s2, vhi = hi * s2;
-            uint2 pk;
-            pk.x = __builtin_bit_cast(uint32_t, vlo);
-            pk.y = __builtin_bit_cast(uint32_t, vhi);
-            *reinterpret_cast<uint2*>(&brow[kk]) = pk;
-          }
-        }
+        const int row = mt * BM + 8 * t + 2 * kb + q;
+        if (row < a.m) a.y[static_cast<size_t>(row) * a.n + col] = acc[h][t][2 * q] + acc[h][t][2 * q + 1];
       }
-    }
-    if (step + 1 < a.steps) prefetch(a, mt, nt, step + 1, p);
-    TQ_LDS_BARRIER();
-    // MFMA: wavefront w covers columns [64w, 64w+64) of the tile, all 64 rows.
-    const int li = lane & 31, lk = (lane >> 5) * 8;
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      half8_t ah[2], al[2], bf[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        ah[i] = *reinterpret_cast<const half8_t*>(&As_h[(i * 32 + li) * LDA + kk + lk]);
-        al[i] = *reinterpret_cast<const half8_t*>(&As_l[(i * 32 + li) * LDA + kk + lk]);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const half8_t*>(&Bs[(wave * 64 + j * 32 + li) * LDA + kk + lk]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bf[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-    }
   }
-  // store: acc[i][j][v] is row 8*(v/4) + 4*(lane/32) + v%4 of the 32x32 block
-  // (i, j), column lane%32.
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = nt * BN + wave * 64 + j * 32 + (lane & 31);
-      if (col >= a.n) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = mt * BM + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
-        if (row < a.m) a.y[static_cast<size_t>(row) * a.n + col] = acc[i][j][v];
-      }
-    }
 }
 
 struct GemmPlan {
