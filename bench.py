@@ -267,7 +267,7 @@ def extra_gemm(tq, torch, synth, np):
             "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 1),
             "mfma_tflops_hi_lo": round(2 * useful / (ms * 1e-3) / 1e12, 1),
             "frac_f16_mfma_peak": round(2 * useful / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-            "compute": "v_mfma_f32_32x32x16_f16, x' split into fp16 hi + lo (2 passes), FP32 accumulate"}
+            "compute": "v_mfma_f32_16x16x32_f16, x' split into fp16 hi + lo A rows, B = fp16 s*t decoded into registers, FP32 accumulate"}
 
 
 def main():

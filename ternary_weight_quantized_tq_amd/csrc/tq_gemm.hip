@@ -159,7 +159,24 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < kATiles; ++t) acc[h][t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const char* cbase = reinterpret_cast<const char*>(codes);
+  // Code-table reads of row quarter h of a unit from its word pair.
+  auto decode = [&](uint2 w, uint2 (&cv)[10]) {
+    uint32_t o[10];
+    word_offsets_s<3, false>(w.x, o);  // no inline asm next to MFMAs
+    word_offsets_s<3, false>(w.y, o + 5);
+#pragma unroll
+    for (int c = 0; c < 10; ++c) cv[c] = *reinterpret_cast<const uint2*>(cbase + o[c]);
+  };
 
+  // Software pipeline: while unit u's MFMAs run, row quarter st of unit
+  // u + 1 is decoded (its words were loaded during unit u - 1), unit u + 1's
+  // activations are loaded for the other LDS buffer and unit u + 2's words
+  // are requested.
+  uint2 cv[4][10];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) decode(wq[h], cv[h]);
+#pragma unroll
+  for (int h = 0; h < 4; ++h) wq[h] = load_pair_cached(pair_ptr(min(1, a.steps - 1), h));  // unit 1
   for (int s = 0; s < nsl; ++s) {
     _Float16 sc[4][kSliceGroups];  // this lane's rows 16 h + j, the slice's five groups
 #pragma unroll
@@ -173,23 +190,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
       if (u >= a.steps) break;
       const int buf = u & 1;
       const bool more = u + 1 < a.steps;
-      // Next unit's loads (clamped to this unit on the last one).
-      const int un = more ? u + 1 : u;
+      const int un = more ? u + 1 : u;  // clamped to this unit on the last one
 #pragma unroll
       for (int i = 0; i < kAVecs; ++i) av[i] = *a_src(un, i);
-#pragma unroll
-      for (int h = 0; h < 4; ++h) wn[h] = load_pair_cached(pair_ptr(un, h));
       if (uu == 3) scq = *scale_ptr(min(s + 1, nsl - 1));
-      // B operands of the unit: offsets and table reads for the four row quarters.
-      uint2 cv[4][10];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        uint32_t o[10];
-        word_offsets_s<3, false>(wq[h].x, o);  // no inline asm next to MFMAs
-        word_offsets_s<3, false>(wq[h].y, o + 5);
-#pragma unroll
-        for (int c = 0; c < 10; ++c) cv[h][c] = *reinterpret_cast<const uint2*>(cbase + o[c]);
-      }
+      uint2 cvn[4][10];
       const _Float16* abase = &As[buf][j * kAStride + 8 * kb];
 #pragma unroll
       for (int st = 0; st < 5; ++st) {
@@ -198,6 +203,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int t = 0; t < kATiles; ++t)
           af[t] = *reinterpret_cast<const half8_t*>(abase + 16 * t * kAStride + 32 * st);
+        if (st < 4) {
+          decode(wq[st], cvn[st]);
+        } else {
+#pragma unroll
+          for (int h = 0; h < 4; ++h) wn[h] = load_pair_cached(pair_ptr(min(u + 2, a.steps - 1), h));
+        }
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
           const uint4 bq = make_uint4(cv[h][2 * st].x, cv[h][2 * st].y, cv[h][2 * st + 1].x, cv[h][2 * st + 1].y);
@@ -213,7 +224,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
       }
       if (uu == 3 && lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
 #pragma unroll
-      for (int h = 0; h < 4; ++h) wq[h] = wn[h];
+      for (int h = 0; h < 4; ++h) {
+        wq[h] = wn[h];
+#pragma unroll
+        for (int c = 0; c < 10; ++c) cv[h][c] = cvn[h][c];
+      }
       TQ_LDS_BARRIER();
     }
   }
