@@ -217,8 +217,8 @@ int tq_moe_gemv(const tq_weights *w_gate_up, const tq_weights *w_down,
 /* Prefill GEMM: Y[m][n] = sum_k fp32(s[n][k/128]) t[n][k] x'[m][k] for any
  * m >= 1 on the matrix cores.  x' (FP32 after the optional transform) is
  * split into an fp16 high part and an fp16 remainder, and each is
- * multiplied by the exact fp16 weights s*t decoded from the packed words in
- * LDS, accumulating in FP32.  w: ROW64, num_experts == 1.  Needs
+ * multiplied by the exact fp16 weights s*t decoded from the packed words
+ * (into registers), accumulating in FP32.  w: ROW64, num_experts == 1.  Needs
  * tq_workspace_bytes(TQ_OP_GEMM, w, m, 0) bytes of workspace. */
 int tq_gemm(const tq_weights *w, const void *x, int x_dtype, int m, float *y,
             unsigned flags, void *workspace, size_t ws_bytes, void *stream);

@@ -6,14 +6,11 @@
 //      hi = fp16(x') and lo = fp16(x' - hi), written to the workspace padded
 //      to whole tiles (zeros outside M x K).  hi + lo carries ~22 bits of x'.
 //   2. gemm: each workgroup computes a 64 x 256 tile of Y on the matrix cores
-//      (v_mfma_f32_32x32x16_f16).  Per 160-trit K step (2 quads of packed
-//      words per weight row) the workgroup decodes its 256 weight rows into
-//      fp16 values s*t, which are exact in fp16 because t is in {-1, 0, 1},
-//      so the per-group scale is applied before the product and no separate
-//      FP32 scale pass is needed; the activation tile (hi and lo) is staged
-//      next to it in LDS.  Both parts are multiplied and accumulated in FP32.
-//      The next step's words, scales and activations are loaded into
-//      registers while the current step's MFMAs run.
+//      (v_mfma_f32_16x16x32_f16; see gemm_kernel).  The weights' B operands
+//      are decoded from the packed words straight into registers as fp16
+//      s*t, which is exact because t is in {-1, 0, 1}, so the per-group
+//      scale is applied before the product and no separate FP32 scale pass
+//      is needed; hi and lo of x' are separate A rows.  FP32 accumulation.
 // Weights stream once per 64-row M tile; tiles are ordered so that all N
 // tiles of one M tile run on one XCD, keeping that activation tile (64 x K x
 // 4 bytes) in the XCD's L2.
