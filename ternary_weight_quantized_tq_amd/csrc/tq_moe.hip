@@ -692,8 +692,8 @@ extern "C" int tq_moe_gemv(const tq_weights* w_gate_up, const tq_weights* w_down
   if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED)) return TQ_EINVAL;
   const int E = w_gate_up->num_experts, hidden = w_gate_up->k, inter = w_gate_up->n / 2;
   if (w_gate_up->n % 2 || inter % 64 || w_down->n != hidden || w_down->k != inter) return TQ_ESHAPE;
-  if (E > kMaxExperts) return TQ_EUNSUPPORTED;
   if (t < 1 || topk < 1 || topk > 32 || static_cast<long long>(t) * topk > INT_MAX / 4) return TQ_ESHAPE;
+  if (E > kMaxExperts && !moe_pairs(t, topk)) return TQ_EUNSUPPORTED;  // the bucket step holds E counters in LDS
   const MoeLayout l = moe_layout(E, t, topk, hidden, inter);
   if (ws_bytes < l.total) return TQ_ENOSPACE;
   char* ws = static_cast<char*>(workspace);

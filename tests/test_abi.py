@@ -97,3 +97,18 @@ def test_binding_raises_with_message():
         tq.tq_gemv(w, 0x3000, 1, 0x4000, stream=0) if False else tq._check("tq_gemv", tq.lib().tq_gemv(
             ctypes.byref(w.desc()), 0x3000, tq.TQ_BF16, 1, 0x4000, 1, 0x5000, 1 << 20, None))
     assert e.value.status == tq.TQ_EFORMAT
+
+
+@pytest.mark.parametrize("experts,t,topk,status", [
+    (1500, 20, 4, tq.TQ_EUNSUPPORTED),   # 80 pairs: bucketed, at most 1024 experts
+    (1500, 16, 4, tq.TQ_ENOSPACE),       # 64 pairs: per-pair path, no expert limit (then: no workspace)
+    (64, 0, 4, tq.TQ_ESHAPE),
+    (64, 2, 33, tq.TQ_ESHAPE),
+])
+def test_moe_limits(experts, t, topk, status):
+    lib = tq.lib()
+    gu = _desc(n=256, k=512, num_experts=experts)
+    dn = _desc(n=512, k=128, num_experts=experts)
+    st = lib.tq_moe_gemv(ctypes.byref(gu), ctypes.byref(dn), 0x3000, tq.TQ_BF16, t, topk, 0x4000, 0x5000, 0x6000,
+                         tq.TQ_FWHT_FUSED, 0x7000, 0, None)
+    assert st == status

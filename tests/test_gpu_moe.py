@@ -148,3 +148,27 @@ def test_moe_expert_layer_workload(wl):
     y_ref = O.moe(act.values, ids, rw, gu_w, gu_s, dn_w, dn_s, wl.hidden, wl.inter, tokens=tokens)
     err = O.rel_l2(y[tokens], y_ref[tokens])
     assert err < 1e-5, err
+
+
+def test_moe_many_experts_few_pairs():
+    """1500 experts (past the bucket step's 1024) on the per-pair path; only
+    the experts in use are packed."""
+    E, hidden, inter, T, topk = 1500, 256, 128, 2, 4
+    ids = np.array([[1499, 1024, 3, 700], [1025, 1499, 0, 1100]], np.int32)
+    w_gu = tq.empty_weights(2 * inter, hidden, num_experts=E)
+    w_dn = tq.empty_weights(hidden, inter, num_experts=E)
+    h = {"gu_w": {}, "gu_s": {}, "dn_w": {}, "dn_s": {}}
+    for e in sorted(set(ids.ravel().tolist())):
+        t = synth.trits(1100 + e, 2 * inter, hidden)
+        s = synth.scales(1101 + e, 2 * inter, hidden // 128)
+        gpu_pack_expert(w_gu, e, trits=t, scales=s)
+        h["gu_w"][e], h["gu_s"][e] = O.pack(t), s
+        t = synth.trits(1102 + e, hidden, inter)
+        s = synth.scales(1103 + e, hidden, inter // 128)
+        gpu_pack_expert(w_dn, e, trits=t, scales=s)
+        h["dn_w"][e], h["dn_s"][e] = O.pack(t), s
+    act = synth.activations(111, T, hidden, "bf16")
+    rw = np.full((T, topk), 0.25)
+    y = run_moe(w_gu, w_dn, act_tensor(act), T, topk, ids, rw)
+    y_ref = O.moe(act.values, ids, rw, h["gu_w"], h["gu_s"], h["dn_w"], h["dn_s"], hidden, inter)
+    assert O.rel_l2(y, y_ref) < 1e-5
