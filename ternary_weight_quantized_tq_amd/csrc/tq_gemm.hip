@@ -25,10 +25,7 @@ namespace {
 constexpr int BM = 64;          // rows of Y per workgroup
 constexpr int BN = 256;         // columns of Y per workgroup (4 wavefronts x 64)
 constexpr int BK = 160;         // trits per K step = 2 quads = 8 words
-constexpr int LDA = BK + 8;     // padded LDS row stride (halves) against bank conflicts
 constexpr int kThreads = 256;
-
-typedef float float16_t __attribute__((ext_vector_type(16)));
 
 #define TQ_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
