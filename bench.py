@@ -21,8 +21,9 @@ serves them.
   cpu_baseline  the FP64 CPU oracle (unpack + transform + dequantised
             matvec) on a bounded row sample, in packed-weight GB/s
 
-`extras` adds the other workloads: the 8-stream transformer block (M = 8),
-the 256-expert MoE layer at T = 1 and T = 64, and the prefill GEMM.
+`extras` adds the other workloads: one transformer block's seven linears at
+M = 1 (single stream) and M = 8, the 256-expert MoE layer at T = 1 and
+T = 64, and the prefill GEMM.
 """
 from __future__ import annotations
 
@@ -53,7 +54,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-extras", action="store_true", help="only the main metric")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--only-extra", choices=["block_m8", "moe", "prefill_gemm"],
+    p.add_argument("--only-extra", choices=["block_m1", "block_m8", "moe", "prefill_gemm"],
                    help="run one extra workload alone and print its JSON (for profiling)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy (for scaling rocprofv3 byte counters)")
@@ -162,17 +163,18 @@ def cpu_baseline(O, synth, lins, w64s, seconds):
 
 
 # --------------------------------------------------------------- extras ---
-def extra_block_m8(tq, torch, synth, np):
-    """One dense block's seven linears at 8 activation rows.  Linears that
-    share an input (q, k, v; gate, up) are also packed as one matrix of
-    concatenated rows (the usual fused projections, same bytes and the same
-    per-row quantisation): one launch per input instead of seven."""
-    wl = synth.DENSE_BLOCK_M8
+def extra_block(tq, torch, synth, np, wl):
+    """One dense block's seven linears at wl.m activation rows (1: single
+    stream, 8: eight streams).  Linears that share an input (q, k, v; gate,
+    up) are also packed as one matrix of concatenated rows (the usual fused
+    projections, same bytes and the same per-row quantisation): one launch
+    per input instead of seven."""
+    m = wl.m
     nbytes = sum(tq.tq_packed_bytes(l.n, l.k) for l in wl.linears)
     groups = {}
     for lin in wl.linears:
         groups.setdefault(lin.x_seed, []).append(lin)
-    xs = {s: bf16(torch, synth.activations(s, 8, g[0].k, "bf16")) for s, g in groups.items()}
+    xs = {s: bf16(torch, synth.activations(s, m, g[0].k, "bf16")) for s, g in groups.items()}
 
     def run(mats, label):
         """mats: [(name, n, k, x_seed, w64)]; timed step and per-matrix kernel time."""
@@ -180,18 +182,18 @@ def extra_block_m8(tq, torch, synth, np):
         torch.cuda.synchronize()
         copies = max(1, -(-ROTATE_BYTES // nbytes))
         sets = [base] + [[clone_w(tq, w) for w in base] for _ in range(copies - 1)]
-        y_all = torch.empty(8 * sum(m[1] for m in mats), dtype=torch.float32, device="cuda")
-        offs = np.cumsum([0] + [8 * m[1] for m in mats])
-        ys = [y_all[offs[i]:offs[i + 1]].view(8, m[1]) for i, m in enumerate(mats)]
+        y_all = torch.empty(m * sum(mt[1] for mt in mats), dtype=torch.float32, device="cuda")
+        offs = np.cumsum([0] + [m * mt[1] for mt in mats])
+        ys = [y_all[offs[i]:offs[i + 1]].view(m, mt[1]) for i, mt in enumerate(mats)]
 
         def step(i):
             y_all.zero_()
-            for j, (m, w) in enumerate(zip(mats, sets[i % copies])):
-                tq.tq_gemv(w, xs[m[3]], 8, ys[j], tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE)
+            for j, (mt, w) in enumerate(zip(mats, sets[i % copies])):
+                tq.tq_gemv(w, xs[mt[3]], m, ys[j], tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE)
         ms = timed(torch, 32, 4, step)
         per = {}
-        for j, m in enumerate(mats):
-            g = capture(torch, copies, lambda i: tq.tq_gemv(sets[i][j], xs[m[3]], 8, ys[j],
+        for j, mt in enumerate(mats):
+            g = capture(torch, copies, lambda i: tq.tq_gemv(sets[i][j], xs[mt[3]], m, ys[j],
                                                              tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE))
             g.replay()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -199,22 +201,31 @@ def extra_block_m8(tq, torch, synth, np):
             g.replay()
             b.record()
             torch.cuda.synchronize()
-            per[m[0]] = round(1e3 * a.elapsed_time(b) / copies, 3)
+            per[mt[0]] = round(1e3 * a.elapsed_time(b) / copies, 3)
         del sets
         torch.cuda.empty_cache()
         return {"launches": len(mats), "ms_per_step": round(ms, 4), "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                 "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "layer_tok_s": round(8 / (ms * 1e-3), 1), "kernel_us": per, "weight_copies_rotated": copies}
+                "layer_tok_s": round(m / (ms * 1e-3), 1), "kernel_us": per, "weight_copies_rotated": copies}
 
     w64 = {l.name: synth.weights(l.w_seed, l.n, l.k) for l in wl.linears}
     fused = run([("|".join(l.name for l in g), sum(l.n for l in g), g[0].k, s,
                   np.concatenate([w64[l.name] for l in g], axis=0)) for s, g in groups.items()], "fused")
     separate = run([(l.name, l.n, l.k, l.x_seed, w64[l.name]) for l in wl.linears], "separate")
-    out = {"workload": wl.name, "m": 8, "packed_bytes_per_step": nbytes}
+    out = {"workload": wl.name, "m": m, "packed_bytes_per_step": nbytes}
     out.update(fused)
     out["separate_linears"] = separate
-    out["compute"] = "v_mfma_f32_16x16x32_f16 (x' as two fp16 parts in the A rows, fp16 trit codes, FP32 accumulate)"
+    out["compute"] = ("LDS partial-sum table, FP32" if m == 1 else
+                      "v_mfma_f32_16x16x32_f16 (x' as two fp16 parts in the A rows, fp16 trit codes, FP32 accumulate)")
     return out
+
+
+def extra_block_m1(tq, torch, synth, np):
+    return extra_block(tq, torch, synth, np, synth.DENSE_BLOCK_M1)
+
+
+def extra_block_m8(tq, torch, synth, np):
+    return extra_block(tq, torch, synth, np, synth.DENSE_BLOCK_M8)
 
 
 def extra_moe(tq, torch, synth, np):
@@ -286,7 +297,8 @@ def main():
     torch.cuda.set_device(0)
 
     if args.only_extra:
-        fn = {"block_m8": extra_block_m8, "moe": extra_moe, "prefill_gemm": extra_gemm}[args.only_extra]
+        fn = {"block_m1": extra_block_m1, "block_m8": extra_block_m8, "moe": extra_moe,
+              "prefill_gemm": extra_gemm}[args.only_extra]
         print(json.dumps({args.only_extra: fn(tq, torch, synth, np)}), flush=True)
         return
 
@@ -413,7 +425,8 @@ def main():
     }
     if not args.no_extras:
         extras = {}
-        for name, fn in (("block_m8", extra_block_m8), ("moe", extra_moe), ("prefill_gemm", extra_gemm)):
+        for name, fn in (("block_m1", extra_block_m1), ("block_m8", extra_block_m8), ("moe", extra_moe),
+                         ("prefill_gemm", extra_gemm)):
             log(f"extra: {name} ...")
             try:
                 extras[name] = fn(tq, torch, synth, np)

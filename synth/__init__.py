@@ -132,8 +132,9 @@ DENSE_DECODE_27B = Workload("dense-27b-decode-up-down-m1", 1, "bf16", [
     Linear("down", 5120, 17408, 2002, 2004),
 ])
 
-# q, k, v share the attention input; gate and up share the MLP input.
-DENSE_BLOCK_M8 = Workload("dense-27b-block-m8", 8, "bf16", [
+# One dense 27B-class decoder block's linears; q, k, v share the attention
+# input, gate and up the MLP input.
+BLOCK_LINEARS = [
     Linear("q", 5120, 5120, 3001, 3010),
     Linear("k", 1024, 5120, 3002, 3010),
     Linear("v", 1024, 5120, 3003, 3010),
@@ -141,8 +142,9 @@ DENSE_BLOCK_M8 = Workload("dense-27b-block-m8", 8, "bf16", [
     Linear("gate", 17408, 5120, 3005, 3012),
     Linear("up", 17408, 5120, 3006, 3012),
     Linear("down", 5120, 17408, 3007, 3013),
-])
-
+]
+DENSE_BLOCK_M8 = Workload("dense-27b-block-m8", 8, "bf16", BLOCK_LINEARS)
+DENSE_BLOCK_M1 = Workload("dense-27b-block-m1", 1, "bf16", BLOCK_LINEARS)  # single-stream decode
 
 @dataclass
 class MoEWorkload:

@@ -247,6 +247,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a)
     }
   }
   TQ_LDS_BARRIER();
+  if (t.wave >= a.bpg) return;  // a prologue-only wavefront (small matrices)
 
   float acc[kSliceGroups] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   if (t.nq_here == kSliceQuads) {
@@ -544,7 +545,10 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
     if (ws_bytes < p.partial_bytes) return TQ_ENOSPACE;
   }
   if (m == 1) {
+    // Row blocks per workgroup as above; at least one wavefront per
+    // transform block, so that a small matrix's prologue runs in parallel.
     plan_waves(p, 1, kMaxWaves);
+    p.waves = max(p.waves, kSliceGroups);
   } else {
     // Row blocks per workgroup so that the grid fills the compute units in
     // one round; every activation row gets a wavefront for the prologue
