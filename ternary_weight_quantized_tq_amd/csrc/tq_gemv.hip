@@ -313,7 +313,11 @@ constexpr int kMfmaMaxWaves = 9;  // 3 per SIMD at most: ~168 registers per lane
 constexpr int kXStride = kSliceTrits + 8;
 constexpr int kMfmaLookahead = 10;  // of 16 word pairs per lane: weights in flight during the prologue
 
-template <int M, int XT>
+// kUs > 1 (small matrices): the four units of a row block's slice are
+// split over kUs wavefronts (wavefront w: block w / kUs, units
+// (w % kUs) 4 / kUs ..), which shortens each wavefront's dependent chain;
+// their sums are added in LDS in a fixed order before the epilogue.
+template <int M, int XT, int kUs>
 __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs a) {
   // A rows padded by 16 bytes: the 16 lanes of a lane group read 16 rows at
   // one offset, which then fall on 16 different 4-bank groups.
@@ -322,10 +326,18 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
   __shared__ __attribute__((aligned(16))) uint2 codes[kLutEntries];
   __shared__ __attribute__((aligned(16))) uint16_t ssc[kMfmaMaxWaves][kSliceGroups * 64];
   __shared__ int xexp[M];
-  const Tile t = make_tile(a);
+  __shared__ float red[kUs > 1 ? kMfmaMaxWaves : 1][16][64];  // unit-split partial sums
+  Tile t = make_tile(a);
   constexpr int kUnits = 4;                       // 8-word units per slice
   constexpr int kIters = 4 * kUnits;              // (unit, row quarter)
   const int j = t.lane & 15, kb = t.lane >> 4;
+  const int part = t.wave % kUs;                  // this wavefront's units: u0 .. u1 - 1
+  const int u0 = part * (kUnits / kUs), u1 = u0 + kUnits / kUs;
+  if (kUs > 1) {  // row block of this wavefront: t.wave / kUs
+    t.rb = t.rg * a.bpg + t.wave / kUs;
+    t.active = t.wave / kUs < a.bpg && t.rb < a.nb;
+    t.rbc = t.active ? t.rb : a.nb - 1;
+  }
 
   // Wavefront w transforms activation row w (and w + waves, ... when there
   // are fewer wavefronts than rows): the slice's five blocks at once, loaded
@@ -343,15 +355,21 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
   // all-zero words), so every unit is read and no clamp is needed.
   // Wavefronts past the workgroup's row blocks (small matrices: more
   // wavefronts than blocks, for the prologue) read one cached line instead.
-  const bool decodes = __builtin_amdgcn_readfirstlane(t.wave < a.bpg ? 1 : 0) != 0;
+  const bool decodes = __builtin_amdgcn_readfirstlane(t.wave < a.bpg * kUs ? 1 : 0) != 0;
   const uint32_t* wbase = reinterpret_cast<const uint32_t*>(a.words) +
                           (decodes ? (row64_quad_base(t.slice, t.rbc, a.nb) + (kb >> 1) * 64 + j) * 4 + 2 * (kb & 1)
                                    : 0);
   const int pstride = decodes ? 1 : 0;
   auto pair_at = [&](int it) { return wbase + pstride * ((2 * (it / 4)) * 64 + 16 * (it % 4)) * 4; };  // it = 4 u + h
   uint2 wq[kIters];
+  if (kUs == 1) {
 #pragma unroll
-  for (int i = 0; i < kMfmaLookahead; ++i) wq[i] = load_pair(pair_at(i));
+    for (int i = 0; i < kMfmaLookahead; ++i) wq[i] = load_pair(pair_at(i));
+  } else {  // all of this wavefront's pairs (at most 8)
+#pragma unroll
+    for (int i = 0; i < kIters; ++i)
+      if (i >= 4 * u0 && i < 4 * u1) wq[i] = load_pair(pair_at(i));
+  }
   TQ_ORDER();
   // The block's 5 x 64 scales (640 contiguous bytes) in one 16-byte load by
   // lanes 0..39, staged in LDS; each lane needs 20 of them at stride 32 B.
@@ -396,7 +414,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
   const _Float16* xrow = (j < 2 * M ? &xh[j < 2 * M ? j : 0][0] : &zeros[0]) + 8 * kb;
   const char* cbase = reinterpret_cast<const char*>(codes);
 
-  if (!decodes) return;
+  if (kUs == 1 && !decodes) return;
   float4_t acc[4];
   float tot[4][4];
 #pragma unroll
@@ -409,13 +427,14 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
   // four quarters' independent accumulation chains.
 #pragma unroll
   for (int u = 0; u < kUnits; ++u) {
+    if (kUs > 1 && (!decodes || u < u0 || u >= u1)) continue;
     half8_t af[5];
 #pragma unroll
     for (int s = 0; s < 5; ++s) af[s] = *reinterpret_cast<const half8_t*>(xrow + 160 * u + 32 * s);
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const int it = u * 4 + h;
-      if (it + kMfmaLookahead < kIters) wq[it + kMfmaLookahead] = load_pair(pair_at(it + kMfmaLookahead));
+      if (kUs == 1 && it + kMfmaLookahead < kIters) wq[it + kMfmaLookahead] = load_pair(pair_at(it + kMfmaLookahead));
       uint32_t o[10];
       word_offsets_s<3, false>(wq[it].x, o);
       word_offsets_s<3, false>(wq[it].y, o + 5);
@@ -427,7 +446,10 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
         const int step = 5 * u + s;  // scale group step / 4
         const uint4 bq = make_uint4(cv[2 * s].x, cv[2 * s].y, cv[2 * s + 1].x, cv[2 * s + 1].y);
         acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s], __builtin_bit_cast(half8_t, bq), acc[h], 0, 0, 0);
-        if ((step & 3) == 3) {
+        // A scale group's four steps can span two units; with the units
+        // split over wavefronts, the last step of a wavefront's range also
+        // closes its share of the group.
+        if ((step & 3) == 3 || (kUs > 1 && s == 4 && u == u1 - 1)) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) tot[h][v] = fmaf(sc[h][step >> 2], acc[h][v], tot[h][v]);
           acc[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -435,6 +457,23 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
       }
     }
     TQ_ORDER();
+  }
+  if (kUs > 1) {
+    // The units' sums of a row block, added in unit order by the wavefront
+    // with the first units.
+    if (decodes)
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[t.wave][4 * h + v][t.lane] = tot[h][v];
+    __syncthreads();
+    if (!decodes || part != 0) return;
+#pragma unroll
+    for (int p = 1; p < kUs; ++p)
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) tot[h][v] += red[t.wave + p][4 * h + v][t.lane];
   }
   // D rows 4 kb + v: v = 0, 1 are the two parts of activation row 2 kb,
   // v = 2, 3 those of row 2 kb + 1.
@@ -493,11 +532,17 @@ void plan_waves(GemvPlan& p, int min_waves, int max_waves) {
   p.ngroups = (p.nb + w - 1) / w;
 }
 
+template <int M, int kUs>
+void launch_mfma_us(int x_dtype, dim3 grid, dim3 block, hipStream_t s, const GemvArgs& a) {
+  if (x_dtype == TQ_F32) hipLaunchKernelGGL((gemv_mfma_kernel<M, TQ_F32, kUs>), grid, block, 0, s, a);
+  else if (x_dtype == TQ_BF16) hipLaunchKernelGGL((gemv_mfma_kernel<M, TQ_BF16, kUs>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((gemv_mfma_kernel<M, TQ_F16, kUs>), grid, block, 0, s, a);
+}
+
 template <int M>
-void launch_mfma(int x_dtype, dim3 grid, dim3 block, hipStream_t s, const GemvArgs& a) {
-  if (x_dtype == TQ_F32) hipLaunchKernelGGL((gemv_mfma_kernel<M, TQ_F32>), grid, block, 0, s, a);
-  else if (x_dtype == TQ_BF16) hipLaunchKernelGGL((gemv_mfma_kernel<M, TQ_BF16>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((gemv_mfma_kernel<M, TQ_F16>), grid, block, 0, s, a);
+void launch_mfma(int x_dtype, int us, dim3 grid, dim3 block, hipStream_t s, const GemvArgs& a) {
+  if (us == 4) launch_mfma_us<M, 4>(x_dtype, grid, block, s, a);
+  else launch_mfma_us<M, 1>(x_dtype, grid, block, s, a);
 }
 
 }  // namespace
@@ -538,6 +583,7 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
   if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED | TQ_ACCUMULATE)) return TQ_EINVAL;
   if (m < 1 || m > 8) return TQ_ESHAPE;
   GemvPlan p = plan_sizes(w->n, w->k, m);
+  int us = 1;
   const bool accumulate = (flags & TQ_ACCUMULATE) != 0;
   const int mode = accumulate ? kAtomic : (p.nsl > 1 ? kPartial : kDirect);
   if (mode == kPartial) {
@@ -552,9 +598,13 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
   } else {
     // Row blocks per workgroup so that the grid fills the compute units in
     // one round; every activation row gets a wavefront for the prologue
-    // (one transform per row), so small matrices have idle decoders.
+    // (one transform per row).
     plan_waves(p, 1, kMfmaMaxWaves);
-    p.waves = max(p.waves, m);
+    // One or two row blocks per workgroup (small matrices): split each
+    // block's units over four wavefronts.  (A split over two wavefronts at
+    // three or four row blocks measured no faster.)
+    us = 4 * p.bpg <= kMfmaMaxWaves ? 4 : 1;
+    p.waves = max(us * p.bpg, m);
   }
   GemvArgs a;
   a.words = reinterpret_cast<const uint4*>(w->words);
@@ -581,13 +631,13 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
       else if (x_dtype == TQ_BF16) hipLaunchKernelGGL(gemv_lut_m1_kernel<TQ_BF16>, grid, block, 0, s, a);
       else hipLaunchKernelGGL(gemv_lut_m1_kernel<TQ_F16>, grid, block, 0, s, a);
       break;
-    case 2: launch_mfma<2>(x_dtype, grid, block, s, a); break;
-    case 3: launch_mfma<3>(x_dtype, grid, block, s, a); break;
-    case 4: launch_mfma<4>(x_dtype, grid, block, s, a); break;
-    case 5: launch_mfma<5>(x_dtype, grid, block, s, a); break;
-    case 6: launch_mfma<6>(x_dtype, grid, block, s, a); break;
-    case 7: launch_mfma<7>(x_dtype, grid, block, s, a); break;
-    default: launch_mfma<8>(x_dtype, grid, block, s, a); break;
+    case 2: launch_mfma<2>(x_dtype, us, grid, block, s, a); break;
+    case 3: launch_mfma<3>(x_dtype, us, grid, block, s, a); break;
+    case 4: launch_mfma<4>(x_dtype, us, grid, block, s, a); break;
+    case 5: launch_mfma<5>(x_dtype, us, grid, block, s, a); break;
+    case 6: launch_mfma<6>(x_dtype, us, grid, block, s, a); break;
+    case 7: launch_mfma<7>(x_dtype, us, grid, block, s, a); break;
+    default: launch_mfma<8>(x_dtype, us, grid, block, s, a); break;
   }
   TQ_LAUNCH_CHECK();
   if (mode == kPartial) {
