@@ -267,18 +267,20 @@ __global__ __launch_bounds__(256) void moe_gate_up_kernel(MoeArgs a) {
       const int u1 = __builtin_amdgcn_readfirstlane(min(u0 + 2, row64_slice_quads(K, s) / 2));
       const uint32_t* wb = wexp + (row64_quad_base(s, rb, nb) + (kb >> 1) * 64 + j) * 4 + 2 * (kb & 1);
       uint2 wq[4][4];
+      // The block's scales first, by every lane (a load under a lane
+      // condition is waited for at once), staged after the transform.
+      const uint4 scq = *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rb, nb) +
+                                                       8 * (lane < kSliceGroups * 8 ? lane : 0));
       for (int m = wave; m < M; m += 4) {
         SliceAct xa;
         const size_t base = static_cast<size_t>(pair_of(q + m) / a.topk) * K;
         load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) { load_act2(a.x, a.x_dtype, base + i, v0, v1); });
         transform_slice(xa, xh, xexp, m, a.fused != 0, lane);
       }
-      if ((wave & 1) == 0 && lane < kSliceGroups * 8)
-        *reinterpret_cast<uint4*>(&ssc[wave >> 1][8 * lane]) =
-            *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rb, nb) + 8 * lane);
+      if ((wave & 1) == 0 && lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[wave >> 1][8 * lane]) = scq;
       __syncthreads();
       // Many workgroups in flight: the weights are requested here, after the
-      // barrier, which measured faster than requesting them early.
+      // barrier (requesting them before the transform measured 1-2 % slower).
       mfma_load(wb, u0, u1, wq);
       float ts[4][4] = {};
       mfma_units(wq, ssc[wave >> 1], xrow, cbase, j, u0, u1, ts);
