@@ -5,6 +5,10 @@
 // wavefront w owns row 64*(W*blockIdx.y + w) + r.  W is chosen on the host so
 // that (row groups) x (slices) fills the compute units in a single round;
 // partial sums of the slices of a row are then combined (see finish()).
+// Small matrices (few row blocks per workgroup): an M == 1 workgroup still
+// has five wavefronts, one per transform block of the prologue; an M >= 2
+// workgroup of one or two row blocks splits each block's four units over
+// four wavefronts.
 // All lanes of a wavefront sit at the same K position, so activations and
 // lookup tables are wavefront-uniform and scale-group boundaries fall at
 // compile-time chunk positions.
