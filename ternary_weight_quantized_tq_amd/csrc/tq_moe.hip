@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256) void moe_gate_up_kernel(MoeArgs a) {
   auto pair_of = [&](int i) { return a.pairs[i]; };
   const int b = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 15, kb = lane >> 4;
-  const int K = a.hidden, nb = row_blocks(2 * a.inter), I2 = 2 * a.inter;
+  const int K = a.hidden, nb = row_blocks(2 * a.inter);
   const uint32_t* wexp = reinterpret_cast<const uint32_t*>(a.gu_words + static_cast<size_t>(e) * a.gu_wstride);
   const uint16_t* sexp = a.gu_scales + static_cast<size_t>(e) * a.gu_sstride;
   const int rb = wave < 2 ? b : b + a.inter / 64;  // this wavefront's gate or up block
