@@ -329,26 +329,34 @@ __global__ __launch_bounds__(256) void moe_down_kernel(MoeArgs a) {
     const int M = min(kTile, p1 - q);
     const _Float16* xrow = (j < 2 * M ? &xh[j < 2 * M ? j : 0][0] : &zeros[0]) + 8 * kb;
     float tot[4][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}};
+    const float* h0 = a.gu + static_cast<size_t>(a.pairs[q + min(wave, M - 1)]) * K;
+    const float* h1 = a.gu + static_cast<size_t>(a.pairs[q + min(wave + 4, M - 1)]) * K;
     for (int s = 0; s < nsl; ++s) {
       __syncthreads();
+      // h rows wave, wave + 4 of the tile, the scales, then the weights, all
+      // before the transform (which waits for h only); every load
+      // unconditional (rows clamped, slices stored whole).
+      SliceAct x0, x1;
+      load_slice(x0, s, K, lane, [&](int i, float& v0, float& v1) {
+        const float2 v = *reinterpret_cast<const float2*>(h0 + i);
+        v0 = v.x;
+        v1 = v.y;
+      });
+      load_slice(x1, s, K, lane, [&](int i, float& v0, float& v1) {
+        const float2 v = *reinterpret_cast<const float2*>(h1 + i);
+        v0 = v.x;
+        v1 = v.y;
+      });
+      const uint4 scq = *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rbc, nb) +
+                                                       8 * (lane < kSliceGroups * 8 ? lane : 0));
       const uint32_t* wb = wexp + (row64_quad_base(s, rbc, nb) + (kb >> 1) * 64 + j) * 4 + 2 * (kb & 1);
-      const int u1 = __builtin_amdgcn_readfirstlane(row64_slice_quads(K, s) / 2);
       uint2 wq[4][4];
-      for (int m = wave; m < M; m += 4) {
-        const float* hrow = a.gu + static_cast<size_t>(a.pairs[q + m]) * K;
-        SliceAct xa;
-        load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) {
-          const float2 v = *reinterpret_cast<const float2*>(hrow + i);
-          v0 = v.x;
-          v1 = v.y;
-        });
-        transform_slice(xa, xh, xexp, m, true, lane);
-      }
-      if (lane < kSliceGroups * 8)
-        *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) =
-            *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rbc, nb) + 8 * lane);
+      mfma_load(wb, 0, 4, wq);
+      if (wave < M) transform_slice(x0, xh, xexp, wave, true, lane);
+      if (wave + 4 < M) transform_slice(x1, xh, xexp, wave + 4, true, lane);
+      if (lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
       __syncthreads();
-      mfma_load(wb, 0, u1, wq);
+      const int u1 = __builtin_amdgcn_readfirstlane(row64_slice_quads(K, s) / 2);
       if (rb < nb) {
         float ts[4][4] = {};
         mfma_units(wq, ssc[wave], xrow, cbase, j, 0, u1, ts);
