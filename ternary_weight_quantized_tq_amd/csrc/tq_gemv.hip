@@ -188,38 +188,32 @@ __device__ __forceinline__ void word_lookups(const float* lut, uint32_t word, in
   }
 }
 
-// Value of the neighbouring lane (lane ^ 1), through DPP.
-__device__ __forceinline__ float lane_xor1(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
-}
-
-// Table rows of the 32 chunk positions of transform block `blk`, built from
-// the registers of the wavefront that transformed it: lane 2j holds x'[4j],
-// x'[4j+1] and lane 2j+1 holds x'[4j+2], x'[4j+3] of position p = 32 blk + j.
-// With A[d0 + 3 d1] = (d0-1) x0 + (d1-1) x1 and B[d2 + 3 d3] likewise for
-// x2, x3, entry c = A[c % 9] + B[c / 9]; the even lane writes c / 9 in
-// 0..4, the odd lane 5..8.
-__device__ __forceinline__ void build_rows(float* lut, int blk, int lane, float v0, float v1) {
-  const float p0 = lane_xor1(v0), p1 = lane_xor1(v1);
-  const bool odd = (lane & 1) != 0;
-  const float x0 = odd ? p0 : v0, x1 = odd ? p1 : v1;
-  const float x2 = odd ? v0 : p0, x3 = odd ? v1 : p1;
-  const float A[9] = {-x0 - x1, -x1, x0 - x1, -x0, 0.0f, x0, x1 - x0, x1, x0 + x1};
-  const float B[9] = {-x2 - x3, -x3, x2 - x3, -x2, 0.0f, x2, x3 - x2, x3, x2 + x3};
-  float* row = lut + (blk * 32 + (lane >> 1)) * kLutEntries + (odd ? 45 : 0);
+// The partial-sum table of the slice from its transformed activations xs
+// (640 floats in LDS): T[p][c] = sum_i (d_i - 1) x'[4p + i] for position p
+// (0..159) and chunk c = d0 + 3 d1 + 9 d2 + 27 d3.  Work item i (< 480):
+// position i / 3, entries 27 t .. 27 t + 26 with t = i % 3 = d3.  Consecutive
+// items write at a stride of 27 words, so a wavefront's stores spread over
+// all banks.  Entries are A[d0 + 3 d1] + ((d2 - 1) x2 + (d3 - 1) x3), the
+// products by -1, 0, 1 being exact.
+__device__ __forceinline__ void build_table(float* lut, const float* xs, int tid, int nthreads) {
+  for (int i = tid; i < kSliceChunks * 3; i += nthreads) {
+    const int p = i / 3, t = i - 3 * p;
+    const float4 x = *reinterpret_cast<const float4*>(xs + 4 * p);
+    const float A[9] = {-x.x - x.y, -x.y, x.x - x.y, -x.x, 0.0f, x.x, x.y - x.x, x.y, x.x + x.y};
+    const float x3 = t == 0 ? -x.w : (t == 1 ? 0.0f : x.w);
+    float* row = lut + p * kLutEntries + 27 * t;
+    const float base[3] = {x3 - x.z, x3, x3 + x.z};
 #pragma unroll
-  for (int r = 0; r < 5; ++r) {
-    if (r < 4 || !odd) {
-      const float h = odd ? B[r < 4 ? r + 5 : 8] : B[r];
+    for (int d2 = 0; d2 < 3; ++d2)
 #pragma unroll
-      for (int s = 0; s < 9; ++s) row[9 * r + s] = A[s] + h;
-    }
+      for (int s2 = 0; s2 < 9; ++s2) row[9 * d2 + s2] = A[s2] + base[d2];
   }
 }
 
 template <int XT>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a) {
   __shared__ float lut[kSliceChunks * kLutEntries];                   // 51840 B
+  __shared__ __attribute__((aligned(16))) float xs[kSliceTrits];       // transformed activations
   const Tile t = make_tile(a);
 
   // Activations first (every wavefront loads a block, branch-free, so that
@@ -238,18 +232,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a)
   load_scales(a, t, sc);
   TQ_ORDER();
 
-  if (t.waves >= kSliceGroups) {
-    if (t.wave < kSliceGroups) {
-      transform(a, v0, v1, valid, t.lane);
-      build_rows(lut, t.wave, t.lane, v0, v1);
-    }
-  } else {  // fewer than 5 wavefronts: some transform several blocks
-    for (int blk = t.wave; blk < kSliceGroups; blk += t.waves) {
-      if (blk != t.wave) load_block_t<XT>(a, t, 0, blk, v0, v1, valid);
-      transform(a, v0, v1, valid, t.lane);
-      build_rows(lut, blk, t.lane, v0, v1);
-    }
+  // The slice's five transform blocks (one per wavefront, wavefronts 0..4
+  // when there are five or more), staged in LDS; then every wavefront
+  // builds a share of the table.
+  for (int blk = t.wave; blk < kSliceGroups; blk += t.waves) {
+    if (blk != t.wave) load_block_t<XT>(a, t, 0, blk, v0, v1, valid);
+    transform(a, v0, v1, valid, t.lane);
+    *reinterpret_cast<float2*>(&xs[128 * blk + 2 * t.lane]) = make_float2(v0, v1);
   }
+  TQ_LDS_BARRIER();
+  build_table(lut, xs, t.tid, blockDim.x);
   TQ_LDS_BARRIER();
   if (t.wave >= a.bpg) return;  // a prologue-only wavefront (small matrices)
 

@@ -84,27 +84,10 @@ __device__ __forceinline__ void load_act2(const void* x, int dtype, size_t i, fl
 }
 
 // ----------------------------------------------- block-128 transform ---
-// Walsh-Hadamard transform of one block of 128 held by a wavefront, lane l
-// owning elements 2l and 2l+1.  Stage stride 1 is inside the lane; strides
-// 2..64 pair lane l with lane l ^ (stride/2).  Scaled by 1/sqrt(128).
-template <typename T>
-__device__ __forceinline__ void wave_fwht128(T& v0, T& v1, int lane, T scale) {
-  T a = v0 + v1, b = v0 - v1;
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const T pa = __shfl_xor(a, s);
-    const T pb = __shfl_xor(b, s);
-    const T sgn = (lane & s) ? T(-1) : T(1);  // lower lane a + p, upper lane p - a
-    a = sgn * a + pa;
-    b = sgn * b + pb;
-  }
-  v0 = a * scale;
-  v1 = b * scale;
-}
-
-// Value of lane (lane ^ S) for S = 1..32: DPP inside 16-lane rows for
-// S <= 8 (quad_perm for 1 and 2, row shifts for 4, row rotate for 8; plain
-// VALU, no LDS traffic), ds_swizzle for 16, ds_bpermute for 32.
+// Value of lane (lane ^ S) for S = 1..32, all on the VALU (no LDS queue, so
+// the exchanges never wait behind another wavefront's LDS traffic): DPP
+// inside 16-lane rows for S <= 8 (quad_perm for 1 and 2, row shifts for 4,
+// row rotate for 8), v_permlane16_swap for 16 and v_permlane32_swap for 32.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
@@ -118,13 +101,25 @@ __device__ __forceinline__ float lane_xor_f32(float v, int lane) {
     const float dn = dpp_f32<0x114>(v);                  // row_shr:4, lane i <- i - 4
     return (lane & 4) ? dn : up;
   } else if constexpr (S == 8) return dpp_f32<0x128>(v);  // row_ror:8
-  else if constexpr (S == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-  else return __shfl_xor(v, S);
+  else if constexpr (S == 16) {
+    // Both operands v: the first result holds v's rows 0, 0, 2, 2 and the
+    // second v's rows 1, 1, 3, 3 (16-lane rows 0..3).
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  } else {
+    static_assert(S == 32, "lane strides 1..32");
+    // Both operands v: the first result holds v's lanes 0..31 twice, the
+    // second v's lanes 32..63 twice.
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  }
 }
 
-// B independent blocks at once (one per v[r]), stage by stage, so that the
-// lane exchanges of all blocks are in flight together; the four narrow
-// strides run on DPP, so only two stages go through the LDS crossbar.
+// Walsh-Hadamard transform of B independent blocks of 128 (one per v[r]),
+// each held by the wavefront with lane l owning elements 2l and 2l+1.
+// Stage stride 1 is inside the lane; strides 2..64 pair lane l with lane
+// l ^ (stride/2).  Scaled by 1/sqrt(128).  The blocks go stage by stage, so
+// that their lane exchanges are in flight together.
 template <int S, int B>
 __device__ __forceinline__ void fwht_batch_stage(float (&a)[B], float (&b)[B], int lane) {
   float pa[B], pb[B];
@@ -159,6 +154,30 @@ __device__ __forceinline__ void wave_fwht128_batch(float (&v)[B][2], int lane, f
   for (int r = 0; r < B; ++r) {
     v[r][0] = a[r] * scale;
     v[r][1] = b[r] * scale;
+  }
+}
+
+// One block: float on the VALU exchanges above; other types (the FP64
+// quantiser) through ds_bpermute.
+template <typename T>
+__device__ __forceinline__ void wave_fwht128(T& v0, T& v1, int lane, T scale) {
+  if constexpr (sizeof(T) == sizeof(float)) {
+    float v[1][2] = {{v0, v1}};
+    wave_fwht128_batch<1>(v, lane, scale);
+    v0 = v[0][0];
+    v1 = v[0][1];
+  } else {
+    T a = v0 + v1, b = v0 - v1;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+      const T pa = __shfl_xor(a, s);
+      const T pb = __shfl_xor(b, s);
+      const T sgn = (lane & s) ? T(-1) : T(1);  // lower lane a + p, upper lane p - a
+      a = sgn * a + pa;
+      b = sgn * b + pb;
+    }
+    v0 = a * scale;
+    v1 = b * scale;
   }
 }
 
