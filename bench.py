@@ -66,9 +66,14 @@ def log(*a):
 
 
 def sources_digest() -> str:
+    """Hash of the GEMV kernel sources with comments and whitespace removed,
+    so that it changes with the code and not with its comments."""
     h = hashlib.sha256()
     for f in GEMV_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        text = open(os.path.join(ROOT, f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -24,12 +24,13 @@
 //      parameter, so the load is branch-free and the transform waits for it
 //      alone), then kLookahead quads of weights (non-temporal: streamed
 //      once), then the scales (needed last; loads complete in order);
-//   2. block-128 transform in registers (wavefront shuffles), and the table
-//      rows of the block built straight from those registers;
+//   2. block-128 transform in registers (lane exchanges on the VALU), the
+//      transformed slice staged in LDS, and the table built by every
+//      wavefront of the workgroup;
 //   3. decode, software-pipelined: the table reads of word w + 2 are in
 //      flight while the sums of word w are formed, and quad i + kLookahead
 //      is loaded while quad i is decoded.
-// The one barrier waits for LDS only (a plain __syncthreads() would also
+// The two barriers wait for LDS only (a plain __syncthreads() would also
 // wait for every outstanding weight load).
 //
 // M >= 2 runs on the matrix cores (v_mfma_f32_16x16x32_f16): x' split into
