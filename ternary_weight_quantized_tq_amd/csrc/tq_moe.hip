@@ -7,11 +7,13 @@
 //   1. gate/up:  grid (pair, 64-row block of the intermediate dimension,
 //                640-trit slice of the hidden size), no bucketing; the
 //                slice's partial sums are stored.
-//   2. down:     grid (pair, 64-row block of the hidden size), one wavefront:
-//                adds the gate/up partials in order, h = silu(gate) * up, the
-//                block-128 transform, the down rows, the route weight; the
-//                last slot of a token to finish adds the slots' rows in slot
-//                order and stores y.
+//   2. down:     below four tokens, grid (pair, 64-row block of the hidden
+//                size), one wavefront per unit: adds the gate/up partials in
+//                order, h = silu(gate) * up, the block-128 transform, the
+//                down rows, the route weight; the last slot of a token to
+//                finish adds the slots' rows in slot order and stores y.
+//                From four tokens on, grid (token, 64-row block), one
+//                wavefront per slot, the slots' rows added in LDS.
 // Otherwise four launches on the caller's stream:
 //   1. bucket:   one workgroup groups the (token, slot) pairs by expert and
 //                lists the experts that received tokens (ascending id).
@@ -560,6 +562,112 @@ __global__ __launch_bounds__(kPairDnWaves * 64) void moe_down_pairs_kernel(MoeAr
   if (row < a.hidden) a.y[static_cast<size_t>(tok) * a.hidden + row] = v;
 }
 
+// Down + combine: workgroup (token, 64-row block rb of the hidden size),
+// the token's slots eight at a time, one wavefront per slot: it adds the
+// gate/up partials in order, forms h = silu(g) * u, transforms it, stages
+// the expert's scales and decodes the four units of each slice of the
+// intermediate dimension.  A slot's row (times the route weight) stays in
+// LDS; y = the valid slots' rows added in slot order.  Nothing leaves the
+// workgroup but y.
+// Used from kTokMinTokens tokens on: with fewer, its workgroups are too few
+// and each slot's four units on one wavefront too long a chain (256-expert
+// layer, top-8: 24.9 against 23.9 us at three tokens, 26.5 against 28.3 at
+// four, 37.5 against 49.7 at eight, for the per-pair kernel).
+constexpr int kTokSlots = 8;
+constexpr int kMaxTopk = 32;
+constexpr int kTokMinTokens = 4;
+__global__ __launch_bounds__(kTokSlots * 64) void moe_down_tok_kernel(MoeArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 xh[kTokSlots][2][kXStride];
+  __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
+  __shared__ __attribute__((aligned(16))) uint2 codes[81];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[kTokSlots][kSliceGroups * 64];
+  __shared__ int xexp[kTokSlots];
+  __shared__ float orow[kMaxTopk][64];
+  const int tok = blockIdx.x, rb = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, kb = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = a.inter, nsl = slices_per_row(K), nb = row_blocks(a.hidden);
+  const size_t P = static_cast<size_t>(a.t) * a.topk;
+  build_code_table(codes, tid, blockDim.x);
+  for (int i = tid; i < kSliceTrits; i += blockDim.x) zeros[i] = static_cast<_Float16>(0.0f);
+  const _Float16* xrow = (j < 2 ? &xh[wave][j < 2 ? j : 0][0] : &zeros[0]) + 8 * kb;
+  const int sl = lane < kSliceGroups * 8 ? lane : 0;
+  __syncthreads();
+  for (int j0 = 0; j0 < a.topk; j0 += kTokSlots) {
+    const int slot = j0 + wave;
+    const int pair = tok * a.topk + min(slot, a.topk - 1);
+    const int e = a.ids[pair];
+    const bool valid = slot < a.topk && e >= 0 && e < a.experts;  // wavefront-uniform
+    float tot[4][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}};
+    if (valid) {  // this wavefront's slot only: no barrier inside
+      const uint32_t* wexp = reinterpret_cast<const uint32_t*>(a.dn_words + static_cast<size_t>(e) * a.dn_wstride);
+      const uint16_t* sexp = a.dn_scales + static_cast<size_t>(e) * a.dn_sstride;
+      const float* grow = a.gu + static_cast<size_t>(pair) * 2 * K;
+      for (int s = 0; s < nsl; ++s) {
+        // The weights, the scales, then h of this slice: the gate/up
+        // partials added in order, four partials' loads in flight at a time.
+        const uint32_t* wb = wexp + (row64_quad_base(s, rb, nb) + (kb >> 1) * 64 + j) * 4 + 2 * (kb & 1);
+        const int u1 = __builtin_amdgcn_readfirstlane(row64_slice_quads(K, s) / 2);
+        uint2 wq[4][4];
+        mfma_load(wb, 0, 4, wq);  // slices are stored whole: every unit can be read
+        const uint4 scq = *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rb, nb) + 8 * sl);
+        float g[kSliceGroups][2] = {}, u[kSliceGroups][2] = {};
+        for (int z0 = 0; z0 < a.gu_parts; z0 += 4) {
+          float2 gv[4][kSliceGroups], uv[4][kSliceGroups];
+#pragma unroll
+          for (int dz = 0; dz < 4; ++dz) {
+            const float* src = grow + static_cast<size_t>(min(z0 + dz, a.gu_parts - 1)) * P * 2 * K;
+#pragma unroll
+            for (int bb = 0; bb < kSliceGroups; ++bb) {
+              const int k0 = s * kSliceTrits + bb * 128;
+              const int i = (k0 < K ? k0 : 0) + 2 * lane;
+              gv[dz][bb] = *reinterpret_cast<const float2*>(src + i);
+              uv[dz][bb] = *reinterpret_cast<const float2*>(src + K + i);
+            }
+          }
+#pragma unroll
+          for (int dz = 0; dz < 4; ++dz)
+            if (z0 + dz < a.gu_parts)
+#pragma unroll
+              for (int bb = 0; bb < kSliceGroups; ++bb) {
+                g[bb][0] += gv[dz][bb].x;
+                g[bb][1] += gv[dz][bb].y;
+                u[bb][0] += uv[dz][bb].x;
+                u[bb][1] += uv[dz][bb].y;
+              }
+        }
+        SliceAct xa;
+#pragma unroll
+        for (int bb = 0; bb < kSliceGroups; ++bb) {
+          xa.ok[bb] = s * kSliceTrits + bb * 128 < K;
+#pragma unroll
+          for (int c = 0; c < 2; ++c) xa.v[bb][c] = g[bb][c] / (1.0f + __expf(-g[bb][c])) * u[bb][c];
+        }
+        transform_slice(xa, xh[wave], &xexp[wave], 0, true, lane);
+        if (lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
+        // The wavefront's own LDS writes are complete before its reads.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        float ts[4][4] = {};
+        mfma_units(wq, ssc[wave], xrow, reinterpret_cast<const char*>(codes), j, 0, u1, ts);
+        add_slice(ts, &xexp[wave], kb, 1, tot);
+      }
+    }
+    if (slot < a.topk && kb == 0)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) orow[slot][16 * h + j] = a.route_w[pair] * tot[h][0];
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int row = rb * 64 + tid;
+    float v = 0.0f;
+    for (int s2 = 0; s2 < a.topk; ++s2) {
+      const int e2 = a.ids[tok * a.topk + s2];
+      if (e2 >= 0 && e2 < a.experts) v += orow[s2][tid];
+    }
+    if (row < a.hidden) a.y[static_cast<size_t>(tok) * a.hidden + row] = v;
+  }
+}
+
 // ---------------------------------------------------------- combine ---
 __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs a) {
   const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -741,7 +849,10 @@ extern "C" int tq_moe_gemv(const tq_weights* w_gate_up, const tq_weights* w_down
     hipLaunchKernelGGL(moe_gate_up_pairs_kernel, dim3(P, inter / 64, slices_per_row(hidden)), dim3(kPairGuWaves * 64), 0,
                        s, a);
     TQ_LAUNCH_CHECK();
-    hipLaunchKernelGGL(moe_down_pairs_kernel, dim3(P, row_blocks(hidden)), dim3(kPairDnWaves * 64), 0, s, a);
+    if (t >= kTokMinTokens)
+      hipLaunchKernelGGL(moe_down_tok_kernel, dim3(t, row_blocks(hidden)), dim3(kTokSlots * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL(moe_down_pairs_kernel, dim3(P, row_blocks(hidden)), dim3(kPairDnWaves * 64), 0, s, a);
     TQ_LAUNCH_CHECK();
     return TQ_OK;
   }

@@ -72,7 +72,7 @@ def test_gemv_single_linear_workload():
 
 @pytest.mark.parametrize("m", [1, 2, 5, 8])
 @pytest.mark.parametrize("n,k", [(1, 128), (63, 640), (65, 768), (300, 1920), (257, 2048)])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 def test_gemv_random_shapes(m, n, k, dtype):
     t, s, w = _rand_packed(1000 + 7 * n + k, n, k)
     act = synth.activations(3000 + m, m, k, dtype)
@@ -81,6 +81,18 @@ def test_gemv_random_shapes(m, n, k, dtype):
     err = O.rel_l2(y, y_ref)
     assert err < TOL, err
     assert err < 1e-5, err
+
+
+@pytest.mark.parametrize("m", [1, 3, 8])
+@pytest.mark.parametrize("n,k", [(130, 1280), (257, 2048)])
+def test_gemv_unfused_random(m, n, k):
+    """Without TQ_FWHT_FUSED the activations are used as given: y = W_hat x
+    (the plain dequantised matvec of the oracle, transform off)."""
+    t, s, w = _rand_packed(1500 + n + k, n, k)
+    act = synth.activations(3100 + m, m, k, "bf16")
+    y = run_gemv(w, act_tensor(act), m, fused=False)
+    y_ref = O.gemv(O.pack(t), s, k, act.values, False)
+    assert O.rel_l2(y, y_ref) < 1e-5
 
 
 @pytest.mark.parametrize("m", [1, 2, 8])

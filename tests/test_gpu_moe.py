@@ -40,7 +40,7 @@ def _random_experts(seed, E, hidden, inter):
     return w_gu, w_dn, host
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 def test_moe_small_random(dtype):
     E, hidden, inter, T, topk = 6, 256, 128, 5, 2
     w_gu, w_dn, h = _random_experts(300, E, hidden, inter)
@@ -98,11 +98,12 @@ def test_moe_many_tokens_per_expert_and_bad_ids(T):
     assert O.rel_l2(y, y_ref) < 1e-5
 
 
-@pytest.mark.parametrize("T,topk", [(2, 12), (2, 32), (3, 22)])
+@pytest.mark.parametrize("T,topk", [(2, 12), (2, 32), (3, 22), (4, 16), (5, 9)])
 def test_moe_wide_topk(T, topk):
-    """12 and 32 slots per token, combined by whichever of a token's slots
-    finishes last (64 pairs is the largest per-pair launch, 66 pairs are
-    bucketed), with two invalid ids."""
+    """9 to 32 slots per token with two invalid ids: below four tokens the
+    slots' rows are combined by whichever slot finishes last, from four on
+    in one workgroup per token and row block, eight slots at a time (64
+    pairs is the largest per-pair launch, 66 pairs are bucketed)."""
     E, hidden, inter = 40, 640, 384
     w_gu, w_dn, h = _random_experts(900, E, hidden, inter)
     act = synth.activations(91, T, hidden, "f32")
