@@ -238,7 +238,9 @@ __device__ __forceinline__ void add_slice(const float (&ts)[4][4], const int* xe
 // the gate rows 64b.., units 0-1 and 2-3 of each slice, wavefronts 2, 3 the
 // up rows I + 64b..; the expert's tokens 8 at a time, all slices;
 // h = silu(g) * u is stored to gu[pair][0, I).
-__global__ __launch_bounds__(256) void moe_gate_up_kernel(MoeArgs a) {
+// Three wavefronts per SIMD (at most 168 registers): three workgroups per
+// CU instead of two, fewer rounds of this latency-bound loop.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void moe_gate_up_kernel(MoeArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 xh[2 * kTile][kXStride];
   __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
   __shared__ __attribute__((aligned(16))) uint2 codes[81];
@@ -308,7 +310,8 @@ __global__ __launch_bounds__(256) void moe_gate_up_kernel(MoeArgs a) {
 }
 
 // ------------------------------------------------------------- down ---
-__global__ __launch_bounds__(256) void moe_down_kernel(MoeArgs a) {
+// Three wavefronts per SIMD, as for gate/up.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void moe_down_kernel(MoeArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 xh[2 * kTile][kXStride];
   __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
   __shared__ __attribute__((aligned(16))) uint2 codes[81];
