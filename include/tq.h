@@ -42,6 +42,10 @@
  *   * Workspaces are caller-owned device memory of tq_workspace_bytes()
  *     bytes; their contents need no initialisation.  Two calls in flight at
  *     the same time must not share a workspace.
+ *   * Alignment (checked; TQ_EINVAL otherwise): packed words, scales and
+ *     workspaces 16 bytes; activations two elements (8 bytes for TQ_F32, 4
+ *     for 16-bit types); FP32 outputs 4 bytes (tq_fwht's 8).  Allocations
+ *     from hipMalloc or PyTorch are 256-byte aligned.
  */
 #ifndef TQ_H
 #define TQ_H

@@ -264,6 +264,7 @@ int tq_unpack(const uint32_t* words, int n, int k, int layout, int8_t* trits, vo
 int tq_fwht(const void* x, int x_dtype, int m, int k, float* x_rot, void* stream) {
   if (!x || !x_rot) return TQ_EINVAL;
   if (bad_dtype(x_dtype)) return TQ_EINVAL;
+  if (!tq_aligned(x, tq_act_align(x_dtype)) || !tq_aligned(x_rot, 8)) return TQ_EINVAL;
   if (m <= 0 || k <= 0 || k % TQ_GROUP) return TQ_ESHAPE;
   const size_t jobs = static_cast<size_t>(m) * (k / 128);
   if (jobs > (static_cast<size_t>(UINT_MAX) / 4)) return TQ_ESHAPE;

@@ -272,6 +272,7 @@ extern "C" int tq_gemm(const tq_weights* w, const void* x, int x_dtype, int m, f
   if (st != TQ_OK) return st;
   if (!x || !y || !workspace) return TQ_EINVAL;
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16 && x_dtype != TQ_F16) return TQ_EINVAL;
+  if (!tq_aligned(x, tq_act_align(x_dtype)) || !tq_aligned(y, 4) || !tq_aligned(workspace, 16)) return TQ_EINVAL;
   if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED)) return TQ_EINVAL;
   if (m < 1) return TQ_ESHAPE;
   const GemmPlan p = plan_gemm(w->n, w->k, m);

@@ -566,6 +566,7 @@ int tq_check_weights(const tq_weights* w, int experts_expected) {
   if (w->num_experts < 1) return TQ_EFORMAT;
   if (w->n <= 0 || w->k <= 0 || w->k % TQ_GROUP) return TQ_ESHAPE;
   if (!w->words || !w->scales) return TQ_EINVAL;
+  if (!tq_aligned(w->words, 16) || !tq_aligned(w->scales, 16)) return TQ_EINVAL;
   return TQ_OK;
 }
 
@@ -577,6 +578,7 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
   if (st != TQ_OK) return st;
   if (!x || !y) return TQ_EINVAL;
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16 && x_dtype != TQ_F16) return TQ_EINVAL;
+  if (!tq_aligned(x, tq_act_align(x_dtype)) || !tq_aligned(y, 4)) return TQ_EINVAL;
   if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED | TQ_ACCUMULATE)) return TQ_EINVAL;
   if (m < 1 || m > 8) return TQ_ESHAPE;
   GemvPlan p = plan_sizes(w->n, w->k, m);
@@ -584,7 +586,7 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
   const bool accumulate = (flags & TQ_ACCUMULATE) != 0;
   const int mode = accumulate ? kAtomic : (p.nsl > 1 ? kPartial : kDirect);
   if (mode == kPartial) {
-    if (!workspace) return TQ_EINVAL;
+    if (!workspace || !tq_aligned(workspace, 16)) return TQ_EINVAL;
     if (ws_bytes < p.partial_bytes) return TQ_ENOSPACE;
   }
   if (m == 1) {

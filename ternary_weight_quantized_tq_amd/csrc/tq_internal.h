@@ -21,6 +21,11 @@ constexpr int kSliceWords = 32;
 constexpr int kSliceQuads = 8;
 constexpr int kSliceGroups = 5;
 
+// Pointer alignment checks of the entry points: p is a multiple of a bytes
+// (a a power of two); activations are read two elements at a time.
+inline bool tq_aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+inline size_t tq_act_align(int dtype) { return dtype == TQ_F32 ? 8 : 4; }
+
 __host__ __device__ inline int words_per_row(int k) { return (k + TQ_TRITS_PER_WORD - 1) / TQ_TRITS_PER_WORD; }
 __host__ __device__ inline int row_blocks(int n) { return (n + 63) / 64; }
 __host__ __device__ inline int slices_per_row(int k) { return (words_per_row(k) + kSliceWords - 1) / kSliceWords; }

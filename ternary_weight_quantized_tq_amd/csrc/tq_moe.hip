@@ -810,6 +810,9 @@ extern "C" int tq_moe_gemv(const tq_weights* w_gate_up, const tq_weights* w_down
   if (st != TQ_OK) return st;
   if (!x || !expert_ids || !route_w || !y || !workspace) return TQ_EINVAL;
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16 && x_dtype != TQ_F16) return TQ_EINVAL;
+  if (!tq_aligned(x, tq_act_align(x_dtype)) || !tq_aligned(y, 4) || !tq_aligned(workspace, 16) ||
+      !tq_aligned(expert_ids, 4) || !tq_aligned(route_w, 4))
+    return TQ_EINVAL;
   if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED)) return TQ_EINVAL;
   const int E = w_gate_up->num_experts, hidden = w_gate_up->k, inter = w_gate_up->n / 2;
   if (w_gate_up->n % 2 || inter % 64 || w_down->n != hidden || w_down->k != inter) return TQ_ESHAPE;

@@ -50,6 +50,8 @@ def _desc(**kw):
     (dict(k=1000), tq.TQ_ESHAPE),
     (dict(n=0), tq.TQ_ESHAPE),
     (dict(words=None), tq.TQ_EINVAL),
+    (dict(words=0x1004), tq.TQ_EINVAL),
+    (dict(scales=0x2002), tq.TQ_EINVAL),
 ])
 def test_gemv_rejects_bad_descriptor(kw, status):
     lib = tq.lib()
@@ -72,6 +74,11 @@ def test_gemv_rejects_bad_arguments():
     assert call(m=9) == tq.TQ_ESHAPE
     assert call(nb=16) == tq.TQ_ENOSPACE
     assert call(ws=None) == tq.TQ_EINVAL
+    # alignment: activations two elements, outputs 4 bytes, workspaces 16
+    assert call(x=0x3002) == tq.TQ_EINVAL
+    assert call(x=0x3004, dt=tq.TQ_F32) == tq.TQ_EINVAL
+    assert call(y=0x4002) == tq.TQ_EINVAL
+    assert call(ws=0x5004) == tq.TQ_EINVAL
     need = lib.tq_workspace_bytes(tq.TQ_OP_GEMV, ctypes.byref(w), 1, 0)
     assert 0 < need < 1 << 20
     assert lib.tq_workspace_bytes(tq.TQ_OP_GEMV, ctypes.byref(_desc(magic=1)), 1, 0) == tq.SIZE_MAX
@@ -88,6 +95,8 @@ def test_format_calls_reject_bad_arguments():
     assert lib.tq_quantize(0x10, tq.TQ_F64, 4, 100, 0x10, 0x10, None) == tq.TQ_ESHAPE
     assert lib.tq_fwht(0x10, tq.TQ_F32, 2, 129, 0x10, None) == tq.TQ_ESHAPE
     assert lib.tq_fwht(0x10, tq.TQ_F64, 2, 128, 0x10, None) == tq.TQ_EINVAL
+    assert lib.tq_fwht(0x12, tq.TQ_BF16, 2, 128, 0x10, None) == tq.TQ_EINVAL
+    assert lib.tq_fwht(0x10, tq.TQ_BF16, 2, 128, 0x14, None) == tq.TQ_EINVAL
     assert lib.tq_strerror(-2).decode().startswith("invalid shape")
 
 
@@ -112,3 +121,22 @@ def test_moe_limits(experts, t, topk, status):
     st = lib.tq_moe_gemv(ctypes.byref(gu), ctypes.byref(dn), 0x3000, tq.TQ_BF16, t, topk, 0x4000, 0x5000, 0x6000,
                          tq.TQ_FWHT_FUSED, 0x7000, 0, None)
     assert st == status
+
+
+def test_moe_and_gemm_check_alignment():
+    lib = tq.lib()
+    gu = _desc(n=256, k=512)
+    dn = _desc(n=512, k=128)
+    moe = lambda x=0x3000, ids=0x4000, rw=0x5000, y=0x6000, ws=0x7000: lib.tq_moe_gemv(
+        ctypes.byref(gu), ctypes.byref(dn), x, tq.TQ_BF16, 1, 1, ids, rw, y, tq.TQ_FWHT_FUSED, ws, 1 << 24, None)
+    assert moe(x=0x3002) == tq.TQ_EINVAL
+    assert moe(ids=0x4002) == tq.TQ_EINVAL
+    assert moe(rw=0x5001) == tq.TQ_EINVAL
+    assert moe(y=0x6002) == tq.TQ_EINVAL
+    assert moe(ws=0x7008) == tq.TQ_EINVAL
+    w = _desc()
+    gemm = lambda x=0x3000, y=0x4000, ws=0x5000: lib.tq_gemm(ctypes.byref(w), x, tq.TQ_F32, 4, y, tq.TQ_FWHT_FUSED,
+                                                           ws, 1 << 24, None)
+    assert gemm(x=0x3004) == tq.TQ_EINVAL
+    assert gemm(y=0x4002) == tq.TQ_EINVAL
+    assert gemm(ws=0x5008) == tq.TQ_EINVAL
