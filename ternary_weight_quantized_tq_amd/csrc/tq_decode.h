@@ -7,7 +7,8 @@
 // straddles a scale group.  word_offsets() returns 4*c_j, the byte offset of
 // entry c_j in a table of 4-byte entries.
 //
-// Every step avoids the quarter-rate 32-bit integer multiply:
+// Every step is one full-rate instruction (no division, no 64-bit
+// arithmetic beyond one FP64 FMA):
 //   a  = floor(w / 3^8):  one FP64 FMA, floor(w * (1/6561) + 0.5/6561).  For
 //        w < 3^20 the FMA is within 1.3e-10 of (w + 0.5)/6561, which lies at
 //        least 0.5/6561 = 7.6e-5 from an integer, so truncation is exact.
@@ -34,11 +35,13 @@
 namespace tq {
 
 // Low 32 bits of sext24(a) * sext24(b) + c  (v_mad_i32_i24).
-// kAsm: emit the instruction as inline asm (the compiler otherwise falls
-// back to quarter-rate 32-bit multiplies here).  Inline asm is hidden from
-// the compiler's hazard tracking, so kernels that issue matrix-core (MFMA)
-// instructions must use kAsm = false: an asm write can land on a register
-// an MFMA is still reading.
+// kAsm: emit the instruction as inline asm, one instruction; the compiler
+// otherwise emits v_mul_lo_u32 and an add (on gfx950 v_mul_lo_u32 issues
+// at the rate of v_add_u32: measured 5.3 against 5.3 clocks per
+// instruction on one wavefront).  Inline asm is hidden from the compiler's
+// hazard tracking, so kernels that issue matrix-core (MFMA) instructions
+// must use kAsm = false: an asm write can land on a register an MFMA is
+// still reading.
 template <bool kAsm = true>
 TQ_HD uint32_t mad_i24(uint32_t a, int32_t b, uint32_t c) {
 #if defined(__HIP_DEVICE_COMPILE__)
