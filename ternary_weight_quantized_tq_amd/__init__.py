@@ -60,11 +60,10 @@ _SIGNATURES = {
     "tq_moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "tq_moe_gemv": (_I, [_W, _W, _P, _I, _I, _I, _P, _P, _P, ctypes.c_uint, _P, _SZ, _P]),
     "tq_gemm": (_I, [_W, _P, _I, _I, _P, ctypes.c_uint, _P, _SZ, _P]),
-    "tq_workspace_bytes": (_SZ, [_W, _I, _I, _I]),
+    "tq_workspace_bytes": (_SZ, [_I, _W, _I, _I]),
     "tq_strerror": (ctypes.c_char_p, [_I]),
     "tq_last_error": (ctypes.c_char_p, []),
 }
-_SIGNATURES["tq_workspace_bytes"] = (_SZ, [_I, _W, _I, _I])
 
 _lib = None
 
@@ -94,10 +93,17 @@ def header_functions() -> list[str]:
 
 # ------------------------------------------------------------- helpers ---
 def _ptr(t) -> int | None:
+    """Device address of a tensor (or a raw address passed as int).  Host
+    tensors and non-contiguous views are refused: the kernels read device
+    memory densely."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError(f"tensor on {t.device}: the library reads device memory only")
+    if not t.is_contiguous():
+        raise ValueError("non-contiguous tensor: pass a contiguous one")
     return t.data_ptr()
 
 

@@ -103,9 +103,16 @@ def test_format_calls_reject_bad_arguments():
 def test_binding_raises_with_message():
     w = tq.Weights(0x1000, 0x2000, 256, 1280, magic=0)
     with pytest.raises(tq.TQError) as e:
-        tq.tq_gemv(w, 0x3000, 1, 0x4000, stream=0) if False else tq._check("tq_gemv", tq.lib().tq_gemv(
-            ctypes.byref(w.desc()), 0x3000, tq.TQ_BF16, 1, 0x4000, 1, 0x5000, 1 << 20, None))
+        tq._check("tq_gemv", tq.lib().tq_gemv(ctypes.byref(w.desc()), 0x3000, tq.TQ_BF16, 1, 0x4000, 1, 0x5000,
+                                              1 << 20, None))
     assert e.value.status == tq.TQ_EFORMAT
+
+
+def test_binding_refuses_host_and_strided_tensors():
+    import torch
+    with pytest.raises(ValueError, match="device memory"):
+        tq._ptr(torch.zeros(8))
+    assert tq._ptr(None) is None and tq._ptr(0x1000) == 0x1000
 
 
 @pytest.mark.parametrize("experts,t,topk,status", [
