@@ -37,8 +37,10 @@
  *     returns a negative tq_status and enqueues nothing (a corrupted
  *     descriptor is an error, never silent garbage).  A failed kernel
  *     launch returns TQ_EHIP.  No exception crosses the ABI.
- *   * The library keeps no mutable global state; calls on different streams
- *     with different workspaces may run concurrently.
+ *   * The library keeps no mutable global state beyond a per-thread
+ *     message for tq_last_error() and a per-device cache of the compute-unit
+ *     count; calls on different streams with different workspaces may run
+ *     concurrently.
  *   * Workspaces are caller-owned device memory of tq_workspace_bytes()
  *     bytes; their contents need no initialisation.  Two calls in flight at
  *     the same time must not share a workspace.

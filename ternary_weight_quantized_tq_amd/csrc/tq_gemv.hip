@@ -38,6 +38,8 @@
 // 81-entry LDS table are the B operand (see gemv_mfma_kernel).
 #include "tq_internal.h"
 
+#include <atomic>
+
 using namespace tq;
 
 namespace {
@@ -545,16 +547,18 @@ void launch_mfma(int x_dtype, int us, dim3 grid, dim3 block, hipStream_t s, cons
 }  // namespace
 
 // Compute units of the current device (queried once per device).
+// (A cache of a device constant: concurrent first calls store the same value,
+// through atomics so that no thread reads a torn one.)
 int tq_device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int v = 0;
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cus[dev] = v;
+    cus[dev].store(v, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return v;
 }
 
 // Shared by the C entry points: validates a compute descriptor.
