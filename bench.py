@@ -290,7 +290,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the decode GEMV shards by "
-              "output rows with no reduction across GPUs; see DESIGN.md).", file=sys.stderr)
+              "output rows with no reduction across GPUs).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

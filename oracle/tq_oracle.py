@@ -36,7 +36,7 @@ Sources (web pages; cited by title and section):
   with weights in {-1,0,1} times a scale the matmul reduces to sign tests
   and additions/subtractions.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * scale estimator: absmean, gamma = mean |w'| over the group (the BitNet
   b1.58 rule; BitNet is named as the lineage in [Bonsai] section 1);
