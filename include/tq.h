@@ -71,7 +71,7 @@ typedef enum {
   TQ_EFORMAT = -3,      /* descriptor magic/version/layout/expert count wrong  */
   TQ_ENOSPACE = -4,     /* workspace too small                                 */
   TQ_EHIP = -5,         /* a HIP launch failed                                 */
-  TQ_EUNSUPPORTED = -6  /* valid request this build does not implement         */
+  TQ_EUNSUPPORTED = -6  /* valid request the library does not implement        */
 } tq_status;
 
 /* Element types of activations / inputs. */

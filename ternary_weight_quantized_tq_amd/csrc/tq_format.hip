@@ -188,7 +188,7 @@ const char* tq_strerror(int status) {
     case TQ_EFORMAT: return "weight descriptor does not match (magic, version, layout or expert count)";
     case TQ_ENOSPACE: return "workspace too small";
     case TQ_EHIP: return "HIP kernel launch failed";
-    case TQ_EUNSUPPORTED: return "request not supported by this build";
+    case TQ_EUNSUPPORTED: return "request not supported by the library";
     default: return "unknown tq status";
   }
 }
