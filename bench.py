@@ -20,6 +20,10 @@ serves them.
             counter summary when it was taken on the current kernel sources
   cpu_baseline  the FP64 CPU oracle (unpack + transform + dequantised
             matvec) on a bounded row sample, in packed-weight GB/s
+  isolated_launch_us_p10_p50_p90  one GEMV launched alone between two HIP
+            events (dispatch and ramp-up included; context)
+  mall_hot_single_copy   the same step on one weight copy (cache-resident,
+            labelled; context, not the metric)
 
 `extras` adds the other workloads: one transformer block's seven linears at
 M = 1 (single stream) and M = 8, the 256-expert MoE layer at T = 1 and
@@ -347,18 +351,8 @@ def main():
         step(i)
     torch.cuda.synchronize()
     # The timed steps run as one HIP graph so that host launch cost does not
-    # pace the GPU.  Timing events around each GEMV are recorded as graph
-    # nodes; where capture of such events is not supported, the kernel time
-    # comes from a graph of back-to-back GEMV launches instead.
-    evs = [[[torch.cuda.Event(enable_timing=True, external=True) for _ in range(2)] for _ in lins]
-           for _ in range(args.steps)]
-    try:
-        g = capture(torch, args.steps, lambda i: step(i, evs[i]))
-        kernel_timing = "events around each launch inside the timed graph"
-    except Exception as e:  # noqa: BLE001 - reported in the output
-        log(f"capture with timing events failed ({type(e).__name__}: {e}); timing kernels separately")
-        torch.cuda.synchronize()
-        g, evs = capture(torch, args.steps, step), None
+    # pace the GPU.  (HIP graphs on ROCm take no timing events as nodes.)
+    g = capture(torch, args.steps, step)
     g.replay()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -367,22 +361,35 @@ def main():
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    if evs is not None:
-        mean_us = [1e3 * float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)]))
-                   for j in range(len(lins))]
-    else:
-        kernel_timing = "graph of back-to-back launches of one linear, divided by the launch count"
-        mean_us = []
+    # Mean launch time of each GEMV: a graph of its back-to-back launches over
+    # the rotated copies, HIP events on its stream around the replay, divided
+    # by the launch count.
+    kernel_timing = "graph of back-to-back launches of one linear, divided by the launch count"
+    mean_us = []
+    for j in range(len(lins)):
+        kg = capture(torch, copies, lambda i: tq.tq_gemv(sets[i][j], xs[j], 1, ys[j],
+                                                          tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE))
+        kg.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        kg.replay()
+        b.record()
+        torch.cuda.synchronize()
+        mean_us.append(1e3 * a.elapsed_time(b) / copies)
+    # Isolated launches: eager, each between two events on an otherwise idle
+    # stream, so each time includes the dispatch and ramp-up that back-to-back
+    # launches overlap (context; per-kernel percentiles come from the trace).
+    per = [[] for _ in lins]
+    for i in range(args.steps):
         for j in range(len(lins)):
-            kg = capture(torch, copies, lambda i: tq.tq_gemv(sets[i][j], xs[j], 1, ys[j],
-                                                              tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE))
-            kg.replay()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            kg.replay()
+            tq.tq_gemv(sets[i % copies][j], xs[j], 1, ys[j], tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE)
             b.record()
-            torch.cuda.synchronize()
-            mean_us.append(1e3 * a.elapsed_time(b) / copies)
+            per[j].append((a, b))
+    torch.cuda.synchronize()
+    spread = {l.name: [round(float(np.percentile([1e3 * a.elapsed_time(b) for a, b in v], q)), 3) for q in (10, 50, 90)]
+              for l, v in zip(lins, per)}
     # Context for the roofline: a plain device copy moving the same bytes per
     # launch (half read, half written), timed the same way, sources rotated.
     half = lin_bytes[0] // 8
@@ -396,6 +403,16 @@ def main():
     b.record()
     torch.cuda.synchronize()
     copy_us = 1e3 * a.elapsed_time(b) / copies
+    # The same step on one copy of the weights (no rotation): they then sit
+    # in the 256 MB Infinity Cache, so this shows the kernels off HBM.
+    hot = capture(torch, args.steps, lambda i: step(0))
+    hot.replay()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    hot.replay()
+    b.record()
+    torch.cuda.synchronize()
+    hot_ms = a.elapsed_time(b) / args.steps
     gbs = step_bytes / (ms * 1e-3) / 1e9
     kern_gbs = sum(lin_bytes) / (sum(mean_us) * 1e-6) / 1e9
     traffic = measured_traffic()
@@ -421,6 +438,10 @@ def main():
         "frac_hbm_peak_step": round(gbs / HBM_PEAK_GBS, 4),
         "kernel_us": {l.name: round(u, 3) for l, u in zip(lins, mean_us)},
         "kernel_timing": kernel_timing,
+        "isolated_launch_us_p10_p50_p90": spread,
+        "mall_hot_single_copy": {"ms_per_step": round(hot_ms, 5),
+                                 "gb_s": round(step_bytes / (hot_ms * 1e-3) / 1e9, 1),
+                                 "note": "one weight copy, cache-resident; not the metric"},
         "plain_copy_same_bytes": {"bytes_moved": 8 * half, "us": round(copy_us, 3),
                                   "gb_s": round(8 * half / (copy_us * 1e-6) / 1e9, 1),
                                   "frac_hbm_peak": round(8 * half / (copy_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
