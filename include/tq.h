@@ -208,11 +208,11 @@ int tq_moe_route(const float *logits, int t, int e, int topk, int32_t *ids,
  * of x_dtype; y FP32 [t][Hd].  The expert products use the m >= 2 decode
  * GEMV arithmetic (fp16 codes, x' and H h as two fp16 parts, FP32
  * accumulation).  With t * topk <= 64 every (token, slot) pair is its own
- * one-row product (two launches; the last slot of a token to finish adds
- * the slots in slot order); otherwise the pairs are grouped by expert and
- * an expert's tokens go 8 at a time (four launches; E <= 1024, else
- * TQ_EUNSUPPORTED).  y is deterministic
- * either way.  Only the experts that receive tokens are read.  Ids outside
+ * one-row product (two launches; below four tokens the last slot of a token
+ * to finish adds the slots in slot order, from four tokens on one
+ * workgroup per token and row block adds them); otherwise the pairs are
+ * grouped by expert and an expert's tokens go 8 at a time (four launches;
+ * E <= 1024, else TQ_EUNSUPPORTED).  y is deterministic either way.  Only the experts that receive tokens are read.  Ids outside
  * [0, E) are an error detected on the device: such slots contribute
  * nothing.  Needs tq_workspace_bytes(TQ_OP_MOE, w_gate_up, t, topk) bytes of
  * workspace, which calls that overlap in time must not share. */
