@@ -262,13 +262,15 @@ def extra_moe(tq, torch, synth, np):
         ws, nb = tq.workspace(tq.TQ_OP_MOE, w_gu, T, wl.topk)
         active = len(set(ids.cpu().numpy().ravel().tolist()))
 
-        def step(i):
+        def step(i, flags=tq.TQ_FWHT_FUSED):
             g, d = sets[i % copies]
-            tq.tq_moe_gemv(g, d, x, T, wl.topk, ids, rw, y, tq.TQ_FWHT_FUSED, ws, nb)
+            tq.tq_moe_gemv(g, d, x, T, wl.topk, ids, rw, y, flags, ws, nb)
         ms = timed(torch, 50, 5, step)
+        ms_acc = timed(torch, 50, 5, lambda i: step(i, tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE))
         bytes_ = active * per_expert
         out.append({"workload": wl.name, "tokens": T, "active_experts": active, "expert_bytes_read": bytes_,
                     "weight_copies_rotated": copies, "us_per_layer": round(ms * 1e3, 2),
+                    "us_per_layer_accumulate": round(ms_acc * 1e3, 2),
                     "gb_s": round(bytes_ / (ms * 1e-3) / 1e9, 1), "tok_s": round(T / (ms * 1e-3), 1),
                     "launches": 2 if T * wl.topk <= 64 else 4})  # per-pair launches up to 64 pairs
     return out

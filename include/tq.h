@@ -110,7 +110,11 @@ enum { TQ_LAYOUT_ROWMAJOR = 0, TQ_LAYOUT_ROW64 = 1 };
  *   launch with device-scope float atomics and no workspace (for example to
  *   add a projection straight into a residual stream); the order in which
  *   the K slices are added is not fixed, so results may differ from run to
- *   run in the last bits.  Without it the call is deterministic. */
+ *   run in the last bits.  Without it the call is deterministic.
+ *   (tq_moe_gemv): y += the layer's output; deterministic except with at
+ *   most 64 (token, slot) pairs and fewer than four tokens, where each
+ *   slot's row is added with device atomics (and the slots' combine step is
+ *   skipped). */
 enum { TQ_FWHT_FUSED = 1u, TQ_ACCUMULATE = 2u };
 
 /* Operation ids for tq_workspace_bytes. */
@@ -202,7 +206,7 @@ int tq_moe_route(const float *logits, int t, int e, int topk, int32_t *ids,
  *     g||u = W_gu[e] . H x_i    (W_gu rows [0, I) gate, [I, 2I) up)
  *     h    = silu(g) * u        (silu(z) = z / (1 + exp(-z)))
  *     o    = W_dn[e] . H h
- *   y[i] = sum_j route_w[i][j] * o.
+ *   y[i] = sum_j route_w[i][j] * o   (TQ_ACCUMULATE: y[i] += ...).
  * w_gate_up: E experts of n = 2I, k = Hd; w_down: E experts of n = Hd,
  * k = I; both ROW64 (I % 64 == 0, Hd and I multiples of 128).  x: [t][Hd]
  * of x_dtype; y FP32 [t][Hd].  The expert products use the m >= 2 decode

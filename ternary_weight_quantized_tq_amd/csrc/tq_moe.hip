@@ -60,6 +60,7 @@ struct MoeArgs {
   float* y;
   int t, topk, experts, hidden, inter;
   int fused;
+  int accumulate;    // TQ_ACCUMULATE: y += the layer's output
   // workspace
   int* num_active;   // [1]
   int* active;       // [experts]   expert id of active slot a
@@ -537,6 +538,12 @@ __global__ __launch_bounds__(kPairDnWaves * 64) void moe_down_pairs_kernel(MoeAr
   if (wave != 0) return;
   const int row = rb * 64 + lane;
   const int rowc = row < a.hidden ? row : 0;
+  if (a.accumulate) {  // y += w o with device atomics: no arrival count, no combine
+    if (valid && row < a.hidden)
+      atomicAdd(a.y + static_cast<size_t>(tok) * a.hidden + row,
+                wgt * (((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]));
+    return;
+  }
   if (valid && row < a.hidden) {
     const float v = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
     __hip_atomic_store(a.o + static_cast<size_t>(pair) * a.hidden + row, wgt * v, __ATOMIC_RELAXED,
@@ -667,7 +674,10 @@ __global__ __launch_bounds__(kTokSlots * 64) void moe_down_tok_kernel(MoeArgs a)
       const int e2 = a.ids[tok * a.topk + s2];
       if (e2 >= 0 && e2 < a.experts) v += orow[s2][tid];
     }
-    if (row < a.hidden) a.y[static_cast<size_t>(tok) * a.hidden + row] = v;
+    if (row < a.hidden) {
+      float* yp = a.y + static_cast<size_t>(tok) * a.hidden + row;
+      *yp = a.accumulate ? *yp + v : v;
+    }
   }
 }
 
@@ -683,7 +693,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs a) {
     const int e = a.ids[p];
     if (e >= 0 && e < a.experts) acc = fmaf(a.route_w[p], a.o[static_cast<size_t>(p) * a.hidden + n], acc);
   }
-  a.y[idx] = acc;
+  a.y[idx] = a.accumulate ? a.y[idx] + acc : acc;
 }
 
 // ----------------------------------------------------------- router ---
@@ -813,7 +823,7 @@ extern "C" int tq_moe_gemv(const tq_weights* w_gate_up, const tq_weights* w_down
   if (!tq_aligned(x, tq_act_align(x_dtype)) || !tq_aligned(y, 4) || !tq_aligned(workspace, 16) ||
       !tq_aligned(expert_ids, 4) || !tq_aligned(route_w, 4))
     return TQ_EINVAL;
-  if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED)) return TQ_EINVAL;
+  if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED | TQ_ACCUMULATE)) return TQ_EINVAL;
   const int E = w_gate_up->num_experts, hidden = w_gate_up->k, inter = w_gate_up->n / 2;
   if (w_gate_up->n % 2 || inter % 64 || w_down->n != hidden || w_down->k != inter) return TQ_ESHAPE;
   if (t < 1 || topk < 1 || topk > 32 || static_cast<long long>(t) * topk > INT_MAX / 4) return TQ_ESHAPE;
@@ -841,6 +851,7 @@ extern "C" int tq_moe_gemv(const tq_weights* w_gate_up, const tq_weights* w_down
   a.hidden = hidden;
   a.inter = inter;
   a.fused = (flags & TQ_FWHT_FUSED) ? 1 : 0;
+  a.accumulate = (flags & TQ_ACCUMULATE) ? 1 : 0;
   a.num_active = reinterpret_cast<int*>(ws + l.num_active);
   a.active = reinterpret_cast<int*>(ws + l.active);
   a.seg = reinterpret_cast<int*>(ws + l.seg);

@@ -173,3 +173,26 @@ def test_moe_many_experts_few_pairs():
     y = run_moe(w_gu, w_dn, act_tensor(act), T, topk, ids, rw)
     y_ref = O.moe(act.values, ids, rw, h["gu_w"], h["gu_s"], h["dn_w"], h["dn_s"], hidden, inter)
     assert O.rel_l2(y, y_ref) < 1e-5
+
+
+@pytest.mark.parametrize("T", [1, 3, 5, 40])
+def test_moe_accumulate(T):
+    """TQ_ACCUMULATE adds the layer into y (a residual stream): per-pair
+    (T = 1, 3: device atomics), per-token (T = 5) and bucketed (T = 40)."""
+    th = torch()
+    E, hidden, inter, topk = 10, 640, 256, 2
+    w_gu, w_dn, h = _random_experts(700, E, hidden, inter)
+    act = synth.activations(71, T, hidden, "bf16")
+    rng = np.random.default_rng(72)
+    ids = np.stack([rng.choice(E, topk, replace=False) for _ in range(T)]).astype(np.int32)
+    rw = rng.random((T, topk))
+    rw /= rw.sum(axis=1, keepdims=True)
+    base = rng.normal(size=(T, hidden)).astype(np.float32)
+    y = dev(base.copy())
+    ws, nbytes = tq.workspace(tq.TQ_OP_MOE, w_gu, T, topk)
+    tq.tq_moe_gemv(w_gu, w_dn, act_tensor(act), T, topk, dev(ids), dev(rw.astype(np.float32)), y,
+                   tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE, ws, nbytes)
+    th.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64) - base
+    y_ref = O.moe(act.values, ids, rw, h["gu_w"], h["gu_s"], h["dn_w"], h["dn_s"], hidden, inter)
+    assert O.rel_l2(got, y_ref) < 1e-5
