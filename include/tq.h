@@ -114,7 +114,8 @@ enum { TQ_LAYOUT_ROWMAJOR = 0, TQ_LAYOUT_ROW64 = 1 };
  *   (tq_moe_gemv): y += the layer's output; deterministic except with at
  *   most 64 (token, slot) pairs and fewer than four tokens, where each
  *   slot's row is added with device atomics (and the slots' combine step is
- *   skipped). */
+ *   skipped).  (tq_gemm): Y += ..., deterministic (one workgroup writes
+ *   each output). */
 enum { TQ_FWHT_FUSED = 1u, TQ_ACCUMULATE = 2u };
 
 /* Operation ids for tq_workspace_bytes. */

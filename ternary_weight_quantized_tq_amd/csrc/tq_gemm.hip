@@ -61,6 +61,7 @@ struct GemmArgs {
   const _Float16* xl;
   float* y;
   int m, n, k, kpad, nb, groups, mtiles, ntiles, steps, xcd_map;
+  int accumulate;  // TQ_ACCUMULATE: y += (one workgroup per output tile: no atomics)
 };
 
 // Tile of this workgroup: all N tiles of an M tile on one XCD (workgroups
@@ -239,7 +240,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int row = mt * BM + 8 * t + 2 * kb + q;
-        if (row < a.m) a.y[static_cast<size_t>(row) * a.n + col] = acc[h][t][2 * q] + acc[h][t][2 * q + 1];
+        if (row < a.m) {
+          float* yp = a.y + static_cast<size_t>(row) * a.n + col;
+          const float v = acc[h][t][2 * q] + acc[h][t][2 * q + 1];
+          *yp = a.accumulate ? *yp + v : v;
+        }
       }
   }
 }
@@ -273,7 +278,7 @@ extern "C" int tq_gemm(const tq_weights* w, const void* x, int x_dtype, int m, f
   if (!x || !y || !workspace) return TQ_EINVAL;
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16 && x_dtype != TQ_F16) return TQ_EINVAL;
   if (!tq_aligned(x, tq_act_align(x_dtype)) || !tq_aligned(y, 4) || !tq_aligned(workspace, 16)) return TQ_EINVAL;
-  if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED)) return TQ_EINVAL;
+  if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED | TQ_ACCUMULATE)) return TQ_EINVAL;
   if (m < 1) return TQ_ESHAPE;
   const GemmPlan p = plan_gemm(w->n, w->k, m);
   if (ws_bytes < p.total) return TQ_ENOSPACE;
@@ -301,6 +306,7 @@ extern "C" int tq_gemm(const tq_weights* w, const void* x, int x_dtype, int m, f
   a.ntiles = p.ntiles;
   a.steps = p.steps;
   a.xcd_map = (p.mtiles % 8 == 0) ? 1 : 0;
+  a.accumulate = (flags & TQ_ACCUMULATE) ? 1 : 0;
   hipLaunchKernelGGL(gemm_kernel, dim3(p.mtiles * p.ntiles), dim3(kThreads), 0, s, a);
   TQ_LAUNCH_CHECK();
   return TQ_OK;

@@ -6,7 +6,7 @@ import synth
 import ternary_weight_quantized_tq_amd as tq
 from oracle import tq_oracle as O
 
-from tqgpu import act_tensor, dev, gpu_pack, gpu_quantize_pack, run_gemm, run_gemv
+from tqgpu import act_tensor, dev, gpu_pack, gpu_quantize_pack, run_gemm, run_gemv, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -63,3 +63,19 @@ def test_gemm_prefill_full_size_sampled():
     y_ref = O.gemv(O.pack(t), s, wl.k, act.values[rows], True)
     err = O.rel_l2(y[np.ix_(rows, cols)], y_ref)
     assert err < 1e-5, err
+
+
+def test_gemm_accumulate():
+    """TQ_ACCUMULATE adds the product into Y (a residual stream)."""
+    th = torch()
+    t, s, w = _rand(95, 300, 1280)
+    m = 70
+    act = synth.activations(96, m, 1280, "bf16")
+    base = np.random.default_rng(97).normal(size=(m, 300)).astype(np.float32)
+    y = dev(base.copy())
+    ws, nbytes = tq.workspace(tq.TQ_OP_GEMM, w, m)
+    tq.tq_gemm(w, act_tensor(act), m, y, tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE, ws, nbytes)
+    th.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64) - base
+    y_ref = O.gemv(O.pack(t), s, 1280, act.values, True)
+    assert O.rel_l2(got, y_ref) < 1e-5
