@@ -24,6 +24,23 @@ def test_router_matches_oracle(t, e, topk, seed):
     assert np.abs(w.cpu().numpy() - w_ref).max() < 1e-5
 
 
+def test_router_ties_go_to_the_lower_id():
+    """Equal logits: the chosen ids ascend from 0 and the weights are equal;
+    a block of tied maxima is taken in id order before lower logits."""
+    th = torch()
+    e, topk = 48, 6
+    lg = np.zeros((2, e), np.float32)
+    lg[1, [40, 7, 23, 31]] = 3.0      # four tied maxima, then the zeros tie
+    ids = th.empty((2, topk), dtype=th.int32, device="cuda")
+    w = th.empty((2, topk), dtype=th.float32, device="cuda")
+    tq.tq_moe_route(dev(lg), 2, e, topk, ids, w)
+    th.cuda.synchronize()
+    ids_ref, w_ref = O.route(lg, topk)
+    assert ids.cpu().numpy().tolist() == ids_ref.tolist()
+    assert ids_ref[0].tolist() == list(range(topk)) and ids_ref[1].tolist() == [7, 23, 31, 40, 0, 1]
+    assert np.abs(w.cpu().numpy() - w_ref).max() < 1e-6
+
+
 def _random_experts(seed, E, hidden, inter):
     w_gu = tq.empty_weights(2 * inter, hidden, num_experts=E)
     w_dn = tq.empty_weights(hidden, inter, num_experts=E)
