@@ -688,10 +688,21 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs a) {
   const int tok = static_cast<int>(idx / a.hidden);
   const int n = static_cast<int>(idx % a.hidden);
   float acc = 0.0f;
-  for (int j = 0; j < a.topk; ++j) {
-    const int p = tok * a.topk + j;
-    const int e = a.ids[p];
-    if (e >= 0 && e < a.experts) acc = fmaf(a.route_w[p], a.o[static_cast<size_t>(p) * a.hidden + n], acc);
+  // Eight slots' loads in flight at a time (unconditional, slots clamped),
+  // then added in slot order.
+  for (int j0 = 0; j0 < a.topk; j0 += 8) {
+    int ev[8];
+    float wv[8], ov[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const int p = tok * a.topk + min(j0 + d, a.topk - 1);
+      ev[d] = a.ids[p];
+      wv[d] = a.route_w[p];
+      ov[d] = a.o[static_cast<size_t>(p) * a.hidden + n];
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+      if (j0 + d < a.topk && ev[d] >= 0 && ev[d] < a.experts) acc = fmaf(wv[d], ov[d], acc);
   }
   a.y[idx] = a.accumulate ? a.y[idx] + acc : acc;
 }
