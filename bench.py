@@ -156,19 +156,37 @@ def cpu_baseline(O, synth, lins, w64s, seconds):
         t, s, _ = O.quantize(w64[:rows])
         x = synth.activations(lin.x_seed, 1, lin.k, "bf16").values
         samples.append((O.pack(t), s, lin.k, x, O.packed_bytes(rows, lin.k), rows))
-    done, t0, reps = 0, time.perf_counter(), 0
-    while True:
-        for words, s, k, x, nbytes, _ in samples:
-            O.gemv(words, s, k, x, True)
-            done += nbytes
-        reps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
+    def run(budget):
+        done, t0, reps = 0, time.perf_counter(), 0
+        while True:
+            for words, s, k, x, nbytes, _ in samples:
+                O.gemv(words, s, k, x, True)
+                done += nbytes
+            reps += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        dt = time.perf_counter() - t0
+        return done / dt / 1e9, reps, dt
+
+    gbs, reps, dt = run(seconds)
+    try:  # the same sample on one thread, for a third of the time
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            gbs1, reps1, dt1 = run(seconds / 3)
+        one = {"value": round(gbs1, 4), "reps": reps1, "seconds": round(dt1, 1)}
+    except Exception as e:  # report, never hide
+        one = {"error": f"{type(e).__name__}: {e}"}
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     desc = " + ".join(f"{smp[5]} rows of {lin.name} ({lin.n}x{lin.k})" for smp, lin in zip(samples, lins))
-    return {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{desc}, repeated {reps}x over {dt:.1f} s (FP64 unpack + dense block-128 transform + "
-                      f"dequantised matvec), packed bytes per second"}
+                      f"dequantised matvec), packed bytes per second",
+            "one_thread": one, "cpu_model": model}
 
 
 # --------------------------------------------------------------- extras ---
