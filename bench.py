@@ -189,6 +189,25 @@ def cpu_baseline(O, synth, lins, w64s, seconds):
             "one_thread": one, "cpu_model": model}
 
 
+def cpu_gemm_rows(O, synth, rows=64):
+    """The oracle on a row subset of the prefill GEMM: `rows` rows of X
+    against the whole weight matrix (offline quantise and pack untimed), one
+    timed call; the full-batch time is extrapolated linearly and flagged."""
+    wl = synth.PREFILL_GEMM
+    lin = wl.linears[0]
+    t, s, _ = O.quantize(synth.weights(lin.w_seed, lin.n, lin.k))
+    words = O.pack(t)
+    del t
+    x = synth.activations(lin.x_seed, rows, lin.k, "bf16").values
+    t0 = time.perf_counter()
+    O.gemm_rows(words, s, lin.k, x, list(range(rows)))
+    dt = time.perf_counter() - t0
+    return {"workload": wl.name, "rows_timed": rows, "seconds": round(dt, 2),
+            "tok_s": round(rows / dt, 2), "useful_gflops": round(2.0 * rows * lin.n * lin.k / dt / 1e9, 2),
+            "extrapolated_ms_full_batch": round(dt * wl.m / rows * 1e3, 1),
+            "note": "extrapolated linearly from the row subset (the dequantised matrix is rebuilt per call)"}
+
+
 # --------------------------------------------------------------- extras ---
 def extra_block(tq, torch, synth, np, wl):
     """One dense block's seven linears at wl.m activation rows (1: single
@@ -483,6 +502,12 @@ def main():
         from oracle import tq_oracle as O
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = cpu_baseline(O, synth, lins, w64s, args.cpu_seconds)
+        if not args.no_extras:
+            log("timing the CPU oracle on prefill GEMM rows ...")
+            try:
+                result["cpu_baseline"]["prefill_gemm_rows"] = cpu_gemm_rows(O, synth)
+            except Exception as e:  # report, never hide
+                result["cpu_baseline"]["prefill_gemm_rows"] = {"error": f"{type(e).__name__}: {e}"}
     print(json.dumps(result), flush=True)
 
 
