@@ -270,8 +270,28 @@ def moe(x, ids, route_w, gu_words, gu_scales, dn_words, dn_scales, hidden, inter
 # Parity metric
 # --------------------------------------------------------------------------
 def rel_l2(y, y_ref) -> float:
+    """||y - y_ref||_2 / ||y_ref||_2 over the whole tensor, in FP64 (the
+    ratio of norms, not of squared norms; the reference in the denominator).
+    A zero reference gives the plain norm of y."""
     y = np.asarray(y, dtype=np.float64)
     y_ref = np.asarray(y_ref, dtype=np.float64)
     den = np.linalg.norm(y_ref.ravel())
     num = np.linalg.norm((y - y_ref).ravel())
     return float(num / den) if den > 0 else float(num)
+
+
+def row_max_rel(y, y_ref) -> float:
+    """Largest, over the rows of a [rows][cols] pair (a 1-D pair is one row),
+    of max_c |y - y_ref| / max_c |y_ref|: a local error that a whole-tensor
+    norm would dilute.  A row whose reference is all zero contributes
+    max |y| of that row."""
+    y = np.atleast_2d(np.asarray(y, dtype=np.float64))
+    y_ref = np.atleast_2d(np.asarray(y_ref, dtype=np.float64))
+    if y.shape != y_ref.shape:
+        raise ValueError("shape mismatch")
+    worst = 0.0
+    for r in range(y.shape[0]):
+        num = float(np.max(np.abs(y[r] - y_ref[r]))) if y.shape[1] else 0.0
+        den = float(np.max(np.abs(y_ref[r]))) if y.shape[1] else 0.0
+        worst = max(worst, num / den if den > 0 else num)
+    return worst

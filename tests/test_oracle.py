@@ -431,3 +431,69 @@ def test_pins_catch_double_rounded_scale(monkeypatch):
         t, s, g = good(w_rot, group)
         return t, g.astype(np.float32).astype(np.float16), g
     _expect_pin_failure(monkeypatch, "ternarize", bad, [test_scale_single_rounding_from_fp64])
+
+
+# ------------------------------------------------------- parity metrics ---
+def test_rel_l2_hand_values():
+    # reference (3, 4) has norm 5; the difference (0.6, 0.8) has norm 1
+    assert O.rel_l2([3.6, 4.8], [3.0, 4.0]) == pytest.approx(0.2, abs=1e-15)
+    # the reference is the denominator: swapping the arguments gives 1/6
+    assert O.rel_l2([3.0, 4.0], [3.6, 4.8]) == pytest.approx(1.0 / 6.0, abs=1e-15)
+    # a sign flip doubles every element's error: 2, whatever the vector
+    assert O.rel_l2([-1.0, 2.0, -2.0], [1.0, -2.0, 2.0]) == pytest.approx(2.0, abs=1e-15)
+    # a whole-tensor norm, not a per-row mean: rows (1, 0), (0, 1) against
+    # (1, 0), (0, 0) -> sqrt(1) / sqrt(2)
+    assert O.rel_l2([[1.0, 0.0], [0.0, 0.0]], [[1.0, 0.0], [0.0, 1.0]]) == pytest.approx(
+        1.0 / math.sqrt(2.0), abs=1e-15)
+    # exact equality, and invariance under a common scale
+    assert O.rel_l2([5.0, -7.0], [5.0, -7.0]) == 0.0
+    a, b = np.array([1.5, -2.0, 0.25]), np.array([1.0, -2.5, 0.5])
+    assert O.rel_l2(1e-30 * a, 1e-30 * b) == pytest.approx(O.rel_l2(a, b), rel=1e-12)
+    # a zero reference reports the plain norm of y
+    assert O.rel_l2([3.0, 4.0], [0.0, 0.0]) == pytest.approx(5.0, abs=1e-15)
+
+
+def test_rel_l2_small_errors_are_not_squared():
+    # a relative error of 1e-4 must read 1e-4 (a squared ratio reads 1e-8,
+    # which would loosen every 1e-5 gate to ~3e-3)
+    ref = np.ones(10000)
+    assert O.rel_l2(ref * (1 + 1e-4), ref) == pytest.approx(1e-4, rel=1e-9)
+
+
+def test_row_max_rel_hand_values():
+    y_ref = np.array([[1.0, -4.0, 2.0], [0.5, 0.25, -0.125]])
+    y = y_ref.copy()
+    y[0, 2] += 0.02        # row 0: 0.02 / 4
+    y[1, 0] -= 0.01        # row 1: 0.01 / 0.5 = 0.02, the worst row
+    assert O.row_max_rel(y, y_ref) == pytest.approx(0.02, abs=1e-15)
+    # the whole-tensor rel-L2 of the same pair is far smaller: a local error
+    # that the norm dilutes
+    assert O.rel_l2(y, y_ref) < 0.006
+    # one row, and the reference in the denominator
+    assert O.row_max_rel([2.0, 0.0], [1.0, 0.0]) == pytest.approx(1.0, abs=1e-15)
+    assert O.row_max_rel([1.0, 0.0], [2.0, 0.0]) == pytest.approx(0.5, abs=1e-15)
+    assert O.row_max_rel(y_ref, y_ref) == 0.0
+
+
+def test_pins_catch_squared_rel_l2(monkeypatch):
+    good = O.rel_l2
+    _expect_pin_failure(monkeypatch, "rel_l2", lambda y, r: good(y, r) ** 2,
+                        [test_rel_l2_hand_values, test_rel_l2_small_errors_are_not_squared])
+
+
+def test_pins_catch_rel_l2_wrong_denominator(monkeypatch):
+    def bad(y, y_ref):
+        y = np.asarray(y, dtype=np.float64)
+        y_ref = np.asarray(y_ref, dtype=np.float64)
+        return float(np.linalg.norm((y - y_ref).ravel()) / np.linalg.norm(y.ravel()))
+    _expect_pin_failure(monkeypatch, "rel_l2", bad, [test_rel_l2_hand_values])
+
+
+def test_pins_catch_rel_l2_per_row_mean(monkeypatch):
+    def bad(y, y_ref):
+        y = np.atleast_2d(np.asarray(y, dtype=np.float64))
+        y_ref = np.atleast_2d(np.asarray(y_ref, dtype=np.float64))
+        num = np.linalg.norm(y - y_ref, axis=1)
+        den = np.linalg.norm(y_ref, axis=1)
+        return float(np.mean(np.where(den > 0, num / np.where(den > 0, den, 1), num)))
+    _expect_pin_failure(monkeypatch, "rel_l2", bad, [test_rel_l2_hand_values])
