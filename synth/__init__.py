@@ -99,6 +99,12 @@ def trits(seed, n: int, k: int, p_zero: float = 0.31) -> np.ndarray:
     return t.astype(np.int8)
 
 
+def trits_uniform(seed, n: int, k: int) -> np.ndarray:
+    """Trits uniform over {-1, 0, 1} (int8), drawn as bytes: cheap at the
+    full decode shapes (hundreds of millions of trits)."""
+    return (_gen(seed).integers(0, 3, size=(n, k), dtype=np.int8) - np.int8(1)).astype(np.int8)
+
+
 def scales(seed, n: int, groups: int, lo: float = 0.005, hi: float = 0.03) -> np.ndarray:
     """Random fp16 scales for kernel-level tests."""
     return _gen(seed).uniform(lo, hi, size=(n, groups)).astype(np.float16)

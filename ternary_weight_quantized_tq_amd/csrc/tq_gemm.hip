@@ -2,9 +2,12 @@
 //   Y[m][n] = sum_k fp32(s[n][k/128]) t[n][k] x'[m][k],  x' = H_128 x.
 //
 // Two launches on the caller's stream:
-//   1. prep: block-128 transform of every activation row (FP32), split into
-//      hi = fp16(x') and lo = fp16(x' - hi), written to the workspace padded
-//      to whole tiles (zeros outside M x K).  hi + lo carries ~22 bits of x'.
+//   1. prep: block-128 transform of every activation row (FP32), scaled by
+//      a power of two 2^e per row (max |x'| 2^e in [2^13, 2^14), so neither
+//      part overflows or goes subnormal whatever the activations' scale),
+//      split into hi = fp16(x' 2^e) and lo = fp16(x' 2^e - hi), written to the
+//      workspace padded to whole tiles (zeros outside M x K) with e per
+//      row.  hi + lo carries ~22 bits of x'; the epilogue multiplies by 2^-e.
 //   2. gemm: each workgroup computes a 64 x 256 tile of Y on the matrix cores
 //      (v_mfma_f32_16x16x32_f16; see gemm_kernel).  The weights' B operands
 //      are decoded from the packed words straight into registers as fp16
@@ -30,28 +33,50 @@ constexpr int kThreads = 256;
 #define TQ_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
 // ------------------------------------------------------------------ prep ---
-// One wavefront per (row, block of 128) of the padded [mpad][kpad] output.
-__global__ __launch_bounds__(256) void gemm_prep_kernel(const void* __restrict__ x, int dtype, int m, int k,
-                                                        int mpad, int kpad, int fused, _Float16* __restrict__ xh,
-                                                        _Float16* __restrict__ xl) {
-  const int bpr = kpad / 128;
-  const long long job = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (job >= static_cast<long long>(mpad) * bpr) return;
-  const int lane = threadIdx.x & 63;
-  const int row = static_cast<int>(job / bpr);
-  const int kb = static_cast<int>(job % bpr) * 128;
-  float v0 = 0.0f, v1 = 0.0f;
+// One workgroup per row of the padded [mpad][kpad] A rows; wavefront w takes
+// blocks of 128 w, w + 4, ...  Pass 1 finds the row's max |x'|, pass 2
+// transforms again (the row is in L2 by then), scales by 2^e and splits.
+__device__ __forceinline__ void prep_block(const void* __restrict__ x, int dtype, int row, int m, int k, int kb,
+                                           int fused, int lane, float& v0, float& v1) {
+  v0 = 0.0f;
+  v1 = 0.0f;
   if (row < m && kb < k) {
     load_act2(x, dtype, static_cast<size_t>(row) * k + kb + 2 * lane, v0, v1);
     if (fused) wave_fwht128<float>(v0, v1, lane, kInvSqrt128);
   }
-  const _Float16 h0 = static_cast<_Float16>(v0), h1 = static_cast<_Float16>(v1);
-  const _Float16 l0 = static_cast<_Float16>(v0 - static_cast<float>(h0));
-  const _Float16 l1 = static_cast<_Float16>(v1 - static_cast<float>(h1));
-  const size_t o = static_cast<size_t>(row) * kpad + kb + 2 * lane;
-  half2_t hh = {h0, h1}, ll = {l0, l1};
-  *reinterpret_cast<half2_t*>(xh + o) = hh;
-  *reinterpret_cast<half2_t*>(xl + o) = ll;
+}
+
+__global__ __launch_bounds__(256) void gemm_prep_kernel(const void* __restrict__ x, int dtype, int m, int k,
+                                                        int kpad, int fused, _Float16* __restrict__ xh,
+                                                        _Float16* __restrict__ xl, int* __restrict__ xe) {
+  __shared__ float wmax[4];
+  const int row = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nblk = kpad / 128;
+  float mx = 0.0f;
+  for (int b = wave; b < nblk; b += 4) {
+    float v0, v1;
+    prep_block(x, dtype, row, m, k, b * 128, fused, lane, v0, v1);
+    mx = fmaxf(mx, fmaxf(fabsf(v0), fabsf(v1)));
+  }
+  mx = wave_max(mx, lane);
+  if (lane == 0) wmax[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const int e = mx > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mx) : 0;
+  if (threadIdx.x == 0) xe[row] = e;
+  for (int b = wave; b < nblk; b += 4) {
+    float v0, v1;
+    prep_block(x, dtype, row, m, k, b * 128, fused, lane, v0, v1);
+    const float s0 = ldexpf(v0, e), s1 = ldexpf(v1, e);
+    const _Float16 h0 = static_cast<_Float16>(s0), h1 = static_cast<_Float16>(s1);
+    const half2_t hh = {h0, h1};
+    const half2_t ll = {static_cast<_Float16>(s0 - static_cast<float>(h0)),
+                        static_cast<_Float16>(s1 - static_cast<float>(h1))};
+    const size_t o = static_cast<size_t>(row) * kpad + b * 128 + 2 * lane;
+    *reinterpret_cast<half2_t*>(xh + o) = hh;
+    *reinterpret_cast<half2_t*>(xl + o) = ll;
+  }
 }
 
 struct GemmArgs {
@@ -59,6 +84,7 @@ struct GemmArgs {
   const uint16_t* scales;
   const _Float16* xh;
   const _Float16* xl;
+  const int* xe;  // per padded row: the power of two applied to x' before the split
   float* y;
   int m, n, k, kpad, nb, groups, mtiles, ntiles, steps, xcd_map;
   int accumulate;  // TQ_ACCUMULATE: y += (one workgroup per output tile: no atomics)
@@ -242,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
         const int row = mt * BM + 8 * t + 2 * kb + q;
         if (row < a.m) {
           float* yp = a.y + static_cast<size_t>(row) * a.n + col;
-          const float v = acc[h][t][2 * q] + acc[h][t][2 * q + 1];
+          const float v = ldexpf(acc[h][t][2 * q] + acc[h][t][2 * q + 1], -a.xe[row]);
           *yp = a.accumulate ? *yp + v : v;
         }
       }
@@ -251,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
 
 struct GemmPlan {
   int mpad, kpad, mtiles, ntiles, steps;
-  size_t xh_bytes, total;
+  size_t xh_bytes, xe_bytes, total;
 };
 
 GemmPlan plan_gemm(int n, int k, int m) {
@@ -263,7 +289,8 @@ GemmPlan plan_gemm(int n, int k, int m) {
   p.kpad = p.steps * BK;
   if (p.kpad % 128) p.kpad = (p.kpad + 127) / 128 * 128;  // prep works in blocks of 128
   p.xh_bytes = (static_cast<size_t>(p.mpad) * p.kpad * 2 + 255) & ~static_cast<size_t>(255);
-  p.total = 2 * p.xh_bytes;
+  p.xe_bytes = (static_cast<size_t>(p.mpad) * 4 + 255) & ~static_cast<size_t>(255);
+  p.total = 2 * p.xh_bytes + p.xe_bytes;
   return p;
 }
 
@@ -285,16 +312,17 @@ extern "C" int tq_gemm(const tq_weights* w, const void* x, int x_dtype, int m, f
   if (static_cast<long long>(p.mtiles) * p.ntiles > INT_MAX) return TQ_ESHAPE;
   _Float16* xh = static_cast<_Float16*>(workspace);
   _Float16* xl = reinterpret_cast<_Float16*>(static_cast<char*>(workspace) + p.xh_bytes);
+  int* xe = reinterpret_cast<int*>(static_cast<char*>(workspace) + 2 * p.xh_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const long long jobs = static_cast<long long>(p.mpad) * (p.kpad / 128);
-  hipLaunchKernelGGL(gemm_prep_kernel, dim3(static_cast<unsigned>((jobs + 3) / 4)), dim3(256), 0, s, x, x_dtype, m,
-                     w->k, p.mpad, p.kpad, (flags & TQ_FWHT_FUSED) ? 1 : 0, xh, xl);
+  hipLaunchKernelGGL(gemm_prep_kernel, dim3(static_cast<unsigned>(p.mpad)), dim3(256), 0, s, x, x_dtype, m, w->k,
+                     p.kpad, (flags & TQ_FWHT_FUSED) ? 1 : 0, xh, xl, xe);
   TQ_LAUNCH_CHECK();
   GemmArgs a;
   a.words = reinterpret_cast<const uint4*>(w->words);
   a.scales = w->scales;
   a.xh = xh;
   a.xl = xl;
+  a.xe = xe;
   a.y = y;
   a.m = m;
   a.n = w->n;

@@ -6,6 +6,7 @@ import synth
 import ternary_weight_quantized_tq_amd as tq
 from oracle import tq_oracle as O
 
+from parity import assert_parity
 from tqgpu import act_tensor, dev, gpu_pack, gpu_quantize_pack, run_gemm, run_gemv, torch
 
 pytestmark = pytest.mark.gpu
@@ -36,8 +37,7 @@ def test_gemm_random_vs_oracle(m, n, k, dtype):
     act = synth.activations(61 + m, m, k, dtype)
     y = run_gemm(w, act_tensor(act), m)
     y_ref = O.gemv(O.pack(t), s, k, act.values, True)
-    err = O.rel_l2(y, y_ref)
-    assert err < 1e-5, err
+    assert_parity(y, y_ref)
 
 
 def test_gemm_row_equals_gemv():
@@ -61,8 +61,7 @@ def test_gemm_prefill_full_size_sampled():
     cols = np.concatenate([rng.choice(wl.n, 190, replace=False), [0, wl.n - 1]])
     t, s, _ = O.quantize(w64[cols])
     y_ref = O.gemv(O.pack(t), s, wl.k, act.values[rows], True)
-    err = O.rel_l2(y[np.ix_(rows, cols)], y_ref)
-    assert err < 1e-5, err
+    assert_parity(y[np.ix_(rows, cols)], y_ref)
 
 
 def test_gemm_accumulate():
@@ -78,4 +77,33 @@ def test_gemm_accumulate():
     th.cuda.synchronize()
     got = y.cpu().numpy().astype(np.float64) - base
     y_ref = O.gemv(O.pack(t), s, 1280, act.values, True)
-    assert O.rel_l2(got, y_ref) < 1e-5
+    assert_parity(got, y_ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [3e-6, 2e4])
+def test_gemm_activation_range(dtype, scale):
+    """Activations of scale 2e4 (x' past fp16's largest value) and 3e-6 (x'
+    below fp16's normal range): the prep step scales each row by a power of
+    two before splitting it into fp16 parts, and the epilogue undoes it."""
+    t, s, w = _rand(120, 300, 1920)
+    m = 70
+    act = synth.activations(121, m, 1920, dtype, scale=scale)
+    y = run_gemm(w, act_tensor(act), m)
+    y_ref = O.gemv(O.pack(t), s, 1920, act.values, True)
+    assert_parity(y, y_ref)
+
+
+def test_gemm_rows_of_very_different_scales():
+    """Each activation row gets its own power of two: rows of scale 1e-5, 1
+    and 3e4 in one call."""
+    t, s, w = _rand(130, 257, 1280)
+    m = 66
+    act = synth.activations(131, m, 1280, "f32")
+    x = act.raw.copy()
+    x[::3] *= 1e-5
+    x[1::3] *= 3e4
+    y = run_gemm(w, dev(x), m)
+    y_ref = O.gemv(O.pack(t), s, 1280, x.astype(np.float64), True)
+    for r in range(m):
+        assert_parity(y[r:r + 1], y_ref[r:r + 1], what=f"row {r}")

@@ -6,6 +6,7 @@ import synth
 import ternary_weight_quantized_tq_amd as tq
 from oracle import tq_oracle as O
 
+from parity import assert_parity
 from tqgpu import act_tensor, dev, gpu_pack_expert, run_moe, torch
 
 pytestmark = pytest.mark.gpu
@@ -68,7 +69,7 @@ def test_moe_small_random(dtype):
     rw /= rw.sum(axis=1, keepdims=True)
     y = run_moe(w_gu, w_dn, act_tensor(act), T, topk, ids, rw)
     y_ref = O.moe(act.values, ids, rw, h["gu_w"], h["gu_s"], h["dn_w"], h["dn_s"], hidden, inter)
-    assert O.rel_l2(y, y_ref) < 1e-5
+    assert_parity(y, y_ref)
 
 
 @pytest.mark.parametrize("T", [2, 40])
@@ -88,7 +89,7 @@ def test_moe_activation_range(T, scale):
     with np.errstate(over="ignore"):  # silu of large negative gates: exp overflows to inf, silu -> 0
         y_ref = O.moe(act.values, ids, rw, h["gu_w"], h["gu_s"], h["dn_w"], h["dn_s"], hidden, inter)
     assert np.all(np.isfinite(y))
-    assert O.rel_l2(y, y_ref) < 1e-5
+    assert_parity(y, y_ref)
 
 
 @pytest.mark.parametrize("T", [21, 40])
@@ -112,7 +113,7 @@ def test_moe_many_tokens_per_expert_and_bad_ids(T):
             if ok[t, j]:
                 y_ref[t] += O.moe(act.values[t:t + 1], ids[t:t + 1, j:j + 1], rw[t:t + 1, j:j + 1], h["gu_w"],
                                   h["gu_s"], h["dn_w"], h["dn_s"], hidden, inter)[0]
-    assert O.rel_l2(y, y_ref) < 1e-5
+    assert_parity(y, y_ref)
 
 
 @pytest.mark.parametrize("T,topk", [(2, 12), (2, 32), (3, 22), (4, 16), (5, 9)])
@@ -134,7 +135,7 @@ def test_moe_wide_topk(T, topk):
     ok = (ids >= 0) & (ids < E)
     y_ref = O.moe(act.values, np.where(ok, ids, 0), np.where(ok, rw, 0.0), h["gu_w"], h["gu_s"], h["dn_w"], h["dn_s"],
                   hidden, inter)
-    assert O.rel_l2(y, y_ref) < 1e-5
+    assert_parity(y, y_ref)
 
 
 @pytest.mark.parametrize("wl", [synth.MOE_T1, synth.MOE_T64], ids=["t1", "t64"])
@@ -164,8 +165,7 @@ def test_moe_expert_layer_workload(wl):
     dn_w = {e: v[2] for e, v in host.items()}
     dn_s = {e: v[3] for e, v in host.items()}
     y_ref = O.moe(act.values, ids, rw, gu_w, gu_s, dn_w, dn_s, wl.hidden, wl.inter, tokens=tokens)
-    err = O.rel_l2(y[tokens], y_ref[tokens])
-    assert err < 1e-5, err
+    assert_parity(y[tokens], y_ref[tokens])
 
 
 def test_moe_many_experts_few_pairs():
@@ -189,7 +189,7 @@ def test_moe_many_experts_few_pairs():
     rw = np.full((T, topk), 0.25)
     y = run_moe(w_gu, w_dn, act_tensor(act), T, topk, ids, rw)
     y_ref = O.moe(act.values, ids, rw, h["gu_w"], h["gu_s"], h["dn_w"], h["dn_s"], hidden, inter)
-    assert O.rel_l2(y, y_ref) < 1e-5
+    assert_parity(y, y_ref)
 
 
 @pytest.mark.parametrize("T", [1, 3, 5, 40])
@@ -212,4 +212,34 @@ def test_moe_accumulate(T):
     th.cuda.synchronize()
     got = y.cpu().numpy().astype(np.float64) - base
     y_ref = O.moe(act.values, ids, rw, h["gu_w"], h["gu_s"], h["dn_w"], h["dn_s"], hidden, inter)
-    assert O.rel_l2(got, y_ref) < 1e-5
+    assert_parity(got, y_ref)
+
+
+@pytest.mark.parametrize("T,topk", [(3, 2), (5, 4), (40, 2)])
+def test_moe_reports_bad_ids(T, topk):
+    """Ids outside [0, E) are counted on the device and reported by
+    tq_moe_bad_ids (per-pair, per-token and bucketed paths); a following
+    call with valid ids on the same workspace reports zero."""
+    th = torch()
+    E, hidden, inter = 5, 256, 128
+    w_gu, w_dn, h = _random_experts(1300, E, hidden, inter)
+    act = synth.activations(131, T, hidden, "bf16")
+    rng = np.random.default_rng(132)
+    ids = np.stack([rng.choice(E, topk, replace=False) for _ in range(T)]).astype(np.int32)
+    good_ids = ids.copy()
+    ids[0, 0] = -1
+    ids[T - 1, topk - 1] = E
+    ids[T // 2, 0] = 1 << 30
+    rw = np.full((T, topk), 1.0 / topk)
+    y = th.empty((T, hidden), dtype=th.float32, device="cuda")
+    ws, nbytes = tq.workspace(tq.TQ_OP_MOE, w_gu, T, topk)
+    x = act_tensor(act)
+    tq.tq_moe_gemv(w_gu, w_dn, x, T, topk, dev(ids), dev(rw.astype(np.float32)), y, tq.TQ_FWHT_FUSED, ws, nbytes)
+    assert tq.tq_moe_bad_ids(ws, nbytes) == 3
+    st = tq.lib().tq_moe_bad_ids(ws.data_ptr(), nbytes, tq.ctypes.byref(tq.ctypes.c_int32()), None)
+    assert st == tq.TQ_EDATA
+    tq.tq_moe_gemv(w_gu, w_dn, x, T, topk, dev(good_ids), dev(rw.astype(np.float32)), y, tq.TQ_FWHT_FUSED, ws,
+                   nbytes)
+    assert tq.tq_moe_bad_ids(ws, nbytes) == 0
+    y_ref = O.moe(act.values, good_ids, rw, h["gu_w"], h["gu_s"], h["dn_w"], h["dn_s"], hidden, inter)
+    assert_parity(y.cpu().numpy(), y_ref)
