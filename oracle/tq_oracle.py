@@ -48,6 +48,12 @@ Readings where the pages are silent:
   straddle group boundaries; the row tail is padded with t = 0 (digit 1);
 * Hadamard: Sylvester, natural order, normalised by 1/sqrt(128), no random
   sign diagonal; rotation blocks coincide with the scale groups;
+* group size: 128 ([Bonsai] section 2 (2)); 64 as the finer-scale variant
+  that [TQ-MLX]'s model id ("...-g64") hints at.  The rotation stays
+  block-128 either way: only the scale granularity changes;
+* binary variant ([TQ-MLX] point 3, pure 1-bit {-c, +c}): the same rotation
+  and absmean scale, t = +1 where w' >= 0 else -1, 32 signs per uint32
+  (bit i of word w is weight 32w + i, 1 for +1);
 * MoE: softmax over all expert logits, top-k (ties to the lower id), weights
   renormalised to sum 1; expert MLP is SwiGLU, h = silu(gate) * up, and the
   block-128 transform is applied to h before the down projection.
@@ -138,9 +144,73 @@ def ternarize(w_rot: np.ndarray, group: int = GROUP):
     return t.reshape(n, k), s, gamma
 
 
-def quantize(w: np.ndarray):
-    """Offline conversion: rotate, then ternarise. Returns (t, s, gamma)."""
-    return ternarize(rotate_weights(w))
+def quantize(w: np.ndarray, group: int = GROUP):
+    """Offline conversion: rotate (blocks of 128), then ternarise per group
+    of `group` weights (128, or 64 for the finer-scale variant). Returns
+    (t, s, gamma)."""
+    return ternarize(rotate_weights(w), group)
+
+
+# --------------------------------------------------------------------------
+# Binary {-c, +c} variant  ([TQ-MLX] point 3: pure 1-bit experts, only -c and
+# +c, compared against ternary)
+# --------------------------------------------------------------------------
+def binarize(w_rot: np.ndarray, group: int = GROUP):
+    """Per (row n, group g): gamma = mean |w'| (for signs this is also the
+    least-squares scale, argmin_c sum (w' - c sign w')^2), t = +1 where
+    w' >= 0 else -1 (no zero level; an exact 0 goes to +1), s = fp16(gamma)
+    rounded once from FP64.  Returns (t int8, s float16, gamma float64)."""
+    w_rot = np.asarray(w_rot, dtype=np.float64)
+    n, k = w_rot.shape
+    if k % group:
+        raise ValueError("K must be a multiple of the group size")
+    g = w_rot.reshape(n, k // group, group)
+    gamma = np.abs(g).mean(axis=2)
+    t = np.where(g >= 0.0, 1, -1).astype(np.int8)
+    return t.reshape(n, k), gamma.astype(np.float16), gamma
+
+
+def quantize_binary(w: np.ndarray, group: int = GROUP):
+    """Offline conversion of the binary variant: rotate, then binarise."""
+    return binarize(rotate_weights(w), group)
+
+
+BITS_PER_WORD = 32
+
+
+def words_per_row_binary(k: int) -> int:
+    return -(-k // BITS_PER_WORD)
+
+
+def pack_binary(t: np.ndarray) -> np.ndarray:
+    """word[n][w] = sum_{i<32} b[n][32w+i] 2^i with b = 1 for +1, 0 for -1;
+    bits past K are 0."""
+    t = np.asarray(t)
+    n, k = t.shape
+    if t.size and not np.all((t == 1) | (t == -1)):
+        raise ValueError("binary weights must be -1 or +1")
+    nw = words_per_row_binary(k)
+    bits = np.zeros((n, nw * BITS_PER_WORD), dtype=np.uint64)
+    bits[:, :k] = (t > 0).astype(np.uint64)
+    bits = bits.reshape(n, nw, BITS_PER_WORD)
+    acc = np.zeros((n, nw), dtype=np.uint64)
+    for i in range(BITS_PER_WORD):
+        acc += bits[:, :, i] * np.uint64(1 << i)
+    return acc.astype(np.uint32)
+
+
+def unpack_binary(words: np.ndarray, k: int) -> np.ndarray:
+    """t[n][k] = 2 ((word[n][k // 32] // 2^(k mod 32)) mod 2) - 1."""
+    words = np.asarray(words, dtype=np.int64)
+    kk = np.arange(k)
+    w = words[:, kk // BITS_PER_WORD]
+    p = np.array([1 << int(i) for i in (kk % BITS_PER_WORD)], dtype=np.int64)
+    return (2 * ((w // p) % 2) - 1).astype(np.int8)
+
+
+def packed_bytes_binary(n: int, k: int, group: int = GROUP) -> int:
+    """Bytes of 1-bit words plus fp16 scales: 4*N*ceil(K/32) + 2*N*K/group."""
+    return 4 * n * words_per_row_binary(k) + 2 * n * (k // group)
 
 
 # --------------------------------------------------------------------------
@@ -186,30 +256,32 @@ def packed_bytes(n: int, k: int, group: int = GROUP) -> int:
 # --------------------------------------------------------------------------
 # Dequantised matvec on packed weights  ([Bonsai] 2 (2)(3); [GSQ-cmp] §1.1)
 # --------------------------------------------------------------------------
-def dequantize(words: np.ndarray, scales: np.ndarray, k: int) -> np.ndarray:
-    """W_hat[n][k] = fp64(s[n][k // 128]) * t[n][k]  (FP64, dense, [N][K])."""
-    t = unpack(words, k).astype(np.float64)
+def dequantize(words: np.ndarray, scales: np.ndarray, k: int, group: int = GROUP,
+               levels: int = 3) -> np.ndarray:
+    """W_hat[n][k] = fp64(s[n][k // group]) * t[n][k]  (FP64, dense, [N][K]);
+    t from base-3 words (levels 3) or 1-bit words (levels 2)."""
+    t = (unpack(words, k) if levels == 3 else unpack_binary(words, k)).astype(np.float64)
     s = np.asarray(scales).astype(np.float64)
-    return t * np.repeat(s, GROUP, axis=1)[:, :k]
+    return t * np.repeat(s, group, axis=1)[:, :k]
 
 
-def matvec(words, scales, k, x_rot) -> np.ndarray:
-    """y[m][n] = sum_k s[n][k/128] t[n][k] x'[m][k] for x' already rotated."""
+def matvec(words, scales, k, x_rot, group: int = GROUP, levels: int = 3) -> np.ndarray:
+    """y[m][n] = sum_k s[n][k/group] t[n][k] x'[m][k] for x' already rotated."""
     x_rot = np.atleast_2d(np.asarray(x_rot, dtype=np.float64))
-    return x_rot @ dequantize(words, scales, k).T
+    return x_rot @ dequantize(words, scales, k, group, levels).T
 
 
-def gemv(words, scales, k, x, fused_fwht: bool = True) -> np.ndarray:
+def gemv(words, scales, k, x, fused_fwht: bool = True, group: int = GROUP, levels: int = 3) -> np.ndarray:
     """Online path: x -> (optional) block-128 transform -> dequantised matvec."""
     x = np.atleast_2d(np.asarray(x, dtype=np.float64))
     xr = fwht(x) if fused_fwht else x
-    return matvec(words, scales, k, xr)
+    return matvec(words, scales, k, xr, group, levels)
 
 
-def gemm_rows(words, scales, k, x, rows) -> np.ndarray:
+def gemm_rows(words, scales, k, x, rows, group: int = GROUP, levels: int = 3) -> np.ndarray:
     """Selected rows of Y = fwht(X) . W_hat^T (the prefill GEMM)."""
     x = np.asarray(x, dtype=np.float64)[np.asarray(rows)]
-    return gemv(words, scales, k, x, True)
+    return gemv(words, scales, k, x, True, group, levels)
 
 
 def unquantized(w: np.ndarray, x: np.ndarray) -> np.ndarray:
@@ -239,7 +311,7 @@ def silu(z):
 
 
 def moe(x, ids, route_w, gu_words, gu_scales, dn_words, dn_scales, hidden, inter,
-        tokens=None):
+        tokens=None, group: int = GROUP):
     """Expert MLP over routed tokens.  Per token t and slot j with e = ids[t][j]:
     g||u = W_gu[e] . H x_t  (rows [0, I) gate, [I, 2I) up),
     h = silu(g) * u,  o = W_dn[e] . H h,  y_t = sum_j w[t][j] * o.
@@ -257,8 +329,8 @@ def moe(x, ids, route_w, gu_words, gu_scales, dn_words, dn_scales, hidden, inter
         for j in range(ids.shape[1]):
             e = int(ids[t, j])
             if e not in gu_cache:
-                gu_cache[e] = dequantize(gu_words[e], gu_scales[e], hidden)
-                dn_cache[e] = dequantize(dn_words[e], dn_scales[e], inter)
+                gu_cache[e] = dequantize(gu_words[e], gu_scales[e], hidden, group)
+                dn_cache[e] = dequantize(dn_words[e], dn_scales[e], inter, group)
             gu = gu_cache[e] @ xr
             h = silu(gu[:inter]) * gu[inter:]
             o = dn_cache[e] @ fwht(h[None, :])[0]

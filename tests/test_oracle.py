@@ -417,9 +417,9 @@ def test_pins_catch_unnormalised_hadamard(monkeypatch):
 def test_pins_catch_wrong_group_index(monkeypatch):
     good = O.dequantize
 
-    def bad(words, scales, k):
+    def bad(words, scales, k, *rest):
         s = np.asarray(scales)
-        return good(words, np.roll(s, 1, axis=1), k)    # off-by-one group
+        return good(words, np.roll(s, 1, axis=1), k, *rest)    # off-by-one group
     _expect_pin_failure(monkeypatch, "dequantize", bad,
                         [test_matvec_one_hot_exact, test_matvec_group_ones_exact])
 
