@@ -19,7 +19,11 @@ serves them.
             the measured HBM bytes per launch from the committed rocprofv3
             counter summary when it was taken on the current kernel sources
   cpu_baseline  the FP64 CPU oracle (unpack + transform + dequantised
-            matvec) on a bounded row sample, in packed-weight GB/s
+            matvec) on a bounded row sample, in packed-weight GB/s: all
+            cores (one process per usable core, one BLAS thread each) as
+            `value`, one thread beside it
+  read_only_same_bytes  one plain read pass over one launch's bytes (the
+            read ceiling at this launch size; context)
   isolated_launch_us_p10_p50_p90  one GEMV launched alone between two HIP
             events (dispatch and ramp-up included; context)
   mall_hot_single_copy   the same step on one weight copy (cache-resident,
@@ -27,7 +31,8 @@ serves them.
 
 `extras` adds the other workloads: one transformer block's seven linears at
 M = 1 (single stream) and M = 8, the 256-expert MoE layer at T = 1 and
-T = 64, and the prefill GEMM.
+T = 64, the prefill GEMM, and the format variants (ternary at group 64,
+binary {-c, +c} at groups 128 and 64) on the decode step's two linears.
 """
 from __future__ import annotations
 
@@ -58,7 +63,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-extras", action="store_true", help="only the main metric")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--only-extra", choices=["block_m1", "block_m8", "moe", "prefill_gemm"],
+    p.add_argument("--only-extra", choices=["block_m1", "block_m8", "moe", "prefill_gemm", "variants"],
                    help="run one extra workload alone and print its JSON (for profiling)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy (for scaling rocprofv3 byte counters)")
@@ -98,12 +103,12 @@ def quantize_pack(tq, torch, w64, n, k, w_out=None, expert=0):
     wt = torch.from_numpy(w64).cuda()
     trits = torch.empty((n, k), dtype=torch.int8, device="cuda")
     scales = torch.empty((n, k // 128), dtype=torch.int16, device="cuda")
-    tq.tq_quantize(wt, n, k, trits, scales)
+    tq.tq_quantize(wt, n, k, 128, 3, trits, scales)
     del wt
     w = w_out if w_out is not None else tq.empty_weights(n, k)
-    nw, ns = tq.tq_layout_words(n, k, tq.TQ_LAYOUT_ROW64), tq.tq_layout_scales(n, k, tq.TQ_LAYOUT_ROW64)
-    tq.tq_pack(trits, n, k, tq.TQ_LAYOUT_ROW64, w.words.data_ptr() + 4 * nw * expert)
-    tq.tq_pack_scales(scales, n, k, tq.TQ_LAYOUT_ROW64, w.scales.data_ptr() + 2 * ns * expert)
+    nw, ns = tq.tq_layout_words(n, k, tq.TQ_LAYOUT_ROW64, 3), tq.tq_layout_scales(n, k, tq.TQ_LAYOUT_ROW64, 128)
+    tq.tq_pack(trits, n, k, tq.TQ_LAYOUT_ROW64, 3, w.words.data_ptr() + 4 * nw * expert)
+    tq.tq_pack_scales(scales, n, k, tq.TQ_LAYOUT_ROW64, 128, w.scales.data_ptr() + 2 * ns * expert)
     return w
 
 
@@ -113,7 +118,7 @@ def bf16(torch, act):
 
 
 def clone_w(tq, w):
-    return tq.Weights(w.words.clone(), w.scales.clone(), w.n, w.k, w.layout, w.num_experts)
+    return w.clone()
 
 
 def capture(torch, n, fn, *extra):
@@ -142,51 +147,114 @@ def timed(torch, steps, warmup, fn):
     return a.elapsed_time(b) / steps
 
 
-def cpu_baseline(O, synth, lins, w64s, seconds):
-    """Oracle unpack + transform + matvec on row samples, repeated for about
-    `seconds`; reported as packed bytes per second."""
+def _oracle_worker(chunks, seconds, barrier, out):
+    """One all-cores worker: the oracle on its row chunks, repeated for
+    `seconds` after every worker is ready; BLAS limited to one thread."""
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
     except Exception:
-        cores = os.cpu_count() or 1
+        pass
+    from oracle import tq_oracle as O
+    barrier.wait()
+    done, reps, t0 = 0, 0, time.perf_counter()
+    while True:
+        for words, s, k, x, nbytes in chunks:
+            O.gemv(words, s, k, x, True)
+            done += nbytes
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    out.put((done, reps, time.perf_counter() - t0))
+
+
+def cpu_model_name():
+    """The host processor as lscpu names it (model name, family, model and
+    stepping), or /proc/cpuinfo's model name if lscpu is missing."""
+    try:
+        import subprocess
+        txt = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        f = {ln.split(":", 1)[0].strip(): ln.split(":", 1)[1].strip() for ln in txt.splitlines() if ":" in ln}
+        if "Model name" in f:
+            return (f"{f['Model name']} (vendor {f.get('Vendor ID', '?')}, family {f.get('CPU family', '?')}, "
+                    f"model {f.get('Model', '?')}, stepping {f.get('Stepping', '?')})")
+    except Exception:
+        pass
+    try:
+        with open("/proc/cpuinfo") as fh:
+            return next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:
+        return None
+
+
+def cpu_baseline(O, synth, lins, w64s, seconds, max_workers=16):
+    """The FP64 oracle (unpack + dense block-128 transform + dequantised
+    matvec) on row samples of the step's linears, in packed bytes per
+    second.  Two legs: one thread (this process, BLAS limited to one
+    thread), and all cores: the same rows cut into one chunk per usable core
+    (at most `max_workers`), each chunk in its own process with one BLAS
+    thread, all started together and run for the same time."""
+    import multiprocessing as mp
     samples = []
     for lin, w64 in zip(lins, w64s):
         rows = 1024 if lin.k <= 8192 else 512
         t, s, _ = O.quantize(w64[:rows])
         x = synth.activations(lin.x_seed, 1, lin.k, "bf16").values
-        samples.append((O.pack(t), s, lin.k, x, O.packed_bytes(rows, lin.k), rows))
-    def run(budget):
-        done, t0, reps = 0, time.perf_counter(), 0
-        while True:
-            for words, s, k, x, nbytes, _ in samples:
-                O.gemv(words, s, k, x, True)
-                done += nbytes
-            reps += 1
-            if time.perf_counter() - t0 >= budget:
-                break
-        dt = time.perf_counter() - t0
-        return done / dt / 1e9, reps, dt
+        samples.append((O.pack(t), s, lin.k, x, rows))
+    desc = " + ".join(f"{smp[4]} rows of {lin.name} ({lin.n}x{lin.k})" for smp, lin in zip(samples, lins))
 
-    gbs, reps, dt = run(seconds)
-    try:  # the same sample on one thread, for a third of the time
+    # one thread
+    one = {}
+    try:
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=1):
-            gbs1, reps1, dt1 = run(seconds / 3)
-        one = {"value": round(gbs1, 4), "reps": reps1, "seconds": round(dt1, 1)}
+            done, reps, t0 = 0, 0, time.perf_counter()
+            while True:
+                for words, s, k, x, rows in samples:
+                    O.gemv(words, s, k, x, True)
+                    done += O.packed_bytes(rows, k)
+                reps += 1
+                if time.perf_counter() - t0 >= seconds / 2:
+                    break
+            dt = time.perf_counter() - t0
+        one = {"value": round(done / dt / 1e9, 5), "threads": 1, "reps": reps, "seconds": round(dt, 1)}
     except Exception as e:  # report, never hide
         one = {"error": f"{type(e).__name__}: {e}"}
-    model = None
+
+    # all cores: one process per usable core, each on its share of the rows
     try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
-    except OSError:
-        pass
-    desc = " + ".join(f"{smp[5]} rows of {lin.name} ({lin.n}x{lin.k})" for smp, lin in zip(samples, lins))
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{desc}, repeated {reps}x over {dt:.1f} s (FP64 unpack + dense block-128 transform + "
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    workers = max(1, min(affinity, max_workers))
+    chunks = [[] for _ in range(workers)]
+    for words, s, k, x, rows in samples:
+        for i, idx in enumerate(np_array_split(rows, workers)):
+            if len(idx):
+                chunks[i].append((words[idx], s[idx], k, x, O.packed_bytes(len(idx), k)))
+    ctx = mp.get_context("spawn")
+    barrier, out = ctx.Barrier(workers), ctx.Queue()
+    procs = [ctx.Process(target=_oracle_worker, args=(chunks[i], seconds / 2, barrier, out)) for i in range(workers)]
+    for p in procs:
+        p.start()
+    res = [out.get(timeout=600) for _ in procs]
+    for p in procs:
+        p.join()
+    total = sum(r[0] for r in res)
+    wall = max(r[2] for r in res)
+    all_cores = total / wall / 1e9
+    return {"value": round(all_cores, 5), "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": f"{desc}: all cores = {workers} processes, one BLAS thread each, each on 1/{workers} of "
+                      f"the rows, run together for {wall:.1f} s (FP64 unpack + dense block-128 transform + "
                       f"dequantised matvec), packed bytes per second",
-            "one_thread": one, "cpu_model": model}
+            "one_thread": one, "nproc": os.cpu_count(), "affinity_cpus": affinity, "workers": workers,
+            "cpu_model": cpu_model_name()}
+
+
+def np_array_split(n, parts):
+    """Index ranges of n rows in `parts` nearly equal consecutive chunks."""
+    import numpy as np
+    return np.array_split(np.arange(n), parts)
 
 
 def cpu_gemm_rows(O, synth, rows=64):
@@ -263,6 +331,58 @@ def extra_block(tq, torch, synth, np, wl):
     out["separate_linears"] = separate
     out["compute"] = ("LDS partial-sum table, FP32" if m == 1 else
                       "v_mfma_f32_16x16x32_f16 (x' as two fp16 parts in the A rows, fp16 trit codes, FP32 accumulate)")
+    return out
+
+
+def extra_variants(tq, torch, synth, np):
+    """The format variants on the single-stream decode step's two linears
+    (up 5120 -> 17408, down 17408 -> 5120): ternary at group 64, and binary
+    {-c, +c} at group 128 and 64, at M = 1 and M = 8.  Each variant's own
+    algorithmic bytes (words + scales) over the kernel time; weights
+    quantised on the GPU from the same seeded matrices, rotated over copies
+    of >= 1 GiB."""
+    lins = synth.DENSE_DECODE_27B.linears
+    w64s = [synth.weights(l.w_seed, l.n, l.k) for l in lins]
+    out = []
+    for name, group, levels in (("ternary-g64", 64, 3), ("binary-g128", 128, 2), ("binary-g64", 64, 2)):
+        base = []
+        for lin, w64 in zip(lins, w64s):
+            wt = torch.from_numpy(w64).cuda()
+            t = torch.empty((lin.n, lin.k), dtype=torch.int8, device="cuda")
+            sc = torch.empty((lin.n, lin.k // group), dtype=torch.int16, device="cuda")
+            tq.tq_quantize(wt, lin.n, lin.k, group, levels, t, sc)
+            del wt
+            w = tq.empty_weights(lin.n, lin.k, group=group, levels=levels)
+            tq.tq_pack(t, lin.n, lin.k, tq.TQ_LAYOUT_ROW64, levels, w.words)
+            tq.tq_pack_scales(sc, lin.n, lin.k, tq.TQ_LAYOUT_ROW64, group, w.scales)
+            base.append(w)
+        torch.cuda.synchronize()
+        nbytes = [tq.tq_format_bytes(l.n, l.k, group, levels) for l in lins]
+        copies = max(1, -(-ROTATE_BYTES // sum(nbytes)))
+        sets = [base] + [[w.clone() for w in base] for _ in range(copies - 1)]
+        row = {"variant": name, "group": group, "levels": levels, "bytes_per_step": sum(nbytes),
+               "weight_copies_rotated": copies}
+        for m in (1, 8):
+            xs = [bf16(torch, synth.activations(l.x_seed, m, l.k, "bf16")) for l in lins]
+            ys = [torch.zeros((m, l.n), dtype=torch.float32, device="cuda") for l in lins]
+            us = []
+            for j in range(len(lins)):
+                g = capture(torch, copies, lambda i: tq.tq_gemv(sets[i][j], xs[j], m, ys[j],
+                                                                 tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE))
+                g.replay()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                b.record()
+                torch.cuda.synchronize()
+                us.append(1e3 * a.elapsed_time(b) / copies)
+            gbs = sum(nbytes) / (sum(us) * 1e-6) / 1e9
+            row[f"m{m}"] = {"kernel_us": {l.name: round(u, 3) for l, u in zip(lins, us)}, "gb_s": round(gbs, 1),
+                            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                            "layer_tok_s": round(m / (sum(us) * 1e-6), 1)}
+        del sets
+        torch.cuda.empty_cache()
+        out.append(row)
     return out
 
 
@@ -346,7 +466,7 @@ def main():
 
     if args.only_extra:
         fn = {"block_m1": extra_block_m1, "block_m8": extra_block_m8, "moe": extra_moe,
-              "prefill_gemm": extra_gemm}[args.only_extra]
+              "prefill_gemm": extra_gemm, "variants": extra_variants}[args.only_extra]
         print(json.dumps({args.only_extra: fn(tq, torch, synth, np)}), flush=True)
         return
 
@@ -442,6 +562,26 @@ def main():
     b.record()
     torch.cuda.synchronize()
     copy_us = 1e3 * a.elapsed_time(b) / copies
+    # The read ceiling at this launch size: one plain read pass over the
+    # bytes of one GEMV launch (16-byte non-temporal loads, the GEMV's load
+    # form), over rotated buffers, timed the same way.
+    rd_bytes = lin_bytes[0] // 16 * 16
+    rd_stride = (rd_bytes + 255) // 256 * 256
+    rd_copies = max(1, -(-ROTATE_BYTES // rd_stride))
+    rd_buf = torch.ones(rd_copies * rd_stride // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rd = lambda i: tq.tq_read_bytes(rd_buf.data_ptr() + i * rd_stride, rd_bytes, sink)
+    for i in range(rd_copies):
+        rd(i)
+    rg = capture(torch, rd_copies, rd)
+    rg.replay()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    rg.replay()
+    b.record()
+    torch.cuda.synchronize()
+    read_us = 1e3 * a.elapsed_time(b) / rd_copies
+    del rd_buf
     # The same step on one copy of the weights (no rotation): they then sit
     # in the 256 MB Infinity Cache, so this shows the kernels off HBM.
     hot = capture(torch, args.steps, lambda i: step(0))
@@ -484,6 +624,12 @@ def main():
         "plain_copy_same_bytes": {"bytes_moved": 8 * half, "us": round(copy_us, 3),
                                   "gb_s": round(8 * half / (copy_us * 1e-6) / 1e9, 1),
                                   "frac_hbm_peak": round(8 * half / (copy_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "read_only_same_bytes": {"bytes_read": rd_bytes, "us": round(read_us, 3),
+                                 "gb_s": round(rd_bytes / (read_us * 1e-6) / 1e9, 1),
+                                 "frac_hbm_peak": round(rd_bytes / (read_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "buffers_rotated": rd_copies,
+                                 "note": "one plain read pass (tq_read_bytes) over one launch's bytes: the read "
+                                         "ceiling at this launch size; context"},
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic)},
@@ -491,7 +637,7 @@ def main():
     if not args.no_extras:
         extras = {}
         for name, fn in (("block_m1", extra_block_m1), ("block_m8", extra_block_m8), ("moe", extra_moe),
-                         ("prefill_gemm", extra_gemm)):
+                         ("prefill_gemm", extra_gemm), ("variants", extra_variants)):
             log(f"extra: {name} ...")
             try:
                 extras[name] = fn(tq, torch, synth, np)

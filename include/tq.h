@@ -29,8 +29,9 @@
  *     section "Why 1.58 bit...", point 1).
  *
  * Conventions for every entry point:
- *   * Array pointers are DEVICE pointers owned by the caller; no call
- *     allocates, frees or synchronises.  Work is enqueued on `stream`, a
+ *   * Array pointers are DEVICE pointers owned by the caller (except the
+ *     host count of tq_moe_bad_ids); no call allocates or frees, and none
+ *     synchronises except tq_moe_bad_ids.  Work is enqueued on `stream`, a
  *     hipStream_t passed as void* (NULL = the default stream), and runs
  *     asynchronously after the call returns.
  *   * Arguments, shapes and descriptors are checked synchronously; a bad one
@@ -46,8 +47,9 @@
  *     the same time must not share a workspace.
  *   * Alignment (checked; TQ_EINVAL otherwise): packed words, scales and
  *     workspaces 16 bytes; activations two elements (8 bytes for TQ_F32, 4
- *     for 16-bit types); FP32 outputs 4 bytes (tq_fwht's 8).  Allocations
- *     from hipMalloc or PyTorch are 256-byte aligned.
+ *     for 16-bit types); FP32 outputs 4 bytes (tq_fwht's 8); offline
+ *     inputs and outputs to their element size (tq_quantize's trits 2
+ *     bytes).  Allocations from hipMalloc or PyTorch are 256-byte aligned.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -60,9 +62,10 @@ extern "C" {
 #endif
 
 #define TQ_MAGIC 0x30325154u /* "TQ20" */
-#define TQ_VERSION 1u
+#define TQ_VERSION 2u
 #define TQ_TRITS_PER_WORD 20
-#define TQ_GROUP 128
+#define TQ_GROUP 128      /* default weights per scale; 64 is the other group size */
+#define TQ_BITS_PER_WORD 32 /* binary variant: one sign bit per weight */
 
 typedef enum {
   TQ_OK = 0,
@@ -71,24 +74,42 @@ typedef enum {
   TQ_EFORMAT = -3,      /* descriptor magic/version/layout/expert count wrong  */
   TQ_ENOSPACE = -4,     /* workspace too small                                 */
   TQ_EHIP = -5,         /* a HIP launch failed                                 */
-  TQ_EUNSUPPORTED = -6  /* valid request the library does not implement        */
+  TQ_EUNSUPPORTED = -6, /* valid request the library does not implement        */
+  TQ_EDATA = -7         /* input values out of range (reported by the checking
+                           calls: trits outside {-1,0,1}, expert ids outside
+                           [0, E))                                             */
 } tq_status;
 
 /* Element types of activations / inputs. */
 enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2, TQ_F64 = 3 };
 
-/* Word / scale layouts.
- * TQ_LAYOUT_ROWMAJOR: the canonical interchange layout. words[n][ceil(K/20)],
- *   scales[n][K/128] (IEEE fp16 bits), rows contiguous.
+/* Formats.  Two parameters describe the weights:
+ *   levels 3 (ternary {-c,0,+c}, the path's format): base-3 words, 20 per
+ *     uint32, as above;
+ *   levels 2 (binary {-c,+c}, the pure 1-bit variant the TurboQuant-MLX page
+ *     compares against, point 3): one sign bit per weight, 32 per uint32,
+ *     bit i of word w is weight 32w + i, 1 for +c;
+ *   group 128 (27B ternary page, section 2 (2)) or 64 (the "-g64" model id
+ *     on the TurboQuant-MLX page): weights per FP16 scale.  The rotation is
+ *     block-128 either way; K stays a multiple of 128.
+ *
+ * Word / scale layouts.
+ * TQ_LAYOUT_ROWMAJOR: the canonical interchange layout. words[n][ceil(K/20)]
+ *   (binary: ceil(K/32)), scales[n][K/group] (IEEE fp16 bits), rows
+ *   contiguous.
  * TQ_LAYOUT_ROW64: the compute layout consumed by tq_gemv / tq_moe_gemv /
  *   tq_gemm.  K is cut into slices of 640 trits (32 words = 8 quads of 4
- *   words = 5 scale groups; 640 is the least common multiple of 20 and 128),
- *   rows into blocks of 64.  Word 32s + 4q + j of row 64b + r is stored at
- *   words[(((s*nb + b)*8 + q)*64 + r)*4 + j], nb = ceil(n/64), and the scale
- *   of group 5s + g of that row at scales[((s*nb + b)*5 + g)*64 + r].  One
- *   16-byte load per lane reads a quad of its row, a 64-lane wavefront reads
- *   1 KiB contiguously, and the 8 KiB of one slice of one row block are
- *   contiguous.
+ *   words; 640 is the least common multiple of 20 and 128), rows into
+ *   blocks of 64.  Word 32s + 4q + j of row 64b + r is stored at
+ *   words[(((s*nb + b)*8 + q)*64 + r)*4 + j], nb = ceil(n/64).  A slice has
+ *   G = 640/group scale groups (5 at group 128, 10 at group 64); the scale
+ *   of group Gs + g of that row is at scales[((s*nb + b)*G + g)*64 + r].
+ *   One 16-byte load per lane reads a quad of its row, a 64-lane wavefront
+ *   reads 1 KiB contiguously, and the 8 KiB of one slice of one row block
+ *   are contiguous.
+ *   Binary words (levels 2): a slice is 640 weights = 20 words = 5 quads;
+ *   word 20s + 4q + j of row 64b + r is at words[(((s*nb + b)*5 + q)*64 + r)*4
+ *   + j], bits in ROWMAJOR order (no reordering); scales as above.
  *   Each word is a base-3 number of 20 trits as in ROWMAJOR, but within
  *   each unit of 160 trits (quads 2u and 2u + 1 of a slice: unit words
  *   wl = 0..7) the trits are grouped into 40 chunks of 4 and reordered:
@@ -97,9 +118,10 @@ enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2, TQ_F64 = 3 };
  *   so that words 2kb and 2kb + 1 hold, in digit order, the trit runs
  *   32i + 8kb .. 32i + 8kb + 7 for i = 0..4 (a 32-trit run of the unit is
  *   spread over the four word pairs and never crosses a scale group).
- *   Rows past n, trits past K and groups past K/128 are padding (zero
+ *   Rows past n, trits past K and groups past K/group are padding (zero
  *   trits, so a word of padding only is the all-zero word 1743392200;
- *   scale 0).  tq_unpack inverts the layout exactly. */
+ *   binary padding bits are 0; scale 0).  tq_unpack inverts the layout
+ *   exactly. */
 enum { TQ_LAYOUT_ROWMAJOR = 0, TQ_LAYOUT_ROW64 = 1 };
 
 /* Flags.
@@ -115,14 +137,23 @@ enum { TQ_LAYOUT_ROWMAJOR = 0, TQ_LAYOUT_ROW64 = 1 };
  *   most 64 (token, slot) pairs and fewer than four tokens, where each
  *   slot's row is added with device atomics (and the slots' combine step is
  *   skipped).  (tq_gemm): Y += ..., deterministic (one workgroup writes
- *   each output). */
-enum { TQ_FWHT_FUSED = 1u, TQ_ACCUMULATE = 2u };
+ *   each output).
+ * TQ_MOE_ONE_LAUNCH (tq_moe_gemv, at most 64 (token, slot) pairs and an
+ *   intermediate size of at most 2560): the whole expert MLP in a single
+ *   launch.  The last workgroup of each (token, slot) pair to finish its
+ *   gate/up share runs that pair's down projection, and the last slot of a
+ *   token combines the slots in slot order (no workgroup waits for
+ *   another).  Its arrival counters reset themselves, so a workspace used
+ *   with this flag must be zero-filled before its first use (each call
+ *   leaves the counters zero).  TQ_EUNSUPPORTED for larger requests. */
+enum { TQ_FWHT_FUSED = 1u, TQ_ACCUMULATE = 2u, TQ_MOE_ONE_LAUNCH = 4u };
 
 /* Operation ids for tq_workspace_bytes. */
 enum { TQ_OP_GEMV = 0, TQ_OP_MOE = 1, TQ_OP_GEMM = 2 };
 
 /* Self-describing weight descriptor.  For MoE, num_experts > 1 and expert e's
- * words start at words + e * tq_layout_words(n, k, layout) (likewise scales). */
+ * words start at words + e * tq_layout_words(n, k, layout, levels) (likewise
+ * scales with tq_layout_scales(n, k, layout, group)). */
 typedef struct {
   uint32_t magic;       /* TQ_MAGIC   */
   uint32_t version;     /* TQ_VERSION */
@@ -130,49 +161,80 @@ typedef struct {
   int32_t k;            /* columns = inputs, a multiple of 128    */
   int32_t num_experts;  /* 1 for a dense layer                    */
   int32_t layout;       /* TQ_LAYOUT_*                            */
+  int32_t group;        /* weights per scale: 128 or 64           */
+  int32_t levels;       /* 3: ternary; 2: binary                  */
   const uint32_t *words;
   const uint16_t *scales;
 } tq_weights;
 
 /* ---- sizes (host only, no GPU work) ------------------------------------ */
-/* ceil(k / 20). */
+/* ceil(k / 20): words per row at 20 trits per 32-bit word (TurboQuant-MLX
+ * page, "Why 1.58 bit did not turn into gibberish", point 3). */
 size_t tq_words_per_row(int k);
-/* Algorithmic packed bytes of one n x k matrix: 4*n*ceil(k/20) + 2*n*(k/128)
- * (the canonical layout's size; ROW64 adds only padding). */
+/* Algorithmic packed bytes of one n x k matrix: 4*n*ceil(k/20) + 2*n*(k/128),
+ * the base-3 words (TurboQuant-MLX page, point 3) plus one FP16 scale per
+ * 128 weights (27B ternary page, section 2 (2)); the canonical layout's
+ * size (ROW64 adds only padding).  0 for n <= 0 or k <= 0. */
 size_t tq_packed_bytes(int n, int k);
-/* Number of uint32 words / uint16 scales a buffer of the given layout holds
- * for one n x k matrix (padding included).  0 for an invalid request. */
-size_t tq_layout_words(int n, int k, int layout);
-size_t tq_layout_scales(int n, int k, int layout);
+/* Algorithmic bytes of one n x k matrix in any format: words (levels 3:
+ * 4*n*ceil(k/20); levels 2: 4*n*ceil(k/32)) plus 2*n*(k/group).  0 for an
+ * invalid request (k not a multiple of group, group not 64 or 128, levels
+ * not 2 or 3). */
+size_t tq_format_bytes(int n, int k, int group, int levels);
+/* Number of uint32 words a buffer of the given layout holds for one n x k
+ * matrix of `levels` (padding included), and of uint16 scales for `group`.
+ * 0 for an invalid request. */
+size_t tq_layout_words(int n, int k, int layout, int levels);
+size_t tq_layout_scales(int n, int k, int layout, int group);
 
 /* ---- offline conversion ------------------------------------------------ */
 /* Rotate and ternarise W (TurboQuant-MLX introduction; 27B ternary page,
  * sections 2 (1) and 2 (2)).  w: [n][k] row-major, w_dtype TQ_F64 or TQ_F32.
- * For every row and group of 128: w' = H_128 applied along K, computed in
- * FP64; gamma = mean |w'|; t = sign(w') where |w'| > gamma/2, else 0 (an
- * exact tie gives 0); s = fp16(gamma) rounded to nearest-even once from FP64
- * (gamma == 0 gives t = 0, s = 0).  Outputs trits int8 [n][k] and scales
- * uint16 (fp16 bits) [n][k/128], both row-major.  k % 128 == 0. */
-int tq_quantize(const void *w, int w_dtype, int n, int k, int8_t *trits,
-                uint16_t *scales, void *stream);
+ * w' = H_128 applied along K on every block of 128, computed in FP64; then
+ * for every row and group of `group` (128 or 64) weights: gamma = mean |w'|,
+ * s = fp16(gamma) rounded to nearest-even once from FP64, and
+ *   levels 3: t = sign(w') where |w'| > gamma/2, else 0 (an exact tie gives
+ *             0; gamma == 0 gives t = 0, s = 0);
+ *   levels 2: t = +1 where w' >= 0, else -1 (the binary variant).
+ * Outputs t int8 [n][k] and scales uint16 (fp16 bits) [n][k/group], both
+ * row-major.  k % 128 == 0. */
+int tq_quantize(const void *w, int w_dtype, int n, int k, int group, int levels,
+                int8_t *trits, uint16_t *scales, void *stream);
 
-/* Base-3 pack (TurboQuant-MLX, "Why 1.58 bit...", point 3): trits int8
- * [n][k] row-major, values in {-1,0,1} (a precondition: other values give
- * unspecified words), into `words` of tq_layout_words(n,k,layout) uint32 in
- * the requested layout, pads included.  Any k >= 1 for ROWMAJOR; ROW64
- * needs k % 128 == 0. */
-int tq_pack(const int8_t *trits, int n, int k, int layout, uint32_t *words,
-            void *stream);
+/* Pack (TurboQuant-MLX, "Why 1.58 bit...", point 3): t int8 [n][k]
+ * row-major into `words` of tq_layout_words(n,k,layout,levels) uint32 in the
+ * requested layout, pads included.
+ *   levels 3: base-3 words of 20 trits, values in {-1,0,1}; a value outside
+ *     is a caller error and is packed as 0, so every word stays a valid
+ *     base-3 number below 3^20;
+ *   levels 2: 32 sign bits per word, values in {-1,+1}; any other value is
+ *     a caller error and is packed as +1 (the sign rule's side for 0).
+ * tq_pack_checked also counts such values.  Any k >= 1 for ROWMAJOR; ROW64
+ * needs k % 128 == 0.  Alignment: words 4 bytes. */
+int tq_pack(const int8_t *trits, int n, int k, int layout, int levels,
+            uint32_t *words, void *stream);
 
-/* Re-lay a row-major scale array [n][k/128] into `layout` (ROWMAJOR copies,
- * ROW64 interleaves as described above and zero-fills padded rows). */
-int tq_pack_scales(const uint16_t *scales, int n, int k, int layout,
+/* tq_pack plus a count of the input values outside the format's set: `bad`
+ * is one device int32 that the call overwrites (two launches: it is
+ * cleared, then every bad value adds one).  For offline conversion that must
+ * not pack garbage silently (27B ternary page, section 2 (3): a runtime
+ * that loads a format it does not understand outputs garbage without a
+ * word).  Read *bad after the stream reaches this work. */
+int tq_pack_checked(const int8_t *trits, int n, int k, int layout, int levels,
+                    uint32_t *words, int32_t *bad, void *stream);
+
+/* Re-lay a row-major scale array [n][k/group] into `layout` (ROWMAJOR
+ * copies, ROW64 interleaves as described above and zero-fills padded rows
+ * and groups). */
+int tq_pack_scales(const uint16_t *scales, int n, int k, int layout, int group,
                    uint16_t *scales_out, void *stream);
 
-/* Inverse of tq_pack (test export): words in `layout` -> trits int8 [n][k]
- * row-major, t = digit - 1. */
-int tq_unpack(const uint32_t *words, int n, int k, int layout, int8_t *trits,
-              void *stream);
+/* Inverse of tq_pack (test export; the base-3 digits of TurboQuant-MLX,
+ * point 3, or the sign bits of the binary variant, read back): words in
+ * `layout` -> t int8 [n][k] row-major (t = digit - 1, or 2 bit - 1).
+ * Alignment: words 4 bytes. */
+int tq_unpack(const uint32_t *words, int n, int k, int layout, int levels,
+              int8_t *trits, void *stream);
 
 /* ---- online path ------------------------------------------------------- */
 /* x_rot[m][k] = H_128 x[m][k] on every aligned block of 128 (27B ternary
@@ -181,7 +243,10 @@ int tq_unpack(const uint32_t *words, int n, int k, int layout, int8_t *trits,
 int tq_fwht(const void *x, int x_dtype, int m, int k, float *x_rot,
             void *stream);
 
-/* Decode GEMV, 1 <= m <= 8 activation rows:
+/* Decode GEMV, 1 <= m <= 8 activation rows (the decode-time product of the
+ * 27B ternary page, sections 2 (1)-(3): the packed weights, their FP16
+ * group scales and the matching transform of the activation; adds and
+ * subtracts only, "Ternary-Bonsai2-27B vs ..." page, section 1.1):
  * y[m][n] = sum_k fp32(s[n][k/128]) t[n][k] x'[m][k], x' = H_128 x if flags
  * has TQ_FWHT_FUSED else x (with TQ_ACCUMULATE: y += ...).  w: ROW64
  * layout, num_experts == 1.  x: [m][k] of x_dtype (F32/BF16/F16); y: FP32
@@ -198,7 +263,8 @@ int tq_gemv(const tq_weights *w, const void *x, int x_dtype, int m, float *y,
 /* Full-precision router (TurboQuant-MLX, point 1): per token, p = softmax of
  * logits[t][0..e) in FP32, the topk largest p (ties to the lower id), and
  * weights p / (sum of the chosen p).  ids int32 [t][topk], weights FP32
- * [t][topk], in decreasing p.  1 <= topk <= 32, e <= 1024. */
+ * [t][topk], in decreasing p.  1 <= topk <= 32, e <= 1024.  Alignment:
+ * logits, ids and weights 4 bytes. */
 int tq_moe_route(const float *logits, int t, int e, int topk, int32_t *ids,
                  float *weights, void *stream);
 
@@ -217,17 +283,32 @@ int tq_moe_route(const float *logits, int t, int e, int topk, int32_t *ids,
  * to finish adds the slots in slot order, from four tokens on one
  * workgroup per token and row block adds them); otherwise the pairs are
  * grouped by expert and an expert's tokens go 8 at a time (four launches;
- * E <= 1024, else TQ_EUNSUPPORTED).  y is deterministic either way.  Only the experts that receive tokens are read.  Ids outside
- * [0, E) are an error detected on the device: such slots contribute
- * nothing.  Needs tq_workspace_bytes(TQ_OP_MOE, w_gate_up, t, topk) bytes of
- * workspace, which calls that overlap in time must not share. */
+ * E <= 1024, else TQ_EUNSUPPORTED).  y is deterministic either way.  Only
+ * the experts that receive tokens are read.  Ids outside [0, E) are a caller
+ * error detected on the device: such slots contribute nothing, and the
+ * number of them is left in the workspace for tq_moe_bad_ids.  Needs
+ * tq_workspace_bytes(TQ_OP_MOE, w_gate_up, t, topk) bytes of workspace,
+ * which calls that overlap in time must not share. */
 int tq_moe_gemv(const tq_weights *w_gate_up, const tq_weights *w_down,
                 const void *x, int x_dtype, int t, int topk,
                 const int32_t *expert_ids, const float *route_w, float *y,
                 unsigned flags, void *workspace, size_t ws_bytes, void *stream);
 
-/* Prefill GEMM: Y[m][n] = sum_k fp32(s[n][k/128]) t[n][k] x'[m][k] for any
+/* Number of (token, slot) entries whose expert id was outside [0, E) in the
+ * last tq_moe_gemv that used this workspace (the router's choice is taken
+ * as input; a bad id must not vanish silently, 27B ternary page, section
+ * 2 (3)).  Copies the count to *count (host memory) and WAITS for `stream`
+ * (the one call in the library that synchronises).  Returns TQ_EDATA if the
+ * count is nonzero, TQ_OK if it is zero. */
+int tq_moe_bad_ids(const void *workspace, size_t ws_bytes, int32_t *count,
+                   void *stream);
+
+/* Prefill GEMM (the same product as tq_gemv for a whole prompt at once;
+ * kernels that work on the packed format directly, 27B ternary page,
+ * section 2 (3)): Y[m][n] = sum_k fp32(s[n][k/128]) t[n][k] x'[m][k] for any
  * m >= 1 on the matrix cores.  x' (FP32 after the optional transform) is
+ * scaled by a power of two per row (max |x'| 2^e in [2^13, 2^14), so any
+ * activation scale stays in fp16's normal range; undone on the output),
  * split into an fp16 high part and an fp16 remainder, and each is
  * multiplied by the exact fp16 weights s*t decoded from the packed words
  * (into registers), accumulating in FP32.  w: ROW64, num_experts == 1.  Needs
@@ -238,6 +319,14 @@ int tq_gemm(const tq_weights *w, const void *x, int x_dtype, int m, float *y,
 /* Workspace bytes an operation needs (0 when it needs none; SIZE_MAX for an
  * invalid request).  m_or_t: activation rows (GEMV/GEMM) or tokens (MoE). */
 size_t tq_workspace_bytes(int op, const tq_weights *w, int m_or_t, int topk);
+
+/* Memory-read reference (a measurement aid, not a step of the product):
+ * reads `bytes` bytes of `src` once with the decode GEMV's load form
+ * (16-byte non-temporal loads, one launch) and writes at most one word to
+ * *sink (device memory).  Timing it on the same bytes as one GEMV launch
+ * gives the read ceiling that launch size allows.  src 16-byte aligned,
+ * bytes a multiple of 16. */
+int tq_read_bytes(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
 /* Static message for a tq_status value. */
 const char *tq_strerror(int status);

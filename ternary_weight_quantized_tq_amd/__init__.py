@@ -18,14 +18,16 @@ LIB_PATH = os.path.join(_HERE, "libtq.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tq.h")
 
 TQ_MAGIC = 0x30325154
-TQ_VERSION = 1
+TQ_VERSION = 2
 TQ_TRITS_PER_WORD = 20
 TQ_GROUP = 128
-TQ_OK, TQ_EINVAL, TQ_ESHAPE, TQ_EFORMAT, TQ_ENOSPACE, TQ_EHIP, TQ_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+TQ_BITS_PER_WORD = 32
+TQ_OK, TQ_EINVAL, TQ_ESHAPE, TQ_EFORMAT, TQ_ENOSPACE, TQ_EHIP, TQ_EUNSUPPORTED, TQ_EDATA = 0, -1, -2, -3, -4, -5, -6, -7
 TQ_F32, TQ_BF16, TQ_F16, TQ_F64 = 0, 1, 2, 3
 TQ_LAYOUT_ROWMAJOR, TQ_LAYOUT_ROW64 = 0, 1
 TQ_FWHT_FUSED = 1
 TQ_ACCUMULATE = 2
+TQ_MOE_ONE_LAUNCH = 4
 TQ_OP_GEMV, TQ_OP_MOE, TQ_OP_GEMM = 0, 1, 2
 SIZE_MAX = 2 ** 64 - 1
 
@@ -39,6 +41,7 @@ class TQError(RuntimeError):
 class tq_weights(ctypes.Structure):
     _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32), ("n", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("num_experts", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("levels", ctypes.c_int32),
                 ("words", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
@@ -49,18 +52,22 @@ _W = ctypes.POINTER(tq_weights)
 _SIGNATURES = {
     "tq_words_per_row": (_SZ, [_I]),
     "tq_packed_bytes": (_SZ, [_I, _I]),
-    "tq_layout_words": (_SZ, [_I, _I, _I]),
-    "tq_layout_scales": (_SZ, [_I, _I, _I]),
-    "tq_quantize": (_I, [_P, _I, _I, _I, _P, _P, _P]),
-    "tq_pack": (_I, [_P, _I, _I, _I, _P, _P]),
-    "tq_pack_scales": (_I, [_P, _I, _I, _I, _P, _P]),
-    "tq_unpack": (_I, [_P, _I, _I, _I, _P, _P]),
+    "tq_format_bytes": (_SZ, [_I, _I, _I, _I]),
+    "tq_layout_words": (_SZ, [_I, _I, _I, _I]),
+    "tq_layout_scales": (_SZ, [_I, _I, _I, _I]),
+    "tq_quantize": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "tq_pack": (_I, [_P, _I, _I, _I, _I, _P, _P]),
+    "tq_pack_checked": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
+    "tq_moe_bad_ids": (_I, [_P, _SZ, ctypes.POINTER(ctypes.c_int32), _P]),
+    "tq_pack_scales": (_I, [_P, _I, _I, _I, _I, _P, _P]),
+    "tq_unpack": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "tq_fwht": (_I, [_P, _I, _I, _I, _P, _P]),
     "tq_gemv": (_I, [_W, _P, _I, _I, _P, ctypes.c_uint, _P, _SZ, _P]),
     "tq_moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "tq_moe_gemv": (_I, [_W, _W, _P, _I, _I, _I, _P, _P, _P, ctypes.c_uint, _P, _SZ, _P]),
     "tq_gemm": (_I, [_W, _P, _I, _I, _P, ctypes.c_uint, _P, _SZ, _P]),
     "tq_workspace_bytes": (_SZ, [_I, _W, _I, _I]),
+    "tq_read_bytes": (_I, [_P, _SZ, _P, _P]),
     "tq_strerror": (ctypes.c_char_p, [_I]),
     "tq_last_error": (ctypes.c_char_p, []),
 }
@@ -140,12 +147,16 @@ def tq_packed_bytes(n: int, k: int) -> int:
     return lib().tq_packed_bytes(n, k)
 
 
-def tq_layout_words(n: int, k: int, layout: int) -> int:
-    return lib().tq_layout_words(n, k, layout)
+def tq_format_bytes(n: int, k: int, group: int, levels: int) -> int:
+    return lib().tq_format_bytes(n, k, group, levels)
 
 
-def tq_layout_scales(n: int, k: int, layout: int) -> int:
-    return lib().tq_layout_scales(n, k, layout)
+def tq_layout_words(n: int, k: int, layout: int, levels: int) -> int:
+    return lib().tq_layout_words(n, k, layout, levels)
+
+
+def tq_layout_scales(n: int, k: int, layout: int, group: int) -> int:
+    return lib().tq_layout_scales(n, k, layout, group)
 
 
 def tq_strerror(status: int) -> str:
@@ -157,22 +168,40 @@ def tq_last_error() -> str:
 
 
 # --------------------------------------------------- entry points ---
-def tq_quantize(w, n, k, trits, scales, stream=None):
-    return _check("tq_quantize", lib().tq_quantize(_ptr(w), dtype_code(w), n, k, _ptr(trits), _ptr(scales),
-                                                   _stream(stream)))
+def tq_quantize(w, n, k, group, levels, trits, scales, stream=None):
+    return _check("tq_quantize", lib().tq_quantize(_ptr(w), dtype_code(w), n, k, group, levels, _ptr(trits),
+                                                   _ptr(scales), _stream(stream)))
 
 
-def tq_pack(trits, n, k, layout, words, stream=None):
-    return _check("tq_pack", lib().tq_pack(_ptr(trits), n, k, layout, _ptr(words), _stream(stream)))
+def tq_pack(trits, n, k, layout, levels, words, stream=None):
+    return _check("tq_pack", lib().tq_pack(_ptr(trits), n, k, layout, levels, _ptr(words), _stream(stream)))
 
 
-def tq_pack_scales(scales, n, k, layout, scales_out, stream=None):
-    return _check("tq_pack_scales", lib().tq_pack_scales(_ptr(scales), n, k, layout, _ptr(scales_out),
+def tq_pack_checked(trits, n, k, layout, levels, words, bad, stream=None):
+    """tq_pack plus the count of input values outside the format's set
+    written to `bad` (a one-element int32 device tensor)."""
+    return _check("tq_pack_checked", lib().tq_pack_checked(_ptr(trits), n, k, layout, levels, _ptr(words),
+                                                           _ptr(bad), _stream(stream)))
+
+
+def tq_moe_bad_ids(workspace, ws_bytes, stream=None) -> int:
+    """Number of expert ids outside [0, E) seen by the last tq_moe_gemv on
+    this workspace (waits for the stream).  Returns the count; TQ_EDATA is
+    not raised here, it is what a nonzero count means."""
+    c = ctypes.c_int32(0)
+    st = lib().tq_moe_bad_ids(_ptr(workspace), ws_bytes, ctypes.byref(c), _stream(stream))
+    if st not in (TQ_OK, TQ_EDATA):
+        _check("tq_moe_bad_ids", st)
+    return int(c.value)
+
+
+def tq_pack_scales(scales, n, k, layout, group, scales_out, stream=None):
+    return _check("tq_pack_scales", lib().tq_pack_scales(_ptr(scales), n, k, layout, group, _ptr(scales_out),
                                                          _stream(stream)))
 
 
-def tq_unpack(words, n, k, layout, trits, stream=None):
-    return _check("tq_unpack", lib().tq_unpack(_ptr(words), n, k, layout, _ptr(trits), _stream(stream)))
+def tq_unpack(words, n, k, layout, levels, trits, stream=None):
+    return _check("tq_unpack", lib().tq_unpack(_ptr(words), n, k, layout, levels, _ptr(trits), _stream(stream)))
 
 
 def tq_fwht(x, m, k, x_rot, stream=None):
@@ -201,6 +230,11 @@ def tq_gemm(w, x, m, y, flags=TQ_FWHT_FUSED, workspace=None, ws_bytes=0, stream=
                                            _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def tq_read_bytes(src, nbytes, sink, stream=None):
+    """Measurement aid: one plain read pass over nbytes of src."""
+    return _check("tq_read_bytes", lib().tq_read_bytes(_ptr(src), nbytes, _ptr(sink), _stream(stream)))
+
+
 def tq_workspace_bytes(op, w, m_or_t, topk=0) -> int:
     return lib().tq_workspace_bytes(op, ctypes.byref(_desc(w)), m_or_t, topk)
 
@@ -215,24 +249,32 @@ class Weights:
     k: int
     layout: int = TQ_LAYOUT_ROW64
     num_experts: int = 1
+    group: int = TQ_GROUP
+    levels: int = 3
     magic: int = TQ_MAGIC
     version: int = TQ_VERSION
 
     def desc(self) -> tq_weights:
-        return tq_weights(self.magic, self.version, self.n, self.k, self.num_experts, self.layout,
-                          _ptr(self.words), _ptr(self.scales))
+        return tq_weights(self.magic, self.version, self.n, self.k, self.num_experts, self.layout, self.group,
+                          self.levels, _ptr(self.words), _ptr(self.scales))
+
+    def clone(self) -> "Weights":
+        return Weights(self.words.clone(), self.scales.clone(), self.n, self.k, self.layout, self.num_experts,
+                       self.group, self.levels)
 
 
 def _desc(w) -> tq_weights:
     return w if isinstance(w, tq_weights) else w.desc()
 
 
-def empty_weights(n, k, layout=TQ_LAYOUT_ROW64, num_experts=1, device="cuda") -> Weights:
+def empty_weights(n, k, layout=TQ_LAYOUT_ROW64, num_experts=1, device="cuda", group=TQ_GROUP,
+                  levels=3) -> Weights:
     import torch
-    nw = tq_layout_words(n, k, layout)
-    ns = tq_layout_scales(n, k, layout)
+    nw = tq_layout_words(n, k, layout, levels)
+    ns = tq_layout_scales(n, k, layout, group)
     return Weights(torch.empty(num_experts * nw, dtype=torch.int32, device=device),
-                   torch.empty(num_experts * ns, dtype=torch.int16, device=device), n, k, layout, num_experts)
+                   torch.empty(num_experts * ns, dtype=torch.int16, device=device), n, k, layout, num_experts,
+                   group, levels)
 
 
 def workspace(op, w, m_or_t, topk=0, device="cuda"):

@@ -9,50 +9,88 @@ using namespace tq;
 namespace {
 
 // ------------------------------------------------------------ quantize ---
-// One wavefront per (row, group of 128): load the group in FP64, transform
-// it (27B ternary page, section 2 (1)), then absmean-ternarise with an fp16
-// scale (section 2 (2); the TurboQuant-MLX page's {-c, 0, +c}).
+// One wavefront per (row, block of 128): load the block in FP64, transform
+// it (27B ternary page, section 2 (1)), then per scale group (the whole
+// block at group 128; lanes 0..31 and 32..63 at group 64, since lane l holds
+// elements 2l, 2l + 1) take gamma = mean |w'| with an fp16 scale (section
+// 2 (2)) and ternarise with the absmean threshold (the TurboQuant-MLX
+// page's {-c, 0, +c}) or take signs (levels 2, its pure 1-bit variant).
 template <typename T>
-__global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ w, int n, int k,
+__global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ w, int n, int k, int group, int levels,
                                                        int8_t* __restrict__ trits,
                                                        uint16_t* __restrict__ scales) {
-  const int groups = k / TQ_GROUP;
+  const int blocks = k / 128, groups = k / group;
   const long long job = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (job >= static_cast<long long>(n) * groups) return;
+  if (job >= static_cast<long long>(n) * blocks) return;
   const int lane = threadIdx.x & 63;
-  const int row = static_cast<int>(job / groups);
-  const int g = static_cast<int>(job % groups);
-  const size_t base = static_cast<size_t>(row) * k + static_cast<size_t>(g) * TQ_GROUP + 2 * lane;
+  const int row = static_cast<int>(job / blocks);
+  const int blk = static_cast<int>(job % blocks);
+  const size_t base = static_cast<size_t>(row) * k + static_cast<size_t>(blk) * 128 + 2 * lane;
   double v0 = static_cast<double>(w[base]);
   double v1 = static_cast<double>(w[base + 1]);
   wave_fwht128<double>(v0, v1, lane, 0.08838834764831845 /* 1/sqrt(128) */);
   double s = fabs(v0) + fabs(v1);
+  // Sum over the lanes of one group: all 64 lanes at group 128, 32 at 64.
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  const double gamma = s / 128.0;
-  const double thr = gamma * 0.5;
-  const int8_t t0 = v0 > thr ? 1 : (v0 < -thr ? -1 : 0);
-  const int8_t t1 = v1 > thr ? 1 : (v1 < -thr ? -1 : 0);
+  for (int off = 16; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  const double s_other_half = __shfl_xor(s, 32);
+  if (group == 128) s += s_other_half;
+  const double gamma = s / static_cast<double>(group);
+  int8_t t0, t1;
+  if (levels == 2) {
+    t0 = v0 >= 0.0 ? 1 : -1;
+    t1 = v1 >= 0.0 ? 1 : -1;
+  } else {
+    const double thr = gamma * 0.5;
+    t0 = v0 > thr ? 1 : (v0 < -thr ? -1 : 0);
+    t1 = v1 > thr ? 1 : (v1 < -thr ? -1 : 0);
+  }
   const uint16_t pair = static_cast<uint16_t>(static_cast<uint8_t>(t0)) |
                         static_cast<uint16_t>(static_cast<uint16_t>(static_cast<uint8_t>(t1)) << 8);
   reinterpret_cast<uint16_t*>(trits + base)[0] = pair;
-  if (lane == 0) scales[static_cast<size_t>(row) * groups + g] = f64_to_f16_rne(gamma);
+  const int g = group == 128 ? blk : 2 * blk + (lane >> 5);
+  if ((lane & (group == 128 ? 63 : 31)) == 0) scales[static_cast<size_t>(row) * groups + g] = f64_to_f16_rne(gamma);
 }
 
 // ---------------------------------------------------------------- pack ---
 // word = sum_{i<20} (t_{20w+i} + 1) 3^i, evaluated by Horner from the top
 // digit (TurboQuant-MLX, "Why 1.58 bit...", point 3).  One thread per word
-// of the destination layout, padding included.
+// of the destination layout, padding included.  A value outside {-1, 0, 1}
+// (a caller error, counted by tq_pack_checked) is packed as 0, so every
+// word stays below 3^20.
+__device__ __forceinline__ uint32_t digit_of(int8_t t) {
+  return (t >= -1 && t <= 1) ? static_cast<uint32_t>(t + 1) : 1u;
+}
+
 __device__ __forceinline__ uint32_t pack_word(const int8_t* __restrict__ row, int k, int w) {
   uint32_t acc = 0;
   const int k0 = w * TQ_TRITS_PER_WORD;
 #pragma unroll
   for (int i = TQ_TRITS_PER_WORD - 1; i >= 0; --i) {
     const int kk = k0 + i;
-    const uint32_t d = kk < k ? static_cast<uint32_t>(row[kk] + 1) : 1u;
+    const uint32_t d = kk < k ? digit_of(row[kk]) : 1u;
     acc = acc * 3u + d;
   }
   return acc;
+}
+
+// tq_pack_checked: the number of input values outside {-1, 0, 1}.  One
+// thread per 16 trits (the last thread of a ragged end reads fewer); one
+// atomic per wavefront that saw any.
+__global__ __launch_bounds__(64) void clear_count_kernel(int32_t* __restrict__ bad) { *bad = 0; }
+
+__global__ __launch_bounds__(256) void count_bad_trits_kernel(const int8_t* __restrict__ t, size_t total, int levels,
+                                                              int32_t* __restrict__ bad) {
+  const size_t i0 = (static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 16;
+  int c = 0;
+  for (int i = 0; i < 16; ++i)
+    if (i0 + i < total) {
+      const int8_t v = t[i0 + i];
+      c += (levels == 2 ? (v != -1 && v != 1) : (v < -1 || v > 1)) ? 1 : 0;
+    }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+  if ((threadIdx.x & 63) == 0 && c) atomicAdd(bad, c);
 }
 
 __global__ __launch_bounds__(256) void pack_rowmajor_kernel(const int8_t* __restrict__ trits, int n,
@@ -77,7 +115,7 @@ __device__ __forceinline__ uint32_t pack_word_row64(const int8_t* __restrict__ r
 #pragma unroll
     for (int d = 3; d >= 0; --d) {
       const int kk = kc + d;
-      acc = acc * 3u + (kk < k ? static_cast<uint32_t>(row[kk] + 1) : 1u);
+      acc = acc * 3u + (kk < k ? digit_of(row[kk]) : 1u);
     }
   }
   return acc;
@@ -98,18 +136,59 @@ __global__ __launch_bounds__(256) void pack_row64_kernel(const int8_t* __restric
   words[idx] = row < n ? pack_word_row64(trits + static_cast<size_t>(row) * k, k, s, qi, j) : kZeroWord;
 }
 
-__global__ __launch_bounds__(256) void scales_row64_kernel(const uint16_t* __restrict__ s, int n, int groups,
-                                                           int nsl, int nb, uint16_t* __restrict__ out) {
+// Binary words (levels 2): bit i of word w is weight 32w + i, 1 for +1; any
+// value other than -1 packs as 1 (the sign rule's side for 0); bits past k
+// are 0.
+__device__ __forceinline__ uint32_t pack_bits(const int8_t* __restrict__ row, int k, int k0) {
+  uint32_t acc = 0;
+#pragma unroll
+  for (int i = 0; i < TQ_BITS_PER_WORD; ++i) {
+    const int kk = k0 + i;
+    if (kk < k && row[kk] != -1) acc |= 1u << i;
+  }
+  return acc;
+}
+
+__global__ __launch_bounds__(256) void pack_bin_rowmajor_kernel(const int8_t* __restrict__ trits, int n, int k,
+                                                                int wpr, uint32_t* __restrict__ words) {
   const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= static_cast<size_t>(nsl) * nb * kSliceGroups * 64) return;
+  if (idx >= static_cast<size_t>(n) * wpr) return;
+  const int row = static_cast<int>(idx / wpr);
+  const int w = static_cast<int>(idx % wpr);
+  words[idx] = pack_bits(trits + static_cast<size_t>(row) * k, k, w * TQ_BITS_PER_WORD);
+}
+
+// Binary ROW64: 20 words (5 quads) per slice, one thread per destination
+// word, padding included (0).
+__global__ __launch_bounds__(256) void pack_bin_row64_kernel(const int8_t* __restrict__ trits, int n, int k, int nsl,
+                                                             int nb, uint32_t* __restrict__ words) {
+  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const size_t total = static_cast<size_t>(nsl) * nb * kSliceQuadsBin * 256;
+  if (idx >= total) return;
+  const int j = static_cast<int>(idx & 3);
+  const int r = static_cast<int>((idx >> 2) & 63);
+  const size_t rest = idx >> 8;
+  const int qi = static_cast<int>(rest % kSliceQuadsBin);
+  const size_t sb = rest / kSliceQuadsBin;
+  const int b = static_cast<int>(sb % nb);
+  const int s = static_cast<int>(sb / nb);
+  const int row = b * 64 + r;
+  const int w = s * kSliceWordsBin + 4 * qi + j;
+  words[idx] = row < n ? pack_bits(trits + static_cast<size_t>(row) * k, k, w * TQ_BITS_PER_WORD) : 0u;
+}
+
+__global__ __launch_bounds__(256) void scales_row64_kernel(const uint16_t* __restrict__ s, int n, int groups,
+                                                           int nsl, int nb, int G, uint16_t* __restrict__ out) {
+  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<size_t>(nsl) * nb * G * 64) return;
   const int r = static_cast<int>(idx & 63);
   const size_t rest = idx >> 6;
-  const int gi = static_cast<int>(rest % kSliceGroups);
-  const size_t sb = rest / kSliceGroups;
+  const int gi = static_cast<int>(rest % G);
+  const size_t sb = rest / G;
   const int b = static_cast<int>(sb % nb);
   const int sl = static_cast<int>(sb / nb);
   const int row = b * 64 + r;
-  const int g = sl * kSliceGroups + gi;
+  const int g = sl * G + gi;
   out[idx] = (row < n && g < groups) ? s[static_cast<size_t>(row) * groups + g] : static_cast<uint16_t>(0);
 }
 
@@ -117,6 +196,20 @@ __global__ __launch_bounds__(256) void scales_row64_kernel(const uint16_t* __res
 // t = ((word / 3^i) mod 3) - 1 for digit i, peeled by repeated division.
 // One thread per word: wpr words per row (ROWMAJOR), or the nsl * 32 words
 // of a ROW64 row, each digit written to the column its chunk maps to.
+__global__ __launch_bounds__(256) void unpack_bin_kernel(const uint32_t* __restrict__ words, int n, int k,
+                                                         int layout, int wpr, int nb, int8_t* __restrict__ trits) {
+  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<size_t>(n) * wpr) return;
+  const int row = static_cast<int>(idx / wpr);
+  const int w = static_cast<int>(idx % wpr);
+  const uint32_t v = layout == TQ_LAYOUT_ROW64 ? words[row64_word_index_bin(row, w, nb)] : words[idx];
+  int8_t* out = trits + static_cast<size_t>(row) * k;
+  for (int i = 0; i < TQ_BITS_PER_WORD; ++i) {
+    const int kk = w * TQ_BITS_PER_WORD + i;
+    if (kk < k) out[kk] = static_cast<int8_t>(2 * static_cast<int>((v >> i) & 1u) - 1);
+  }
+}
+
 __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict__ words, int n, int k,
                                                      int layout, int wpr, int nb,
                                                      int8_t* __restrict__ trits) {
@@ -166,17 +259,24 @@ size_t tq_packed_bytes(int n, int k) {
   return 4ull * n * words_per_row(k) + 2ull * n * (k / TQ_GROUP);
 }
 
-size_t tq_layout_words(int n, int k, int layout) {
-  if (n <= 0 || k <= 0) return 0;
-  if (layout == TQ_LAYOUT_ROWMAJOR) return static_cast<size_t>(n) * words_per_row(k);
-  if (layout == TQ_LAYOUT_ROW64) return static_cast<size_t>(slices_per_row(k)) * row_blocks(n) * kSliceQuads * 256;
+size_t tq_format_bytes(int n, int k, int group, int levels) {
+  if (n <= 0 || k <= 0 || !tq_group_ok(group) || !tq_levels_ok(levels) || k % group) return 0;
+  const size_t wpr = levels == 3 ? words_per_row(k) : words_per_row_bin(k);
+  return 4ull * n * wpr + 2ull * n * (k / group);
+}
+
+size_t tq_layout_words(int n, int k, int layout, int levels) {
+  if (n <= 0 || k <= 0 || !tq_levels_ok(levels)) return 0;
+  if (layout == TQ_LAYOUT_ROWMAJOR)
+    return static_cast<size_t>(n) * (levels == 3 ? words_per_row(k) : words_per_row_bin(k));
+  if (layout == TQ_LAYOUT_ROW64) return tq_row64_words(n, k, levels);
   return 0;
 }
 
-size_t tq_layout_scales(int n, int k, int layout) {
-  if (n <= 0 || k <= 0 || k % TQ_GROUP) return 0;
-  if (layout == TQ_LAYOUT_ROWMAJOR) return static_cast<size_t>(n) * (k / TQ_GROUP);
-  if (layout == TQ_LAYOUT_ROW64) return static_cast<size_t>(slices_per_row(k)) * row_blocks(n) * kSliceGroups * 64;
+size_t tq_layout_scales(int n, int k, int layout, int group) {
+  if (n <= 0 || k <= 0 || !tq_group_ok(group) || k % TQ_GROUP) return 0;
+  if (layout == TQ_LAYOUT_ROWMAJOR) return static_cast<size_t>(n) * (k / group);
+  if (layout == TQ_LAYOUT_ROW64) return tq_row64_scales(n, k, group);
   return 0;
 }
 
@@ -189,34 +289,53 @@ const char* tq_strerror(int status) {
     case TQ_ENOSPACE: return "workspace too small";
     case TQ_EHIP: return "HIP kernel launch failed";
     case TQ_EUNSUPPORTED: return "request not supported by the library";
+    case TQ_EDATA: return "input values out of range (trits outside {-1,0,1} or expert ids outside [0, E))";
     default: return "unknown tq status";
   }
 }
 
-int tq_quantize(const void* w, int w_dtype, int n, int k, int8_t* trits, uint16_t* scales, void* stream) {
+int tq_quantize(const void* w, int w_dtype, int n, int k, int group, int levels, int8_t* trits, uint16_t* scales,
+                void* stream) {
   if (!w || !trits || !scales) return TQ_EINVAL;
   if (w_dtype != TQ_F64 && w_dtype != TQ_F32) return TQ_EINVAL;
+  if (!tq_group_ok(group) || !tq_levels_ok(levels)) return TQ_EINVAL;
+  if (!tq_aligned(w, w_dtype == TQ_F64 ? 8 : 4) || !tq_aligned(trits, 2) || !tq_aligned(scales, 2)) return TQ_EINVAL;
   if (n <= 0 || k <= 0 || k % TQ_GROUP) return TQ_ESHAPE;
-  const size_t jobs = static_cast<size_t>(n) * (k / TQ_GROUP);
+  const size_t jobs = static_cast<size_t>(n) * (k / 128);
   if (jobs > (static_cast<size_t>(UINT_MAX) / 4)) return TQ_ESHAPE;
   const unsigned grid = static_cast<unsigned>((jobs + 3) / 4);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w_dtype == TQ_F64)
     hipLaunchKernelGGL(quantize_kernel<double>, dim3(grid), dim3(256), 0, s, static_cast<const double*>(w), n, k,
-                       trits, scales);
+                       group, levels, trits, scales);
   else
     hipLaunchKernelGGL(quantize_kernel<float>, dim3(grid), dim3(256), 0, s, static_cast<const float*>(w), n, k,
-                       trits, scales);
+                       group, levels, trits, scales);
   TQ_LAUNCH_CHECK();
   return TQ_OK;
 }
 
-int tq_pack(const int8_t* trits, int n, int k, int layout, uint32_t* words, void* stream) {
+int tq_pack(const int8_t* trits, int n, int k, int layout, int levels, uint32_t* words, void* stream) {
   if (!trits || !words) return TQ_EINVAL;
   if (layout != TQ_LAYOUT_ROWMAJOR && layout != TQ_LAYOUT_ROW64) return TQ_EINVAL;
+  if (!tq_levels_ok(levels)) return TQ_EINVAL;
+  if (!tq_aligned(words, 4)) return TQ_EINVAL;
   if (n <= 0 || k <= 0) return TQ_ESHAPE;
   if (layout == TQ_LAYOUT_ROW64 && k % TQ_GROUP) return TQ_ESHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (levels == 2) {
+    if (layout == TQ_LAYOUT_ROWMAJOR) {
+      const int wpr = words_per_row_bin(k);
+      hipLaunchKernelGGL(pack_bin_rowmajor_kernel, dim3(grid_for(static_cast<size_t>(n) * wpr)), dim3(256), 0, s,
+                         trits, n, k, wpr, words);
+    } else {
+      const int nsl = slices_per_row(k), nb = row_blocks(n);
+      hipLaunchKernelGGL(pack_bin_row64_kernel, dim3(grid_for(static_cast<size_t>(nsl) * nb * kSliceQuadsBin * 256)),
+                         dim3(256), 0, s, trits, n, k, nsl, nb, words);
+    }
+    TQ_LAUNCH_CHECK();
+    return TQ_OK;
+  }
   const int wpr = words_per_row(k);
   if (layout == TQ_LAYOUT_ROWMAJOR) {
     hipLaunchKernelGGL(pack_rowmajor_kernel, dim3(grid_for(static_cast<size_t>(n) * wpr)), dim3(256), 0, s,
@@ -230,30 +349,60 @@ int tq_pack(const int8_t* trits, int n, int k, int layout, uint32_t* words, void
   return TQ_OK;
 }
 
-int tq_pack_scales(const uint16_t* scales, int n, int k, int layout, uint16_t* scales_out, void* stream) {
-  if (!scales || !scales_out) return TQ_EINVAL;
-  if (layout != TQ_LAYOUT_ROWMAJOR && layout != TQ_LAYOUT_ROW64) return TQ_EINVAL;
-  if (n <= 0 || k <= 0 || k % TQ_GROUP) return TQ_ESHAPE;
+int tq_pack_checked(const int8_t* trits, int n, int k, int layout, int levels, uint32_t* words, int32_t* bad,
+                    void* stream) {
+  if (!bad || !tq_aligned(bad, 4)) return TQ_EINVAL;
+  const int st = tq_pack(trits, n, k, layout, levels, words, stream);
+  if (st != TQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int groups = k / TQ_GROUP;
-  if (layout == TQ_LAYOUT_ROWMAJOR) {
-    if (hipMemcpyAsync(scales_out, scales, static_cast<size_t>(n) * groups * 2, hipMemcpyDeviceToDevice, s) !=
-        hipSuccess)
-      return TQ_EHIP;
-    return TQ_OK;
-  }
-  const int nb = row_blocks(n), nsl = slices_per_row(k);
-  hipLaunchKernelGGL(scales_row64_kernel, dim3(grid_for(static_cast<size_t>(nsl) * nb * kSliceGroups * 64)),
-                     dim3(256), 0, s, scales, n, groups, nsl, nb, scales_out);
+  const size_t total = static_cast<size_t>(n) * k;
+  const size_t threads = (total + 15) / 16;
+  if (threads > static_cast<size_t>(UINT_MAX)) return TQ_ESHAPE;
+  hipLaunchKernelGGL(clear_count_kernel, dim3(1), dim3(64), 0, s, bad);
+  TQ_LAUNCH_CHECK();
+  hipLaunchKernelGGL(count_bad_trits_kernel, dim3(grid_for(threads)), dim3(256), 0, s, trits, total, levels, bad);
   TQ_LAUNCH_CHECK();
   return TQ_OK;
 }
 
-int tq_unpack(const uint32_t* words, int n, int k, int layout, int8_t* trits, void* stream) {
+int tq_pack_scales(const uint16_t* scales, int n, int k, int layout, int group, uint16_t* scales_out, void* stream) {
+  if (!scales || !scales_out) return TQ_EINVAL;
+  if (layout != TQ_LAYOUT_ROWMAJOR && layout != TQ_LAYOUT_ROW64) return TQ_EINVAL;
+  if (!tq_group_ok(group)) return TQ_EINVAL;
+  if (!tq_aligned(scales, 2) || !tq_aligned(scales_out, 2)) return TQ_EINVAL;
+  if (n <= 0 || k <= 0 || k % TQ_GROUP) return TQ_ESHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int groups = k / group, G = slice_groups(group);
+  if (layout == TQ_LAYOUT_ROWMAJOR) {
+    const hipError_t e =
+        hipMemcpyAsync(scales_out, scales, static_cast<size_t>(n) * groups * 2, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) {
+      tq_set_hip_error(e, __func__);
+      return TQ_EHIP;
+    }
+    return TQ_OK;
+  }
+  const int nb = row_blocks(n), nsl = slices_per_row(k);
+  hipLaunchKernelGGL(scales_row64_kernel, dim3(grid_for(static_cast<size_t>(nsl) * nb * G * 64)), dim3(256), 0, s,
+                     scales, n, groups, nsl, nb, G, scales_out);
+  TQ_LAUNCH_CHECK();
+  return TQ_OK;
+}
+
+int tq_unpack(const uint32_t* words, int n, int k, int layout, int levels, int8_t* trits, void* stream) {
   if (!words || !trits) return TQ_EINVAL;
   if (layout != TQ_LAYOUT_ROWMAJOR && layout != TQ_LAYOUT_ROW64) return TQ_EINVAL;
+  if (!tq_levels_ok(levels)) return TQ_EINVAL;
+  if (!tq_aligned(words, 4)) return TQ_EINVAL;
   if (n <= 0 || k <= 0) return TQ_ESHAPE;
   if (layout == TQ_LAYOUT_ROW64 && k % TQ_GROUP) return TQ_ESHAPE;
+  if (levels == 2) {
+    const int wpr = layout == TQ_LAYOUT_ROW64 ? slices_per_row(k) * kSliceWordsBin : words_per_row_bin(k);
+    hipLaunchKernelGGL(unpack_bin_kernel, dim3(grid_for(static_cast<size_t>(n) * wpr)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), words, n, k, layout, wpr, row_blocks(n), trits);
+    TQ_LAUNCH_CHECK();
+    return TQ_OK;
+  }
   const int wpr = layout == TQ_LAYOUT_ROW64 ? slices_per_row(k) * kSliceWords : words_per_row(k);
   hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(static_cast<size_t>(n) * wpr)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), words, n, k, layout, wpr, row_blocks(n), trits);

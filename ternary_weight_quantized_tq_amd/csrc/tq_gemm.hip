@@ -124,10 +124,15 @@ constexpr int kAVecs = kARows * BK / 8 / kThreads;  // uint4 per thread per unit
 
 __device__ __forceinline__ uint2 load_pair_cached(const uint32_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
+// G: scale groups per slice (5 at group 128, 10 at group 64).
+template <int G>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
+  constexpr int kGroup = kSliceTrits / G;
+  constexpr int kScaleVecs = G * 64 / 8;  // 16-byte vectors of one block's slice scales
+  constexpr int kScaleLoads = (kScaleVecs + 63) / 64;
   __shared__ __attribute__((aligned(16))) _Float16 As[2][kARows * kAStride];   // 86,016 B
   __shared__ __attribute__((aligned(16))) uint2 codes[81];
-  __shared__ __attribute__((aligned(16))) uint16_t ssc[kThreads / 64][kSliceGroups * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[kThreads / 64][G * 64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 15, kb = lane >> 4;
   int mt, nt;
   tile_of(a, mt, nt);
@@ -156,9 +161,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
     return reinterpret_cast<const uint32_t*>(a.words) +
            (row64_quad_base(s, rbc, a.nb) + (2 * uu + (kb >> 1)) * 64 + 16 * h + j) * 4 + 2 * (kb & 1);
   };
-  const int sl = lane < kSliceGroups * 8 ? lane : 0;
-  auto scale_ptr = [&](int s) {
-    return reinterpret_cast<const uint4*>(a.scales + row64_scale_base(s, rbc, a.nb) + 8 * sl);
+  // A block's slice scales are kScaleVecs 16-byte vectors: lane l loads
+  // vector l (clamped; every lane loads, since a load under a lane condition
+  // is waited for at once) and, at group 64, vector 64 + l.
+  static_assert(kScaleLoads <= 2, "at most two scale vectors per lane");
+  const int sl = lane < kScaleVecs ? lane : 0;
+  const int sl2 = lane + 64 < kScaleVecs ? lane + 64 : 0;
+  auto scale_ptr = [&](int s, int v) {
+    return reinterpret_cast<const uint4*>(a.scales + row64_scale_base(s, rbc, a.nb, G) + 8 * v);
   };
 
   // Unit 0 into buffer 0, slice 0's scales.
@@ -168,10 +178,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
   for (int i = 0; i < kAVecs; ++i) av[i] = *a_src(0, i);
 #pragma unroll
   for (int h = 0; h < 4; ++h) wq[h] = load_pair_cached(pair_ptr(0, h));
-  uint4 scq = *scale_ptr(0);
+  uint4 scq = *scale_ptr(0, sl), scq2 = scq;
+  if constexpr (kScaleLoads > 1) scq2 = *scale_ptr(0, sl2);
 #pragma unroll
   for (int i = 0; i < kAVecs; ++i) *a_dst(0, i) = av[i];
-  if (lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
+  if (lane < kScaleVecs) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
+  if constexpr (kScaleLoads > 1)
+    if (lane + 64 < kScaleVecs) *reinterpret_cast<uint4*>(&ssc[wave][8 * (lane + 64)]) = scq2;
   TQ_LDS_BARRIER();
 
   float4_t acc[4][kATiles];
@@ -199,11 +212,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int h = 0; h < 4; ++h) wq[h] = load_pair_cached(pair_ptr(min(1, a.steps - 1), h));  // unit 1
   for (int s = 0; s < nsl; ++s) {
-    _Float16 sc[4][kSliceGroups];  // this lane's rows 16 h + j, the slice's five groups
+    _Float16 sc[4][G];  // this lane's rows 16 h + j, the slice's G groups
 #pragma unroll
     for (int h = 0; h < 4; ++h)
 #pragma unroll
-      for (int g = 0; g < kSliceGroups; ++g)
+      for (int g = 0; g < G; ++g)
         sc[h][g] = __builtin_bit_cast(_Float16, ssc[wave][g * 64 + 16 * h + j]);
 #pragma unroll
     for (int uu = 0; uu < 4; ++uu) {
@@ -214,12 +227,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
       const int un = more ? u + 1 : u;  // clamped to this unit on the last one
 #pragma unroll
       for (int i = 0; i < kAVecs; ++i) av[i] = *a_src(un, i);
-      if (uu == 3) scq = *scale_ptr(min(s + 1, nsl - 1));
+      if (uu == 3) {
+        scq = *scale_ptr(min(s + 1, nsl - 1), sl);
+        if constexpr (kScaleLoads > 1) scq2 = *scale_ptr(min(s + 1, nsl - 1), sl2);
+      }
       uint2 cvn[4][10];
       const _Float16* abase = &As[buf][j * kAStride + 8 * kb];
 #pragma unroll
       for (int st = 0; st < 5; ++st) {
-        const int g = (160 * uu + 32 * st) / 128;  // compile-time: one scale group per step
+        const int g = (160 * uu + 32 * st) / kGroup;  // compile-time: one scale group per step
         half8_t af[kATiles];
 #pragma unroll
         for (int t = 0; t < kATiles; ++t)
@@ -243,7 +259,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < kAVecs; ++i) *a_dst(buf ^ 1, i) = av[i];
       }
-      if (uu == 3 && lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
+      if (uu == 3) {
+        if (lane < kScaleVecs) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
+        if constexpr (kScaleLoads > 1)
+          if (lane + 64 < kScaleVecs) *reinterpret_cast<uint4*>(&ssc[wave][8 * (lane + 64)]) = scq2;
+      }
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         wq[h] = wn[h];
@@ -256,6 +276,143 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
 
   // D rows 4 kb + v of A tile t: v = 0, 1 the parts of token 8 t + 2 kb,
   // v = 2, 3 those of token 8 t + 2 kb + 1; column j = row 16 h + j.
+  if (!active) return;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int col = rb * 64 + 16 * h + j;
+    if (col >= a.n) continue;
+#pragma unroll
+    for (int t = 0; t < kATiles; ++t)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int row = mt * BM + 8 * t + 2 * kb + q;
+        if (row < a.m) {
+          float* yp = a.y + static_cast<size_t>(row) * a.n + col;
+          const float v = ldexpf(acc[h][t][2 * q] + acc[h][t][2 * q + 1], -a.xe[row]);
+          *yp = a.accumulate ? *yp + v : v;
+        }
+      }
+  }
+}
+
+// Binary {-c, +c} variant (32 sign bits per word, bit i of slice word w is
+// weight 32 w + i).  Same tile and A staging as gemm_kernel; the B operand of
+// step s (weights 32 s .. 32 s + 31 of the slice) for lane group kb is byte
+// kb of word s of the lane's row, mapped by a 256-entry LDS table to its
+// eight fp16 signs and multiplied by the row's fp16 scale (exact).  Each
+// lane loads its five bytes of a unit directly (byte loads of the words'
+// cache lines); the next unit's bytes and activations are loaded while the
+// current unit's MFMAs run.
+template <int G>
+__global__ __launch_bounds__(kThreads) void gemm_bin_kernel(GemmArgs a) {
+  constexpr int kStepsPerGroup = kSliceTrits / G / 32;
+  constexpr int kScaleVecs = G * 64 / 8;
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][kARows * kAStride];
+  __shared__ __attribute__((aligned(16))) uint4 codes[256];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[kThreads / 64][G * 64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 15, kb = lane >> 4;
+  int mt, nt;
+  tile_of(a, mt, nt);
+  const int rb = nt * (BN / 64) + wave;
+  const bool active = rb < a.nb;
+  const int rbc = active ? rb : a.nb - 1;
+  const int nsl = slices_per_row(a.k);
+  for (int c = tid; c < 256; c += kThreads) {
+    uint32_t d[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      d[i] = (((c >> (2 * i)) & 1) ? 0x3c00u : 0xbc00u) | ((((c >> (2 * i + 1)) & 1) ? 0x3c00u : 0xbc00u) << 16);
+    codes[c] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  auto a_src = [&](int u, int i) {
+    const int idx = tid + i * kThreads;
+    const int part = idx / (BM * BK / 8), rem = idx % (BM * BK / 8);
+    const int t = rem / (BK / 8), c = rem % (BK / 8);
+    const _Float16* src = part ? a.xl : a.xh;
+    return reinterpret_cast<const u32x4_t*>(src + static_cast<size_t>(mt * BM + t) * a.kpad + u * BK + 8 * c);
+  };
+  auto a_dst = [&](int buf, int i) {
+    const int idx = tid + i * kThreads;
+    const int part = idx / (BM * BK / 8), rem = idx % (BM * BK / 8);
+    const int t = rem / (BK / 8), c = rem % (BK / 8);
+    return reinterpret_cast<u32x4_t*>(&As[buf][(2 * t + part) * kAStride + 8 * c]);
+  };
+  // Byte kb of word 5 (u % 4) + st of slice u / 4, row 64 rb + 16 h + j.
+  const uint8_t* wbytes = reinterpret_cast<const uint8_t*>(a.words);
+  auto byte_ptr = [&](int u, int h, int st) {
+    const int w = 5 * (u & 3) + st;
+    const size_t qb = row64_quad_base_bin(u >> 2, rbc, a.nb);
+    return wbytes + ((qb + (w >> 2) * 64 + 16 * h + j) * 4 + (w & 3)) * 4 + kb;
+  };
+  auto stage_scales = [&](int sl) {
+    const uint16_t* sb = a.scales + row64_scale_base(sl, rbc, a.nb, G);
+    for (int v = lane; v < kScaleVecs; v += 64)
+      *reinterpret_cast<uint4*>(&ssc[wave][8 * v]) = *reinterpret_cast<const uint4*>(sb + 8 * v);
+  };
+  auto scale16 = [&](int h, int g) {
+    const uint16_t v = reinterpret_cast<const volatile uint16_t*>(&ssc[wave][0])[g * 64 + 16 * h + j];
+    return active ? __builtin_bit_cast(_Float16, v) : static_cast<_Float16>(0.0f);
+  };
+
+  u32x4_t av[kAVecs];
+  uint32_t bcur[4][5], bnext[4][5];
+#pragma unroll
+  for (int i = 0; i < kAVecs; ++i) av[i] = *a_src(0, i);
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int st = 0; st < 5; ++st) bcur[h][st] = *byte_ptr(0, h, st);
+#pragma unroll
+  for (int i = 0; i < kAVecs; ++i) *a_dst(0, i) = av[i];
+  stage_scales(0);
+  __syncthreads();
+
+  float4_t acc[4][kATiles];
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int t = 0; t < kATiles; ++t) acc[h][t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const char* cbase = reinterpret_cast<const char*>(codes);
+  for (int u = 0; u < a.steps; ++u) {
+    const int buf = u & 1, uu = u & 3, sl = u >> 2;
+    const bool more = u + 1 < a.steps;
+    const int un = more ? u + 1 : u;
+#pragma unroll
+    for (int i = 0; i < kAVecs; ++i) av[i] = *a_src(un, i);
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int st = 0; st < 5; ++st) bnext[h][st] = *byte_ptr(un, h, st);
+    const _Float16* abase = &As[buf][j * kAStride + 8 * kb];
+#pragma unroll
+    for (int st = 0; st < 5; ++st) {
+      const int step = 5 * uu + st;  // step of the slice
+      half8_t af[kATiles];
+#pragma unroll
+      for (int t = 0; t < kATiles; ++t) af[t] = *reinterpret_cast<const half8_t*>(abase + 16 * t * kAStride + 32 * st);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const half8_t b = *reinterpret_cast<const half8_t*>(cbase + (bcur[h][st] << 4)) *
+                          scale16(h, step / kStepsPerGroup);
+#pragma unroll
+        for (int t = 0; t < kATiles; ++t)
+          acc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t], b, acc[h][t], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wavefront is done with buffer buf ^ 1 and with this slice's scales
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < kAVecs; ++i) *a_dst(buf ^ 1, i) = av[i];
+      if (uu == 3) stage_scales(min(sl + 1, nsl - 1));
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int st = 0; st < 5; ++st) bcur[h][st] = bnext[h][st];
+    __syncthreads();
+  }
+
   if (!active) return;
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
@@ -335,7 +492,15 @@ extern "C" int tq_gemm(const tq_weights* w, const void* x, int x_dtype, int m, f
   a.steps = p.steps;
   a.xcd_map = (p.mtiles % 8 == 0) ? 1 : 0;
   a.accumulate = (flags & TQ_ACCUMULATE) ? 1 : 0;
-  hipLaunchKernelGGL(gemm_kernel, dim3(p.mtiles * p.ntiles), dim3(kThreads), 0, s, a);
+  const dim3 grid(p.mtiles * p.ntiles);
+  const bool g5 = slice_groups(w->group) == 5;
+  if (w->levels == 2) {
+    if (g5) hipLaunchKernelGGL(gemm_bin_kernel<5>, grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL(gemm_bin_kernel<10>, grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (g5) hipLaunchKernelGGL(gemm_kernel<5>, grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL(gemm_kernel<10>, grid, dim3(kThreads), 0, s, a);
+  }
   TQ_LAUNCH_CHECK();
   return TQ_OK;
 }

@@ -96,10 +96,11 @@ __device__ __forceinline__ Tile make_tile(const GemvArgs& a) {
   return t;
 }
 
-__device__ __forceinline__ void load_scales(const GemvArgs& a, const Tile& t, float (&sc)[kSliceGroups]) {
-  const uint16_t* sp = a.scales + row64_scale_base(t.slice, t.rbc, a.nb) + t.lane;
+template <int G>
+__device__ __forceinline__ void load_scales(const GemvArgs& a, const Tile& t, float (&sc)[G]) {
+  const uint16_t* sp = a.scales + row64_scale_base(t.slice, t.rbc, a.nb, G) + t.lane;
 #pragma unroll
-  for (int j = 0; j < kSliceGroups; ++j) {
+  for (int j = 0; j < G; ++j) {
     const float v = f16_to_f32(sp[j * 64]);
     sc[j] = t.active ? v : 0.0f;
   }
@@ -213,8 +214,10 @@ __device__ __forceinline__ void build_table(float* lut, const float* xs, int tid
   }
 }
 
-template <int XT>
+// G: scale groups per slice (5 at group 128, 10 at group 64).
+template <int XT, int G>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a) {
+  constexpr int kChunksPerGroup = kSliceChunks / G;  // 4-trit chunks per scale group
   __shared__ float lut[kSliceChunks * kLutEntries];                   // 51840 B
   __shared__ __attribute__((aligned(16))) float xs[kSliceTrits];       // transformed activations
   const Tile t = make_tile(a);
@@ -224,21 +227,21 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a)
   // then the scales, which are needed last.
   float v0 = 0.0f, v1 = 0.0f;
   bool valid = false;
-  load_block_t<XT>(a, t, 0, min(t.wave, kSliceGroups - 1), v0, v1, valid);
+  load_block_t<XT>(a, t, 0, min(t.wave, kSliceBlocks - 1), v0, v1, valid);
   TQ_ORDER();
   const uint4* wp = a.words + row64_quad_base(t.slice, t.rbc, a.nb) + t.lane;
   uint4 wq[kSliceQuads];
 #pragma unroll
   for (int i = 0; i < kLookahead; ++i) wq[i] = load_quad(wp + min(i, t.nq_here - 1) * 64);
   TQ_ORDER();
-  float sc[kSliceGroups];
-  load_scales(a, t, sc);
+  float sc[G];
+  load_scales<G>(a, t, sc);
   TQ_ORDER();
 
   // The slice's five transform blocks (one per wavefront, wavefronts 0..4
   // when there are five or more), staged in LDS; then every wavefront
   // builds a share of the table.
-  for (int blk = t.wave; blk < kSliceGroups; blk += t.waves) {
+  for (int blk = t.wave; blk < kSliceBlocks; blk += t.waves) {
     if (blk != t.wave) load_block_t<XT>(a, t, 0, blk, v0, v1, valid);
     transform(a, v0, v1, valid, t.lane);
     *reinterpret_cast<float2*>(&xs[128 * blk + 2 * t.lane]) = make_float2(v0, v1);
@@ -248,7 +251,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a)
   TQ_LDS_BARRIER();
   if (t.wave >= a.bpg) return;  // a prologue-only wavefront (small matrices)
 
-  float acc[kSliceGroups] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  float acc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = 0.0f;
   if (t.nq_here == kSliceQuads) {
     // Software-pipelined: the table reads of word w + 2 are in flight while
     // the sums of word w are formed, so the LDS and VALU pipes overlap
@@ -266,7 +271,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a)
         word_lookups(lut, wn, w + 2, v[(w + 2) % 3]);
       }
 #pragma unroll
-      for (int h = 0; h < 5; ++h) acc[slice_chunk(w, h) / 32] += v[w % 3][h];
+      for (int h = 0; h < 5; ++h) acc[slice_chunk(w, h) / kChunksPerGroup] += v[w % 3][h];
       if ((w & 3) == 3) TQ_ORDER();
     }
   } else {
@@ -279,14 +284,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_lut_m1_kernel(GemvArgs a)
 #pragma unroll
         for (int j = 0; j < 4; ++j) word_lookups(lut, wv[j], i * 4 + j, *reinterpret_cast<float(*)[5]>(&v[j * 5]));
 #pragma unroll
-        for (int c = 0; c < 20; ++c) acc[slice_chunk(4 * i + c / 5, c % 5) / 32] += v[c];
+        for (int c = 0; c < 20; ++c) acc[slice_chunk(4 * i + c / 5, c % 5) / kChunksPerGroup] += v[c];
       }
       TQ_ORDER();
     }
   }
   float part[1] = {0.0f};
 #pragma unroll
-  for (int g = 0; g < kSliceGroups; ++g) part[0] = fmaf(sc[g], acc[g], part[0]);
+  for (int g = 0; g < G; ++g) part[0] = fmaf(sc[g], acc[g], part[0]);
   finish<1>(a, t, part);
 }
 
@@ -316,14 +321,16 @@ constexpr int kMfmaLookahead = 10;  // of 16 word pairs per lane: weights in fli
 // split over kUs wavefronts (wavefront w: block w / kUs, units
 // (w % kUs) 4 / kUs ..), which shortens each wavefront's dependent chain;
 // their sums are added in LDS in a fixed order before the epilogue.
-template <int M, int XT, int kUs>
+template <int M, int XT, int kUs, int G>
 __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs a) {
+  constexpr int kStepsPerGroup = kSliceTrits / G / 32;  // 32-trit matrix-core steps per scale group (4 or 2)
+  constexpr int kScaleVecs = G * 64 / 8;                // 16-byte vectors of one block's scales (40 or 80)
   // A rows padded by 16 bytes: the 16 lanes of a lane group read 16 rows at
   // one offset, which then fall on 16 different 4-bank groups.
   __shared__ __attribute__((aligned(16))) _Float16 xh[2 * M][kXStride];
   __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
   __shared__ __attribute__((aligned(16))) uint2 codes[kLutEntries];
-  __shared__ __attribute__((aligned(16))) uint16_t ssc[kMfmaMaxWaves][kSliceGroups * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[kMfmaMaxWaves][G * 64];
   __shared__ int xexp[M];
   __shared__ float red[kUs > 1 ? kMfmaMaxWaves : 1][16][64];  // unit-split partial sums
   Tile t = make_tile(a);
@@ -341,12 +348,12 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
   // Wavefront w transforms activation row w (and w + waves, ... when there
   // are fewer wavefronts than rows): the slice's five blocks at once, loaded
   // before the weights.
-  float xv[kSliceGroups][2];
-  bool xok[kSliceGroups];
+  float xv[kSliceBlocks][2];
+  bool xok[kSliceBlocks];
   {
     const int m = t.wave < M ? t.wave : 0;
 #pragma unroll
-    for (int r = 0; r < kSliceGroups; ++r) load_block_t<XT>(a, t, m, r, xv[r][0], xv[r][1], xok[r]);
+    for (int r = 0; r < kSliceBlocks; ++r) load_block_t<XT>(a, t, m, r, xv[r][0], xv[r][1], xok[r]);
   }
   TQ_ORDER();
   // Word pair of (row quarter h, unit u): quad 2u + kb / 2, words 2 (kb % 2)
@@ -370,11 +377,17 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
       if (i >= 4 * u0 && i < 4 * u1) wq[i] = load_pair(pair_at(i));
   }
   TQ_ORDER();
-  // The block's 5 x 64 scales (640 contiguous bytes) in one 16-byte load by
-  // lanes 0..39, staged in LDS; each lane needs 20 of them at stride 32 B.
-  // (Every lane loads: a load under a lane condition is waited for at once.)
-  const int sl = t.lane < kSliceGroups * 8 ? t.lane : 0;
-  const uint4 scq = *reinterpret_cast<const uint4*>(a.scales + row64_scale_base(t.slice, t.rbc, a.nb) + 8 * sl);
+  // The block's G x 64 scales (640 or 1280 contiguous bytes) in 16-byte
+  // loads (lanes 0..39, or all lanes and then lanes 0..15), staged in LDS;
+  // each lane needs 4 G of them.  (Every lane loads, indices clamped: a load
+  // under a lane condition is waited for at once.)
+  constexpr int kScaleLoads = (kScaleVecs + 63) / 64;
+  static_assert(kScaleLoads <= 2, "at most two scale vectors per lane");
+  const uint16_t* sbase = a.scales + row64_scale_base(t.slice, t.rbc, a.nb, G);
+  const uint4 scq = *reinterpret_cast<const uint4*>(sbase + 8 * (t.lane < kScaleVecs ? t.lane : 0));
+  uint4 scq2 = scq;
+  if constexpr (kScaleLoads > 1)
+    scq2 = *reinterpret_cast<const uint4*>(sbase + 8 * (t.lane + 64 < kScaleVecs ? t.lane + 64 : 0));
   TQ_ORDER();
 
   build_code_table(codes, t.tid, blockDim.x);
@@ -382,31 +395,47 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
   for (int m = t.wave; m < M; m += t.waves) {
     if (m != t.wave) {
 #pragma unroll
-      for (int r = 0; r < kSliceGroups; ++r) load_block_t<XT>(a, t, m, r, xv[r][0], xv[r][1], xok[r]);
+      for (int r = 0; r < kSliceBlocks; ++r) load_block_t<XT>(a, t, m, r, xv[r][0], xv[r][1], xok[r]);
     }
-    if (a.fused) wave_fwht128_batch<kSliceGroups>(xv, t.lane, kInvSqrt128);
+    if (a.fused) wave_fwht128_batch<kSliceBlocks>(xv, t.lane, kInvSqrt128);
 #pragma unroll
-    for (int r = 0; r < kSliceGroups; ++r) {
+    for (int r = 0; r < kSliceBlocks; ++r) {
       if (!xok[r]) {
         xv[r][0] = 0.0f;
         xv[r][1] = 0.0f;
       }
     }
-    const int e = split_two_fp16<kSliceGroups>(xv, t.lane, &xh[2 * m][0], &xh[2 * m + 1][0]);
+    const int e = split_two_fp16<kSliceBlocks>(xv, t.lane, &xh[2 * m][0], &xh[2 * m + 1][0]);
     if (t.lane == 0) xexp[m] = e;
   }
   // Stored after the transform, which then waits for the activations only.
-  if (t.lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[t.wave][8 * t.lane]) = scq;
+  if (t.lane < kScaleVecs) *reinterpret_cast<uint4*>(&ssc[t.wave][8 * t.lane]) = scq;
+  if constexpr (kScaleLoads > 1)
+    if (t.lane + 64 < kScaleVecs) *reinterpret_cast<uint4*>(&ssc[t.wave][8 * (t.lane + 64)]) = scq2;
   TQ_LDS_BARRIER();
 
-  float sc[4][kSliceGroups];
+  // Scales of this lane's rows.  Five groups per slice (group 128): FP32 in
+  // registers, each group's sum scaled when its last step is done.  Ten
+  // (group 64): the B operand itself is scaled, s * t being exact in fp16,
+  // so the accumulation runs through the slice without per-group closes
+  // (closing every two steps needs more registers than the kernel has).
+  constexpr bool kScaleB = G > 5;
+  float sc[4][kScaleB ? 1 : G];
+  if constexpr (!kScaleB) {
 #pragma unroll
-  for (int h = 0; h < 4; ++h)
+    for (int h = 0; h < 4; ++h)
 #pragma unroll
-    for (int g = 0; g < kSliceGroups; ++g) {
-      const float v = f16_to_f32(ssc[t.wave][g * 64 + 16 * h + j]);
-      sc[h][g] = t.active ? v : 0.0f;
-    }
+      for (int g = 0; g < G; ++g) {
+        const float v = f16_to_f32(ssc[t.wave][g * 64 + 16 * h + j]);
+        sc[h][g] = t.active ? v : 0.0f;
+      }
+  }
+  // fp16 scale of row quarter h, group g (read at its use: volatile keeps
+  // the compiler from hoisting all of them into registers).
+  auto scale16 = [&](int h, int g) {
+    const uint16_t v = reinterpret_cast<const volatile uint16_t*>(&ssc[t.wave][0])[g * 64 + 16 * h + j];
+    return t.active ? __builtin_bit_cast(_Float16, v) : static_cast<_Float16>(0.0f);
+  };
 
   // This lane's A row (part j % 2 of activation row j / 2, at its 8-trit
   // offset of each step), or the zero row past the M activation rows.
@@ -440,22 +469,35 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
       uint2 cv[10];
 #pragma unroll
       for (int c = 0; c < 10; ++c) cv[c] = *reinterpret_cast<const uint2*>(cbase + o[c]);
+      _Float16 s16 = static_cast<_Float16>(0.0f);
 #pragma unroll
       for (int s = 0; s < 5; ++s) {
-        const int step = 5 * u + s;  // scale group step / 4
+        const int step = 5 * u + s;  // scale group step / kStepsPerGroup
         const uint4 bq = make_uint4(cv[2 * s].x, cv[2 * s].y, cv[2 * s + 1].x, cv[2 * s + 1].y);
-        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s], __builtin_bit_cast(half8_t, bq), acc[h], 0, 0, 0);
-        // A scale group's four steps can span two units; with the units
-        // split over wavefronts, the last step of a wavefront's range also
-        // closes its share of the group.
-        if ((step & 3) == 3 || (kUs > 1 && s == 4 && u == u1 - 1)) {
+        if constexpr (kScaleB) {
+          if (s == 0 || step % kStepsPerGroup == 0) s16 = scale16(h, step / kStepsPerGroup);
+          const half8_t b = __builtin_bit_cast(half8_t, bq) * s16;
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s], b, acc[h], 0, 0, 0);
+        } else {
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s], __builtin_bit_cast(half8_t, bq), acc[h], 0, 0, 0);
+          // A scale group's steps can span two units; with the units split
+          // over wavefronts, the last step of a wavefront's range also
+          // closes its share of the group.
+          if (step % kStepsPerGroup == kStepsPerGroup - 1 || (kUs > 1 && s == 4 && u == u1 - 1)) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) tot[h][v] = fmaf(sc[h][step >> 2], acc[h][v], tot[h][v]);
-          acc[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int v = 0; v < 4; ++v) tot[h][v] = fmaf(sc[h][step / kStepsPerGroup], acc[h][v], tot[h][v]);
+            acc[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          }
         }
       }
     }
     TQ_ORDER();
+  }
+  if constexpr (kScaleB) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tot[h][v] = acc[h][v];
   }
   if (kUs > 1) {
     // The units' sums of a row block, added in unit order by the wavefront
@@ -498,6 +540,208 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(GemvArgs 
   }
 }
 
+// ------------------------------------------- binary {-c, +c}, M == 1 ---
+// The pure 1-bit variant the TurboQuant-MLX page compares ternary against
+// (point 3): 32 sign bits per word, bit i of slice word w is weight 32 w + i.
+// Partial-sum table over bytes: for byte position p (0..79, weights
+// 8p .. 8p + 7 of the slice) and byte value c, T[p][c] = sum_{i<8} (2 bit_i(c)
+// - 1) x'[8p + i] in FP32 (81,920 B of LDS); each 8 weights then cost one
+// table read and one add.  Work split and prologue as for the ternary M == 1
+// kernel; a lane's 20 words of the slice (5 quads) are all requested up front.
+constexpr int kBinBytes = 80;  // byte positions per slice
+
+// T[p][c] = L(p, c & 15) + Hl(p, (c >> 4) & 3) + Hh(p, c >> 6), each part a
+// sum of +-x' over 4, 2 and 2 weights.  Work item (p, lane pair hl, lo)
+// writes the four entries c = 16 (4 hh + hl) + lo, hh = 0..3: the 64 lanes of
+// one store touch every bank twice.
+__device__ __forceinline__ void build_bin_table(float* lut, const float* xs, int tid, int nthreads) {
+  for (int i = tid; i < kBinBytes * 64; i += nthreads) {
+    const int p = i >> 6, hl = (i >> 4) & 3, lo = i & 15;
+    const float* x = xs + 8 * p;
+    float l = 0.0f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) l += ((lo >> b) & 1) ? x[b] : -x[b];
+    const float mid = l + (((hl & 1) ? x[4] : -x[4]) + ((hl & 2) ? x[5] : -x[5]));
+    float* row = lut + p * 256 + 16 * hl + lo;
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) row[64 * hh] = mid + (((hh & 1) ? x[6] : -x[6]) + ((hh & 2) ? x[7] : -x[7]));
+  }
+}
+
+template <int XT, int G>
+__global__ __launch_bounds__(kMaxWaves * 64) void gemv_bin_m1_kernel(GemvArgs a) {
+  constexpr int kBytesPerGroup = kBinBytes / G;  // 16 at group 128, 8 at 64
+  __shared__ float lut[kBinBytes * 256];                               // 81920 B
+  __shared__ __attribute__((aligned(16))) float xs[kSliceTrits];
+  const Tile t = make_tile(a);
+  float v0 = 0.0f, v1 = 0.0f;
+  bool valid = false;
+  load_block_t<XT>(a, t, 0, min(t.wave, kSliceBlocks - 1), v0, v1, valid);
+  TQ_ORDER();
+  const uint4* wp = a.words + row64_quad_base_bin(t.slice, t.rbc, a.nb) + t.lane;
+  uint4 wq[kSliceQuadsBin];
+#pragma unroll
+  for (int i = 0; i < kSliceQuadsBin; ++i) wq[i] = load_quad(wp + i * 64);
+  TQ_ORDER();
+  float sc[G];
+  load_scales<G>(a, t, sc);
+  TQ_ORDER();
+  for (int blk = t.wave; blk < kSliceBlocks; blk += t.waves) {
+    if (blk != t.wave) load_block_t<XT>(a, t, 0, blk, v0, v1, valid);
+    transform(a, v0, v1, valid, t.lane);
+    *reinterpret_cast<float2*>(&xs[128 * blk + 2 * t.lane]) = make_float2(v0, v1);
+  }
+  TQ_LDS_BARRIER();
+  build_bin_table(lut, xs, t.tid, blockDim.x);
+  TQ_LDS_BARRIER();
+  if (t.wave >= a.bpg) return;
+  float acc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = 0.0f;
+  // Words past K hold zero bits, and x' past K is zero, so their table
+  // entries are zero: the whole slice is read unconditionally.
+#pragma unroll
+  for (int q = 0; q < kSliceQuadsBin; ++q) {
+    const uint32_t wv[4] = {wq[q].x, wq[q].y, wq[q].z, wq[q].w};
+#pragma unroll
+    for (int jw = 0; jw < 4; ++jw)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int p = 4 * (4 * q + jw) + b;  // compile-time
+        const uint32_t c = (wv[jw] >> (8 * b)) & 0xffu;
+        acc[p / kBytesPerGroup] += lut[p * 256 + c];
+      }
+  }
+  float part[1] = {0.0f};
+#pragma unroll
+  for (int g = 0; g < G; ++g) part[0] = fmaf(sc[g], acc[g], part[0]);
+  finish<1>(a, t, part);
+}
+
+// --------------------------------- binary {-c, +c}, 2 <= M <= 8, matrix cores ---
+// As gemv_mfma_kernel (x' as two fp16 parts in the A rows, one wavefront per
+// 64-row block, lane j = l % 16 on row 16 h + j of row quarter h, lane group
+// kb = l / 16), with the B operand of step s (weights 32 s .. 32 s + 31 of the
+// slice) taken from byte kb of word s: a 256-entry LDS table maps a byte to
+// its eight fp16 signs (+-1), multiplied by the row's fp16 scale (exact).
+// Lanes of one row read the same quads (four lane groups, one cache line).
+template <int M, int XT, int G>
+__global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_bin_mfma_kernel(GemvArgs a) {
+  constexpr int kStepsPerGroup = kSliceTrits / G / 32;
+  constexpr int kScaleVecs = G * 64 / 8;
+  __shared__ __attribute__((aligned(16))) _Float16 xh[2 * M][kXStride];
+  __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
+  __shared__ __attribute__((aligned(16))) uint4 codes[256];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[kMfmaMaxWaves][G * 64];
+  __shared__ int xexp[M];
+  const Tile t = make_tile(a);
+  const int j = t.lane & 15, kb = t.lane >> 4;
+  float xv[kSliceBlocks][2];
+  bool xok[kSliceBlocks];
+  {
+    const int m = t.wave < M ? t.wave : 0;
+#pragma unroll
+    for (int r = 0; r < kSliceBlocks; ++r) load_block_t<XT>(a, t, m, r, xv[r][0], xv[r][1], xok[r]);
+  }
+  TQ_ORDER();
+  // Quads 0..2 of the four row quarters now; quad q + 3 after unit q.
+  const uint4* qbase = a.words + row64_quad_base_bin(t.slice, t.rbc, a.nb) + j;
+  uint4 wq[4][kSliceQuadsBin];
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) wq[h][q] = load_quad(qbase + q * 64 + 16 * h);
+  TQ_ORDER();
+  const uint16_t* sbase = a.scales + row64_scale_base(t.slice, t.rbc, a.nb, G);
+  const uint4 scq = *reinterpret_cast<const uint4*>(sbase + 8 * (t.lane < kScaleVecs ? t.lane : 0));
+  uint4 scq2 = scq;
+  if constexpr (kScaleVecs > 64)
+    scq2 = *reinterpret_cast<const uint4*>(sbase + 8 * (t.lane + 64 < kScaleVecs ? t.lane + 64 : 0));
+  TQ_ORDER();
+  for (int c = t.tid; c < 256; c += blockDim.x) {
+    uint32_t d[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      d[i] = (((c >> (2 * i)) & 1) ? 0x3c00u : 0xbc00u) | ((((c >> (2 * i + 1)) & 1) ? 0x3c00u : 0xbc00u) << 16);
+    codes[c] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+  for (int i = t.tid; i < kSliceTrits; i += blockDim.x) zeros[i] = static_cast<_Float16>(0.0f);
+  for (int m = t.wave; m < M; m += t.waves) {
+    if (m != t.wave) {
+#pragma unroll
+      for (int r = 0; r < kSliceBlocks; ++r) load_block_t<XT>(a, t, m, r, xv[r][0], xv[r][1], xok[r]);
+    }
+    if (a.fused) wave_fwht128_batch<kSliceBlocks>(xv, t.lane, kInvSqrt128);
+#pragma unroll
+    for (int r = 0; r < kSliceBlocks; ++r)
+      if (!xok[r]) {
+        xv[r][0] = 0.0f;
+        xv[r][1] = 0.0f;
+      }
+    const int e = split_two_fp16<kSliceBlocks>(xv, t.lane, &xh[2 * m][0], &xh[2 * m + 1][0]);
+    if (t.lane == 0) xexp[m] = e;
+  }
+  if (t.lane < kScaleVecs) *reinterpret_cast<uint4*>(&ssc[t.wave][8 * t.lane]) = scq;
+  if constexpr (kScaleVecs > 64)
+    if (t.lane + 64 < kScaleVecs) *reinterpret_cast<uint4*>(&ssc[t.wave][8 * (t.lane + 64)]) = scq2;
+  TQ_LDS_BARRIER();
+  if (t.wave >= a.bpg) return;  // a prologue-only wavefront
+
+  const _Float16* xrow = (j < 2 * M ? &xh[j < 2 * M ? j : 0][0] : &zeros[0]) + 8 * kb;
+  const char* cbase = reinterpret_cast<const char*>(codes);
+  auto scale16 = [&](int h, int g) {
+    const uint16_t v = reinterpret_cast<const volatile uint16_t*>(&ssc[t.wave][0])[g * 64 + 16 * h + j];
+    return t.active ? __builtin_bit_cast(_Float16, v) : static_cast<_Float16>(0.0f);
+  };
+  float4_t acc[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) acc[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // Unit u: steps 5u .. 5u + 4, words 5u .. 5u + 4, quads u and u + 1.
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    half8_t af[5];
+#pragma unroll
+    for (int s = 0; s < 5; ++s) af[s] = *reinterpret_cast<const half8_t*>(xrow + 160 * u + 32 * s);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      _Float16 s16 = static_cast<_Float16>(0.0f);
+#pragma unroll
+      for (int s = 0; s < 5; ++s) {
+        const int step = 5 * u + s, w = step;  // word w of the slice
+        const uint4 q = wq[h][w >> 2];
+        const uint32_t word = (w & 3) == 0 ? q.x : (w & 3) == 1 ? q.y : (w & 3) == 2 ? q.z : q.w;
+        const uint32_t off = ((word >> (8 * kb)) & 0xffu) << 4;
+        if (s == 0 || step % kStepsPerGroup == 0) s16 = scale16(h, step / kStepsPerGroup);
+        const half8_t b = *reinterpret_cast<const half8_t*>(cbase + off) * s16;
+        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s], b, acc[h], 0, 0, 0);
+      }
+    }
+    if (u + 3 < kSliceQuadsBin) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) wq[h][u + 3] = load_quad(qbase + (u + 3) * 64 + 16 * h);
+    }
+    TQ_ORDER();
+  }
+  // D rows 4 kb + v: v = 0, 1 the parts of activation row 2 kb, 2, 3 those of 2 kb + 1.
+  const int mrow[2] = {2 * kb, 2 * kb + 1};
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int row = t.rb * 64 + 16 * h + j;
+    if (t.active && row < a.n) {
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int m = mrow[q2];
+        if (m < M) {
+          const float val = ldexpf(acc[h][2 * q2] + acc[h][2 * q2 + 1], -xexp[m]);
+          if (a.mode == kPartial) a.partial[(static_cast<size_t>(t.slice) * M + m) * a.npad + row] = val;
+          else if (a.mode == kAtomic) atomicAdd(&a.y[static_cast<size_t>(m) * a.n + row], val);
+          else a.y[static_cast<size_t>(m) * a.n + row] = val;
+        }
+      }
+    }
+  }
+}
+
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 struct GemvPlan {
@@ -531,17 +775,49 @@ void plan_waves(GemvPlan& p, int min_waves, int max_waves) {
   p.ngroups = (p.nb + w - 1) / w;
 }
 
-template <int M, int kUs>
+template <int M, int kUs, int G>
 void launch_mfma_us(int x_dtype, dim3 grid, dim3 block, hipStream_t s, const GemvArgs& a) {
-  if (x_dtype == TQ_F32) hipLaunchKernelGGL((gemv_mfma_kernel<M, TQ_F32, kUs>), grid, block, 0, s, a);
-  else if (x_dtype == TQ_BF16) hipLaunchKernelGGL((gemv_mfma_kernel<M, TQ_BF16, kUs>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((gemv_mfma_kernel<M, TQ_F16, kUs>), grid, block, 0, s, a);
+  if (x_dtype == TQ_F32) hipLaunchKernelGGL((gemv_mfma_kernel<M, TQ_F32, kUs, G>), grid, block, 0, s, a);
+  else if (x_dtype == TQ_BF16) hipLaunchKernelGGL((gemv_mfma_kernel<M, TQ_BF16, kUs, G>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((gemv_mfma_kernel<M, TQ_F16, kUs, G>), grid, block, 0, s, a);
 }
 
 template <int M>
-void launch_mfma(int x_dtype, int us, dim3 grid, dim3 block, hipStream_t s, const GemvArgs& a) {
-  if (us == 4) launch_mfma_us<M, 4>(x_dtype, grid, block, s, a);
-  else launch_mfma_us<M, 1>(x_dtype, grid, block, s, a);
+void launch_mfma(int x_dtype, int us, int G, dim3 grid, dim3 block, hipStream_t s, const GemvArgs& a) {
+  if (G == 5) {
+    if (us == 4) launch_mfma_us<M, 4, 5>(x_dtype, grid, block, s, a);
+    else launch_mfma_us<M, 1, 5>(x_dtype, grid, block, s, a);
+  } else {
+    if (us == 4) launch_mfma_us<M, 4, 10>(x_dtype, grid, block, s, a);
+    else launch_mfma_us<M, 1, 10>(x_dtype, grid, block, s, a);
+  }
+}
+
+template <int G>
+void launch_bin_m1(int x_dtype, dim3 grid, dim3 block, hipStream_t s, const GemvArgs& a) {
+  if (x_dtype == TQ_F32) hipLaunchKernelGGL((gemv_bin_m1_kernel<TQ_F32, G>), grid, block, 0, s, a);
+  else if (x_dtype == TQ_BF16) hipLaunchKernelGGL((gemv_bin_m1_kernel<TQ_BF16, G>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((gemv_bin_m1_kernel<TQ_F16, G>), grid, block, 0, s, a);
+}
+
+template <int M, int G>
+void launch_bin_mfma_g(int x_dtype, dim3 grid, dim3 block, hipStream_t s, const GemvArgs& a) {
+  if (x_dtype == TQ_F32) hipLaunchKernelGGL((gemv_bin_mfma_kernel<M, TQ_F32, G>), grid, block, 0, s, a);
+  else if (x_dtype == TQ_BF16) hipLaunchKernelGGL((gemv_bin_mfma_kernel<M, TQ_BF16, G>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((gemv_bin_mfma_kernel<M, TQ_F16, G>), grid, block, 0, s, a);
+}
+
+template <int M>
+void launch_bin_mfma(int x_dtype, int G, dim3 grid, dim3 block, hipStream_t s, const GemvArgs& a) {
+  if (G == 5) launch_bin_mfma_g<M, 5>(x_dtype, grid, block, s, a);
+  else launch_bin_mfma_g<M, 10>(x_dtype, grid, block, s, a);
+}
+
+template <int G>
+void launch_m1(int x_dtype, dim3 grid, dim3 block, hipStream_t s, const GemvArgs& a) {
+  if (x_dtype == TQ_F32) hipLaunchKernelGGL((gemv_lut_m1_kernel<TQ_F32, G>), grid, block, 0, s, a);
+  else if (x_dtype == TQ_BF16) hipLaunchKernelGGL((gemv_lut_m1_kernel<TQ_BF16, G>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((gemv_lut_m1_kernel<TQ_F16, G>), grid, block, 0, s, a);
 }
 
 }  // namespace
@@ -562,9 +838,18 @@ int tq_device_cus() {
 }
 
 // Shared by the C entry points: validates a compute descriptor.
+size_t tq_row64_words(int n, int k, int levels) {
+  return static_cast<size_t>(slices_per_row(k)) * row_blocks(n) * (levels == 3 ? kSliceQuads : kSliceQuadsBin) * 256;
+}
+
+size_t tq_row64_scales(int n, int k, int group) {
+  return static_cast<size_t>(slices_per_row(k)) * row_blocks(n) * slice_groups(group) * 64;
+}
+
 int tq_check_weights(const tq_weights* w, int experts_expected) {
   if (!w) return TQ_EINVAL;
   if (w->magic != TQ_MAGIC || w->version != TQ_VERSION) return TQ_EFORMAT;
+  if (!tq_group_ok(w->group) || !tq_levels_ok(w->levels)) return TQ_EFORMAT;
   if (w->layout != TQ_LAYOUT_ROW64) return w->layout == TQ_LAYOUT_ROWMAJOR ? TQ_EUNSUPPORTED : TQ_EFORMAT;
   if (experts_expected > 0 && w->num_experts != experts_expected) return TQ_EFORMAT;
   if (w->num_experts < 1) return TQ_EFORMAT;
@@ -576,8 +861,9 @@ int tq_check_weights(const tq_weights* w, int experts_expected) {
 
 size_t tq_gemv_workspace(int n, int k, int m) { return plan_sizes(n, k, m).partial_bytes; }
 
-extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, float* y, unsigned flags,
-                       void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+int gemv_impl(const tq_weights* w, const void* x, int x_dtype, int m, float* y, unsigned flags, void* workspace,
+              size_t ws_bytes, void* stream) {
   int st = tq_check_weights(w, 1);
   if (st != TQ_OK) return st;
   if (!x || !y) return TQ_EINVAL;
@@ -585,6 +871,7 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
   if (!tq_aligned(x, tq_act_align(x_dtype)) || !tq_aligned(y, 4)) return TQ_EINVAL;
   if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED | TQ_ACCUMULATE)) return TQ_EINVAL;
   if (m < 1 || m > 8) return TQ_ESHAPE;
+  const bool binary = w->levels == 2;
   GemvPlan p = plan_sizes(w->n, w->k, m);
   int us = 1;
   const bool accumulate = (flags & TQ_ACCUMULATE) != 0;
@@ -597,7 +884,7 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
     // Row blocks per workgroup as above; at least one wavefront per
     // transform block, so that a small matrix's prologue runs in parallel.
     plan_waves(p, 1, kMaxWaves);
-    p.waves = max(p.waves, kSliceGroups);
+    p.waves = max(p.waves, kSliceBlocks);
   } else {
     // Row blocks per workgroup so that the grid fills the compute units in
     // one round; every activation row gets a wavefront for the prologue
@@ -606,7 +893,7 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
     // One or two row blocks per workgroup (small matrices): split each
     // block's units over four wavefronts.  (A split over two wavefronts at
     // three or four row blocks measured no faster.)
-    us = 4 * p.bpg <= kMfmaMaxWaves ? 4 : 1;
+    us = (!binary && 4 * p.bpg <= kMfmaMaxWaves) ? 4 : 1;
     p.waves = max(us * p.bpg, m);
   }
   GemvArgs a;
@@ -628,19 +915,42 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
   const dim3 grid(p.nsl, p.ngroups);
   const dim3 block(p.waves * 64);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int G = slice_groups(w->group);
+  if (binary) {
+    if (m == 1) {
+      if (G == 5) launch_bin_m1<5>(x_dtype, grid, block, s, a);
+      else launch_bin_m1<10>(x_dtype, grid, block, s, a);
+    } else {
+      switch (m) {
+        case 2: launch_bin_mfma<2>(x_dtype, G, grid, block, s, a); break;
+        case 3: launch_bin_mfma<3>(x_dtype, G, grid, block, s, a); break;
+        case 4: launch_bin_mfma<4>(x_dtype, G, grid, block, s, a); break;
+        case 5: launch_bin_mfma<5>(x_dtype, G, grid, block, s, a); break;
+        case 6: launch_bin_mfma<6>(x_dtype, G, grid, block, s, a); break;
+        case 7: launch_bin_mfma<7>(x_dtype, G, grid, block, s, a); break;
+        default: launch_bin_mfma<8>(x_dtype, G, grid, block, s, a); break;
+      }
+    }
+    TQ_LAUNCH_CHECK();
+    if (mode == kPartial) {
+      hipLaunchKernelGGL(reduce_kernel, dim3((w->n + 255) / 256, m), dim3(256), 0, s, a.partial, y, m, w->n, p.npad,
+                         p.nsl);
+      TQ_LAUNCH_CHECK();
+    }
+    return TQ_OK;
+  }
   switch (m) {
     case 1:
-      if (x_dtype == TQ_F32) hipLaunchKernelGGL(gemv_lut_m1_kernel<TQ_F32>, grid, block, 0, s, a);
-      else if (x_dtype == TQ_BF16) hipLaunchKernelGGL(gemv_lut_m1_kernel<TQ_BF16>, grid, block, 0, s, a);
-      else hipLaunchKernelGGL(gemv_lut_m1_kernel<TQ_F16>, grid, block, 0, s, a);
+      if (G == 5) launch_m1<5>(x_dtype, grid, block, s, a);
+      else launch_m1<10>(x_dtype, grid, block, s, a);
       break;
-    case 2: launch_mfma<2>(x_dtype, us, grid, block, s, a); break;
-    case 3: launch_mfma<3>(x_dtype, us, grid, block, s, a); break;
-    case 4: launch_mfma<4>(x_dtype, us, grid, block, s, a); break;
-    case 5: launch_mfma<5>(x_dtype, us, grid, block, s, a); break;
-    case 6: launch_mfma<6>(x_dtype, us, grid, block, s, a); break;
-    case 7: launch_mfma<7>(x_dtype, us, grid, block, s, a); break;
-    default: launch_mfma<8>(x_dtype, us, grid, block, s, a); break;
+    case 2: launch_mfma<2>(x_dtype, us, G, grid, block, s, a); break;
+    case 3: launch_mfma<3>(x_dtype, us, G, grid, block, s, a); break;
+    case 4: launch_mfma<4>(x_dtype, us, G, grid, block, s, a); break;
+    case 5: launch_mfma<5>(x_dtype, us, G, grid, block, s, a); break;
+    case 6: launch_mfma<6>(x_dtype, us, G, grid, block, s, a); break;
+    case 7: launch_mfma<7>(x_dtype, us, G, grid, block, s, a); break;
+    default: launch_mfma<8>(x_dtype, us, G, grid, block, s, a); break;
   }
   TQ_LAUNCH_CHECK();
   if (mode == kPartial) {
@@ -649,4 +959,10 @@ extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, f
     TQ_LAUNCH_CHECK();
   }
   return TQ_OK;
+}
+}  // namespace
+
+extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, float* y, unsigned flags,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  return gemv_impl(w, x, x_dtype, m, y, flags, workspace, ws_bytes, stream);
 }

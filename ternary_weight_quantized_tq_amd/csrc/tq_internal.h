@@ -14,12 +14,19 @@ constexpr int kWave = 64;
 constexpr float kInvSqrt128 = 0.08838834764831845f;
 
 // ---------------------------------------------------------------- sizes ---
-// A slice is 640 trits = 32 words = 8 quads of 4 words = 5 scale groups;
-// 640 = lcm(20, 128), so slices start on word and group boundaries.
+// A slice is 640 trits = 32 words = 8 quads of 4 words = 5 transform blocks
+// of 128 = G scale groups (G = 640 / group: 5 at group 128, 10 at group 64);
+// 640 = lcm(20, 128), so slices start on word, block and group boundaries.
+// Binary words: a slice is 20 words = 5 quads.
 constexpr int kSliceTrits = 640;
 constexpr int kSliceWords = 32;
 constexpr int kSliceQuads = 8;
-constexpr int kSliceGroups = 5;
+constexpr int kSliceBlocks = 5;
+constexpr int kSliceWordsBin = 20;
+constexpr int kSliceQuadsBin = 5;
+__host__ __device__ constexpr int slice_groups(int group) { return kSliceTrits / group; }
+inline bool tq_group_ok(int group) { return group == 64 || group == 128; }
+inline bool tq_levels_ok(int levels) { return levels == 2 || levels == 3; }
 
 // Pointer alignment checks of the entry points: p is a multiple of a bytes
 // (a a power of two); activations are read two elements at a time.
@@ -27,29 +34,38 @@ inline bool tq_aligned(const void* p, size_t a) { return (reinterpret_cast<uintp
 inline size_t tq_act_align(int dtype) { return dtype == TQ_F32 ? 8 : 4; }
 
 __host__ __device__ inline int words_per_row(int k) { return (k + TQ_TRITS_PER_WORD - 1) / TQ_TRITS_PER_WORD; }
+__host__ __device__ inline int words_per_row_bin(int k) { return (k + TQ_BITS_PER_WORD - 1) / TQ_BITS_PER_WORD; }
 __host__ __device__ inline int row_blocks(int n) { return (n + 63) / 64; }
 __host__ __device__ inline int slices_per_row(int k) { return (words_per_row(k) + kSliceWords - 1) / kSliceWords; }
 
 // TQ_LAYOUT_ROW64 addressing: slice s, row block b (64 rows), quad qi of
 // the slice, row r of the block, word j of the quad:
-//   word index  = (((s*nb + b)*8 + qi)*64 + r)*4 + j
-//   scale index = ((s*nb + b)*5 + gi)*64 + r        (group g = 5s + gi)
-// so the words of one slice of one row block are 8 KiB contiguous and a
-// wavefront reading quad qi of its 64 rows reads 1 KiB contiguously.
+//   word index  = (((s*nb + b)*Q + qi)*64 + r)*4 + j   (Q = 8, binary 5)
+//   scale index = ((s*nb + b)*G + gi)*64 + r           (group g = Gs + gi)
+// so the words of one slice of one row block are contiguous (8 KiB, binary
+// 5 KiB) and a wavefront reading quad qi of its 64 rows reads 1 KiB
+// contiguously.
 __host__ __device__ inline size_t row64_word_index(int row, int w, int nb) {
   const int s = w / kSliceWords, qi = (w % kSliceWords) >> 2, j = w & 3, b = row >> 6, r = row & 63;
   return ((((static_cast<size_t>(s) * nb + b) * kSliceQuads + qi) * 64 + r) << 2) + j;
 }
-__host__ __device__ inline size_t row64_scale_index(int row, int g, int nb) {
-  const int s = g / kSliceGroups, gi = g % kSliceGroups, b = row >> 6, r = row & 63;
-  return ((static_cast<size_t>(s) * nb + b) * kSliceGroups + gi) * 64 + r;
+__host__ __device__ inline size_t row64_word_index_bin(int row, int w, int nb) {
+  const int s = w / kSliceWordsBin, qi = (w % kSliceWordsBin) >> 2, j = w & 3, b = row >> 6, r = row & 63;
+  return ((((static_cast<size_t>(s) * nb + b) * kSliceQuadsBin + qi) * 64 + r) << 2) + j;
+}
+__host__ __device__ inline size_t row64_scale_index(int row, int g, int nb, int G) {
+  const int s = g / G, gi = g % G, b = row >> 6, r = row & 63;
+  return ((static_cast<size_t>(s) * nb + b) * G + gi) * 64 + r;
 }
 // Quad / scale base of (slice, row block) in units of uint4 / uint16.
 __host__ __device__ inline size_t row64_quad_base(int s, int b, int nb) {
   return (static_cast<size_t>(s) * nb + b) * kSliceQuads * 64;
 }
-__host__ __device__ inline size_t row64_scale_base(int s, int b, int nb) {
-  return (static_cast<size_t>(s) * nb + b) * kSliceGroups * 64;
+__host__ __device__ inline size_t row64_quad_base_bin(int s, int b, int nb) {
+  return (static_cast<size_t>(s) * nb + b) * kSliceQuadsBin * 64;
+}
+__host__ __device__ inline size_t row64_scale_base(int s, int b, int nb, int G) {
+  return (static_cast<size_t>(s) * nb + b) * G * 64;
 }
 // Quads of slice s that hold trits below k: whole 160-trit units (a unit's
 // chunks are reordered within it, see row64_chunk), 2 quads each.
@@ -305,6 +321,9 @@ void tq_set_hip_error(hipError_t e, const char* where);
 
 // Host-side helpers defined in the kernel sources.
 int tq_check_weights(const tq_weights* w, int experts_expected);
+// Words / scales of one matrix in the ROW64 layout.
+size_t tq_row64_words(int n, int k, int levels);
+size_t tq_row64_scales(int n, int k, int group);
 int tq_device_cus();
 size_t tq_gemv_workspace(int n, int k, int m);
 size_t tq_moe_workspace(const tq_weights* gu, int t, int topk);

@@ -44,6 +44,8 @@ using namespace tq;
 namespace {
 
 constexpr int kTile = 8;          // tokens per pass
+constexpr int kFusedMaxPairs = 64;  // the one-launch and per-pair paths: at most 64 (token, slot) pairs
+constexpr int kMoeG = 5;          // scale groups per slice: the expert path takes group 128
 constexpr int kMaxExperts = 1024;
 
 
@@ -62,6 +64,7 @@ struct MoeArgs {
   int fused;
   int accumulate;    // TQ_ACCUMULATE: y += the layer's output
   // workspace
+  int* bad;          // [1] number of (token, slot) ids outside [0, E) (written by one workgroup per call)
   int* num_active;   // [1]
   int* active;       // [experts]   expert id of active slot a
   int* seg;          // [experts+1] pair range of slot a
@@ -71,6 +74,8 @@ struct MoeArgs {
   int gu_parts;
   float* o;          // [t*topk][hidden]
   int* cnt;          // few pairs: [t][row_blocks(hidden)] arrival counters
+  int* pcnt;         // one launch: [t*topk] pair counters, self-resetting
+  int* tcnt;         // one launch: [t] token counters, self-resetting
 };
 
 
@@ -80,18 +85,22 @@ __global__ __launch_bounds__(1024) void moe_bucket_kernel(MoeArgs a) {
   __shared__ int fill[kMaxExperts];
   __shared__ int start[kMaxExperts];
   __shared__ int wsum_c[kMaxExperts / 64], wsum_f[kMaxExperts / 64];
+  __shared__ int nbad;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = a.t * a.topk;
   for (int e = tid; e < a.experts; e += blockDim.x) {
     cnt[e] = 0;
     fill[e] = 0;
   }
+  if (tid == 0) nbad = 0;
   __syncthreads();
   for (int p = tid; p < P; p += blockDim.x) {
     const int e = a.ids[p];
     if (e >= 0 && e < a.experts) atomicAdd(&cnt[e], 1);
+    else atomicAdd(&nbad, 1);
   }
   __syncthreads();
+  if (tid == 0) *a.bad = nbad;
   // Exclusive prefix sums over experts (one per thread, blockDim >= experts)
   // of the pair counts (segment starts) and of "has pairs" (active slots).
   const int e = tid;
@@ -195,13 +204,13 @@ __device__ __forceinline__ void mfma_units(const uint2 (&wq)[4][4], const uint16
 // the weight loads can be issued in between: loads complete in order, and
 // the transform should wait for the activations only.
 struct SliceAct {
-  float v[kSliceGroups][2];
-  bool ok[kSliceGroups];
+  float v[kSliceBlocks][2];
+  bool ok[kSliceBlocks];
 };
 template <typename Load>
 __device__ __forceinline__ void load_slice(SliceAct& x, int s, int K, int lane, Load load) {
 #pragma unroll
-  for (int b = 0; b < kSliceGroups; ++b) {
+  for (int b = 0; b < kSliceBlocks; ++b) {
     const int k0 = s * kSliceTrits + b * 128;
     x.ok[b] = k0 < K;
     load((x.ok[b] ? k0 : 0) + 2 * lane, x.v[b][0], x.v[b][1]);
@@ -210,15 +219,15 @@ __device__ __forceinline__ void load_slice(SliceAct& x, int s, int K, int lane, 
 // Transforms a loaded slice and splits it into A rows 2m, 2m + 1 of xh.
 __device__ __forceinline__ void transform_slice(SliceAct& x, _Float16 (*xh)[kXStride], int* xexp, int m, bool fused,
                                                 int lane) {
-  if (fused) wave_fwht128_batch<kSliceGroups>(x.v, lane, kInvSqrt128);
+  if (fused) wave_fwht128_batch<kSliceBlocks>(x.v, lane, kInvSqrt128);
 #pragma unroll
-  for (int b = 0; b < kSliceGroups; ++b) {
+  for (int b = 0; b < kSliceBlocks; ++b) {
     if (!x.ok[b]) {
       x.v[b][0] = 0.0f;
       x.v[b][1] = 0.0f;
     }
   }
-  const int e = split_two_fp16<kSliceGroups>(x.v, lane, &xh[2 * m][0], &xh[2 * m + 1][0]);
+  const int e = split_two_fp16<kSliceBlocks>(x.v, lane, &xh[2 * m][0], &xh[2 * m + 1][0]);
   if (lane == 0) xexp[m] = e;
 }
 
@@ -245,7 +254,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
   __shared__ __attribute__((aligned(16))) _Float16 xh[2 * kTile][kXStride];
   __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
   __shared__ __attribute__((aligned(16))) uint2 codes[81];
-  __shared__ __attribute__((aligned(16))) uint16_t ssc[2][kSliceGroups * 64];  // gate, up block
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[2][kMoeG * 64];  // gate, up block
   __shared__ int xexp[kTile];
   __shared__ float red[4][kTile][64];
   const int slot = blockIdx.x;
@@ -274,15 +283,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
       uint2 wq[4][4];
       // The block's scales first, by every lane (a load under a lane
       // condition is waited for at once), staged after the transform.
-      const uint4 scq = *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rb, nb) +
-                                                       8 * (lane < kSliceGroups * 8 ? lane : 0));
+      const uint4 scq = *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rb, nb, kMoeG) +
+                                                       8 * (lane < kMoeG * 8 ? lane : 0));
       for (int m = wave; m < M; m += 4) {
         SliceAct xa;
         const size_t base = static_cast<size_t>(pair_of(q + m) / a.topk) * K;
         load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) { load_act2(a.x, a.x_dtype, base + i, v0, v1); });
         transform_slice(xa, xh, xexp, m, a.fused != 0, lane);
       }
-      if ((wave & 1) == 0 && lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[wave >> 1][8 * lane]) = scq;
+      if ((wave & 1) == 0 && lane < kMoeG * 8) *reinterpret_cast<uint4*>(&ssc[wave >> 1][8 * lane]) = scq;
       __syncthreads();
       // Many workgroups in flight: the weights are requested here, after the
       // barrier (requesting them before the transform measured 1-2 % slower).
@@ -316,7 +325,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
   __shared__ __attribute__((aligned(16))) _Float16 xh[2 * kTile][kXStride];
   __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
   __shared__ __attribute__((aligned(16))) uint2 codes[81];
-  __shared__ __attribute__((aligned(16))) uint16_t ssc[4][kSliceGroups * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[4][kMoeG * 64];
   __shared__ int xexp[kTile];
   const int slot = blockIdx.x;
   if (slot >= a.num_active[0]) return;
@@ -353,14 +362,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
         v0 = v.x;
         v1 = v.y;
       });
-      const uint4 scq = *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rbc, nb) +
-                                                       8 * (lane < kSliceGroups * 8 ? lane : 0));
+      const uint4 scq = *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rbc, nb, kMoeG) +
+                                                       8 * (lane < kMoeG * 8 ? lane : 0));
       const uint32_t* wb = wexp + (row64_quad_base(s, rbc, nb) + (kb >> 1) * 64 + j) * 4 + 2 * (kb & 1);
       uint2 wq[4][4];
       mfma_load(wb, 0, 4, wq);
       if (wave < M) transform_slice(x0, xh, xexp, wave, true, lane);
       if (wave + 4 < M) transform_slice(x1, xh, xexp, wave + 4, true, lane);
-      if (lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
+      if (lane < kMoeG * 8) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
       __syncthreads();
       const int u1 = __builtin_amdgcn_readfirstlane(row64_slice_quads(K, s) / 2);
       if (rb < nb) {
@@ -396,7 +405,7 @@ __global__ __launch_bounds__(kPairGuWaves * 64) void moe_gate_up_pairs_kernel(Mo
   __shared__ __attribute__((aligned(16))) _Float16 xh[2][kXStride];
   __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
   __shared__ __attribute__((aligned(16))) uint2 codes[81];
-  __shared__ __attribute__((aligned(16))) uint16_t ssc[2][kSliceGroups * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[2][kMoeG * 64];
   __shared__ int xexp[1];
   __shared__ float red[kPairGuWaves][64];
   const int pair = blockIdx.x, b = blockIdx.y, s = blockIdx.z;
@@ -405,8 +414,20 @@ __global__ __launch_bounds__(kPairGuWaves * 64) void moe_gate_up_pairs_kernel(Mo
   const int up = wave >> 2, unit = wave & 3;
   const int K = a.hidden, I = a.inter, nb = row_blocks(2 * I);
   const size_t P = static_cast<size_t>(a.t) * a.topk;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
     for (int i = tid; i < a.t * row_blocks(a.hidden); i += blockDim.x) a.cnt[i] = 0;
+    // The call's count of ids outside [0, E) (at most 64 pairs: one wavefront).
+    if (tid < 64) {
+      int c = 0;
+      if (tid < P) {
+        const int ei = a.ids[tid];
+        c = (ei < 0 || ei >= a.experts) ? 1 : 0;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+      if (tid == 0) *a.bad = c;
+    }
+  }
   const int e = a.ids[pair];
   if (e < 0 || e >= a.experts) return;  // contributes nothing; its partials are never read
   SliceAct xa;
@@ -423,9 +444,9 @@ __global__ __launch_bounds__(kPairGuWaves * 64) void moe_gate_up_pairs_kernel(Mo
   mfma_load(wb, unit, u1, wq);
   build_code_table(codes, tid, blockDim.x);
   for (int i = tid; i < kSliceTrits; i += blockDim.x) zeros[i] = static_cast<_Float16>(0.0f);
-  if (unit == 3 && lane < kSliceGroups * 8)  // not wavefront 0: its transform waits for nothing else
+  if (unit == 3 && lane < kMoeG * 8)  // not wavefront 0: its transform waits for nothing else
     *reinterpret_cast<uint4*>(&ssc[up][8 * lane]) =
-        *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rb, nb) + 8 * lane);
+        *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rb, nb, kMoeG) + 8 * lane);
   if (wave == 0) transform_slice(xa, xh, xexp, 0, a.fused != 0, lane);
   __syncthreads();
   const _Float16* xrow = (j < 2 ? &xh[j < 2 ? j : 0][0] : &zeros[0]) + 8 * kb;
@@ -451,14 +472,15 @@ __global__ __launch_bounds__(kPairGuWaves * 64) void moe_gate_up_pairs_kernel(Mo
 // scaled by the route weight and stored to o[pair][.]; the arrival is
 // counted, and the last of the token's slots to arrive adds the slots' rows
 // in slot order and stores y.  The o rows are written and read with
-// device-scope atomic accesses (they bypass the per-die caches), so waiting
-// for the stores before counting is enough: no cache-wide write-back.
+// device-scope atomic accesses (coherent across the dies); each slot waits
+// for its row's stores to complete before it counts its arrival, and the
+// last slot reads the rows only after its count has returned.
 constexpr int kPairDnWaves = 4;
 __global__ __launch_bounds__(kPairDnWaves * 64) void moe_down_pairs_kernel(MoeArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 xh[2][kXStride];
   __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
   __shared__ __attribute__((aligned(16))) uint2 codes[81];
-  __shared__ __attribute__((aligned(16))) uint16_t ssc[kSliceGroups * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[kMoeG * 64];
   __shared__ int xexp[1];
   __shared__ float red[kPairDnWaves][64];
   const int pair = blockIdx.x, rb = blockIdx.y;
@@ -488,16 +510,16 @@ __global__ __launch_bounds__(kPairDnWaves * 64) void moe_down_pairs_kernel(MoeAr
       uint2 wq[4][4];
       mfma_load(wb, wave, u1, wq);
       if (wave == 0) {
-        const uint4 scq = *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rb, nb) +
-                                                         8 * (lane < kSliceGroups * 8 ? lane : 0));
-        float g[kSliceGroups][2] = {}, u[kSliceGroups][2] = {};
+        const uint4 scq = *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rb, nb, kMoeG) +
+                                                         8 * (lane < kMoeG * 8 ? lane : 0));
+        float g[kSliceBlocks][2] = {}, u[kSliceBlocks][2] = {};
         for (int z0 = 0; z0 < a.gu_parts; z0 += 4) {
-          float2 gv[4][kSliceGroups], uv[4][kSliceGroups];
+          float2 gv[4][kSliceBlocks], uv[4][kSliceBlocks];
 #pragma unroll
           for (int dz = 0; dz < 4; ++dz) {
             const float* src = grow + static_cast<size_t>(min(z0 + dz, a.gu_parts - 1)) * P * 2 * K;
 #pragma unroll
-            for (int bb = 0; bb < kSliceGroups; ++bb) {
+            for (int bb = 0; bb < kSliceBlocks; ++bb) {
               const int k0 = s * kSliceTrits + bb * 128;
               const int i = (k0 < K ? k0 : 0) + 2 * lane;
               gv[dz][bb] = *reinterpret_cast<const float2*>(src + i);
@@ -508,7 +530,7 @@ __global__ __launch_bounds__(kPairDnWaves * 64) void moe_down_pairs_kernel(MoeAr
           for (int dz = 0; dz < 4; ++dz)
             if (z0 + dz < a.gu_parts)
 #pragma unroll
-              for (int bb = 0; bb < kSliceGroups; ++bb) {
+              for (int bb = 0; bb < kSliceBlocks; ++bb) {
                 g[bb][0] += gv[dz][bb].x;
                 g[bb][1] += gv[dz][bb].y;
                 u[bb][0] += uv[dz][bb].x;
@@ -517,13 +539,13 @@ __global__ __launch_bounds__(kPairDnWaves * 64) void moe_down_pairs_kernel(MoeAr
         }
         SliceAct xa;
 #pragma unroll
-        for (int bb = 0; bb < kSliceGroups; ++bb) {
+        for (int bb = 0; bb < kSliceBlocks; ++bb) {
           xa.ok[bb] = s * kSliceTrits + bb * 128 < K;
 #pragma unroll
           for (int c = 0; c < 2; ++c) xa.v[bb][c] = g[bb][c] / (1.0f + __expf(-g[bb][c])) * u[bb][c];
         }
         transform_slice(xa, xh, xexp, 0, true, lane);
-        if (lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[8 * lane]) = scq;
+        if (lane < kMoeG * 8) *reinterpret_cast<uint4*>(&ssc[8 * lane]) = scq;
       }
       __syncthreads();
       float ts[4][4] = {};
@@ -549,11 +571,21 @@ __global__ __launch_bounds__(kPairDnWaves * 64) void moe_down_pairs_kernel(MoeAr
     __hip_atomic_store(a.o + static_cast<size_t>(pair) * a.hidden + row, wgt * v, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this slot's row is stored before its arrival is counted
+  // Publication without a release fence (a device-scope release writes back
+  // the whole L2 and measured +2.5 us per launch at one token): the row was
+  // stored with device-scope atomic stores, which gfx950 writes through to
+  // the device-coherent level; waiting for their completion (vmcnt 0) before
+  // the counter's device-scope read-modify-write orders them before the
+  // count.  The last arriver reads the rows with device-scope atomic loads,
+  // which read the device-coherent level, issued only after its
+  // read-modify-write has returned (the branch on its result, and a compiler
+  // barrier that keeps the loads below it).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   int prev = 0;
   if (lane == 0) prev = __hip_atomic_fetch_add(&a.cnt[tok * nb + rb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   prev = __shfl(prev, 0);
   if (prev != a.topk - 1) return;
+  asm volatile("" ::: "memory");
   const int32_t* tok_ids = a.ids + static_cast<size_t>(tok) * a.topk;
   float* orow = a.o + static_cast<size_t>(tok) * a.topk * a.hidden + rowc;
   float v = 0.0f;
@@ -590,7 +622,7 @@ __global__ __launch_bounds__(kTokSlots * 64) void moe_down_tok_kernel(MoeArgs a)
   __shared__ __attribute__((aligned(16))) _Float16 xh[kTokSlots][2][kXStride];
   __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
   __shared__ __attribute__((aligned(16))) uint2 codes[81];
-  __shared__ __attribute__((aligned(16))) uint16_t ssc[kTokSlots][kSliceGroups * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[kTokSlots][kMoeG * 64];
   __shared__ int xexp[kTokSlots];
   __shared__ float orow[kMaxTopk][64];
   const int tok = blockIdx.x, rb = blockIdx.y;
@@ -601,7 +633,7 @@ __global__ __launch_bounds__(kTokSlots * 64) void moe_down_tok_kernel(MoeArgs a)
   build_code_table(codes, tid, blockDim.x);
   for (int i = tid; i < kSliceTrits; i += blockDim.x) zeros[i] = static_cast<_Float16>(0.0f);
   const _Float16* xrow = (j < 2 ? &xh[wave][j < 2 ? j : 0][0] : &zeros[0]) + 8 * kb;
-  const int sl = lane < kSliceGroups * 8 ? lane : 0;
+  const int sl = lane < kMoeG * 8 ? lane : 0;
   __syncthreads();
   for (int j0 = 0; j0 < a.topk; j0 += kTokSlots) {
     const int slot = j0 + wave;
@@ -620,15 +652,15 @@ __global__ __launch_bounds__(kTokSlots * 64) void moe_down_tok_kernel(MoeArgs a)
         const int u1 = __builtin_amdgcn_readfirstlane(row64_slice_quads(K, s) / 2);
         uint2 wq[4][4];
         mfma_load(wb, 0, 4, wq);  // slices are stored whole: every unit can be read
-        const uint4 scq = *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rb, nb) + 8 * sl);
-        float g[kSliceGroups][2] = {}, u[kSliceGroups][2] = {};
+        const uint4 scq = *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rb, nb, kMoeG) + 8 * sl);
+        float g[kSliceBlocks][2] = {}, u[kSliceBlocks][2] = {};
         for (int z0 = 0; z0 < a.gu_parts; z0 += 4) {
-          float2 gv[4][kSliceGroups], uv[4][kSliceGroups];
+          float2 gv[4][kSliceBlocks], uv[4][kSliceBlocks];
 #pragma unroll
           for (int dz = 0; dz < 4; ++dz) {
             const float* src = grow + static_cast<size_t>(min(z0 + dz, a.gu_parts - 1)) * P * 2 * K;
 #pragma unroll
-            for (int bb = 0; bb < kSliceGroups; ++bb) {
+            for (int bb = 0; bb < kSliceBlocks; ++bb) {
               const int k0 = s * kSliceTrits + bb * 128;
               const int i = (k0 < K ? k0 : 0) + 2 * lane;
               gv[dz][bb] = *reinterpret_cast<const float2*>(src + i);
@@ -639,7 +671,7 @@ __global__ __launch_bounds__(kTokSlots * 64) void moe_down_tok_kernel(MoeArgs a)
           for (int dz = 0; dz < 4; ++dz)
             if (z0 + dz < a.gu_parts)
 #pragma unroll
-              for (int bb = 0; bb < kSliceGroups; ++bb) {
+              for (int bb = 0; bb < kSliceBlocks; ++bb) {
                 g[bb][0] += gv[dz][bb].x;
                 g[bb][1] += gv[dz][bb].y;
                 u[bb][0] += uv[dz][bb].x;
@@ -648,13 +680,13 @@ __global__ __launch_bounds__(kTokSlots * 64) void moe_down_tok_kernel(MoeArgs a)
         }
         SliceAct xa;
 #pragma unroll
-        for (int bb = 0; bb < kSliceGroups; ++bb) {
+        for (int bb = 0; bb < kSliceBlocks; ++bb) {
           xa.ok[bb] = s * kSliceTrits + bb * 128 < K;
 #pragma unroll
           for (int c = 0; c < 2; ++c) xa.v[bb][c] = g[bb][c] / (1.0f + __expf(-g[bb][c])) * u[bb][c];
         }
         transform_slice(xa, xh[wave], &xexp[wave], 0, true, lane);
-        if (lane < kSliceGroups * 8) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
+        if (lane < kMoeG * 8) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
         // The wavefront's own LDS writes are complete before its reads.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         float ts[4][4] = {};
@@ -678,6 +710,187 @@ __global__ __launch_bounds__(kTokSlots * 64) void moe_down_tok_kernel(MoeArgs a)
       float* yp = a.y + static_cast<size_t>(tok) * a.hidden + row;
       *yp = a.accumulate ? *yp + v : v;
     }
+  }
+}
+
+// ------------------------------------------------ one launch (few pairs) ---
+// The whole expert MLP in one launch, with no workgroup ever waiting for
+// another (so dispatch order cannot deadlock it).  Grid and phase 1 as
+// moe_gate_up_pairs_kernel: workgroup (pair, 64-row block b of I, hidden
+// slice s), eight wavefronts, the slice's gate and up sums of the block
+// stored with device-scope atomic stores.  Each workgroup then counts its
+// arrival on its pair's counter; the last of the pair's (I / 64) x slices
+// workgroups to arrive runs phase 2 for the whole pair: it adds the gate/up
+// partials in slice order, forms h = silu(gate) * up, transforms h (all
+// slices of I into LDS), and computes all of the pair's down rows (row
+// blocks spread over its eight wavefronts, every unit of a block on one
+// wavefront), scaled by the route weight.  The rows are published as in
+// moe_down_pairs_kernel, and the last of the token's slots to arrive adds
+// them in slot order into y (TQ_ACCUMULATE: each row is added into y with
+// device atomics instead).  The counters reset themselves: the workspace's
+// counter area must be zero before the first call and every call leaves it
+// zero.
+constexpr int kFusedMaxInterSlices = 4;  // I <= 2560
+__global__ __launch_bounds__(kPairGuWaves * 64) void moe_fused_pairs_kernel(MoeArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 xh[kFusedMaxInterSlices][2][kXStride];
+  __shared__ __attribute__((aligned(16))) _Float16 zeros[kSliceTrits];
+  __shared__ __attribute__((aligned(16))) uint2 codes[81];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[kPairGuWaves][kMoeG * 64];
+  __shared__ __attribute__((aligned(16))) float hs[kFusedMaxInterSlices * kSliceTrits];
+  __shared__ int xexp[kFusedMaxInterSlices];
+  __shared__ float red[kPairGuWaves][64];
+  __shared__ int last;
+  const int pair = blockIdx.x, b = blockIdx.y, s = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, kb = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int up = wave >> 2, unit = wave & 3;
+  const int K = a.hidden, I = a.inter, nb = row_blocks(2 * I);
+  const size_t P = static_cast<size_t>(a.t) * a.topk;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid < 64) {
+    int c = 0;
+    if (tid < P) {
+      const int ei = a.ids[tid];
+      c = (ei < 0 || ei >= a.experts) ? 1 : 0;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+    if (tid == 0) *a.bad = c;
+  }
+  const int e = a.ids[pair];
+  const bool valid = e >= 0 && e < a.experts;  // workgroup-uniform
+  build_code_table(codes, tid, blockDim.x);
+  for (int i = tid; i < kSliceTrits; i += blockDim.x) zeros[i] = static_cast<_Float16>(0.0f);
+
+  // ---- phase 1: this workgroup's gate and up sums for the slice
+  if (valid) {
+    SliceAct xa;
+    if (wave == 0) {
+      const size_t base = static_cast<size_t>(pair / a.topk) * K;
+      load_slice(xa, s, K, lane, [&](int i, float& v0, float& v1) { load_act2(a.x, a.x_dtype, base + i, v0, v1); });
+    }
+    const int rb = up ? b + I / 64 : b;
+    const int u1 = __builtin_amdgcn_readfirstlane(min(unit + 1, row64_slice_quads(K, s) / 2));
+    const uint32_t* wexp = reinterpret_cast<const uint32_t*>(a.gu_words + static_cast<size_t>(e) * a.gu_wstride);
+    const uint16_t* sexp = a.gu_scales + static_cast<size_t>(e) * a.gu_sstride;
+    const uint32_t* wb = wexp + (row64_quad_base(s, rb, nb) + (kb >> 1) * 64 + j) * 4 + 2 * (kb & 1);
+    uint2 wq[4][4];
+    mfma_load(wb, unit, u1, wq);
+    if (unit == 3 && lane < kMoeG * 8)
+      *reinterpret_cast<uint4*>(&ssc[up][8 * lane]) =
+          *reinterpret_cast<const uint4*>(sexp + row64_scale_base(s, rb, nb, kMoeG) + 8 * lane);
+    if (wave == 0) transform_slice(xa, xh[0], xexp, 0, a.fused != 0, lane);
+    __syncthreads();
+    const _Float16* xrow = (j < 2 ? &xh[0][j < 2 ? j : 0][0] : &zeros[0]) + 8 * kb;
+    float ts[4][4] = {};
+    mfma_units(wq, ssc[up], xrow, reinterpret_cast<const char*>(codes), j, unit, u1, ts);
+    float tot[4][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}};
+    add_slice(ts, xexp, kb, 1, tot);
+    if (kb == 0)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) red[wave][16 * h + j] = tot[h][0];
+    __syncthreads();
+    if (tid < 128) {
+      const int g = tid >> 6, l = tid & 63;  // g = 0: gate, 1: up
+      const float v = ((red[4 * g][l] + red[4 * g + 1][l]) + red[4 * g + 2][l]) + red[4 * g + 3][l];
+      __hip_atomic_store(a.gu + (static_cast<size_t>(s) * P + pair) * 2 * I + g * I + b * 64 + l, v,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // Arrival on the pair's counter (stores complete first; see
+  // moe_down_pairs_kernel for why this ordering suffices on gfx950).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int parts = (I / 64) * slices_per_row(K);
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(&a.pcnt[pair], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == parts - 1;
+    if (last) __hip_atomic_store(&a.pcnt[pair], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
+  }
+  __syncthreads();
+  if (!last) return;
+  asm volatile("" ::: "memory");
+
+  // ---- phase 2 (the pair's last workgroup): h, its transform, all down rows
+  const int tok = pair / a.topk;
+  const int KI = I, nsl_i = slices_per_row(KI), nbd = row_blocks(a.hidden);
+  if (valid) {
+    for (int k = tid; k < KI; k += blockDim.x) {
+      float g = 0.0f, u = 0.0f;
+      for (int z = 0; z < a.gu_parts; ++z) {  // slice order
+        const float* src = a.gu + (static_cast<size_t>(z) * P + pair) * 2 * I;
+        g += __hip_atomic_load(src + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        u += __hip_atomic_load(src + I + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      hs[k] = g / (1.0f + __expf(-g)) * u;
+    }
+    __syncthreads();
+    if (wave < nsl_i) {  // wavefront si transforms slice si of h
+      SliceAct xa;
+      load_slice(xa, wave, KI, lane, [&](int i, float& v0, float& v1) {
+        v0 = hs[i];
+        v1 = hs[i + 1];
+      });
+      transform_slice(xa, xh[wave], &xexp[wave], 0, true, lane);
+    }
+    __syncthreads();
+  }
+  const float wgt = a.route_w[pair];
+  float* orow = a.o + static_cast<size_t>(pair) * a.hidden;
+  if (valid) {
+    const uint32_t* wexp = reinterpret_cast<const uint32_t*>(a.dn_words + static_cast<size_t>(e) * a.dn_wstride);
+    const uint16_t* sexp = a.dn_scales + static_cast<size_t>(e) * a.dn_sstride;
+    for (int rbd = wave; rbd < nbd; rbd += kPairGuWaves) {
+      float tot[4][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}};
+      for (int si = 0; si < nsl_i; ++si) {
+        const uint32_t* wb = wexp + (row64_quad_base(si, rbd, nbd) + (kb >> 1) * 64 + j) * 4 + 2 * (kb & 1);
+        const int u1 = __builtin_amdgcn_readfirstlane(row64_slice_quads(KI, si) / 2);
+        uint2 wq[4][4];
+        mfma_load(wb, 0, 4, wq);  // slices are stored whole
+        const uint4 scq = *reinterpret_cast<const uint4*>(sexp + row64_scale_base(si, rbd, nbd, kMoeG) +
+                                                         8 * (lane < kMoeG * 8 ? lane : 0));
+        if (lane < kMoeG * 8) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wavefront's own scale stores, before its reads
+        const _Float16* xrow = (j < 2 ? &xh[si][j < 2 ? j : 0][0] : &zeros[0]) + 8 * kb;
+        float ts[4][4] = {};
+        mfma_units(wq, ssc[wave], xrow, reinterpret_cast<const char*>(codes), j, 0, u1, ts);
+        add_slice(ts, &xexp[si], kb, 1, tot);
+      }
+      if (kb == 0)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int row = rbd * 64 + 16 * h + j;
+          if (row < a.hidden) {
+            if (a.accumulate)
+              atomicAdd(a.y + static_cast<size_t>(tok) * a.hidden + row, wgt * tot[h][0]);
+            else
+              __hip_atomic_store(orow + row, wgt * tot[h][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+    }
+  }
+  if (a.accumulate) return;
+  // ---- the token's combine: the last of its slots adds the rows in slot order
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(&a.tcnt[tok], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == a.topk - 1;
+    if (last) __hip_atomic_store(&a.tcnt[tok], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last) return;
+  asm volatile("" ::: "memory");
+  const int32_t* tok_ids = a.ids + static_cast<size_t>(tok) * a.topk;
+  const float* obase = a.o + static_cast<size_t>(tok) * a.topk * a.hidden;
+  for (int row = tid; row < a.hidden; row += blockDim.x) {
+    float v = 0.0f;
+    for (int sj = 0; sj < a.topk; ++sj) {
+      const int ej = tok_ids[sj];
+      if (ej >= 0 && ej < a.experts)
+        v += __hip_atomic_load(obase + static_cast<size_t>(sj) * a.hidden + row, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    a.y[static_cast<size_t>(tok) * a.hidden + row] = v;
   }
 }
 
@@ -774,18 +987,24 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 struct MoeLayout {
-  size_t num_active, active, seg, pairs, gu, o, cnt, total;
+  size_t bad, num_active, active, seg, pairs, gu, o, cnt, fcnt, total;
 };
 
 // Few (token, slot) pairs: no bucketing, one workgroup per pair for gate/up
 // (split over hidden slices), down and combine in one launch.
-bool moe_pairs(int t, int topk) { return static_cast<long long>(t) * topk <= 64; }
+bool moe_pairs(int t, int topk) { return static_cast<long long>(t) * topk <= kFusedMaxPairs; }
 
 MoeLayout moe_layout(int experts, int t, int topk, int hidden, int inter) {
   const bool pairs = moe_pairs(t, topk);
   MoeLayout l;
   const size_t P = static_cast<size_t>(t) * topk;
   size_t off = 0;
+  l.bad = off;  // first: tq_moe_bad_ids reads it at offset 0
+  off += align256(sizeof(int));
+  // One launch: pair then token counters, at a fixed place whatever the
+  // call's size (they must stay zero between calls on one workspace).
+  l.fcnt = off;
+  off += align256(sizeof(int) * 2 * kFusedMaxPairs);
   l.num_active = off;
   off += align256(sizeof(int));
   l.active = off;
@@ -812,9 +1031,25 @@ size_t tq_moe_workspace(const tq_weights* gu, int t, int topk) {
   return moe_layout(gu->num_experts, t, topk, hidden, inter).total;
 }
 
+extern "C" int tq_moe_bad_ids(const void* workspace, size_t ws_bytes, int32_t* count, void* stream) {
+  if (!workspace || !count || !tq_aligned(workspace, 16)) return TQ_EINVAL;
+  if (ws_bytes < sizeof(int32_t)) return TQ_ENOSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    tq_set_hip_error(e, __func__);
+    return TQ_EHIP;
+  }
+  *count = v;
+  return v ? TQ_EDATA : TQ_OK;
+}
+
 extern "C" int tq_moe_route(const float* logits, int t, int e, int topk, int32_t* ids, float* weights,
                             void* stream) {
   if (!logits || !ids || !weights) return TQ_EINVAL;
+  if (!tq_aligned(logits, 4) || !tq_aligned(ids, 4) || !tq_aligned(weights, 4)) return TQ_EINVAL;
   if (t < 1 || e < 1 || e > kMaxExperts || topk < 1 || topk > 32 || topk > e) return TQ_ESHAPE;
   hipLaunchKernelGGL(moe_route_kernel, dim3((t + 3) / 4), dim3(256), 0, static_cast<hipStream_t>(stream), logits,
                      t, e, topk, ids, weights);
@@ -834,7 +1069,10 @@ extern "C" int tq_moe_gemv(const tq_weights* w_gate_up, const tq_weights* w_down
   if (!tq_aligned(x, tq_act_align(x_dtype)) || !tq_aligned(y, 4) || !tq_aligned(workspace, 16) ||
       !tq_aligned(expert_ids, 4) || !tq_aligned(route_w, 4))
     return TQ_EINVAL;
-  if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED | TQ_ACCUMULATE)) return TQ_EINVAL;
+  if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED | TQ_ACCUMULATE | TQ_MOE_ONE_LAUNCH)) return TQ_EINVAL;
+  // The expert path takes the ternary format at group 128.
+  if (w_gate_up->levels != 3 || w_down->levels != 3 || w_gate_up->group != 128 || w_down->group != 128)
+    return TQ_EUNSUPPORTED;
   const int E = w_gate_up->num_experts, hidden = w_gate_up->k, inter = w_gate_up->n / 2;
   if (w_gate_up->n % 2 || inter % 64 || w_down->n != hidden || w_down->k != inter) return TQ_ESHAPE;
   if (t < 1 || topk < 1 || topk > 32 || static_cast<long long>(t) * topk > INT_MAX / 4) return TQ_ESHAPE;
@@ -847,10 +1085,10 @@ extern "C" int tq_moe_gemv(const tq_weights* w_gate_up, const tq_weights* w_down
   a.gu_scales = w_gate_up->scales;
   a.dn_words = reinterpret_cast<const uint4*>(w_down->words);
   a.dn_scales = w_down->scales;
-  a.gu_wstride = tq_layout_words(w_gate_up->n, hidden, TQ_LAYOUT_ROW64) / 4;
-  a.gu_sstride = tq_layout_scales(w_gate_up->n, hidden, TQ_LAYOUT_ROW64);
-  a.dn_wstride = tq_layout_words(hidden, inter, TQ_LAYOUT_ROW64) / 4;
-  a.dn_sstride = tq_layout_scales(hidden, inter, TQ_LAYOUT_ROW64);
+  a.gu_wstride = tq_row64_words(w_gate_up->n, hidden, 3) / 4;
+  a.gu_sstride = tq_row64_scales(w_gate_up->n, hidden, 128);
+  a.dn_wstride = tq_row64_words(hidden, inter, 3) / 4;
+  a.dn_sstride = tq_row64_scales(hidden, inter, 128);
   a.x = x;
   a.x_dtype = x_dtype;
   a.ids = expert_ids;
@@ -863,6 +1101,7 @@ extern "C" int tq_moe_gemv(const tq_weights* w_gate_up, const tq_weights* w_down
   a.inter = inter;
   a.fused = (flags & TQ_FWHT_FUSED) ? 1 : 0;
   a.accumulate = (flags & TQ_ACCUMULATE) ? 1 : 0;
+  a.bad = reinterpret_cast<int*>(ws + l.bad);
   a.num_active = reinterpret_cast<int*>(ws + l.num_active);
   a.active = reinterpret_cast<int*>(ws + l.active);
   a.seg = reinterpret_cast<int*>(ws + l.seg);
@@ -870,9 +1109,18 @@ extern "C" int tq_moe_gemv(const tq_weights* w_gate_up, const tq_weights* w_down
   a.gu = reinterpret_cast<float*>(ws + l.gu);
   a.gu_parts = slices_per_row(hidden);
   a.cnt = reinterpret_cast<int*>(ws + l.cnt);
+  a.pcnt = reinterpret_cast<int*>(ws + l.fcnt);
+  a.tcnt = a.pcnt + kFusedMaxPairs;
   a.o = reinterpret_cast<float*>(ws + l.o);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int P = t * topk;
+  if (flags & TQ_MOE_ONE_LAUNCH) {
+    if (!moe_pairs(t, topk) || slices_per_row(inter) > kFusedMaxInterSlices) return TQ_EUNSUPPORTED;
+    hipLaunchKernelGGL(moe_fused_pairs_kernel, dim3(P, inter / 64, slices_per_row(hidden)), dim3(kPairGuWaves * 64),
+                       0, s, a);
+    TQ_LAUNCH_CHECK();
+    return TQ_OK;
+  }
   if (moe_pairs(t, topk)) {
     hipLaunchKernelGGL(moe_gate_up_pairs_kernel, dim3(P, inter / 64, slices_per_row(hidden)), dim3(kPairGuWaves * 64), 0,
                        s, a);

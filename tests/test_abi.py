@@ -22,15 +22,24 @@ def test_sizes_match_closed_forms():
         assert tq.tq_words_per_row(k) == O.words_per_row(k)
         if k % 128 == 0:
             assert tq.tq_packed_bytes(n, k) == O.packed_bytes(n, k)
-        assert tq.tq_layout_words(n, k, tq.TQ_LAYOUT_ROWMAJOR) == n * O.words_per_row(k)
+        assert tq.tq_layout_words(n, k, tq.TQ_LAYOUT_ROWMAJOR, 3) == n * O.words_per_row(k)
+        assert tq.tq_layout_words(n, k, tq.TQ_LAYOUT_ROWMAJOR, 2) == n * O.words_per_row_binary(k)
         nb, nsl = -(-n // 64), -(-O.words_per_row(k) // 32)   # 64-row blocks, 640-trit slices
-        assert tq.tq_layout_words(n, k, tq.TQ_LAYOUT_ROW64) == nsl * nb * 64 * 32
+        assert tq.tq_layout_words(n, k, tq.TQ_LAYOUT_ROW64, 3) == nsl * nb * 64 * 32
+        assert tq.tq_layout_words(n, k, tq.TQ_LAYOUT_ROW64, 2) == nsl * nb * 64 * 20
         if k % 128 == 0:
-            assert tq.tq_layout_scales(n, k, tq.TQ_LAYOUT_ROW64) == nsl * nb * 64 * 5
+            assert tq.tq_layout_scales(n, k, tq.TQ_LAYOUT_ROW64, 128) == nsl * nb * 64 * 5
+            assert tq.tq_layout_scales(n, k, tq.TQ_LAYOUT_ROW64, 64) == nsl * nb * 64 * 10
+            for g in (64, 128):
+                assert tq.tq_format_bytes(n, k, g, 3) == O.packed_bytes(n, k, g)
+                assert tq.tq_format_bytes(n, k, g, 2) == O.packed_bytes_binary(n, k, g)
     assert tq.tq_packed_bytes(17408, 5120) == 19218432
     assert tq.tq_packed_bytes(5120, 17408) == 19230720
-    assert tq.tq_layout_scales(10, 100, tq.TQ_LAYOUT_ROWMAJOR) == 0      # K % 128 != 0
-    assert tq.tq_layout_words(10, 128, 7) == 0
+    assert tq.tq_layout_scales(10, 100, tq.TQ_LAYOUT_ROWMAJOR, 128) == 0      # K % 128 != 0
+    assert tq.tq_layout_scales(10, 128, tq.TQ_LAYOUT_ROWMAJOR, 32) == 0       # group not 64 or 128
+    assert tq.tq_layout_words(10, 128, 7, 3) == 0
+    assert tq.tq_layout_words(10, 128, tq.TQ_LAYOUT_ROW64, 4) == 0
+    assert tq.tq_format_bytes(10, 128, 96, 3) == 0 and tq.tq_format_bytes(10, 128, 128, 1) == 0
 
 
 def _desc(**kw):
@@ -38,12 +47,14 @@ def _desc(**kw):
              layout=tq.TQ_LAYOUT_ROW64, words=0x1000, scales=0x2000)
     d.update(kw)
     return tq.tq_weights(d["magic"], d["version"], d["n"], d["k"], d["num_experts"], d["layout"],
-                         d["words"], d["scales"])
+                         d.get("group", 128), d.get("levels", 3), d["words"], d["scales"])
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(magic=0), tq.TQ_EFORMAT),
-    (dict(version=2), tq.TQ_EFORMAT),
+    (dict(version=1), tq.TQ_EFORMAT),
+    (dict(group=32), tq.TQ_EFORMAT),
+    (dict(levels=4), tq.TQ_EFORMAT),
     (dict(layout=5), tq.TQ_EFORMAT),
     (dict(layout=tq.TQ_LAYOUT_ROWMAJOR), tq.TQ_EUNSUPPORTED),
     (dict(num_experts=4), tq.TQ_EFORMAT),
@@ -86,13 +97,18 @@ def test_gemv_rejects_bad_arguments():
 
 def test_format_calls_reject_bad_arguments():
     lib = tq.lib()
-    assert lib.tq_pack(None, 4, 20, 0, 0x10, None) == tq.TQ_EINVAL
-    assert lib.tq_pack(0x10, 4, 20, 3, 0x10, None) == tq.TQ_EINVAL
-    assert lib.tq_pack(0x10, 0, 20, 0, 0x10, None) == tq.TQ_ESHAPE
-    assert lib.tq_pack(0x10, 4, 100, tq.TQ_LAYOUT_ROW64, 0x10, None) == tq.TQ_ESHAPE
-    assert lib.tq_unpack(0x10, 4, 100, tq.TQ_LAYOUT_ROW64, 0x10, None) == tq.TQ_ESHAPE
-    assert lib.tq_quantize(0x10, tq.TQ_BF16, 4, 128, 0x10, 0x10, None) == tq.TQ_EINVAL
-    assert lib.tq_quantize(0x10, tq.TQ_F64, 4, 100, 0x10, 0x10, None) == tq.TQ_ESHAPE
+    assert lib.tq_pack(None, 4, 20, 0, 3, 0x10, None) == tq.TQ_EINVAL
+    assert lib.tq_pack(0x10, 4, 20, 3, 3, 0x10, None) == tq.TQ_EINVAL
+    assert lib.tq_pack(0x10, 4, 20, 0, 1, 0x10, None) == tq.TQ_EINVAL         # levels
+    assert lib.tq_pack(0x10, 0, 20, 0, 3, 0x10, None) == tq.TQ_ESHAPE
+    assert lib.tq_pack(0x10, 4, 100, tq.TQ_LAYOUT_ROW64, 3, 0x10, None) == tq.TQ_ESHAPE
+    assert lib.tq_unpack(0x10, 4, 100, tq.TQ_LAYOUT_ROW64, 3, 0x10, None) == tq.TQ_ESHAPE
+    assert lib.tq_unpack(0x10, 4, 128, tq.TQ_LAYOUT_ROW64, 5, 0x10, None) == tq.TQ_EINVAL
+    assert lib.tq_quantize(0x10, tq.TQ_BF16, 4, 128, 128, 3, 0x10, 0x10, None) == tq.TQ_EINVAL
+    assert lib.tq_quantize(0x10, tq.TQ_F64, 4, 100, 128, 3, 0x10, 0x10, None) == tq.TQ_ESHAPE
+    assert lib.tq_quantize(0x10, tq.TQ_F64, 4, 128, 32, 3, 0x10, 0x10, None) == tq.TQ_EINVAL   # group
+    assert lib.tq_quantize(0x10, tq.TQ_F64, 4, 128, 64, 1, 0x10, 0x10, None) == tq.TQ_EINVAL   # levels
+    assert lib.tq_pack_scales(0x10, 4, 128, 1, 100, 0x10, None) == tq.TQ_EINVAL              # group
     assert lib.tq_fwht(0x10, tq.TQ_F32, 2, 129, 0x10, None) == tq.TQ_ESHAPE
     assert lib.tq_fwht(0x10, tq.TQ_F64, 2, 128, 0x10, None) == tq.TQ_EINVAL
     assert lib.tq_fwht(0x12, tq.TQ_BF16, 2, 128, 0x10, None) == tq.TQ_EINVAL
@@ -147,3 +163,43 @@ def test_moe_and_gemm_check_alignment():
     assert gemm(x=0x3004) == tq.TQ_EINVAL
     assert gemm(y=0x4002) == tq.TQ_EINVAL
     assert gemm(ws=0x5008) == tq.TQ_EINVAL
+
+
+def test_offline_calls_check_alignment():
+    lib = tq.lib()
+    assert lib.tq_pack(0x10, 4, 20, 0, 3, 0x12, None) == tq.TQ_EINVAL             # words 4 bytes
+    assert lib.tq_unpack(0x12, 4, 20, 0, 3, 0x10, None) == tq.TQ_EINVAL           # words 4 bytes
+    assert lib.tq_quantize(0x14, tq.TQ_F64, 4, 128, 128, 3, 0x10, 0x10, None) == tq.TQ_EINVAL   # f64 8 bytes
+    assert lib.tq_quantize(0x12, tq.TQ_F32, 4, 128, 128, 3, 0x10, 0x10, None) == tq.TQ_EINVAL   # f32 4 bytes
+    assert lib.tq_quantize(0x10, tq.TQ_F32, 4, 128, 128, 3, 0x11, 0x10, None) == tq.TQ_EINVAL   # trits 2 bytes
+    assert lib.tq_quantize(0x10, tq.TQ_F32, 4, 128, 128, 3, 0x10, 0x11, None) == tq.TQ_EINVAL   # scales 2 bytes
+    assert lib.tq_pack_scales(0x11, 4, 128, 1, 128, 0x10, None) == tq.TQ_EINVAL
+    assert lib.tq_pack_scales(0x10, 4, 128, 1, 128, 0x11, None) == tq.TQ_EINVAL
+    assert lib.tq_moe_route(0x12, 1, 8, 2, 0x10, 0x10, None) == tq.TQ_EINVAL
+    assert lib.tq_moe_route(0x10, 1, 8, 2, 0x12, 0x10, None) == tq.TQ_EINVAL
+    assert lib.tq_moe_route(0x10, 1, 8, 2, 0x10, 0x13, None) == tq.TQ_EINVAL
+
+
+def test_checking_calls_reject_bad_arguments():
+    lib = tq.lib()
+    assert lib.tq_pack_checked(0x10, 4, 20, 0, 3, 0x10, None, None) == tq.TQ_EINVAL
+    assert lib.tq_pack_checked(0x10, 4, 20, 0, 3, 0x10, 0x22, None) == tq.TQ_EINVAL
+    assert lib.tq_pack_checked(0x10, 0, 20, 0, 3, 0x10, 0x20, None) == tq.TQ_ESHAPE
+    c = ctypes.c_int32(5)
+    assert lib.tq_moe_bad_ids(None, 256, ctypes.byref(c), None) == tq.TQ_EINVAL
+    assert lib.tq_moe_bad_ids(0x1008, 256, ctypes.byref(c), None) == tq.TQ_EINVAL
+    assert lib.tq_moe_bad_ids(0x1000, 2, ctypes.byref(c), None) == tq.TQ_ENOSPACE
+    assert lib.tq_moe_bad_ids(0x1000, 256, None, None) == tq.TQ_EINVAL
+    assert lib.tq_strerror(tq.TQ_EDATA).decode().startswith("input values out of range")
+
+
+def test_moe_rejects_variant_formats():
+    """The expert path takes the ternary format at group 128 only."""
+    d = lambda g, lv: tq.tq_weights(tq.TQ_MAGIC, tq.TQ_VERSION, 256, 512, 4, tq.TQ_LAYOUT_ROW64, g, lv, 0x1000, 0x2000)
+    lib = tq.lib()
+    for g, lv in ((64, 3), (128, 2)):
+        gu, dn = d(g, lv), tq.tq_weights(tq.TQ_MAGIC, tq.TQ_VERSION, 512, 128, 4, tq.TQ_LAYOUT_ROW64, g, lv, 0x1000,
+                                         0x2000)
+        st = lib.tq_moe_gemv(tq.ctypes.byref(gu), tq.ctypes.byref(dn), 0x3000, tq.TQ_BF16, 1, 1, 0x4000, 0x5000, 0x6000,
+                             tq.TQ_FWHT_FUSED, 0x7000, 1 << 24, None)
+        assert st == tq.TQ_EUNSUPPORTED

@@ -22,12 +22,12 @@ ROW64_SHAPES = [(1, 128), (63, 256), (64, 640), (65, 768), (130, 1024), (7, 2048
 def test_pack_rowmajor_bit_exact(n, k):
     t = synth.trits(10 + n + k, n, k)
     want = O.pack(t)
-    words = torch().empty(tq.tq_layout_words(n, k, tq.TQ_LAYOUT_ROWMAJOR), dtype=torch().int32, device="cuda")
-    tq.tq_pack(dev(t), n, k, tq.TQ_LAYOUT_ROWMAJOR, words)
+    words = torch().empty(tq.tq_layout_words(n, k, tq.TQ_LAYOUT_ROWMAJOR, 3), dtype=torch().int32, device="cuda")
+    tq.tq_pack(dev(t), n, k, tq.TQ_LAYOUT_ROWMAJOR, 3, words)
     got = host_u32(words).reshape(n, -1)
     assert np.array_equal(got, want)
     back = torch().empty((n, k), dtype=torch().int8, device="cuda")
-    tq.tq_unpack(words, n, k, tq.TQ_LAYOUT_ROWMAJOR, back)
+    tq.tq_unpack(words, n, k, tq.TQ_LAYOUT_ROWMAJOR, 3, back)
     assert np.array_equal(back.cpu().numpy(), t)
 
 
@@ -46,7 +46,7 @@ def test_pack_row64_layout(n, k):
     spad[:n, :k // 128] = False
     assert np.all(sc_full[spad].view(np.uint16) == 0)
     back = torch().empty((n, k), dtype=torch().int8, device="cuda")
-    tq.tq_unpack(w.words, n, k, tq.TQ_LAYOUT_ROW64, back)
+    tq.tq_unpack(w.words, n, k, tq.TQ_LAYOUT_ROW64, 3, back)
     assert np.array_equal(back.cpu().numpy(), t)
 
 
@@ -106,3 +106,34 @@ def test_fwht_one_hot_exact_columns():
     got = out.cpu().numpy()[0]
     assert np.all(got[:128] == 0)
     assert np.allclose(got[128:], O.hadamard(128)[3], rtol=0, atol=1e-7)
+
+
+@pytest.mark.parametrize("layout", [tq.TQ_LAYOUT_ROWMAJOR, tq.TQ_LAYOUT_ROW64])
+def test_pack_checked_counts_bad_trits(layout):
+    """Values outside {-1, 0, 1} are counted by tq_pack_checked and packed
+    as 0 by both pack calls (every word stays a base-3 number below 3^20)."""
+    th = torch()
+    n, k = 70, 1280
+    t = synth.trits(31, n, k)
+    bad = t.copy()
+    rng = np.random.default_rng(32)
+    pos = rng.choice(n * k, 37, replace=False)
+    bad.ravel()[pos] = rng.choice(np.array([2, -2, 5, 127, -128], np.int8), 37)
+    clean = bad.copy()
+    clean.ravel()[pos] = 0
+    count = th.full((1,), -1, dtype=th.int32, device="cuda")
+    w_checked = th.empty(tq.tq_layout_words(n, k, layout, 3), dtype=th.int32, device="cuda")
+    w_plain = th.empty_like(w_checked)
+    w_clean = th.empty_like(w_checked)
+    tq.tq_pack_checked(dev(bad), n, k, layout, 3, w_checked, count)
+    tq.tq_pack(dev(bad), n, k, layout, 3, w_plain)
+    tq.tq_pack(dev(clean), n, k, layout, 3, w_clean)
+    th.cuda.synchronize()
+    assert int(count.item()) == 37
+    assert np.array_equal(host_u32(w_checked), host_u32(w_clean))
+    assert np.array_equal(host_u32(w_plain), host_u32(w_clean))
+    assert host_u32(w_checked).max() < 3 ** 20
+    # a clean input reports zero, on the same counter
+    tq.tq_pack_checked(dev(clean), n, k, layout, 3, w_checked, count)
+    th.cuda.synchronize()
+    assert int(count.item()) == 0

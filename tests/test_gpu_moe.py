@@ -243,3 +243,107 @@ def test_moe_reports_bad_ids(T, topk):
     assert tq.tq_moe_bad_ids(ws, nbytes) == 0
     y_ref = O.moe(act.values, good_ids, rw, h["gu_w"], h["gu_s"], h["dn_w"], h["dn_s"], hidden, inter)
     assert_parity(y.cpu().numpy(), y_ref)
+
+
+def _run_moe_flags(w_gu, w_dn, x, t, topk, ids, rw, flags, ws=None, nbytes=None, y=None):
+    th = torch()
+    if y is None:
+        y = th.empty((t, w_dn.n), dtype=th.float32, device="cuda")
+    if ws is None:
+        ws, nbytes = tq.workspace(tq.TQ_OP_MOE, w_gu, t, topk)
+    tq.tq_moe_gemv(w_gu, w_dn, x, t, topk, dev(ids.astype(np.int32)), dev(rw.astype(np.float32)), y, flags, ws,
+                   nbytes)
+    th.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("T,topk", [(1, 2), (3, 4), (2, 12), (5, 9), (8, 8)])
+def test_moe_one_launch_matches_oracle(T, topk):
+    """TQ_MOE_ONE_LAUNCH: the last gate/up workgroup of a pair runs its down
+    projection, the last slot of a token combines; with invalid ids."""
+    E, hidden, inter = 12, 640, 384
+    w_gu, w_dn, h = _random_experts(1700, E, hidden, inter)
+    act = synth.activations(171, T, hidden, "bf16")
+    rng = np.random.default_rng(172)
+    ids = np.stack([rng.choice(E, topk, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[0, topk - 1] = -2
+    rw = rng.random((T, topk))
+    rw /= rw.sum(axis=1, keepdims=True)
+    y = _run_moe_flags(w_gu, w_dn, act_tensor(act), T, topk, ids, rw, tq.TQ_FWHT_FUSED | tq.TQ_MOE_ONE_LAUNCH)
+    ok = (ids >= 0) & (ids < E)
+    y_ref = O.moe(act.values, np.where(ok, ids, 0), np.where(ok, rw, 0.0), h["gu_w"], h["gu_s"], h["dn_w"],
+                  h["dn_s"], hidden, inter)
+    assert_parity(y, y_ref)
+
+
+def test_moe_one_launch_repeated_calls_and_accumulate():
+    """Counters reset themselves: three calls in a row on one workspace
+    (different token counts), then TQ_ACCUMULATE, all against the oracle and
+    bit-identical across repeats."""
+    th = torch()
+    E, hidden, inter, topk = 6, 1280, 512, 4
+    w_gu, w_dn, h = _random_experts(1800, E, hidden, inter)
+    ws, nbytes = tq.workspace(tq.TQ_OP_MOE, w_gu, 16, topk)   # sized for the largest call
+    outs = []
+    for T in (3, 1, 3):
+        act = synth.activations(181 + T, T, hidden, "bf16")
+        rng = np.random.default_rng(182 + T)
+        ids = np.stack([rng.choice(E, topk, replace=False) for _ in range(T)]).astype(np.int32)
+        rw = rng.random((T, topk))
+        rw /= rw.sum(axis=1, keepdims=True)
+        y = _run_moe_flags(w_gu, w_dn, act_tensor(act), T, topk, ids, rw, tq.TQ_FWHT_FUSED | tq.TQ_MOE_ONE_LAUNCH,
+                           ws, nbytes)
+        assert_parity(y, O.moe(act.values, ids, rw, h["gu_w"], h["gu_s"], h["dn_w"], h["dn_s"], hidden, inter))
+        outs.append(y)
+    assert np.array_equal(outs[0], outs[2])
+    base = np.random.default_rng(190).normal(size=(3, hidden)).astype(np.float32)
+    yd = dev(base.copy())
+    act = synth.activations(184, 3, hidden, "bf16")
+    rng = np.random.default_rng(185)
+    ids = np.stack([rng.choice(E, topk, replace=False) for _ in range(3)]).astype(np.int32)
+    rw = np.full((3, topk), 1.0 / topk)
+    got = _run_moe_flags(w_gu, w_dn, act_tensor(act), 3, topk, ids, rw,
+                         tq.TQ_FWHT_FUSED | tq.TQ_MOE_ONE_LAUNCH | tq.TQ_ACCUMULATE, ws, nbytes, y=yd) - base
+    assert_parity(got, O.moe(act.values, ids, rw, h["gu_w"], h["gu_s"], h["dn_w"], h["dn_s"], hidden, inter))
+
+
+def test_moe_one_launch_expert_layer_t1():
+    """256 experts (hidden 2048, intermediate 512), top-8, one token, experts
+    quantised on the GPU: one launch against the oracle and equal to the
+    two-launch path up to rounding order."""
+    wl = synth.MOE_T1
+    lg = synth.logits(wl.logit_seed, 1, wl.experts)
+    ids, rw = O.route(lg, wl.topk)
+    act = synth.activations(wl.x_seed, 1, wl.hidden, "bf16")
+    w_gu = tq.empty_weights(2 * wl.inter, wl.hidden, num_experts=wl.experts)
+    w_dn = tq.empty_weights(wl.hidden, wl.inter, num_experts=wl.experts)
+    host = {}
+    for e in sorted(set(ids.ravel().tolist())):
+        gu64, dn64 = synth.expert_weights(e, wl.hidden, wl.inter)
+        gpu_pack_expert(w_gu, e, weights64=gu64)
+        gpu_pack_expert(w_dn, e, weights64=dn64)
+        t, s, _ = O.quantize(gu64)
+        t2, s2, _ = O.quantize(dn64)
+        host[e] = (O.pack(t), s, O.pack(t2), s2)
+    x = act_tensor(act)
+    y1 = _run_moe_flags(w_gu, w_dn, x, 1, wl.topk, ids, rw, tq.TQ_FWHT_FUSED | tq.TQ_MOE_ONE_LAUNCH)
+    y2 = _run_moe_flags(w_gu, w_dn, x, 1, wl.topk, ids, rw, tq.TQ_FWHT_FUSED)
+    y_ref = O.moe(act.values, ids, rw, {e: v[0] for e, v in host.items()}, {e: v[1] for e, v in host.items()},
+                  {e: v[2] for e, v in host.items()}, {e: v[3] for e, v in host.items()}, wl.hidden, wl.inter)
+    assert_parity(y1, y_ref)
+    assert_parity(y1, y2, rel_l2=1e-6, row_max=1e-5)
+
+
+def test_moe_one_launch_limits():
+    lib = tq.lib()
+    E = 4
+    w_gu = tq.empty_weights(2 * 256, 512, num_experts=E)
+    w_dn = tq.empty_weights(512, 256, num_experts=E)
+    for t, topk, inter_ok in ((9, 8, True), (2, 2, False)):
+        gu, dn = w_gu.desc(), w_dn.desc()
+        if not inter_ok:   # intermediate 3200: five slices of 640
+            gu = tq.tq_weights(tq.TQ_MAGIC, tq.TQ_VERSION, 6400, 512, E, tq.TQ_LAYOUT_ROW64, 128, 3, gu.words, gu.scales)
+            dn = tq.tq_weights(tq.TQ_MAGIC, tq.TQ_VERSION, 512, 3200, E, tq.TQ_LAYOUT_ROW64, 128, 3, dn.words, dn.scales)
+        st = lib.tq_moe_gemv(tq.ctypes.byref(gu), tq.ctypes.byref(dn), 0x3000, tq.TQ_BF16, t, topk, 0x4000, 0x5000,
+                             0x6000, tq.TQ_FWHT_FUSED | tq.TQ_MOE_ONE_LAUNCH, 0x7000, 1 << 30, None)
+        assert st == tq.TQ_EUNSUPPORTED, (t, topk, st)

@@ -41,33 +41,33 @@ def host_f16(x) -> np.ndarray:
     return x.cpu().numpy().view(np.float16)
 
 
-def gpu_pack(trits: np.ndarray, scales: np.ndarray, layout=tq.TQ_LAYOUT_ROW64) -> tq.Weights:
-    """Pack given trits/scales on the GPU into `layout`."""
+def gpu_pack(trits: np.ndarray, scales: np.ndarray, layout=tq.TQ_LAYOUT_ROW64, group=128, levels=3) -> tq.Weights:
+    """Pack given trits (or signs) and scales on the GPU into `layout`."""
     n, k = trits.shape
-    w = tq.empty_weights(n, k, layout)
-    tq.tq_pack(dev(trits), n, k, layout, w.words)
-    tq.tq_pack_scales(dev(scales.view(np.uint16)), n, k, layout, w.scales)
+    w = tq.empty_weights(n, k, layout, group=group, levels=levels)
+    tq.tq_pack(dev(trits), n, k, layout, levels, w.words)
+    tq.tq_pack_scales(dev(scales.view(np.uint16)), n, k, layout, group, w.scales)
     return w
 
 
-def gpu_quantize(weights: np.ndarray, dtype="f64"):
+def gpu_quantize(weights: np.ndarray, dtype="f64", group=128, levels=3):
     """Offline conversion on the GPU: returns (trits tensor [n][k] int8, scales tensor int16)."""
     t = torch()
     n, k = weights.shape
     w = dev(weights.astype(np.float64 if dtype == "f64" else np.float32))
     trits = t.empty((n, k), dtype=t.int8, device="cuda")
-    scales = t.empty((n, k // 128), dtype=t.int16, device="cuda")
-    tq.tq_quantize(w, n, k, trits, scales)
+    scales = t.empty((n, k // group), dtype=t.int16, device="cuda")
+    tq.tq_quantize(w, n, k, group, levels, trits, scales)
     del w
     return trits, scales
 
 
-def gpu_quantize_pack(weights: np.ndarray, layout=tq.TQ_LAYOUT_ROW64) -> tq.Weights:
+def gpu_quantize_pack(weights: np.ndarray, layout=tq.TQ_LAYOUT_ROW64, group=128, levels=3) -> tq.Weights:
     n, k = weights.shape
-    trits, scales = gpu_quantize(weights)
-    w = tq.empty_weights(n, k, layout)
-    tq.tq_pack(trits, n, k, layout, w.words)
-    tq.tq_pack_scales(scales, n, k, layout, w.scales)
+    trits, scales = gpu_quantize(weights, group=group, levels=levels)
+    w = tq.empty_weights(n, k, layout, group=group, levels=levels)
+    tq.tq_pack(trits, n, k, layout, levels, w.words)
+    tq.tq_pack_scales(scales, n, k, layout, group, w.scales)
     return w
 
 
@@ -128,14 +128,14 @@ def gpu_pack_expert(w: "tq.Weights", e: int, weights64: np.ndarray = None, trits
     """Quantise (or take given trits/scales) and pack one expert into slot e
     of an E-expert ROW64 buffer."""
     n, k = w.n, w.k
-    nw = tq.tq_layout_words(n, k, tq.TQ_LAYOUT_ROW64)
-    ns = tq.tq_layout_scales(n, k, tq.TQ_LAYOUT_ROW64)
+    nw = tq.tq_layout_words(n, k, tq.TQ_LAYOUT_ROW64, 3)
+    ns = tq.tq_layout_scales(n, k, tq.TQ_LAYOUT_ROW64, 128)
     if weights64 is not None:
         t_dev, s_dev = gpu_quantize(weights64)
     else:
         t_dev, s_dev = dev(trits), dev(scales.view(np.uint16))
-    tq.tq_pack(t_dev, n, k, tq.TQ_LAYOUT_ROW64, w.words.data_ptr() + 4 * nw * e)
-    tq.tq_pack_scales(s_dev, n, k, tq.TQ_LAYOUT_ROW64, w.scales.data_ptr() + 2 * ns * e)
+    tq.tq_pack(t_dev, n, k, tq.TQ_LAYOUT_ROW64, 3, w.words.data_ptr() + 4 * nw * e)
+    tq.tq_pack_scales(s_dev, n, k, tq.TQ_LAYOUT_ROW64, 128, w.scales.data_ptr() + 2 * ns * e)
     torch().cuda.synchronize()
 
 
