@@ -1,0 +1,201 @@
+"""Plain CPU oracle for the TurboQuant-style KV-cache quantiser.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/`` (and nothing on the product
+path).  It shares no code with the HIP library and imports nothing from the
+package; the random rotation signs and the JL matrix are inputs drawn by
+``synth``.  FP64 throughout, straight from the definitions.
+
+What the pages say (cited by title and section):
+
+* [oMLX-Gemma] "Mac users can use TurboQuant in oMLX, with Gemma-4-31B"
+  (aitntnews), section "What TurboQuant is and what problem it solves":
+  it compresses the KV cache (not the weights) in two steps: a random
+  orthogonal rotation of each KV vector and a conversion to polar form
+  (PolarQuant) with the radius kept at high precision; then a 1-bit
+  Johnson-Lindenstrauss projection (QJL) that removes the remaining bias.
+  It is data-oblivious (no per-block scale), giving about 4-5x at 3 bits.
+  The decode path does "coordinate rotation and table lookups" (section
+  "Why these results").
+* [TQ+] "TurboQuant+" (hugong.cc): the KV cache shrinks to 1/4 - 1/6.
+
+Readings (where the pages are silent):
+
+* vectors are per-head K or V rows of dimension d = 128;
+* rotation Pi x = H (sigma * x): the Sylvester Hadamard of order 128
+  (normalised) after a seeded random sign flip sigma, a fast random
+  orthogonal transform; Pi^T y = sigma * (H y);
+* polar form: radius r = |x|_2 stored in fp16 (round to nearest even once),
+  direction u = Pi x / r (u = 0 when r = 0);
+* the direction's coordinates are quantised with a fixed codebook, the
+  Lloyd-Max quantiser of N(0, 1/d) (a coordinate of a random unit vector in
+  R^d is close to N(0, 1/d) at d = 128), nearest level, a tie to the lower
+  level;
+* keys (inner products with queries): b - 1 bits of codebook, then the
+  residual e = u - u~ through the 1-bit projection: z = sign(S e) with
+  S in R^{d x d} of N(0, 1) entries (sign(0) = +1), and gamma = |e|_2 in fp16;
+  score(q, k) = r (<Pi q, u~> + gamma sqrt(pi/2) / d <S Pi q, z>);
+* values (reconstructed): b bits of codebook; v^ = r Pi^T u~;
+* storage: the codes as bit planes (plane p, word w, bit i = bit p of the
+  code of coordinate 32 w + i), the signs z as one more plane for keys;
+  per vector only r (and gamma for keys) beside the codes.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+D = 128
+
+
+# --------------------------------------------------------------------------
+# rotation  ([oMLX-Gemma]: random orthogonal rotation)
+# --------------------------------------------------------------------------
+def hadamard(n: int = D) -> np.ndarray:
+    h = np.empty((n, n))
+    for i in range(n):
+        for j in range(n):
+            h[i, j] = -1.0 if bin(i & j).count("1") % 2 else 1.0
+    return h / math.sqrt(n)
+
+
+def rotation(signs) -> np.ndarray:
+    """Pi = H diag(sigma) as a dense d x d matrix."""
+    s = np.asarray(signs, dtype=np.float64)
+    return hadamard(len(s)) * s[None, :]
+
+
+def rotate(x, signs) -> np.ndarray:
+    """Rows of x mapped by Pi: y = Pi x for each row x."""
+    return np.atleast_2d(np.asarray(x, dtype=np.float64)) @ rotation(signs).T
+
+
+def unrotate(y, signs) -> np.ndarray:
+    """Rows of y mapped by Pi^T."""
+    return np.atleast_2d(np.asarray(y, dtype=np.float64)) @ rotation(signs)
+
+
+# --------------------------------------------------------------------------
+# the codebook: Lloyd-Max quantiser of a Gaussian (data-oblivious)
+# --------------------------------------------------------------------------
+def _phi(x):
+    return math.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi) if math.isfinite(x) else 0.0
+
+
+def _cdf(x):
+    return 0.5 * (1.0 + math.erf(x / math.sqrt(2.0))) if math.isfinite(x) else (1.0 if x > 0 else 0.0)
+
+
+def lloyd_max_gaussian(levels: int, iters: int = 2000):
+    """Lloyd's iteration for N(0, 1): alternate the nearest-level cells
+    (boundaries at midpoints) and the cell means E[X | a < X < b] =
+    (phi(a) - phi(b)) / (Phi(b) - Phi(a)), from uniform starting levels,
+    until a fixed point.  Returns (levels ascending, boundaries, mse)."""
+    c = np.linspace(-2.0, 2.0, levels) if levels > 1 else np.zeros(1)
+    for _ in range(iters):
+        b = np.concatenate([[-math.inf], (c[:-1] + c[1:]) / 2.0, [math.inf]])
+        new = np.array([(_phi(b[i]) - _phi(b[i + 1])) / (_cdf(b[i + 1]) - _cdf(b[i])) for i in range(levels)])
+        if np.max(np.abs(new - c)) < 1e-15:
+            c = new
+            break
+        c = new
+    b = np.concatenate([[-math.inf], (c[:-1] + c[1:]) / 2.0, [math.inf]])
+    # E[(X - c)^2] over each cell: E[X^2 | cell] - 2 c E[X | cell] + c^2, with
+    # E[X^2 1(a<X<b)] = (Phi(b) - Phi(a)) + a phi(a) - b phi(b)
+    mse = 0.0
+    for i in range(levels):
+        a, bb = b[i], b[i + 1]
+        p = _cdf(bb) - _cdf(a)
+        m1 = _phi(a) - _phi(bb)
+        m2 = p + (a * _phi(a) if math.isfinite(a) else 0.0) - (bb * _phi(bb) if math.isfinite(bb) else 0.0)
+        mse += m2 - 2.0 * c[i] * m1 + c[i] * c[i] * p
+    return c, b[1:-1], mse
+
+
+_LM_CACHE: dict = {}
+
+
+def codebook(bits: int, d: int = D) -> np.ndarray:
+    """Levels of the b-bit quantiser of one rotated unit-vector coordinate:
+    Lloyd-Max of N(0, 1) scaled by 1/sqrt(d)."""
+    if bits not in _LM_CACHE:
+        _LM_CACHE[bits] = lloyd_max_gaussian(2 ** bits)[0]
+    return _LM_CACHE[bits] / math.sqrt(d)
+
+
+def nearest_level(u, levels) -> np.ndarray:
+    """Index of the nearest level (levels ascending); a value exactly halfway
+    between two levels goes to the lower one."""
+    u = np.asarray(u, dtype=np.float64)
+    mids = (levels[:-1] + levels[1:]) / 2.0
+    return np.searchsorted(mids, u, side="left").astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# quantise, estimate, reconstruct
+# --------------------------------------------------------------------------
+def kv_quantize(x, signs, bits: int, keys: bool, jl=None):
+    """Quantise rows of x.  keys=True: (bits - 1)-bit codes, the residual's
+    1-bit projection z = sign(S e) and gamma = |e|; keys=False: bits-bit codes.
+    Returns a dict of r (fp16), codes (int), and for keys gamma (fp16), z (+-1)."""
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    d = x.shape[1]
+    r = np.linalg.norm(x, axis=1)
+    y = rotate(x, signs)
+    u = np.where(r[:, None] > 0, y / np.where(r > 0, r, 1.0)[:, None], 0.0)
+    mb = bits - 1 if keys else bits
+    cb = codebook(mb, d)
+    codes = nearest_level(u, cb)
+    out = {"r": r.astype(np.float16), "codes": codes, "bits": bits, "keys": keys}
+    if keys:
+        e = u - cb[codes]
+        s = np.asarray(jl, dtype=np.float64) @ e.T           # [d][n]
+        out["z"] = np.where(s.T >= 0.0, 1, -1).astype(np.int8)
+        out["gamma"] = np.linalg.norm(e, axis=1).astype(np.float16)
+    return out
+
+
+def kv_scores(q, kq, signs, jl) -> np.ndarray:
+    """score(q, k_i) = r_i (<Pi q, u~_i> + gamma_i sqrt(pi/2) / d <S Pi q, z_i>)
+    for one query q against the quantised keys kq (stored r, gamma)."""
+    q = np.asarray(q, dtype=np.float64).reshape(-1)
+    d = q.shape[0]
+    qr = rotate(q, signs)[0]
+    cb = codebook(kq["bits"] - 1, d)
+    mse = cb[kq["codes"]] @ qr
+    sq = np.asarray(jl, dtype=np.float64) @ qr
+    qjl = kq["gamma"].astype(np.float64) * math.sqrt(math.pi / 2.0) / d * (kq["z"].astype(np.float64) @ sq)
+    return kq["r"].astype(np.float64) * (mse + qjl)
+
+
+def kv_values(p, vq, signs) -> np.ndarray:
+    """sum_i p_i v^_i with v^_i = r_i Pi^T u~_i (accumulated in the rotated
+    frame, one Pi^T at the end)."""
+    p = np.asarray(p, dtype=np.float64).reshape(-1)
+    d = vq["codes"].shape[1]
+    cb = codebook(vq["bits"], d)
+    acc = (p * vq["r"].astype(np.float64)) @ cb[vq["codes"]]
+    return unrotate(acc, signs)[0]
+
+
+def kv_dequantize_values(vq, signs) -> np.ndarray:
+    d = vq["codes"].shape[1]
+    return vq["r"].astype(np.float64)[:, None] * unrotate(codebook(vq["bits"], d)[vq["codes"]], signs)
+
+
+def pack_planes(codes, nbits: int) -> np.ndarray:
+    """Bit planes: out[n][p][w] bit i = bit p of codes[n][32 w + i]."""
+    codes = np.asarray(codes, dtype=np.int64)
+    n, d = codes.shape
+    out = np.zeros((n, nbits, d // 32), dtype=np.uint64)
+    for p in range(nbits):
+        bits = (codes >> p) & 1
+        for i in range(32):
+            out[:, p, :] += bits[:, i::32].astype(np.uint64) << np.uint64(i)
+    return out.astype(np.uint32)
+
+
+def stored_bits(bits: int, keys: bool, d: int = D) -> int:
+    """Bits per stored vector: d b code and sign bits, plus the fp16 radius
+    (and the fp16 residual norm for keys)."""
+    return d * bits + (32 if keys else 16)

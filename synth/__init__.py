@@ -169,3 +169,29 @@ MOE_T64 = MoEWorkload("moe-256x-top8-h2048-i512-t64", 64, logit_seed=4903, x_see
 
 PREFILL_GEMM = Workload("prefill-gemm-2048x5120x17408", 2048, "bf16",
                         [Linear("up", 17408, 5120, 5001, 5002)])
+
+
+# ---------------------------------------------------------------------------
+# KV-cache quantiser inputs: the random rotation's sign flips and the
+# Johnson-Lindenstrauss projection matrix are random draws of the method,
+# passed to both sides as inputs.
+# ---------------------------------------------------------------------------
+def kv_signs(seed, d: int = 128) -> np.ndarray:
+    """Random +-1 (float32) of the KV rotation."""
+    return np.where(_gen(seed).random(d) < 0.5, -1.0, 1.0).astype(np.float32)
+
+
+def kv_jl(seed, d: int = 128) -> np.ndarray:
+    """d x d projection matrix with N(0, 1) entries (float32, row-major)."""
+    return _gen(seed).standard_normal((d, d)).astype(np.float32)
+
+
+def kv_vectors(seed, n: int, d: int = 128, dtype: str = "bf16") -> Activations:
+    """n K or V rows of N(0, 1) with a per-row scale drawn log-uniformly in
+    [0.25, 4] (rows of different norms, as keys and values of real layers)."""
+    g = _gen(seed)
+    x = (g.standard_normal((n, d)) * np.exp(g.uniform(np.log(0.25), np.log(4.0), size=(n, 1)))).astype(np.float32)
+    if dtype == "f32":
+        return Activations(x.astype(np.float64), x, "f32")
+    bits = bf16_bits(x)
+    return Activations(bf16_to_f32(bits).astype(np.float64), bits, "bf16")
