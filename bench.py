@@ -425,11 +425,15 @@ def extra_moe(tq, torch, synth, np):
         ms = timed(torch, 50, 5, step)
         ms_acc = timed(torch, 50, 5, lambda i: step(i, tq.TQ_FWHT_FUSED | tq.TQ_ACCUMULATE))
         bytes_ = active * per_expert
-        out.append({"workload": wl.name, "tokens": T, "active_experts": active, "expert_bytes_read": bytes_,
-                    "weight_copies_rotated": copies, "us_per_layer": round(ms * 1e3, 2),
-                    "us_per_layer_accumulate": round(ms_acc * 1e3, 2),
-                    "gb_s": round(bytes_ / (ms * 1e-3) / 1e9, 1), "tok_s": round(T / (ms * 1e-3), 1),
-                    "launches": 2 if T * wl.topk <= 64 else 4})  # per-pair launches up to 64 pairs
+        row = {"workload": wl.name, "tokens": T, "active_experts": active, "expert_bytes_read": bytes_,
+               "weight_copies_rotated": copies, "us_per_layer": round(ms * 1e3, 2),
+               "us_per_layer_accumulate": round(ms_acc * 1e3, 2),
+               "gb_s": round(bytes_ / (ms * 1e-3) / 1e9, 1), "tok_s": round(T / (ms * 1e-3), 1),
+               "launches": 2 if T * wl.topk <= 64 else 4}  # per-pair launches up to 64 pairs
+        if T * wl.topk <= 64:  # the one-launch form (its counters start zeroed in this workspace)
+            ms1 = timed(torch, 50, 5, lambda i: step(i, tq.TQ_FWHT_FUSED | tq.TQ_MOE_ONE_LAUNCH))
+            row["us_per_layer_one_launch"] = round(ms1 * 1e3, 2)
+        out.append(row)
     return out
 
 
@@ -441,12 +445,18 @@ def extra_gemm(tq, torch, synth, np):
     y = torch.empty((wl.m, lin.n), dtype=torch.float32, device="cuda")
     ws, nb = tq.workspace(tq.TQ_OP_GEMM, w, wl.m)
     ms = timed(torch, 10, 2, lambda i: tq.tq_gemm(w, x, wl.m, y, tq.TQ_FWHT_FUSED, ws, nb))
+    ms_fast = timed(torch, 10, 2, lambda i: tq.tq_gemm(w, x, wl.m, y, tq.TQ_FWHT_FUSED | tq.TQ_FAST_F16, ws, nb))
     useful = 2.0 * wl.m * lin.n * lin.k
     return {"workload": wl.name, "ms": round(ms, 4), "tok_s": round(wl.m / (ms * 1e-3), 1),
             "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 1),
+            "frac_f16_mfma_peak_useful": round(useful / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
             "mfma_tflops_hi_lo": round(2 * useful / (ms * 1e-3) / 1e12, 1),
             "frac_f16_mfma_peak": round(2 * useful / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-            "compute": "v_mfma_f32_16x16x32_f16, x' split into fp16 hi + lo A rows, B = fp16 s*t decoded into registers, FP32 accumulate"}
+            "compute": "v_mfma_f32_16x16x32_f16, x' split into fp16 hi + lo A rows, B = fp16 s*t decoded into registers, FP32 accumulate",
+            "fast_f16": {"ms": round(ms_fast, 4), "tok_s": round(wl.m / (ms_fast * 1e-3), 1),
+                         "useful_tflops": round(useful / (ms_fast * 1e-3) / 1e12, 1),
+                         "frac_f16_mfma_peak": round(useful / (ms_fast * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                         "compute": "TQ_FAST_F16: x' as one fp16 part (128 tokens per workgroup), rel-L2 ~3e-4"}}
 
 
 def main():

@@ -145,8 +145,14 @@ enum { TQ_LAYOUT_ROWMAJOR = 0, TQ_LAYOUT_ROW64 = 1 };
  *   token combines the slots in slot order (no workgroup waits for
  *   another).  Its arrival counters reset themselves, so a workspace used
  *   with this flag must be zero-filled before its first use (each call
- *   leaves the counters zero).  TQ_EUNSUPPORTED for larger requests. */
-enum { TQ_FWHT_FUSED = 1u, TQ_ACCUMULATE = 2u, TQ_MOE_ONE_LAUNCH = 4u };
+ *   leaves the counters zero).  TQ_EUNSUPPORTED for larger requests.
+ * TQ_FAST_F16 (tq_gemm): x' (after its power-of-two scaling per row) as a
+ *   single fp16 part instead of hi + lo: about 2^-12 relative rounding per
+ *   activation, a relative L2 error near 3e-4 on Gaussian activations
+ *   (within the path's 1e-3 bound, against about 1e-7 for the default),
+ *   for half the matrix-core work and weight re-reads (128 tokens per
+ *   workgroup instead of 64). */
+enum { TQ_FWHT_FUSED = 1u, TQ_ACCUMULATE = 2u, TQ_MOE_ONE_LAUNCH = 4u, TQ_FAST_F16 = 8u };
 
 /* Operation ids for tq_workspace_bytes. */
 enum { TQ_OP_GEMV = 0, TQ_OP_MOE = 1, TQ_OP_GEMM = 2 };

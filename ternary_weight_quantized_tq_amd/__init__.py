@@ -28,6 +28,7 @@ TQ_LAYOUT_ROWMAJOR, TQ_LAYOUT_ROW64 = 0, 1
 TQ_FWHT_FUSED = 1
 TQ_ACCUMULATE = 2
 TQ_MOE_ONE_LAUNCH = 4
+TQ_FAST_F16 = 8
 TQ_OP_GEMV, TQ_OP_MOE, TQ_OP_GEMM = 0, 1, 2
 SIZE_MAX = 2 ** 64 - 1
 

@@ -25,7 +25,7 @@ using namespace tq;
 
 namespace {
 
-constexpr int BM = 64;          // rows of Y per workgroup
+constexpr int BM = 64;          // rows of Y per workgroup with x' in two fp16 parts (128 with one)
 constexpr int BN = 256;         // columns of Y per workgroup (4 wavefronts x 64)
 constexpr int BK = 160;         // trits per K step = 2 quads = 8 words
 constexpr int kThreads = 256;
@@ -47,7 +47,7 @@ __device__ __forceinline__ void prep_block(const void* __restrict__ x, int dtype
 }
 
 __global__ __launch_bounds__(256) void gemm_prep_kernel(const void* __restrict__ x, int dtype, int m, int k,
-                                                        int kpad, int fused, _Float16* __restrict__ xh,
+                                                        int kpad, int fused, int parts, _Float16* __restrict__ xh,
                                                         _Float16* __restrict__ xl, int* __restrict__ xe) {
   __shared__ float wmax[4];
   const int row = blockIdx.x;
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const void* __restrict__
                         static_cast<_Float16>(s1 - static_cast<float>(h1))};
     const size_t o = static_cast<size_t>(row) * kpad + b * 128 + 2 * lane;
     *reinterpret_cast<half2_t*>(xh + o) = hh;
-    *reinterpret_cast<half2_t*>(xl + o) = ll;
+    if (parts == 2) *reinterpret_cast<half2_t*>(xl + o) = ll;
   }
 }
 
@@ -117,16 +117,28 @@ __device__ __forceinline__ void tile_of(const GemmArgs& a, int& mt, int& nt) {
 // tokens x 160 trits, hi and lo rows) is double-buffered in LDS; the next
 // unit's activations, word pairs and (at a slice boundary) scales are
 // loaded while the current unit's MFMAs run.  One barrier per unit.
-constexpr int kATiles = BM / 8;           // A tiles of 8 tokens (16 A rows)
+constexpr int kATiles = 8;                // A tiles of 16 A rows
 constexpr int kAStride = BK + 8;          // halves per A row in LDS (16-byte pad)
-constexpr int kARows = 2 * BM;            // A row 2 t + p: part p (hi, lo) of token t
+constexpr int kARows = 16 * kATiles;      // 128 A rows: 64 tokens x (hi, lo), or 128 tokens (one fp16 part)
 constexpr int kAVecs = kARows * BK / 8 / kThreads;  // uint4 per thread per unit (10)
+// A rows of a workgroup: with P = 2 parts (the default), A row 2 t + p is
+// part p (hi, lo) of token t, 64 tokens; with P = 1 (TQ_FAST_F16) A row t is
+// token t, 128 tokens.
+template <int P>
+__device__ __forceinline__ void a_row_of(int idx, int& t, int& part, int& c) {
+  constexpr int kTok = kARows / P;
+  part = P == 2 ? idx / (kTok * BK / 8) : 0;
+  const int rem = P == 2 ? idx % (kTok * BK / 8) : idx;
+  t = rem / (BK / 8);
+  c = rem % (BK / 8);
+}
 
 __device__ __forceinline__ uint2 load_pair_cached(const uint32_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
 // G: scale groups per slice (5 at group 128, 10 at group 64).
-template <int G>
+template <int G, int P>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
+  constexpr int kTok = kARows / P;  // tokens per workgroup
   constexpr int kGroup = kSliceTrits / G;
   constexpr int kScaleVecs = G * 64 / 8;  // 16-byte vectors of one block's slice scales
   constexpr int kScaleLoads = (kScaleVecs + 63) / 64;
@@ -145,16 +157,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
   // Loaders.  Unit u: slice u / 4, unit u % 4 of the slice.
   auto a_src = [&](int u, int i) {  // i-th uint4 of this thread in unit u
     const int idx = tid + i * kThreads;               // 0 .. 2559
-    const int part = idx / (BM * BK / 8), rem = idx % (BM * BK / 8);
-    const int t = rem / (BK / 8), c = rem % (BK / 8);
+    int t, part, c;
+    a_row_of<P>(idx, t, part, c);
     const _Float16* src = part ? a.xl : a.xh;
-    return reinterpret_cast<const uint4*>(src + static_cast<size_t>(mt * BM + t) * a.kpad + u * BK + 8 * c);
+    return reinterpret_cast<const uint4*>(src + static_cast<size_t>(mt * kTok + t) * a.kpad + u * BK + 8 * c);
   };
   auto a_dst = [&](int buf, int i) {
     const int idx = tid + i * kThreads;
-    const int part = idx / (BM * BK / 8), rem = idx % (BM * BK / 8);
-    const int t = rem / (BK / 8), c = rem % (BK / 8);
-    return reinterpret_cast<uint4*>(&As[buf][(2 * t + part) * kAStride + 8 * c]);
+    int t, part, c;
+    a_row_of<P>(idx, t, part, c);
+    return reinterpret_cast<uint4*>(&As[buf][(P * t + part) * kAStride + 8 * c]);
   };
   auto pair_ptr = [&](int u, int h) {
     const int s = u >> 2, uu = u & 3;
@@ -284,11 +296,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < kATiles; ++t)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int row = mt * BM + 8 * t + 2 * kb + q;
+      for (int q = 0; q < 4 / P; ++q) {
+        // D row 4 kb + v of A tile t: P = 2, token 8 t + 2 kb + q from v = 2q (hi)
+        // and 2q + 1 (lo); P = 1, token 16 t + 4 kb + q.
+        const int row = mt * kTok + (16 / P) * t + (4 / P) * kb + q;
         if (row < a.m) {
           float* yp = a.y + static_cast<size_t>(row) * a.n + col;
-          const float v = ldexpf(acc[h][t][2 * q] + acc[h][t][2 * q + 1], -a.xe[row]);
+          const float sum = P == 2 ? acc[h][t][2 * q] + acc[h][t][2 * q + 1] : acc[h][t][q];
+          const float v = ldexpf(sum, -a.xe[row]);
           *yp = a.accumulate ? *yp + v : v;
         }
       }
@@ -303,8 +318,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
 // lane loads its five bytes of a unit directly (byte loads of the words'
 // cache lines); the next unit's bytes and activations are loaded while the
 // current unit's MFMAs run.
-template <int G>
+template <int G, int P>
 __global__ __launch_bounds__(kThreads) void gemm_bin_kernel(GemmArgs a) {
+  constexpr int kTok = kARows / P;  // tokens per workgroup
   constexpr int kStepsPerGroup = kSliceTrits / G / 32;
   constexpr int kScaleVecs = G * 64 / 8;
   __shared__ __attribute__((aligned(16))) _Float16 As[2][kARows * kAStride];
@@ -327,16 +343,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bin_kernel(GemmArgs a) {
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   auto a_src = [&](int u, int i) {
     const int idx = tid + i * kThreads;
-    const int part = idx / (BM * BK / 8), rem = idx % (BM * BK / 8);
-    const int t = rem / (BK / 8), c = rem % (BK / 8);
+    int t, part, c;
+    a_row_of<P>(idx, t, part, c);
     const _Float16* src = part ? a.xl : a.xh;
-    return reinterpret_cast<const u32x4_t*>(src + static_cast<size_t>(mt * BM + t) * a.kpad + u * BK + 8 * c);
+    return reinterpret_cast<const u32x4_t*>(src + static_cast<size_t>(mt * kTok + t) * a.kpad + u * BK + 8 * c);
   };
   auto a_dst = [&](int buf, int i) {
     const int idx = tid + i * kThreads;
-    const int part = idx / (BM * BK / 8), rem = idx % (BM * BK / 8);
-    const int t = rem / (BK / 8), c = rem % (BK / 8);
-    return reinterpret_cast<u32x4_t*>(&As[buf][(2 * t + part) * kAStride + 8 * c]);
+    int t, part, c;
+    a_row_of<P>(idx, t, part, c);
+    return reinterpret_cast<u32x4_t*>(&As[buf][(P * t + part) * kAStride + 8 * c]);
   };
   // Byte kb of word 5 (u % 4) + st of slice u / 4, row 64 rb + 16 h + j.
   const uint8_t* wbytes = reinterpret_cast<const uint8_t*>(a.words);
@@ -421,11 +437,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bin_kernel(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < kATiles; ++t)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int row = mt * BM + 8 * t + 2 * kb + q;
+      for (int q = 0; q < 4 / P; ++q) {
+        // D row 4 kb + v of A tile t: P = 2, token 8 t + 2 kb + q from v = 2q (hi)
+        // and 2q + 1 (lo); P = 1, token 16 t + 4 kb + q.
+        const int row = mt * kTok + (16 / P) * t + (4 / P) * kb + q;
         if (row < a.m) {
           float* yp = a.y + static_cast<size_t>(row) * a.n + col;
-          const float v = ldexpf(acc[h][t][2 * q] + acc[h][t][2 * q + 1], -a.xe[row]);
+          const float sum = P == 2 ? acc[h][t][2 * q] + acc[h][t][2 * q + 1] : acc[h][t][q];
+          const float v = ldexpf(sum, -a.xe[row]);
           *yp = a.accumulate ? *yp + v : v;
         }
       }
@@ -441,7 +460,7 @@ GemmPlan plan_gemm(int n, int k, int m) {
   GemmPlan p;
   p.mtiles = (m + BM - 1) / BM;
   p.ntiles = (n + BN - 1) / BN;
-  p.mpad = p.mtiles * BM;
+  p.mpad = (m + kARows - 1) / kARows * kARows;  // whole tiles of either A-row mode
   p.steps = (k + BK - 1) / BK;
   p.kpad = p.steps * BK;
   if (p.kpad % 128) p.kpad = (p.kpad + 127) / 128 * 128;  // prep works in blocks of 128
@@ -462,9 +481,11 @@ extern "C" int tq_gemm(const tq_weights* w, const void* x, int x_dtype, int m, f
   if (!x || !y || !workspace) return TQ_EINVAL;
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16 && x_dtype != TQ_F16) return TQ_EINVAL;
   if (!tq_aligned(x, tq_act_align(x_dtype)) || !tq_aligned(y, 4) || !tq_aligned(workspace, 16)) return TQ_EINVAL;
-  if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED | TQ_ACCUMULATE)) return TQ_EINVAL;
+  if (flags & ~static_cast<unsigned>(TQ_FWHT_FUSED | TQ_ACCUMULATE | TQ_FAST_F16)) return TQ_EINVAL;
   if (m < 1) return TQ_ESHAPE;
-  const GemmPlan p = plan_gemm(w->n, w->k, m);
+  GemmPlan p = plan_gemm(w->n, w->k, m);
+  const int parts = (flags & TQ_FAST_F16) ? 1 : 2;
+  p.mtiles = (m + kARows / parts - 1) / (kARows / parts);
   if (ws_bytes < p.total) return TQ_ENOSPACE;
   if (static_cast<long long>(p.mtiles) * p.ntiles > INT_MAX) return TQ_ESHAPE;
   _Float16* xh = static_cast<_Float16*>(workspace);
@@ -472,7 +493,7 @@ extern "C" int tq_gemm(const tq_weights* w, const void* x, int x_dtype, int m, f
   int* xe = reinterpret_cast<int*>(static_cast<char*>(workspace) + 2 * p.xh_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(gemm_prep_kernel, dim3(static_cast<unsigned>(p.mpad)), dim3(256), 0, s, x, x_dtype, m, w->k,
-                     p.kpad, (flags & TQ_FWHT_FUSED) ? 1 : 0, xh, xl, xe);
+                     p.kpad, (flags & TQ_FWHT_FUSED) ? 1 : 0, parts, xh, xl, xe);
   TQ_LAUNCH_CHECK();
   GemmArgs a;
   a.words = reinterpret_cast<const uint4*>(w->words);
@@ -494,12 +515,23 @@ extern "C" int tq_gemm(const tq_weights* w, const void* x, int x_dtype, int m, f
   a.accumulate = (flags & TQ_ACCUMULATE) ? 1 : 0;
   const dim3 grid(p.mtiles * p.ntiles);
   const bool g5 = slice_groups(w->group) == 5;
+  const dim3 blk(kThreads);
   if (w->levels == 2) {
-    if (g5) hipLaunchKernelGGL(gemm_bin_kernel<5>, grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL(gemm_bin_kernel<10>, grid, dim3(kThreads), 0, s, a);
+    if (parts == 2) {
+      if (g5) hipLaunchKernelGGL((gemm_bin_kernel<5, 2>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((gemm_bin_kernel<10, 2>), grid, blk, 0, s, a);
+    } else {
+      if (g5) hipLaunchKernelGGL((gemm_bin_kernel<5, 1>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((gemm_bin_kernel<10, 1>), grid, blk, 0, s, a);
+    }
   } else {
-    if (g5) hipLaunchKernelGGL(gemm_kernel<5>, grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL(gemm_kernel<10>, grid, dim3(kThreads), 0, s, a);
+    if (parts == 2) {
+      if (g5) hipLaunchKernelGGL((gemm_kernel<5, 2>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((gemm_kernel<10, 2>), grid, blk, 0, s, a);
+    } else {
+      if (g5) hipLaunchKernelGGL((gemm_kernel<5, 1>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((gemm_kernel<10, 1>), grid, blk, 0, s, a);
+    }
   }
   TQ_LAUNCH_CHECK();
   return TQ_OK;

@@ -107,3 +107,77 @@ def test_gemm_rows_of_very_different_scales():
     y_ref = O.gemv(O.pack(t), s, 1280, x.astype(np.float64), True)
     for r in range(m):
         assert_parity(y[r:r + 1], y_ref[r:r + 1], what=f"row {r}")
+
+
+# TQ_FAST_F16: x' as one fp16 part after the per-row power of two.  fp16
+# rounding is at most 2^-11 relative, about 2.8e-4 RMS, so the output error
+# sits near 3e-4: the tests hold it to 6e-4 rel-L2 (the path's bound is 1e-3)
+# and 3e-3 of each row's largest value.
+FAST = dict(rel_l2=6e-4, row_max=3e-3)
+
+
+def _run_gemm_flags(w, x, m, flags):
+    th = torch()
+    y = th.empty((m, w.n), dtype=th.float32, device="cuda")
+    ws, nbytes = tq.workspace(tq.TQ_OP_GEMM, w, m)
+    tq.tq_gemm(w, x, m, y, flags, ws, nbytes)
+    th.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("m,n,k,dtype", [(1, 256, 640, "bf16"), (70, 300, 1280, "bf16"), (130, 257, 2048, "f32"),
+                                         (200, 1024, 5120, "bf16"), (129, 320, 17408, "f16")])
+def test_gemm_fast_f16_vs_oracle(m, n, k, dtype):
+    t, s, w = _rand(160 + m + n, n, k)
+    act = synth.activations(161 + m, m, k, dtype)
+    y = _run_gemm_flags(w, act_tensor(act), m, tq.TQ_FWHT_FUSED | tq.TQ_FAST_F16)
+    assert_parity(y, O.gemv(O.pack(t), s, k, act.values, True), **FAST)
+
+
+@pytest.mark.parametrize("scale", [3e-6, 2e4])
+def test_gemm_fast_f16_activation_range(scale):
+    t, s, w = _rand(170, 300, 1920)
+    act = synth.activations(171, 130, 1920, "bf16", scale=scale)
+    y = _run_gemm_flags(w, act_tensor(act), 130, tq.TQ_FWHT_FUSED | tq.TQ_FAST_F16)
+    assert_parity(y, O.gemv(O.pack(t), s, 1920, act.values, True), **FAST)
+
+
+def test_gemm_fast_f16_one_hot_exact():
+    """A one-hot row is exact in one fp16 part too (1 * 2^e is a power of two)."""
+    n, k, m = 300, 1280, 140
+    t, s, w = _rand(180, n, k)
+    cols = np.random.default_rng(181).integers(0, k, m)
+    x = np.zeros((m, k), np.float32)
+    x[np.arange(m), cols] = 1.0
+    y = _run_gemm_flags(w, dev(x), m, tq.TQ_FAST_F16)
+    assert np.array_equal(y, (s[:, cols // 128].astype(np.float64) * t[:, cols]).T)
+
+
+@pytest.mark.parametrize("group,levels", [(64, 3), (128, 2), (64, 2)])
+def test_gemm_fast_f16_variants(group, levels):
+    n, k, m = 320, 2560, 150
+    if levels == 3:
+        t = synth.trits(190, n, k)
+    else:
+        t = np.where(np.random.default_rng(190).random((n, k)) < 0.5, -1, 1).astype(np.int8)
+    s = synth.scales(191, n, k // group)
+    w = gpu_pack(t, s, group=group, levels=levels)
+    act = synth.activations(192, m, k, "bf16")
+    y = _run_gemm_flags(w, act_tensor(act), m, tq.TQ_FWHT_FUSED | tq.TQ_FAST_F16)
+    words = O.pack(t) if levels == 3 else O.pack_binary(t)
+    assert_parity(y, O.gemv(words, s, k, act.values, True, group, levels), **FAST)
+
+
+def test_gemm_fast_f16_prefill_full_size_sampled():
+    """2048 x 5120 x 17408 with TQ_FAST_F16, weights quantised on the GPU;
+    8 rows x 192 columns against the oracle."""
+    wl = synth.PREFILL_GEMM.linears[0]
+    w64 = synth.weights(wl.w_seed, wl.n, wl.k)
+    act = synth.activations(wl.x_seed, 2048, wl.k, "bf16")
+    w = gpu_quantize_pack(w64)
+    y = _run_gemm_flags(w, act_tensor(act), 2048, tq.TQ_FWHT_FUSED | tq.TQ_FAST_F16)
+    rng = np.random.default_rng(6)
+    rows = np.concatenate([rng.choice(2048, 6, replace=False), [0, 2047]])
+    cols = np.concatenate([rng.choice(wl.n, 190, replace=False), [0, wl.n - 1]])
+    t, s, _ = O.quantize(w64[cols])
+    assert_parity(y[np.ix_(rows, cols)], O.gemv(O.pack(t), s, wl.k, act.values[rows], True), **FAST)
