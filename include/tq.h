@@ -39,8 +39,9 @@
  *     descriptor is an error, never silent garbage).  A failed kernel
  *     launch returns TQ_EHIP.  No exception crosses the ABI.
  *   * The library keeps no mutable global state beyond a per-thread
- *     message for tq_last_error() and a per-device cache of the compute-unit
- *     count; calls on different streams with different workspaces may run
+ *     message for tq_last_error(), a per-device cache of the compute-unit
+ *     count, and tq_gemv_noalloc's per-device scratch array and its address;
+ *     calls on different streams with different workspaces may run
  *     concurrently.
  *   * Workspaces are caller-owned device memory of tq_workspace_bytes()
  *     bytes; their contents need no initialisation.  Two calls in flight at
@@ -265,6 +266,21 @@ int tq_fwht(const void *x, int x_dtype, int m, int k, float *x_rot,
  * launch when K > 640 and TQ_ACCUMULATE is not set. */
 int tq_gemv(const tq_weights *w, const void *x, int x_dtype, int m, float *y,
             unsigned flags, void *workspace, size_t ws_bytes, void *stream);
+
+/* tq_gemv for callers that cannot allocate device memory, not even a
+ * workspace: code under HIP graph capture where allocation is forbidden,
+ * tight serving loops, harnesses that forbid it.  Same arguments, result and
+ * flags as tq_gemv without the workspace: the slice partial sums of the
+ * default (deterministic) mode go to a library-owned device array of
+ * 16 MiB per GPU (held from the library's loading until the process ends),
+ * so the call allocates nothing.  Returns TQ_ENOSPACE, before any GPU work,
+ * when the partial sums (4 * ceil(k/640) * m * 64 * ceil(n/64) bytes) exceed
+ * 16 MiB; TQ_ACCUMULATE needs no array.  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU race (for example on
+ * two streams); serialise them.  Nothing in the array needs to start at
+ * zero (each call writes every element it reads). */
+int tq_gemv_noalloc(const tq_weights *w, const void *x, int x_dtype, int m,
+                    float *y, unsigned flags, void *stream);
 
 /* Full-precision router (TurboQuant-MLX, point 1): per token, p = softmax of
  * logits[t][0..e) in FP32, the topk largest p (ties to the lower id), and

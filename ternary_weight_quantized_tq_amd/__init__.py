@@ -64,6 +64,7 @@ _SIGNATURES = {
     "tq_unpack": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "tq_fwht": (_I, [_P, _I, _I, _I, _P, _P]),
     "tq_gemv": (_I, [_W, _P, _I, _I, _P, ctypes.c_uint, _P, _SZ, _P]),
+    "tq_gemv_noalloc": (_I, [_W, _P, _I, _I, _P, ctypes.c_uint, _P]),
     "tq_moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "tq_moe_gemv": (_I, [_W, _W, _P, _I, _I, _I, _P, _P, _P, ctypes.c_uint, _P, _SZ, _P]),
     "tq_gemm": (_I, [_W, _P, _I, _I, _P, ctypes.c_uint, _P, _SZ, _P]),
@@ -212,6 +213,11 @@ def tq_fwht(x, m, k, x_rot, stream=None):
 def tq_gemv(w, x, m, y, flags=TQ_FWHT_FUSED, workspace=None, ws_bytes=0, stream=None):
     return _check("tq_gemv", lib().tq_gemv(ctypes.byref(_desc(w)), _ptr(x), dtype_code(x), m, _ptr(y), flags,
                                            _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def tq_gemv_noalloc(w, x, m, y, flags=TQ_FWHT_FUSED, stream=None):
+    return _check("tq_gemv_noalloc", lib().tq_gemv_noalloc(ctypes.byref(_desc(w)), _ptr(x), dtype_code(x), m,
+                                                           _ptr(y), flags, _stream(stream)))
 
 
 def tq_moe_route(logits, t, e, topk, ids, weights, stream=None):

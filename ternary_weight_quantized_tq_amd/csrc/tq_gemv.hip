@@ -39,6 +39,7 @@
 #include "tq_internal.h"
 
 #include <atomic>
+#include <mutex>
 
 using namespace tq;
 
@@ -965,4 +966,64 @@ int gemv_impl(const tq_weights* w, const void* x, int x_dtype, int m, float* y, 
 extern "C" int tq_gemv(const tq_weights* w, const void* x, int x_dtype, int m, float* y, unsigned flags,
                        void* workspace, size_t ws_bytes, void* stream) {
   return gemv_impl(w, x, x_dtype, m, y, flags, workspace, ws_bytes, stream);
+}
+
+// ------------------------------------------ no-allocation entry point ---
+// For callers that cannot allocate device memory (a workspace included):
+// the slice partial sums go to one library-owned array per GPU.  In host
+// code `scratch` names a host-side stand-in, never the device array: its
+// device address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is passed to kernels.
+namespace {
+constexpr size_t kScratchBytes = size_t{16} << 20;
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+struct ScratchAddr {
+  std::atomic<void*> ptr{nullptr};
+  std::mutex mu;
+};
+ScratchAddr g_scratch_addr[64];
+
+// Device address of this device's scratch array (looked up on the first
+// call on each device).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  ScratchAddr& slot = g_scratch_addr[dev];
+  void* p = slot.ptr.load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(slot.mu);
+    p = slot.ptr.load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      slot.ptr.store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" int tq_gemv_noalloc(const tq_weights* w, const void* x, int x_dtype, int m, float* y, unsigned flags,
+                               void* stream) {
+  const int st = tq_check_weights(w, 1);
+  if (st != TQ_OK) return st;
+  if (m < 1 || m > 8) return TQ_ESHAPE;
+  // The partial sums of the default (deterministic) mode must fit the array;
+  // checked before any HIP call.
+  const size_t need = (flags & TQ_ACCUMULATE) ? 0 : plan_sizes(w->n, w->k, m).partial_bytes;
+  if (need > kScratchBytes) return TQ_ENOSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) {
+      tq_set_hip_error(e, __func__);
+      return TQ_EHIP;
+    }
+  }
+  return gemv_impl(w, x, x_dtype, m, y, flags, ws, need > 0 ? kScratchBytes : 0, stream);
 }
