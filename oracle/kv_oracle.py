@@ -82,30 +82,71 @@ def _phi(x):
     return math.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi) if math.isfinite(x) else 0.0
 
 
-def _cdf(x):
-    return 0.5 * (1.0 + math.erf(x / math.sqrt(2.0))) if math.isfinite(x) else (1.0 if x > 0 else 0.0)
+def _upper(x):
+    """P(X > x) for X ~ N(0, 1), from erfc so that far tails keep full precision."""
+    if not math.isfinite(x):
+        return 0.0 if x > 0 else 1.0
+    return 0.5 * math.erfc(x / math.sqrt(2.0))
+
+
+def _cell_prob(a, b):
+    """P(a < X < b); cells on one side of 0 use tail differences there."""
+    if a >= 0.0:
+        return _upper(a) - _upper(b)
+    if b <= 0.0:
+        return _upper(-b) - _upper(-a)
+    return 1.0 - _upper(b) - _upper(-a)
+
+
+def _cells(c):
+    """Boundaries (midpoints, with -inf and +inf at the ends), cell
+    probabilities and cell means E[X | cell] = (phi(a) - phi(b)) / P."""
+    b = np.concatenate([[-math.inf], (c[:-1] + c[1:]) / 2.0, [math.inf]])
+    p = np.array([_cell_prob(b[i], b[i + 1]) for i in range(len(c))])
+    m = np.array([(_phi(b[i]) - _phi(b[i + 1])) / p[i] for i in range(len(c))])
+    return b, p, m
 
 
 def lloyd_max_gaussian(levels: int, iters: int = 2000):
-    """Lloyd's iteration for N(0, 1): alternate the nearest-level cells
-    (boundaries at midpoints) and the cell means E[X | a < X < b] =
-    (phi(a) - phi(b)) / (Phi(b) - Phi(a)), from uniform starting levels,
-    until a fixed point.  Returns (levels ascending, boundaries, mse)."""
+    """The Lloyd-Max quantiser of N(0, 1): levels that are the means of their
+    nearest-level cells.  Lloyd's iteration (cells from the levels, levels
+    from the cell means) from uniform starting levels, at most `iters`
+    steps; from 16 levels up it approaches the fixed point too slowly, so
+    Newton's method on the same equations c_i = E[X | cell_i(c)] finishes
+    it (the Jacobian of a cell mean with respect to its ends a, b is
+    phi(a)(m - a)/P and phi(b)(b - m)/P, and each end moves by half of each
+    neighbouring level's step).  Returns (levels ascending, boundaries, mse)."""
     c = np.linspace(-2.0, 2.0, levels) if levels > 1 else np.zeros(1)
     for _ in range(iters):
-        b = np.concatenate([[-math.inf], (c[:-1] + c[1:]) / 2.0, [math.inf]])
-        new = np.array([(_phi(b[i]) - _phi(b[i + 1])) / (_cdf(b[i + 1]) - _cdf(b[i])) for i in range(levels)])
-        if np.max(np.abs(new - c)) < 1e-15:
-            c = new
-            break
+        new = _cells(c)[2]
+        done = np.max(np.abs(new - c)) < 1e-15
         c = new
-    b = np.concatenate([[-math.inf], (c[:-1] + c[1:]) / 2.0, [math.inf]])
+        if done:
+            break
+    for _ in range(100):
+        b, p, m = _cells(c)
+        if np.max(np.abs(c - m)) < 1e-15:
+            break
+        jac = np.eye(levels)
+        for i in range(levels):
+            da = _phi(b[i]) * (m[i] - b[i]) / p[i] if math.isfinite(b[i]) else 0.0
+            db = _phi(b[i + 1]) * (b[i + 1] - m[i]) / p[i] if math.isfinite(b[i + 1]) else 0.0
+            if i > 0:
+                jac[i, i - 1] -= da / 2.0
+            jac[i, i] -= (da + db) / 2.0
+            if i + 1 < levels:
+                jac[i, i + 1] -= db / 2.0
+        step = np.linalg.solve(jac, m - c)
+        c = c + step
+        if np.max(np.abs(step)) < 1e-15:
+            break
+    b = _cells(c)[0]
     # E[(X - c)^2] over each cell: E[X^2 | cell] - 2 c E[X | cell] + c^2, with
-    # E[X^2 1(a<X<b)] = (Phi(b) - Phi(a)) + a phi(a) - b phi(b)
+    # E[X^2 1(a<X<b)] = P(a<X<b) + a phi(a) - b phi(b)
     mse = 0.0
     for i in range(levels):
         a, bb = b[i], b[i + 1]
-        p = _cdf(bb) - _cdf(a)
+        p = _cell_prob(a, bb)
         m1 = _phi(a) - _phi(bb)
         m2 = p + (a * _phi(a) if math.isfinite(a) else 0.0) - (bb * _phi(bb) if math.isfinite(bb) else 0.0)
         mse += m2 - 2.0 * c[i] * m1 + c[i] * c[i] * p
@@ -193,6 +234,17 @@ def pack_planes(codes, nbits: int) -> np.ndarray:
         for i in range(32):
             out[:, p, :] += bits[:, i::32].astype(np.uint64) << np.uint64(i)
     return out.astype(np.uint32)
+
+
+def kv_records(kq) -> np.ndarray:
+    """The stored code record of each vector, uint32 [n][bits][d/32]: the
+    codebook codes' bit planes, then (keys) the plane of z (bit set where
+    z = +1)."""
+    mb = kq["bits"] - 1 if kq["keys"] else kq["bits"]
+    planes = pack_planes(kq["codes"], mb)
+    if kq["keys"]:
+        planes = np.concatenate([planes, pack_planes((kq["z"] > 0).astype(np.int64), 1)], axis=1)
+    return planes
 
 
 def stored_bits(bits: int, keys: bool, d: int = D) -> int:

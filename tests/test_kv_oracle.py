@@ -18,10 +18,11 @@ GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_co
 
 # J. Max, "Quantizing for minimum distortion", IRE Trans. Information Theory,
 # 1960, Table I (normal density): output levels and mean-square error.
-MAX_1960 = {2: ([0.7980], 0.3634), 4: ([0.4528, 1.5104], 0.1175), 8: ([0.2451, 0.7560, 1.3440, 2.1520], 0.03455)}
+MAX_1960 = {2: ([0.7980], 0.3634), 4: ([0.4528, 1.5104], 0.1175), 8: ([0.2451, 0.7560, 1.3440, 2.1520], 0.03455),
+             16: ([0.1284, 0.3881, 0.6568, 0.9424, 1.2562, 1.6180, 2.0690, 2.7326], 0.009497)}
 
 
-@pytest.mark.parametrize("levels", [2, 4, 8])
+@pytest.mark.parametrize("levels", [2, 4, 8, 16])
 def test_lloyd_max_matches_published_table(levels):
     c, b, mse = K.lloyd_max_gaussian(levels)
     want, want_mse = MAX_1960[levels]
@@ -30,7 +31,7 @@ def test_lloyd_max_matches_published_table(levels):
     assert mse == pytest.approx(want_mse, rel=2e-3)
 
 
-@pytest.mark.parametrize("levels", [2, 4, 8, 16])
+@pytest.mark.parametrize("levels", [2, 4, 8, 16, 32, 128, 256])
 def test_lloyd_max_optimality_conditions(levels):
     """Each level is the mean of its cell and each boundary the midpoint of
     its two levels (checked by numerical integration, not by the closed
@@ -38,13 +39,21 @@ def test_lloyd_max_optimality_conditions(levels):
     c, b, mse = K.lloyd_max_gaussian(levels)
     assert np.allclose(b, (c[:-1] + c[1:]) / 2, atol=1e-12)
     edges = np.concatenate([[-12.0], b, [12.0]])
+    pts = 200001 if levels <= 16 else 20001
     for i in range(levels):
-        xs = np.linspace(edges[i], edges[i + 1], 200001)
+        xs = np.linspace(edges[i], edges[i + 1], pts)
         w = np.exp(-xs ** 2 / 2)
         assert np.trapezoid(xs * w, xs) / np.trapezoid(w, xs) == pytest.approx(c[i], abs=1e-6)
-    x = np.random.default_rng(levels).standard_normal(2_000_000)
-    q = c[K.nearest_level(x, c)]
-    assert np.mean((x - q) ** 2) == pytest.approx(mse, rel=0.01)
+    # the distortion against the integral of (x - c_i)^2 over each cell
+    dist = 0.0
+    for i in range(levels):
+        xs = np.linspace(edges[i], edges[i + 1], pts)
+        dist += np.trapezoid((xs - c[i]) ** 2 * np.exp(-xs ** 2 / 2), xs) / math.sqrt(2 * math.pi)
+    assert dist == pytest.approx(mse, rel=1e-5)
+    if levels <= 16:
+        x = np.random.default_rng(levels).standard_normal(2_000_000)
+        q = c[K.nearest_level(x, c)]
+        assert np.mean((x - q) ** 2) == pytest.approx(mse, rel=0.01)
 
 
 def test_nearest_level_ties_and_order():
@@ -169,6 +178,20 @@ def test_compression_matches_pages():
     assert a <= fp16 / K.stored_bits(4, True) * 1.07 and fp16 / K.stored_bits(2, True) >= b
 
 
+def test_key_record_planes():
+    """A key record holds the (bits - 1) code planes, then z's plane."""
+    kq = {"bits": 3, "keys": True, "codes": np.zeros((2, K.D), np.int64), "z": -np.ones((2, K.D), np.int8)}
+    kq["codes"][1, 40] = 3
+    kq["z"][1, 127] = 1
+    rec = K.kv_records(kq)
+    assert rec.shape == (2, 3, 4) and rec.dtype == np.uint32
+    assert rec[0].sum() == 0
+    assert rec[1, 0, 1] == 1 << 8 and rec[1, 1, 1] == 1 << 8 and rec[1, 2, 3] == 1 << 31
+    assert rec[1].astype(np.int64).sum() == 2 * (1 << 8) + (1 << 31)
+    vq = {"bits": 2, "keys": False, "codes": np.full((1, K.D), 2, np.int64)}
+    assert K.kv_records(vq)[0].tolist() == [[0] * 4, [0xFFFFFFFF] * 4]
+
+
 def test_bit_planes():
     codes = np.zeros((1, K.D), np.int64)
     codes[0, 33] = 0b101
@@ -203,6 +226,20 @@ def test_pins_catch_unscaled_codebook(monkeypatch):
     good = K.codebook
     _expect_pin_failure(monkeypatch, "codebook", lambda bits, d=K.D: good(bits, d) * math.sqrt(d),
                         [test_more_bits_converge_to_exact])
+
+
+def test_pins_catch_newton_sign_error(monkeypatch):
+    """A wrong-sign Newton step leaves a point that is not the fixed point
+    (or diverges); the optimality pin at 32 levels catches it."""
+    good_solve = np.linalg.solve
+    monkeypatch.setattr(K, "_LM_CACHE", {})
+    monkeypatch.setattr(K.np.linalg, "solve", lambda a, b: -good_solve(a, b))
+    failed = 0
+    try:
+        test_lloyd_max_optimality_conditions(32)
+    except (AssertionError, ValueError, FloatingPointError, ZeroDivisionError):
+        failed = 1
+    assert failed, "no pin caught the wrong-sign Newton step"
 
 
 def test_pins_catch_transposed_rotation(monkeypatch):
