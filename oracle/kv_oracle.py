@@ -35,9 +35,11 @@ Readings (where the pages are silent):
   S in R^{d x d} of N(0, 1) entries (sign(0) = +1), and gamma = |e|_2 in fp16;
   score(q, k) = r (<Pi q, u~> + gamma sqrt(pi/2) / d <S Pi q, z>);
 * values (reconstructed): b bits of codebook; v^ = r Pi^T u~;
-* storage: the codes as bit planes (plane p, word w, bit i = bit p of the
-  code of coordinate 32 w + i), the signs z as one more plane for keys;
-  per vector only r (and gamma for keys) beside the codes.
+* storage: the codes as packed little-endian fields (the code of
+  coordinate j in bits m j .. m j + m - 1 of the record, m bits per code,
+  word w holding record bits 32 w .. 32 w + 31), then for keys the signs z
+  as 128 more bits (bit j set where z_j = +1); per vector only r (and gamma
+  for keys) beside the codes.
 """
 from __future__ import annotations
 
@@ -224,27 +226,30 @@ def kv_dequantize_values(vq, signs) -> np.ndarray:
     return vq["r"].astype(np.float64)[:, None] * unrotate(codebook(vq["bits"], d)[vq["codes"]], signs)
 
 
-def pack_planes(codes, nbits: int) -> np.ndarray:
-    """Bit planes: out[n][p][w] bit i = bit p of codes[n][32 w + i]."""
+def pack_fields(codes, nbits: int) -> np.ndarray:
+    """Codes as packed little-endian nbits-bit fields: out[n][w] holds bits
+    32 w .. 32 w + 31 of the concatenation, code j in bits nbits j ..
+    nbits j + nbits - 1."""
     codes = np.asarray(codes, dtype=np.int64)
     n, d = codes.shape
-    out = np.zeros((n, nbits, d // 32), dtype=np.uint64)
-    for p in range(nbits):
-        bits = (codes >> p) & 1
-        for i in range(32):
-            out[:, p, :] += bits[:, i::32].astype(np.uint64) << np.uint64(i)
+    words = d * nbits // 32
+    out = np.zeros((n, words), dtype=np.uint64)
+    for j in range(d):
+        for t in range(nbits):
+            bit = nbits * j + t
+            out[:, bit // 32] |= ((codes[:, j] >> t) & 1).astype(np.uint64) << np.uint64(bit % 32)
     return out.astype(np.uint32)
 
 
 def kv_records(kq) -> np.ndarray:
-    """The stored code record of each vector, uint32 [n][bits][d/32]: the
-    codebook codes' bit planes, then (keys) the plane of z (bit set where
+    """The stored record of each vector, uint32 [n][4 bits]: the codebook
+    codes as packed fields, then (keys) the 128 bits of z (set where
     z = +1)."""
     mb = kq["bits"] - 1 if kq["keys"] else kq["bits"]
-    planes = pack_planes(kq["codes"], mb)
+    rec = pack_fields(kq["codes"], mb)
     if kq["keys"]:
-        planes = np.concatenate([planes, pack_planes((kq["z"] > 0).astype(np.int64), 1)], axis=1)
-    return planes
+        rec = np.concatenate([rec, pack_fields((kq["z"] > 0).astype(np.int64), 1)], axis=1)
+    return rec
 
 
 def stored_bits(bits: int, keys: bool, d: int = D) -> int:

@@ -178,26 +178,36 @@ def test_compression_matches_pages():
     assert a <= fp16 / K.stored_bits(4, True) * 1.07 and fp16 / K.stored_bits(2, True) >= b
 
 
-def test_key_record_planes():
-    """A key record holds the (bits - 1) code planes, then z's plane."""
+def test_key_record_fields():
+    """A key record holds the (bits - 1)-bit codes as packed fields, then z."""
     kq = {"bits": 3, "keys": True, "codes": np.zeros((2, K.D), np.int64), "z": -np.ones((2, K.D), np.int8)}
-    kq["codes"][1, 40] = 3
-    kq["z"][1, 127] = 1
+    kq["codes"][1, 40] = 3                               # bits 80, 81: word 2, bits 16, 17
+    kq["codes"][1, 15] = 2                               # bit 31 of word 0
+    kq["z"][1, 127] = 1                                  # last bit of the record
     rec = K.kv_records(kq)
-    assert rec.shape == (2, 3, 4) and rec.dtype == np.uint32
+    assert rec.shape == (2, 12) and rec.dtype == np.uint32
     assert rec[0].sum() == 0
-    assert rec[1, 0, 1] == 1 << 8 and rec[1, 1, 1] == 1 << 8 and rec[1, 2, 3] == 1 << 31
-    assert rec[1].astype(np.int64).sum() == 2 * (1 << 8) + (1 << 31)
+    assert rec[1, 2] == 3 << 16 and rec[1, 0] == 1 << 31 and rec[1, 11] == 1 << 31
+    assert rec[1].astype(np.int64).sum() == (3 << 16) + 2 * (1 << 31)
     vq = {"bits": 2, "keys": False, "codes": np.full((1, K.D), 2, np.int64)}
-    assert K.kv_records(vq)[0].tolist() == [[0] * 4, [0xFFFFFFFF] * 4]
+    assert K.kv_records(vq)[0].tolist() == [0xAAAAAAAA] * 8
 
 
-def test_bit_planes():
+def test_fields_straddle_words():
+    """3-bit fields cross word boundaries (code 10 spans bits 30..32)."""
     codes = np.zeros((1, K.D), np.int64)
-    codes[0, 33] = 0b101
-    pl = K.pack_planes(codes, 3)
-    assert pl.shape == (1, 3, 4)
-    assert pl[0, 0, 1] == 2 and pl[0, 1, 1] == 0 and pl[0, 2, 1] == 2 and pl.sum() == 4
+    codes[0, 10] = 0b111
+    f = K.pack_fields(codes, 3)
+    assert f.shape == (1, 12)
+    assert f[0, 0] == 0b11 << 30 and f[0, 1] == 1 and f[0].astype(np.int64).sum() == (0b11 << 30) + 1
+    # every code recovered by reading its bits back
+    rng = np.random.default_rng(3)
+    for nb in (1, 2, 3, 5, 7, 8):
+        c = rng.integers(0, 2 ** nb, size=(4, K.D))
+        f = K.pack_fields(c, nb).astype(np.uint64)
+        bits = ((f[:, :, None] >> np.arange(32, dtype=np.uint64)) & np.uint64(1)).reshape(4, -1)
+        back = sum(bits[:, t::nb].astype(np.int64) << t for t in range(nb))
+        assert np.array_equal(back, c)
 
 
 # --------------------------------------------- planted-mistake checks ---
