@@ -142,6 +142,10 @@ def lloyd_max_gaussian(levels: int, iters: int = 2000):
         c = c + step
         if np.max(np.abs(step)) < 1e-15:
             break
+    # N(0, 1) is symmetric, and so is its quantiser; rounding in the solves
+    # leaves a mismatch near 1e-13, removed here so that 0 sits exactly on
+    # the middle boundary (a zero vector then takes the lower middle level).
+    c = (c - c[::-1]) / 2.0
     b = _cells(c)[0]
     # E[(X - c)^2] over each cell: E[X^2 | cell] - 2 c E[X | cell] + c^2, with
     # E[X^2 1(a<X<b)] = P(a<X<b) + a phi(a) - b phi(b)

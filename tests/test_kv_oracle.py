@@ -37,6 +37,7 @@ def test_lloyd_max_optimality_conditions(levels):
     its two levels (checked by numerical integration, not by the closed
     forms the iteration uses); the distortion matches Monte Carlo."""
     c, b, mse = K.lloyd_max_gaussian(levels)
+    assert np.array_equal(c, -c[::-1]) and b[levels // 2 - 1] == 0.0
     assert np.allclose(b, (c[:-1] + c[1:]) / 2, atol=1e-12)
     edges = np.concatenate([[-12.0], b, [12.0]])
     pts = 200001 if levels <= 16 else 20001
