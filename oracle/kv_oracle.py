@@ -67,14 +67,31 @@ def rotation(signs) -> np.ndarray:
     return hadamard(len(s)) * s[None, :]
 
 
+_PM1: dict = {}
+
+
+def _hadamard_pm1(n: int) -> np.ndarray:
+    """The Sylvester Hadamard matrix with its +-1 entries (unscaled)."""
+    if n not in _PM1:
+        _PM1[n] = hadamard(n) * math.sqrt(n)
+    return _PM1[n]
+
+
 def rotate(x, signs) -> np.ndarray:
-    """Rows of x mapped by Pi: y = Pi x for each row x."""
-    return np.atleast_2d(np.asarray(x, dtype=np.float64)) @ rotation(signs).T
+    """Rows of x mapped by Pi: y = H (sigma * x), summed with the exact +-1
+    entries and scaled by 1/sqrt(d) once, so that a coordinate whose terms
+    cancel exactly (bf16 inputs can) is exactly 0 rather than a rounding
+    residue of the scaled entries."""
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    s = np.asarray(signs, dtype=np.float64)
+    return ((x * s[None, :]) @ _hadamard_pm1(len(s)).T) / math.sqrt(len(s))
 
 
 def unrotate(y, signs) -> np.ndarray:
-    """Rows of y mapped by Pi^T."""
-    return np.atleast_2d(np.asarray(y, dtype=np.float64)) @ rotation(signs)
+    """Rows of y mapped by Pi^T: sigma * (H y), scaled the same way."""
+    y = np.atleast_2d(np.asarray(y, dtype=np.float64))
+    s = np.asarray(signs, dtype=np.float64)
+    return ((y @ _hadamard_pm1(len(s))) / math.sqrt(len(s))) * s[None, :]
 
 
 # --------------------------------------------------------------------------

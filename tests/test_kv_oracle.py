@@ -254,6 +254,7 @@ def test_pins_catch_newton_sign_error(monkeypatch):
 
 
 def test_pins_catch_transposed_rotation(monkeypatch):
-    good = K.rotation
-    _expect_pin_failure(monkeypatch, "rotation", lambda s: good(s).T,
-                        [test_rotation_is_orthogonal_and_random_signs_matter])
+    """Pi^T in place of Pi (the sign flip after the transform, not before)."""
+    def bad(x, s):
+        return (np.atleast_2d(np.asarray(x, np.float64)) @ K._hadamard_pm1(len(s))) / np.sqrt(len(s)) * s
+    _expect_pin_failure(monkeypatch, "rotate", bad, [test_rotation_is_orthogonal_and_random_signs_matter])
