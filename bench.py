@@ -63,7 +63,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-extras", action="store_true", help="only the main metric")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--only-extra", choices=["block_m1", "block_m8", "moe", "prefill_gemm", "variants"],
+    p.add_argument("--only-extra", choices=["block_m1", "block_m8", "moe", "prefill_gemm", "variants", "kv_cache"],
                    help="run one extra workload alone and print its JSON (for profiling)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy (for scaling rocprofv3 byte counters)")
@@ -459,6 +459,70 @@ def extra_gemm(tq, torch, synth, np):
                          "compute": "TQ_FAST_F16: x' as one fp16 part (128 tokens per workgroup), rel-L2 ~3e-4"}}
 
 
+def extra_kv(tq, torch, synth, np):
+    """TurboQuant KV cache at 128K tokens, 8 KV heads, 4 queries per head,
+    3 bits: quantisation of the whole cache (prefill rate), then one decode
+    step's scores and value sums over copies of the cache rotated past the
+    caches (>= 1 GiB).  Algorithmic bytes: every record, radius and gamma
+    once, plus the scores written (scores) or the weights read (values)."""
+    wl = synth.KV_DECODE_128K
+    n, H, G, bits = wl.tokens, wl.heads, wl.queries, wl.bits
+    signs = torch.from_numpy(synth.kv_signs(wl.sign_seed)).cuda()
+    jl = torch.from_numpy(synth.kv_jl(wl.jl_seed)).cuda()
+    lk = torch.from_numpy(tq.tq_kv_codebook(bits - 1)).cuda()
+    lv = torch.from_numpy(tq.tq_kv_codebook(bits)).cuda()
+    rb = tq.tq_kv_record_bytes(bits)
+
+    def cache():
+        return (torch.empty((H * n, rb // 4), dtype=torch.int32, device="cuda"),
+                torch.empty(H * n, dtype=torch.int16, device="cuda"),
+                torch.empty(H * n, dtype=torch.int16, device="cuda"))
+    kx = bf16(torch, synth.kv_vectors(wl.key_seed, H * n, 128, "bf16"))
+    kc = cache()
+    ms_qk = timed(torch, 3, 1, lambda i: tq.tq_kv_quantize(kx, H * n, signs, jl, lk, bits, True, *kc))
+    del kx
+    vx = bf16(torch, synth.kv_vectors(wl.value_seed, H * n, 128, "bf16"))
+    vc = cache()
+    ms_qv = timed(torch, 3, 1, lambda i: tq.tq_kv_quantize(vx, H * n, signs, None, lv, bits, False, vc[0], vc[1]))
+    del vx
+    torch.cuda.synchronize()
+    cache_bytes = H * n * (2 * rb + 6)
+    copies = max(1, -(-ROTATE_BYTES // cache_bytes))
+    sets = [(kc, vc)] + [(tuple(t.clone() for t in kc), tuple(t.clone() for t in vc)) for _ in range(copies - 1)]
+    q = torch.from_numpy(synth.kv_vectors(wl.query_seed, H * G, 128, "f32").raw.astype(np.float32)).cuda()
+    scores = torch.empty((H, G, n), dtype=torch.float32, device="cuda")
+    out = torch.empty((H, G, 128), dtype=torch.float32, device="cuda")
+    ws_s, nb_s = tq.kv_workspace(tq.TQ_KV_OP_SCORES, n, H, G)
+    ws_v, nb_v = tq.kv_workspace(tq.TQ_KV_OP_VALUES, n, H, G)
+
+    def score(i):
+        k = sets[i % copies][0]
+        tq.tq_kv_scores(q, H, G, k[0], k[1], k[2], n, bits, signs, jl, lk, scores, ws_s, nb_s)
+    ms_s = timed(torch, copies, 2, score)
+    p = torch.softmax(scores / float(np.sqrt(128.0)), dim=-1).contiguous()
+
+    def values(i):
+        v = sets[i % copies][1]
+        tq.tq_kv_values(p, H, G, v[0], v[1], n, bits, signs, lv, out, ws_v, nb_v)
+    ms_v = timed(torch, copies, 2, values)
+    ms_sm = timed(torch, 10, 2, lambda i: torch.softmax(scores, dim=-1))
+    b_s = H * n * (rb + 4) + H * G * n * 4
+    b_v = H * n * (rb + 2) + H * G * n * 4
+    row = lambda ms, b: {"us": round(ms * 1e3, 2), "bytes": b, "gb_s": round(b / (ms * 1e-3) / 1e9, 1),
+                         "frac_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    fp16_bytes = 2 * H * n * 128 * 2
+    return {"workload": wl.name, "tokens": n, "kv_heads": H, "queries_per_head": G, "bits": bits,
+            "cache_bytes": cache_bytes, "fp16_cache_bytes": fp16_bytes,
+            "compression_vs_fp16": round(fp16_bytes / cache_bytes, 3), "cache_copies_rotated": copies,
+            "scores": row(ms_s, b_s), "values": row(ms_v, b_v),
+            "softmax_torch_us": round(ms_sm * 1e3, 2),
+            "decode_attention_us": round((ms_s + ms_v + ms_sm) * 1e3, 2),
+            "quantize_keys": {"ms": round(ms_qk, 3), "vectors_per_s": round(H * n / (ms_qk * 1e-3), 1)},
+            "quantize_values": {"ms": round(ms_qv, 3), "vectors_per_s": round(H * n / (ms_qv * 1e-3), 1)},
+            "note": "scores and values each read every record once per query head of a KV head (one "
+                    "workgroup per query); the bytes count them once"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -476,7 +540,7 @@ def main():
 
     if args.only_extra:
         fn = {"block_m1": extra_block_m1, "block_m8": extra_block_m8, "moe": extra_moe,
-              "prefill_gemm": extra_gemm, "variants": extra_variants}[args.only_extra]
+              "prefill_gemm": extra_gemm, "variants": extra_variants, "kv_cache": extra_kv}[args.only_extra]
         print(json.dumps({args.only_extra: fn(tq, torch, synth, np)}), flush=True)
         return
 
@@ -647,7 +711,7 @@ def main():
     if not args.no_extras:
         extras = {}
         for name, fn in (("block_m1", extra_block_m1), ("block_m8", extra_block_m8), ("moe", extra_moe),
-                         ("prefill_gemm", extra_gemm), ("variants", extra_variants)):
+                         ("prefill_gemm", extra_gemm), ("variants", extra_variants), ("kv_cache", extra_kv)):
             log(f"extra: {name} ...")
             try:
                 extras[name] = fn(tq, torch, synth, np)

@@ -350,6 +350,90 @@ size_t tq_workspace_bytes(int op, const tq_weights *w, int m_or_t, int topk);
  * bytes a multiple of 16. */
 int tq_read_bytes(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
+/* ---- KV-cache quantiser (TurboQuant) ----------------------------------- *
+ * A second workload beside the ternary weights: compressing the attention
+ * KV cache ("Mac users can use TurboQuant in oMLX, with Gemma-4-31B" page,
+ * aitntnews, section "What TurboQuant is and what problem it solves"): each
+ * K or V vector is rotated by a random orthogonal matrix and kept in polar
+ * form, a high-precision radius and a quantised direction (PolarQuant); a
+ * 1-bit Johnson-Lindenstrauss projection of the direction's residual (QJL)
+ * removes the bias of key inner products; no per-block scale is stored.
+ * Decoding costs a rotation and table lookups (section "Why these results").
+ * Readings where the page is silent:
+ *   * vectors have TQ_KV_DIM = 128 coordinates; Pi = H diag(sigma), H the
+ *     Sylvester Hadamard of order 128 scaled by 1/sqrt(128), sigma = signs;
+ *   * r = |x| stored as fp16 (one rounding); u = Pi x / r (0 if r = 0);
+ *   * each coordinate of u takes the nearest level of the m-bit codebook
+ *     (tq_kv_codebook, a value on a boundary takes the lower level);
+ *   * keys (bits b): m = b - 1 codebook bits, then z = sign(S e) for the
+ *     residual e = u - u~, S = jl (128 x 128, row-major fp32), sign(0) = +1,
+ *     and gamma = |e| as fp16;
+ *     score(q, k) = r (<Pi q, u~> + gamma sqrt(pi/2)/128 <S Pi q, z>);
+ *   * values (bits b): m = b codebook bits; v^ = r Pi^T u~;
+ *   * record of a vector (16 b bytes, uint32 words): code j in record bits
+ *     m j .. m j + m - 1, little-endian (word w holds bits 32 w .. 32 w + 31),
+ *     then for keys 128 bits with bit j set where z_j = +1.
+ * Arithmetic: quantisation in FP64 (the codes and signs are the ones an FP64
+ * evaluation gives); scores and value sums in FP32. */
+#define TQ_KV_DIM 128
+#define TQ_KV_MAX_BITS 8
+enum { TQ_KV_OP_SCORES = 0, TQ_KV_OP_VALUES = 1 };
+
+/* The 2^bits levels, ascending, of the Lloyd-Max quantiser of N(0, 1/128)
+ * (the distribution of one coordinate of a random unit vector in R^128):
+ * each level is the mean of the values nearest to it.  Host function, no
+ * GPU work; `levels` is host memory of 2^bits doubles.  bits 1..8. Upload
+ * the result for tq_kv_quantize, tq_kv_scores and tq_kv_values (keys use
+ * the bits - 1 codebook).  TQ_EUNSUPPORTED if the solve did not converge. */
+int tq_kv_codebook(int bits, double *levels);
+
+/* Bytes of one record: 16 * bits (0 for bits outside 1..8). */
+size_t tq_kv_record_bytes(int bits);
+
+/* Quantise n vectors x [n][128] (TQ_F32, TQ_BF16 or TQ_F16) as keys
+ * (keys != 0, bits 2..8) or values (bits 1..8).  Vector i is written to
+ * record i * stride (records uint32 [..][4 bits], 16-byte aligned), its
+ * radius to radius[i * stride] and, for keys, gamma to gamma[i * stride]
+ * (fp16 bits).  A stride > 1 writes one token of several heads into a
+ * head-major cache.  signs: 128 floats +-1; jl: 128 x 128 floats (keys
+ * only, NULL for values); levels: the codebook of the code bits (device,
+ * 2^m doubles).  n = 0 is a no-op. */
+int tq_kv_quantize(const void *x, int x_dtype, int64_t n, const float *signs,
+                   const float *jl, const double *levels, int bits, int keys,
+                   int64_t stride, uint32_t *records, uint16_t *radius,
+                   uint16_t *gamma, void *stream);
+
+/* Workspace bytes of tq_kv_scores (op TQ_KV_OP_SCORES) or tq_kv_values
+ * (TQ_KV_OP_VALUES) for n cached vectors per head, `heads` heads and nq
+ * queries per head; SIZE_MAX for an invalid request. */
+size_t tq_kv_workspace(int op, int64_t n, int heads, int nq);
+
+/* Scores of queries against quantised keys: for head h and query j,
+ * scores[h][j][i] = score(q[h][j], key i of head h), the estimator above.
+ * q fp32 [heads][nq][128]; keys records [heads][n][4 bits]; radius, gamma
+ * fp16 bits [heads][n]; scores fp32 [heads][nq][n]; levels the bits - 1
+ * codebook; jl 16-byte aligned.  heads * nq <= 65535.  Two launches (the
+ * rotated query and S Pi q into the workspace, then one lane per key over
+ * table lookups). */
+int tq_kv_scores(const float *q, int heads, int nq, const uint32_t *keys,
+                 const uint16_t *radius, const uint16_t *gamma, int64_t n,
+                 int bits, const float *signs, const float *jl,
+                 const double *levels, float *scores, void *workspace,
+                 size_t ws_bytes, void *stream);
+
+/* Probability-weighted sums of quantised values: for head h and query j,
+ * out[h][j] = sum_i p[h][j][i] v^_i over the n values of head h, with
+ * v^ = r Pi^T u~ (the sum is taken in the rotated frame and rotated back
+ * once).  p fp32 [heads][nq][n] (any weights; softmax of the scores in
+ * attention); values records [heads][n][4 bits]; radius fp16 bits
+ * [heads][n]; out fp32 [heads][nq][128] (8-byte aligned); levels the
+ * bits codebook.  heads * nq <= 65535.  Deterministic: the partial sums
+ * of the key chunks are added in a fixed order. */
+int tq_kv_values(const float *p, int heads, int nq, const uint32_t *values,
+                 const uint16_t *radius, int64_t n, int bits,
+                 const float *signs, const double *levels, float *out,
+                 void *workspace, size_t ws_bytes, void *stream);
+
 /* Static message for a tq_status value. */
 const char *tq_strerror(int status);
 

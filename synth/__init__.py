@@ -195,3 +195,26 @@ def kv_vectors(seed, n: int, d: int = 128, dtype: str = "bf16") -> Activations:
         return Activations(x.astype(np.float64), x, "f32")
     bits = bf16_bits(x)
     return Activations(bf16_to_f32(bits).astype(np.float64), bits, "bf16")
+
+
+@dataclass
+class KVWorkload:
+    """Decode attention over a quantised KV cache: `tokens` cached K and V
+    vectors (d = 128) for each of `heads` KV heads, `queries` query heads per
+    KV head, `bits` bits per coordinate for keys and for values."""
+    name: str
+    tokens: int
+    heads: int
+    queries: int
+    bits: int
+    key_seed: int
+    value_seed: int
+    query_seed: int
+    sign_seed: int
+    jl_seed: int
+
+
+# 128K context at 3 bits (the oMLX/Gemma page's long-context case), 8 KV
+# heads with 4 query heads each.
+KV_DECODE_128K = KVWorkload("kv-decode-128k-h8-g4-3bit", 131072, 8, 4, 3, 6001, 6002, 6003, 6004, 6005)
+KV_SMALL = KVWorkload("kv-small-3000-h2-g3-3bit", 3000, 2, 3, 3, 6101, 6102, 6103, 6104, 6105)

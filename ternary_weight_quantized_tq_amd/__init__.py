@@ -30,6 +30,9 @@ TQ_ACCUMULATE = 2
 TQ_MOE_ONE_LAUNCH = 4
 TQ_FAST_F16 = 8
 TQ_OP_GEMV, TQ_OP_MOE, TQ_OP_GEMM = 0, 1, 2
+TQ_KV_DIM = 128
+TQ_KV_MAX_BITS = 8
+TQ_KV_OP_SCORES, TQ_KV_OP_VALUES = 0, 1
 SIZE_MAX = 2 ** 64 - 1
 
 
@@ -49,6 +52,7 @@ class tq_weights(ctypes.Structure):
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SZ = ctypes.c_size_t
+_I64 = ctypes.c_int64
 _W = ctypes.POINTER(tq_weights)
 _SIGNATURES = {
     "tq_words_per_row": (_SZ, [_I]),
@@ -70,6 +74,12 @@ _SIGNATURES = {
     "tq_gemm": (_I, [_W, _P, _I, _I, _P, ctypes.c_uint, _P, _SZ, _P]),
     "tq_workspace_bytes": (_SZ, [_I, _W, _I, _I]),
     "tq_read_bytes": (_I, [_P, _SZ, _P, _P]),
+    "tq_kv_codebook": (_I, [_I, ctypes.POINTER(ctypes.c_double)]),
+    "tq_kv_record_bytes": (_SZ, [_I]),
+    "tq_kv_quantize": (_I, [_P, _I, _I64, _P, _P, _P, _I, _I, _I64, _P, _P, _P, _P]),
+    "tq_kv_workspace": (_SZ, [_I, _I64, _I, _I]),
+    "tq_kv_scores": (_I, [_P, _I, _I, _P, _P, _P, _I64, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "tq_kv_values": (_I, [_P, _I, _I, _P, _P, _I64, _I, _P, _P, _P, _P, _SZ, _P]),
     "tq_strerror": (ctypes.c_char_p, [_I]),
     "tq_last_error": (ctypes.c_char_p, []),
 }
@@ -240,6 +250,50 @@ def tq_gemm(w, x, m, y, flags=TQ_FWHT_FUSED, workspace=None, ws_bytes=0, stream=
 def tq_read_bytes(src, nbytes, sink, stream=None):
     """Measurement aid: one plain read pass over nbytes of src."""
     return _check("tq_read_bytes", lib().tq_read_bytes(_ptr(src), nbytes, _ptr(sink), _stream(stream)))
+
+
+def tq_kv_codebook(bits) -> "numpy.ndarray":
+    """The 2^bits codebook levels (host float64 array)."""
+    import numpy as np
+    buf = (ctypes.c_double * (1 << TQ_KV_MAX_BITS))()
+    _check("tq_kv_codebook", lib().tq_kv_codebook(bits, buf))
+    return np.array(buf[:1 << bits], dtype=np.float64)
+
+
+def tq_kv_record_bytes(bits) -> int:
+    return lib().tq_kv_record_bytes(bits)
+
+
+def tq_kv_quantize(x, n, signs, jl, levels, bits, keys, records, radius, gamma=None, stride=1, stream=None):
+    return _check("tq_kv_quantize", lib().tq_kv_quantize(
+        _ptr(x), dtype_code(x), n, _ptr(signs), _ptr(jl), _ptr(levels), bits, int(bool(keys)), stride,
+        _ptr(records), _ptr(radius), _ptr(gamma), _stream(stream)))
+
+
+def tq_kv_workspace(op, n, heads, nq) -> int:
+    return lib().tq_kv_workspace(op, n, heads, nq)
+
+
+def tq_kv_scores(q, heads, nq, keys, radius, gamma, n, bits, signs, jl, levels, scores, workspace, ws_bytes,
+                 stream=None):
+    return _check("tq_kv_scores", lib().tq_kv_scores(
+        _ptr(q), heads, nq, _ptr(keys), _ptr(radius), _ptr(gamma), n, bits, _ptr(signs), _ptr(jl), _ptr(levels),
+        _ptr(scores), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def tq_kv_values(p, heads, nq, values, radius, n, bits, signs, levels, out, workspace, ws_bytes, stream=None):
+    return _check("tq_kv_values", lib().tq_kv_values(
+        _ptr(p), heads, nq, _ptr(values), _ptr(radius), n, bits, _ptr(signs), _ptr(levels), _ptr(out),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kv_workspace(op, n, heads, nq, device="cuda"):
+    """Workspace of the size tq_kv_scores / tq_kv_values needs."""
+    import torch
+    nbytes = tq_kv_workspace(op, n, heads, nq)
+    if nbytes == SIZE_MAX:
+        raise TQError("tq_kv_workspace", TQ_EINVAL, "invalid request")
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device), nbytes
 
 
 def tq_workspace_bytes(op, w, m_or_t, topk=0) -> int:

@@ -1,0 +1,662 @@
+// TurboQuant-style KV-cache quantiser: quantise K/V rows of dimension 128,
+// score queries against quantised keys, and take probability-weighted sums
+// of quantised values, all on the packed records.
+//
+// Source: "Mac users can use TurboQuant in oMLX, with Gemma-4-31B" (aitntnews),
+// section "What TurboQuant is and what problem it solves": each KV vector is
+// rotated by a random orthogonal matrix and put in polar form with a
+// high-precision radius (PolarQuant); a 1-bit Johnson-Lindenstrauss
+// projection (QJL) then removes the remaining bias of inner products; the
+// method is data-oblivious (no per-block scale).  Section "Why these
+// results": decoding costs a coordinate rotation and table lookups.
+//
+// Readings where the page is silent: d = 128; rotation Pi = H diag(sigma)
+// (normalised Sylvester Hadamard after random signs); radius r = |x| in fp16;
+// direction u = Pi x / r quantised per coordinate with the Lloyd-Max
+// codebook of N(0, 1/d), nearest level, a tie to the lower level; keys keep
+// bits - 1 codebook bits and z = sign(S e) of the residual e = u - u~ with
+// gamma = |e| in fp16; score = r (<Pi q, u~> + gamma sqrt(pi/2)/d <S Pi q, z>);
+// values keep bits codebook bits, v^ = r Pi^T u~.  A record stores the codes
+// as packed little-endian fields (code j at bits m j .. m j + m - 1), then
+// for keys the 128 bits of z (set where z = +1): 16 bytes per bit of the
+// mode in both cases.
+#include "tq_internal.h"
+
+#include <limits.h>
+
+#include <cmath>
+#include <utility>
+#include <vector>
+
+using namespace tq;
+
+namespace {
+
+constexpr int kD = TQ_KV_DIM;
+constexpr double kInvSqrtD = 0.08838834764831845;  // 1/sqrt(128)
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------ codebook ---
+// The Lloyd-Max levels of N(0, 1) with L = 2^bits levels: each level the
+// mean of its nearest-level cell (Lloyd's and Max's optimality conditions).
+// By symmetry only the positive half y_1 < ... < y_h (h = L/2) is solved:
+// y_j = E[X | a_j < X < b_j] with a_1 = 0, a_j = (y_{j-1} + y_j)/2,
+// b_j = (y_j + y_{j+1})/2 and b_h = infinity, by damped Newton steps from
+// the companding start (levels at the quantiles of N(0, 3), the asymptotic
+// optimum of Panter and Dite).  The Jacobian is tridiagonal: a cell mean m
+// moves by phi(a)(m - a)/P with its lower end a and by phi(b)(b - m)/P with
+// its upper end b, and each end by half of each neighbouring level's step.
+double upper_tail(double x) {
+  if (std::isinf(x)) return x > 0 ? 0.0 : 1.0;
+  return 0.5 * std::erfc(x / std::sqrt(2.0));
+}
+double normal_pdf(double x) { return std::isinf(x) ? 0.0 : std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI); }
+
+// x >= 0 with upper_tail(x) = p, 0 < p <= 1/2, by bisection.
+double upper_tail_inverse(double p) {
+  double lo = 0.0, hi = 40.0;
+  for (int i = 0; i < 200; ++i) {
+    const double mid = 0.5 * (lo + hi);
+    if (upper_tail(mid) > p)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+// Residual f_j = y_j - m_j and the three diagonals of its Jacobian.
+double half_residual(const std::vector<double>& y, std::vector<double>* f, std::vector<double>* sub,
+                     std::vector<double>* dia, std::vector<double>* sup) {
+  const int h = static_cast<int>(y.size());
+  double worst = 0.0;
+  for (int j = 0; j < h; ++j) {
+    const double a = j == 0 ? 0.0 : 0.5 * (y[j - 1] + y[j]);
+    const double b = j == h - 1 ? INFINITY : 0.5 * (y[j] + y[j + 1]);
+    const double p = upper_tail(a) - upper_tail(b);
+    const double m = (normal_pdf(a) - normal_pdf(b)) / p;
+    (*f)[j] = y[j] - m;
+    worst = std::fmax(worst, std::fabs((*f)[j]));
+    if (sub) {
+      const double dma = j == 0 ? 0.0 : normal_pdf(a) * (m - a) / p;
+      const double dmb = j == h - 1 ? 0.0 : normal_pdf(b) * (b - m) / p;
+      (*sub)[j] = -0.5 * dma;
+      (*sup)[j] = -0.5 * dmb;
+      (*dia)[j] = 1.0 - 0.5 * dma - 0.5 * dmb;
+    }
+  }
+  return worst;
+}
+
+bool lloyd_max_half(int h, std::vector<double>* yout) {
+  const int levels = 2 * h;
+  std::vector<double> y(h), f(h), sub(h), dia(h), sup(h), step(h), trial(h), ftrial(h), cp(h), dp(h);
+  for (int j = 0; j < h; ++j) y[j] = std::sqrt(3.0) * upper_tail_inverse(0.5 - (j + 0.5) / levels);
+  double res = half_residual(y, &f, &sub, &dia, &sup);
+  for (int it = 0; it < 200 && res > 1e-15; ++it) {
+    // Thomas algorithm for J step = -f.
+    cp[0] = sup[0] / dia[0];
+    dp[0] = -f[0] / dia[0];
+    for (int j = 1; j < h; ++j) {
+      const double den = dia[j] - sub[j] * cp[j - 1];
+      cp[j] = sup[j] / den;
+      dp[j] = (-f[j] - sub[j] * dp[j - 1]) / den;
+    }
+    step[h - 1] = dp[h - 1];
+    for (int j = h - 2; j >= 0; --j) step[j] = dp[j] - cp[j] * step[j + 1];
+    // Halve the step until the levels stay ordered and positive and the
+    // residual does not grow.
+    double t = 1.0, rt = res;
+    for (int k = 0; k < 60; ++k, t *= 0.5) {
+      bool ordered = true;
+      for (int j = 0; j < h; ++j) {
+        trial[j] = y[j] + t * step[j];
+        if (trial[j] <= (j ? trial[j - 1] : 0.0)) ordered = false;
+      }
+      if (!ordered) continue;
+      rt = half_residual(trial, &ftrial, nullptr, nullptr, nullptr);
+      if (rt <= res || rt < 1e-15) break;
+    }
+    double moved = 0.0;
+    for (int j = 0; j < h; ++j) moved = std::fmax(moved, std::fabs(trial[j] - y[j]));
+    y = trial;
+    res = half_residual(y, &f, &sub, &dia, &sup);
+    if (moved < 1e-16) break;
+  }
+  for (double v : y)
+    if (!std::isfinite(v)) return false;
+  *yout = y;
+  return res < 1e-12;
+}
+
+// ---------------------------------------------------- record fields ---
+// Field of W bits at bit offset O of a record held in registers (O and W
+// compile-time; a field may straddle two words).
+template <int O, int W, int N>
+__device__ __forceinline__ uint32_t field(const uint32_t (&w)[N]) {
+  constexpr int wi = O / 32, sh = O % 32;
+  constexpr uint32_t mask = (1u << W) - 1u;
+  if constexpr (sh + W <= 32) {
+    return (w[wi] >> sh) & mask;
+  } else {
+    return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & mask;
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void load_record(const uint32_t* p, uint32_t (&w)[N]) {
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p) + i);
+    w[4 * i] = v.x;
+    w[4 * i + 1] = v.y;
+    w[4 * i + 2] = v.z;
+    w[4 * i + 3] = v.w;
+  }
+}
+
+__device__ __forceinline__ float half_bits_to_f32(uint16_t b) { return static_cast<float>(__builtin_bit_cast(_Float16, b)); }
+
+// Sum over groups g of tab[g * TE + field g], in group order.
+template <int TE, int IB, int O, int N, int... G>
+__device__ __forceinline__ float lut_sum(const float* tab, const uint32_t (&w)[N], std::integer_sequence<int, G...>) {
+  return (0.0f + ... + tab[G * TE + field<O + IB * G, IB>(w)]);
+}
+
+// acc[C g + t] += wt * level t of the C-tuple that field g selects.
+template <int C, int IB, int G, int N>
+__device__ __forceinline__ void lut_fma_one(const float* tab, const uint32_t (&w)[N], float wt, float (&acc)[kD]) {
+  const uint32_t idx = field<IB * G, IB>(w);
+  if constexpr (C == 2) {
+    const float2 lv = *reinterpret_cast<const float2*>(&tab[2 * idx]);
+    acc[2 * G] = fmaf(wt, lv.x, acc[2 * G]);
+    acc[2 * G + 1] = fmaf(wt, lv.y, acc[2 * G + 1]);
+  } else {
+    acc[G] = fmaf(wt, tab[idx], acc[G]);
+  }
+}
+template <int C, int IB, int N, int... G>
+__device__ __forceinline__ void lut_fma(const float* tab, const uint32_t (&w)[N], float wt, float (&acc)[kD],
+                                        std::integer_sequence<int, G...>) {
+  (lut_fma_one<C, IB, G>(tab, w, wt, acc), ...);
+}
+
+// ------------------------------------------------------------ quantise ---
+// One wavefront per vector, lane l holding coordinates 2l and 2l + 1, all
+// in FP64: radius, sign flip and block-128 transform, direction, nearest
+// level (binary search over the cell boundaries, a value on a boundary to
+// the lower level), and for keys the residual, its norm and z = sign(S e)
+// with S^T staged in LDS.  The workgroup's four wavefronts walk the vectors
+// together so that the barriers around the shared staging are uniform.
+template <bool KEYS>
+__global__ __launch_bounds__(256) void kv_quantize_kernel(const void* __restrict__ x, int x_dtype, long long n,
+                                                          const float* __restrict__ signs,
+                                                          const float* __restrict__ jl,
+                                                          const double* __restrict__ levels, int mb, long long stride,
+                                                          int rec_words, uint32_t* __restrict__ rec,
+                                                          uint16_t* __restrict__ radius,
+                                                          uint16_t* __restrict__ gamma) {
+  __shared__ float st[KEYS ? kD * kD : 1];  // st[k][row] = S[row][k]
+  __shared__ double lv[256];
+  __shared__ double mids[256];
+  __shared__ double ebuf[4][KEYS ? kD : 1];
+  __shared__ uint32_t chunk[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nl = 1 << mb;
+  for (int i = tid; i < nl; i += 256) lv[i] = levels[i];
+  for (int i = tid; i < nl - 1; i += 256) mids[i] = (levels[i] + levels[i + 1]) / 2.0;
+  if constexpr (KEYS) {
+    for (int i = tid; i < kD * kD; i += 256) st[(i % kD) * kD + i / kD] = jl[i];
+  }
+  __syncthreads();
+  const double sg0 = signs[2 * lane], sg1 = signs[2 * lane + 1];
+  const int code_words = 4 * mb;
+  for (long long base = static_cast<long long>(blockIdx.x) * 4; base < n; base += static_cast<long long>(gridDim.x) * 4) {
+    const long long v = base + wv;
+    const bool ok = v < n;
+    double x0 = 0.0, x1 = 0.0;
+    if (ok) {
+      x0 = static_cast<double>(load_act(x, x_dtype, static_cast<size_t>(v) * kD + 2 * lane));
+      x1 = static_cast<double>(load_act(x, x_dtype, static_cast<size_t>(v) * kD + 2 * lane + 1));
+    }
+    double ss = x0 * x0 + x1 * x1;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    const double r = sqrt(ss);
+    double y0 = sg0 * x0, y1 = sg1 * x1;
+    wave_fwht128<double>(y0, y1, lane, kInvSqrtD);
+    const double u0 = r > 0.0 ? y0 / r : 0.0;
+    const double u1 = r > 0.0 ? y1 / r : 0.0;
+    int c0 = 0, c1 = 0;
+    for (int s = nl >> 1; s >= 1; s >>= 1) {
+      if (mids[c0 + s - 1] < u0) c0 += s;
+      if (mids[c1 + s - 1] < u1) c1 += s;
+    }
+    chunk[wv][lane] = static_cast<uint32_t>(c0) | (static_cast<uint32_t>(c1) << mb);
+    double gam = 0.0;
+    if constexpr (KEYS) {
+      const double e0 = u0 - lv[c0], e1 = u1 - lv[c1];
+      ebuf[wv][2 * lane] = e0;
+      ebuf[wv][2 * lane + 1] = e1;
+      double g2 = e0 * e0 + e1 * e1;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) g2 += __shfl_xor(g2, off);
+      gam = sqrt(g2);
+    }
+    __syncthreads();
+    const size_t rbase = static_cast<size_t>(v) * static_cast<size_t>(stride);
+    if constexpr (KEYS) {
+      double sa = 0.0, sb = 0.0;
+      for (int k = 0; k < kD; ++k) {
+        const double e = ebuf[wv][k];
+        sa = fma(static_cast<double>(st[k * kD + lane]), e, sa);
+        sb = fma(static_cast<double>(st[k * kD + lane + 64]), e, sb);
+      }
+      const unsigned long long za = __ballot(sa >= 0.0);
+      const unsigned long long zb = __ballot(sb >= 0.0);
+      const int zi = lane - code_words;
+      if (ok && zi >= 0 && zi < 4) {
+        const unsigned long long zm = zi < 2 ? za : zb;
+        rec[rbase * rec_words + code_words + zi] = static_cast<uint32_t>((zi & 1) ? (zm >> 32) : zm);
+      }
+    }
+    if (ok && lane < code_words) {
+      // Word `lane` of the code fields: bits 32 lane .. 32 lane + 31, from
+      // the 2 mb-bit chunks of the lanes that overlap them.
+      const int cw = 2 * mb;
+      const int l0 = (32 * lane) / cw, l1 = (32 * lane + 31) / cw;
+      uint32_t word = 0;
+      for (int l = l0; l <= l1; ++l) {
+        const uint32_t c = chunk[wv][l];
+        const int off = l * cw - 32 * lane;
+        word |= off >= 0 ? (c << off) : (c >> (-off));
+      }
+      rec[rbase * rec_words + lane] = word;
+    }
+    if (ok && lane == 0) {
+      radius[rbase] = f64_to_f16_rne(r);
+      if constexpr (KEYS) gamma[rbase] = f64_to_f16_rne(gam);
+    }
+    __syncthreads();
+  }
+}
+
+// --------------------------------------------------- score: the query ---
+// One workgroup per query: q' = Pi q (sign flip, block-128 transform) and
+// S q', both FP32, to the workspace as [q' (128) | S q' (128)].  Thread t
+// takes half of row t mod 128 of S (64 contiguous entries, 16-byte loads);
+// the two halves meet in LDS.
+__global__ __launch_bounds__(256) void kv_query_kernel(const float* __restrict__ q, const float* __restrict__ signs,
+                                                       const float* __restrict__ jl, float* __restrict__ qws) {
+  __shared__ float qr[kD];
+  __shared__ float part[kD];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const size_t qi = blockIdx.x;
+  const int row = tid & (kD - 1), half = tid >> 7;
+  // This thread's 64 entries of S, loaded before the transform so that the
+  // two memory latencies overlap.
+  const float4* srow = reinterpret_cast<const float4*>(jl + row * kD + half * 64);
+  float4 sv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sv[i] = srow[i];
+  if (tid < 64) {
+    float y0 = signs[2 * lane] * q[qi * kD + 2 * lane];
+    float y1 = signs[2 * lane + 1] * q[qi * kD + 2 * lane + 1];
+    wave_fwht128<float>(y0, y1, lane, static_cast<float>(kInvSqrtD));
+    qr[2 * lane] = y0;
+    qr[2 * lane + 1] = y1;
+    qws[qi * 256 + 2 * lane] = y0;
+    qws[qi * 256 + 2 * lane + 1] = y1;
+  }
+  __syncthreads();
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float4 v = sv[i];
+    const int k = half * 64 + 4 * i;
+    acc = fmaf(v.x, qr[k], acc);
+    acc = fmaf(v.y, qr[k + 1], acc);
+    acc = fmaf(v.z, qr[k + 2], acc);
+    acc = fmaf(v.w, qr[k + 3], acc);
+  }
+  if (half) part[row] = acc;
+  __syncthreads();
+  if (!half) qws[qi * 256 + kD + row] = acc + part[row];
+}
+
+// Codes per table lookup: as many as fit in 8 index bits (a power of two).
+template <int MB>
+constexpr int codes_per_lookup() {
+  return MB == 1 ? 8 : MB == 2 ? 4 : MB <= 4 ? 2 : 1;
+}
+
+// ----------------------------------------------------- score: the keys ---
+// Lane per key.  Tables in LDS, built once per workgroup from the query:
+// for every group g of C adjacent codes, T_g[i] = sum_t q'_{Cg+t} c[code_t(i)]
+// over the 2^(C mb) concatenations i of C codes, and for every byte of z,
+// Z_g[beta] = sum_t (+-1) (S q')_{8g+t}.  A key's score is then one table
+// read per group plus one per byte of z: r (sum_g T_g + gamma kappa sum_g Z_g)
+// with kappa = sqrt(pi/2)/128.
+template <int MB>
+__global__ __launch_bounds__(256) void kv_scores_kernel(const float* __restrict__ qws, int nq,
+                                                        const uint32_t* __restrict__ keys,
+                                                        const uint16_t* __restrict__ radius,
+                                                        const uint16_t* __restrict__ gamma, long long n,
+                                                        const double* __restrict__ levels, int kpt,
+                                                        float* __restrict__ scores) {
+  constexpr int C = codes_per_lookup<MB>();
+  constexpr int IB = C * MB;
+  constexpr int NG = kD / C;
+  constexpr int TE = 1 << IB;
+  constexpr int RW = 4 * (MB + 1);
+  constexpr float kKappa = 0.0097916731f;  // sqrt(pi/2) / 128
+  __shared__ float tab[NG * TE];
+  __shared__ float ztab[16 * 256];
+  __shared__ float qv[2 * kD];
+  __shared__ float lvf[1 << MB];
+  const int tid = threadIdx.x;
+  const int qi = blockIdx.y;
+  const int head = qi / nq;
+  qv[tid] = qws[static_cast<size_t>(qi) * 256 + tid];
+  if (tid < (1 << MB)) lvf[tid] = static_cast<float>(levels[tid]);
+  __syncthreads();
+  for (int e = tid; e < NG * TE; e += 256) {
+    const int g = e / TE, idx = e % TE;
+    float acc = 0.0f;
+#pragma unroll
+    for (int t = 0; t < C; ++t) acc = fmaf(qv[C * g + t], lvf[(idx >> (MB * t)) & ((1 << MB) - 1)], acc);
+    tab[e] = acc;
+  }
+  for (int e = tid; e < 16 * 256; e += 256) {
+    const int g = e >> 8, beta = e & 255;
+    float acc = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float s = qv[kD + 8 * g + t];
+      acc += ((beta >> t) & 1) ? s : -s;
+    }
+    ztab[e] = acc;
+  }
+  __syncthreads();
+  const size_t hn = static_cast<size_t>(head) * static_cast<size_t>(n);
+  const long long k0 = static_cast<long long>(blockIdx.x) * 256 * kpt + tid;
+  for (int i = 0; i < kpt; ++i) {
+    const long long k = k0 + static_cast<long long>(i) * 256;
+    if (k >= n) break;
+    uint32_t w[RW];
+    load_record(keys + (hn + k) * RW, w);
+    const float mse = lut_sum<TE, IB, 0>(tab, w, std::make_integer_sequence<int, NG>{});
+    const float qjl = lut_sum<256, 8, 128 * MB>(ztab, w, std::make_integer_sequence<int, 16>{});
+    const float r = half_bits_to_f32(radius[hn + k]);
+    const float gm = half_bits_to_f32(gamma[hn + k]);
+    scores[static_cast<size_t>(qi) * static_cast<size_t>(n) + k] = r * fmaf(gm * kKappa, qjl, mse);
+  }
+}
+
+// ------------------------------------------------------------ values ---
+// Lane per value vector; each lane accumulates p_i r_i c[code] into 128
+// registers (a table of C-level tuples turns C adjacent codes into C
+// levels with one LDS read).  The workgroup then reduces its lanes by
+// recursive halving (each exchange hands half of the remaining coordinates
+// to the partner lane, so lane l ends with coordinates 2l, 2l + 1), sums
+// its four wavefronts in LDS and writes one partial vector per key chunk.
+template <int M, int H>
+__device__ __forceinline__ void halve(float (&a)[kD], int lane) {
+  const bool up = (lane & M) != 0;
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const float send = up ? a[i] : a[i + H];
+    const float keep = up ? a[i + H] : a[i];
+    a[i] = keep + lane_xor_f32<M>(send, lane);
+  }
+}
+
+template <int MB>
+__global__ __launch_bounds__(256) void kv_values_kernel(const float* __restrict__ p, int nq,
+                                                        const uint32_t* __restrict__ vals,
+                                                        const uint16_t* __restrict__ radius, long long n,
+                                                        const double* __restrict__ levels, int kpt,
+                                                        float* __restrict__ partial) {
+  constexpr int C = MB <= 4 ? 2 : 1;
+  constexpr int IB = C * MB;
+  constexpr int NG = kD / C;
+  constexpr int TE = 1 << IB;
+  constexpr int RW = 4 * MB;
+  __shared__ __align__(16) float tab[TE * C];
+  __shared__ float red[4][kD];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int qi = blockIdx.y;
+  const int head = qi / nq;
+  for (int e = tid; e < TE; e += 256) {
+#pragma unroll
+    for (int t = 0; t < C; ++t) tab[e * C + t] = static_cast<float>(levels[(e >> (MB * t)) & ((1 << MB) - 1)]);
+  }
+  __syncthreads();
+  float acc[kD];
+#pragma unroll
+  for (int j = 0; j < kD; ++j) acc[j] = 0.0f;
+  const size_t hn = static_cast<size_t>(head) * static_cast<size_t>(n);
+  const long long k0 = static_cast<long long>(blockIdx.x) * 256 * kpt + tid;
+  for (int i = 0; i < kpt; ++i) {
+    const long long k = k0 + static_cast<long long>(i) * 256;
+    if (k >= n) break;
+    uint32_t w[RW];
+    load_record(vals + (hn + k) * RW, w);
+    const float wt = p[static_cast<size_t>(qi) * static_cast<size_t>(n) + k] * half_bits_to_f32(radius[hn + k]);
+    lut_fma<C, IB>(tab, w, wt, acc, std::make_integer_sequence<int, NG>{});
+  }
+  halve<32, 64>(acc, lane);
+  halve<16, 32>(acc, lane);
+  halve<8, 16>(acc, lane);
+  halve<4, 8>(acc, lane);
+  halve<2, 4>(acc, lane);
+  halve<1, 2>(acc, lane);
+  red[wv][2 * lane] = acc[0];
+  red[wv][2 * lane + 1] = acc[1];
+  __syncthreads();
+  if (wv == 0) {
+    const float s0 = (red[0][2 * lane] + red[1][2 * lane]) + (red[2][2 * lane] + red[3][2 * lane]);
+    const float s1 = (red[0][2 * lane + 1] + red[1][2 * lane + 1]) + (red[2][2 * lane + 1] + red[3][2 * lane + 1]);
+    float2* out = reinterpret_cast<float2*>(partial + (static_cast<size_t>(qi) * gridDim.x + blockIdx.x) * kD);
+    out[lane] = make_float2(s0, s1);
+  }
+}
+
+// Sum of the chunks' partial vectors, then Pi^T: the block-128 transform
+// (H is symmetric) and the sign flip.  Wavefront w adds chunks w, w + 4,
+// ... into four running sums (four independent loads in flight per step),
+// then wavefront 0 adds the wavefronts' sums: a fixed order, so the result
+// is deterministic.
+__global__ __launch_bounds__(256) void kv_values_finish_kernel(const float* __restrict__ partial, int chunks,
+                                                               const float* __restrict__ signs,
+                                                               float* __restrict__ out) {
+  __shared__ float2 red[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const size_t qi = blockIdx.x;
+  const float2* base = reinterpret_cast<const float2*>(partial + qi * static_cast<size_t>(chunks) * kD) + lane;
+  float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f, d0 = 0.f, d1 = 0.f;
+  int c = wv;
+  for (; c + 12 < chunks; c += 16) {
+    const float2 pa = base[static_cast<size_t>(c) * (kD / 2)];
+    const float2 pb = base[static_cast<size_t>(c + 4) * (kD / 2)];
+    const float2 pc = base[static_cast<size_t>(c + 8) * (kD / 2)];
+    const float2 pd = base[static_cast<size_t>(c + 12) * (kD / 2)];
+    a0 += pa.x, a1 += pa.y, b0 += pb.x, b1 += pb.y, c0 += pc.x, c1 += pc.y, d0 += pd.x, d1 += pd.y;
+  }
+  for (; c < chunks; c += 4) {
+    const float2 pa = base[static_cast<size_t>(c) * (kD / 2)];
+    a0 += pa.x, a1 += pa.y;
+  }
+  red[wv][lane] = make_float2((a0 + b0) + (c0 + d0), (a1 + b1) + (c1 + d1));
+  __syncthreads();
+  if (wv == 0) {
+    float v0 = (red[0][lane].x + red[1][lane].x) + (red[2][lane].x + red[3][lane].x);
+    float v1 = (red[0][lane].y + red[1][lane].y) + (red[2][lane].y + red[3][lane].y);
+    wave_fwht128<float>(v0, v1, lane, static_cast<float>(kInvSqrtD));
+    out[qi * kD + 2 * lane] = signs[2 * lane] * v0;
+    out[qi * kD + 2 * lane + 1] = signs[2 * lane + 1] * v1;
+  }
+}
+
+// --------------------------------------------------------------- plans ---
+// Keys (values) per thread: enough chunks for about 2048 workgroups over
+// all queries, at least 2 (4) keys per thread so that building the tables
+// (reducing the lanes) stays a small part of a workgroup's work.
+int kv_kpt(long long n, long long queries, int lo, int hi) {
+  const long long target = 2048;
+  const long long per_query = (target + queries - 1) / queries;
+  long long kpt = (n + 256 * per_query - 1) / (256 * per_query);
+  if (kpt < lo) kpt = lo;
+  if (kpt > hi) kpt = hi;
+  return static_cast<int>(kpt);
+}
+constexpr int kScoreKptLo = 2, kScoreKptHi = 16;
+constexpr int kValueKptLo = 4, kValueKptHi = 32;
+
+long long kv_chunks(long long n, int kpt) { return (n + 256LL * kpt - 1) / (256LL * kpt); }
+
+bool kv_dtype_ok(int d) { return d == TQ_F32 || d == TQ_BF16 || d == TQ_F16; }
+
+template <int MB>
+void launch_scores(dim3 grid, hipStream_t s, const float* qws, int nq, const uint32_t* keys, const uint16_t* r,
+                   const uint16_t* g, long long n, const double* levels, int kpt, float* scores) {
+  hipLaunchKernelGGL(kv_scores_kernel<MB>, grid, dim3(256), 0, s, qws, nq, keys, r, g, n, levels, kpt, scores);
+}
+
+template <int MB>
+void launch_values(dim3 grid, hipStream_t s, const float* p, int nq, const uint32_t* vals, const uint16_t* r,
+                   long long n, const double* levels, int kpt, float* partial) {
+  hipLaunchKernelGGL(kv_values_kernel<MB>, grid, dim3(256), 0, s, p, nq, vals, r, n, levels, kpt, partial);
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_kv_codebook(int bits, double* levels) {
+  if (!levels || bits < 1 || bits > TQ_KV_MAX_BITS) return TQ_EINVAL;
+  const int h = 1 << (bits - 1);
+  std::vector<double> y;
+  if (!lloyd_max_half(h, &y)) return TQ_EUNSUPPORTED;
+  for (int j = 0; j < h; ++j) {
+    levels[h + j] = y[j] * kInvSqrtD;
+    levels[h - 1 - j] = -y[j] * kInvSqrtD;
+  }
+  return TQ_OK;
+}
+
+size_t tq_kv_record_bytes(int bits) { return bits >= 1 && bits <= TQ_KV_MAX_BITS ? 16u * bits : 0; }
+
+int tq_kv_quantize(const void* x, int x_dtype, int64_t n, const float* signs, const float* jl, const double* levels,
+                   int bits, int keys, int64_t stride, uint32_t* records, uint16_t* radius, uint16_t* gamma,
+                   void* stream) {
+  if (!x || !signs || !levels || !records || !radius) return TQ_EINVAL;
+  if (keys && (!jl || !gamma)) return TQ_EINVAL;
+  if (!kv_dtype_ok(x_dtype)) return TQ_EINVAL;
+  if (bits < (keys ? 2 : 1) || bits > TQ_KV_MAX_BITS) return TQ_EINVAL;
+  if (!tq_aligned(x, tq_act_align(x_dtype)) || !tq_aligned(signs, 4) || !tq_aligned(levels, 8) ||
+      !tq_aligned(records, 16) || !tq_aligned(radius, 2) || (jl && !tq_aligned(jl, 4)) ||
+      (gamma && !tq_aligned(gamma, 2)))
+    return TQ_EINVAL;
+  if (n < 0 || stride < 1) return TQ_ESHAPE;
+  if (n == 0) return TQ_OK;
+  const int mb = keys ? bits - 1 : bits;
+  const long long groups = (n + 3) / 4;
+  const unsigned grid = static_cast<unsigned>(groups < 4096 ? groups : 4096);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int rw = 4 * bits;
+if (keys)
+    hipLaunchKernelGGL(kv_quantize_kernel<true>, dim3(grid), dim3(256), 0, s, x, x_dtype, n, signs, jl, levels, mb,
+                       stride, rw, records, radius, gamma);
+  else
+    hipLaunchKernelGGL(kv_quantize_kernel<false>, dim3(grid), dim3(256), 0, s, x, x_dtype, n, signs, jl, levels, mb,
+                       stride, rw, records, radius, gamma);
+  TQ_LAUNCH_CHECK();
+  return TQ_OK;
+}
+
+size_t tq_kv_workspace(int op, int64_t n, int heads, int nq) {
+  if (n < 0 || heads < 1 || nq < 1) return SIZE_MAX;
+  const long long queries = static_cast<long long>(heads) * nq;
+  if (op == TQ_KV_OP_SCORES) return static_cast<size_t>(queries) * 256 * sizeof(float);
+  if (op == TQ_KV_OP_VALUES) {
+    const long long chunks = kv_chunks(n, kv_kpt(n, queries, kValueKptLo, kValueKptHi));
+    return static_cast<size_t>(queries) * static_cast<size_t>(chunks > 0 ? chunks : 1) * kD * sizeof(float);
+  }
+  return SIZE_MAX;
+}
+
+int tq_kv_scores(const float* q, int heads, int nq, const uint32_t* keys, const uint16_t* radius,
+                 const uint16_t* gamma, int64_t n, int bits, const float* signs, const float* jl,
+                 const double* levels, float* scores, void* workspace, size_t ws_bytes, void* stream) {
+  if (!q || !keys || !radius || !gamma || !signs || !jl || !levels || !scores || !workspace) return TQ_EINVAL;
+  if (bits < 2 || bits > TQ_KV_MAX_BITS) return TQ_EINVAL;
+  if (!tq_aligned(q, 8) || !tq_aligned(keys, 16) || !tq_aligned(radius, 2) || !tq_aligned(gamma, 2) ||
+      !tq_aligned(signs, 4) || !tq_aligned(jl, 16) || !tq_aligned(levels, 8) || !tq_aligned(scores, 4) ||
+      !tq_aligned(workspace, 16))
+    return TQ_EINVAL;
+  if (heads < 1 || nq < 1 || n < 0) return TQ_ESHAPE;
+  const long long queries = static_cast<long long>(heads) * nq;
+  if (queries > 65535) return TQ_ESHAPE;
+  if (ws_bytes < tq_kv_workspace(TQ_KV_OP_SCORES, n, heads, nq)) return TQ_ENOSPACE;
+  if (n == 0) return TQ_OK;
+  const int kpt = kv_kpt(n, queries, kScoreKptLo, kScoreKptHi);
+  const long long chunks = kv_chunks(n, kpt);
+  if (chunks > INT_MAX) return TQ_ESHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* qws = static_cast<float*>(workspace);
+  hipLaunchKernelGGL(kv_query_kernel, dim3(static_cast<unsigned>(queries)), dim3(256), 0, s, q, signs, jl, qws);
+  TQ_LAUNCH_CHECK();
+  const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(queries));
+  switch (bits - 1) {
+    case 1: launch_scores<1>(grid, s, qws, nq, keys, radius, gamma, n, levels, kpt, scores); break;
+    case 2: launch_scores<2>(grid, s, qws, nq, keys, radius, gamma, n, levels, kpt, scores); break;
+    case 3: launch_scores<3>(grid, s, qws, nq, keys, radius, gamma, n, levels, kpt, scores); break;
+    case 4: launch_scores<4>(grid, s, qws, nq, keys, radius, gamma, n, levels, kpt, scores); break;
+    case 5: launch_scores<5>(grid, s, qws, nq, keys, radius, gamma, n, levels, kpt, scores); break;
+    case 6: launch_scores<6>(grid, s, qws, nq, keys, radius, gamma, n, levels, kpt, scores); break;
+    default: launch_scores<7>(grid, s, qws, nq, keys, radius, gamma, n, levels, kpt, scores); break;
+  }
+  TQ_LAUNCH_CHECK();
+  return TQ_OK;
+}
+
+int tq_kv_values(const float* p, int heads, int nq, const uint32_t* values, const uint16_t* radius, int64_t n,
+                 int bits, const float* signs, const double* levels, float* out, void* workspace, size_t ws_bytes,
+                 void* stream) {
+  if (!p || !values || !radius || !signs || !levels || !out || !workspace) return TQ_EINVAL;
+  if (bits < 1 || bits > TQ_KV_MAX_BITS) return TQ_EINVAL;
+  if (!tq_aligned(p, 4) || !tq_aligned(values, 16) || !tq_aligned(radius, 2) || !tq_aligned(signs, 4) ||
+      !tq_aligned(levels, 8) || !tq_aligned(out, 8) || !tq_aligned(workspace, 16))
+    return TQ_EINVAL;
+  if (heads < 1 || nq < 1 || n < 0) return TQ_ESHAPE;
+  const long long queries = static_cast<long long>(heads) * nq;
+  if (queries > 65535) return TQ_ESHAPE;
+  if (ws_bytes < tq_kv_workspace(TQ_KV_OP_VALUES, n, heads, nq)) return TQ_ENOSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int kpt = kv_kpt(n, queries, kValueKptLo, kValueKptHi);
+  const long long chunks = kv_chunks(n, kpt);
+  if (chunks > INT_MAX) return TQ_ESHAPE;
+  float* partial = static_cast<float*>(workspace);
+  if (chunks > 0) {
+    const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(queries));
+    switch (bits) {
+      case 1: launch_values<1>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
+      case 2: launch_values<2>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
+      case 3: launch_values<3>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
+      case 4: launch_values<4>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
+      case 5: launch_values<5>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
+      case 6: launch_values<6>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
+      case 7: launch_values<7>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
+      default: launch_values<8>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
+    }
+    TQ_LAUNCH_CHECK();
+  }
+  hipLaunchKernelGGL(kv_values_finish_kernel, dim3(static_cast<unsigned>(queries)), dim3(256), 0, s, partial,
+                     static_cast<int>(chunks), signs, out);
+  TQ_LAUNCH_CHECK();
+  return TQ_OK;
+}
+
+}  // extern "C"

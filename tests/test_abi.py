@@ -203,3 +203,47 @@ def test_moe_rejects_variant_formats():
         st = lib.tq_moe_gemv(tq.ctypes.byref(gu), tq.ctypes.byref(dn), 0x3000, tq.TQ_BF16, 1, 1, 0x4000, 0x5000, 0x6000,
                              tq.TQ_FWHT_FUSED, 0x7000, 1 << 24, None)
         assert st == tq.TQ_EUNSUPPORTED
+
+
+def test_kv_calls_reject_bad_arguments():
+    lib = tq.lib()
+    A = 0x1000  # aligned stand-in address (nothing is launched)
+    q = lambda **kw: lib.tq_kv_quantize(*[kw.get(k, v) for k, v in (
+        ("x", A), ("dt", tq.TQ_BF16), ("n", 4), ("signs", A), ("jl", A), ("levels", A), ("bits", 3), ("keys", 1),
+        ("stride", 1), ("rec", A), ("r", A), ("g", A), ("s", None))])
+    assert q(x=None) == tq.TQ_EINVAL
+    assert q(jl=None) == tq.TQ_EINVAL and q(g=None) == tq.TQ_EINVAL          # keys need S and gamma
+    assert q(dt=tq.TQ_F64) == tq.TQ_EINVAL
+    assert q(bits=1) == tq.TQ_EINVAL and q(bits=9) == tq.TQ_EINVAL           # keys: 2..8
+    assert q(rec=A + 4) == tq.TQ_EINVAL and q(levels=A + 4) == tq.TQ_EINVAL and q(x=A + 2) == tq.TQ_EINVAL
+    assert q(n=-1) == tq.TQ_ESHAPE and q(stride=0) == tq.TQ_ESHAPE
+    assert q(n=0) == tq.TQ_OK                                                  # no-op, nothing launched
+    sc = lambda **kw: lib.tq_kv_scores(*[kw.get(k, v) for k, v in (
+        ("q", A), ("h", 2), ("nq", 2), ("keys", A), ("r", A), ("g", A), ("n", 100), ("bits", 3), ("signs", A),
+        ("jl", A), ("levels", A), ("out", A), ("ws", A), ("wsb", 1 << 20), ("s", None))])
+    assert sc(keys=None) == tq.TQ_EINVAL and sc(bits=1) == tq.TQ_EINVAL and sc(keys=A + 8) == tq.TQ_EINVAL
+    assert sc(h=0) == tq.TQ_ESHAPE and sc(h=300, nq=300) == tq.TQ_ESHAPE
+    assert sc(wsb=tq.tq_kv_workspace(tq.TQ_KV_OP_SCORES, 100, 2, 2) - 1) == tq.TQ_ENOSPACE
+    assert sc(n=0) == tq.TQ_OK
+    va = lambda **kw: lib.tq_kv_values(*[kw.get(k, v) for k, v in (
+        ("p", A), ("h", 2), ("nq", 2), ("vals", A), ("r", A), ("n", 100), ("bits", 3), ("signs", A),
+        ("levels", A), ("out", A), ("ws", A), ("wsb", 1 << 20), ("s", None))])
+    assert va(vals=None) == tq.TQ_EINVAL and va(bits=0) == tq.TQ_EINVAL and va(out=A + 4) == tq.TQ_EINVAL
+    assert va(wsb=tq.tq_kv_workspace(tq.TQ_KV_OP_VALUES, 100, 2, 2) - 1) == tq.TQ_ENOSPACE
+    assert lib.tq_kv_workspace(tq.TQ_KV_OP_SCORES, 10, 0, 1) == tq.SIZE_MAX
+    assert lib.tq_kv_workspace(7, 10, 1, 1) == tq.SIZE_MAX
+    assert [tq.tq_kv_record_bytes(b) for b in (0, 1, 3, 8, 9)] == [0, 16, 48, 128, 0]
+    buf = (ctypes.c_double * 512)()
+    assert lib.tq_kv_codebook(0, buf) == tq.TQ_EINVAL and lib.tq_kv_codebook(9, buf) == tq.TQ_EINVAL
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+def test_kv_codebook_matches_oracle(bits):
+    """The library's codebook (its own Newton solve on the positive half) is
+    the oracle's Lloyd-Max fixed point, exactly symmetric."""
+    from oracle import kv_oracle as K
+    got = tq.tq_kv_codebook(bits)
+    want = K.codebook(bits)
+    assert got.shape == want.shape
+    assert abs(got - want).max() <= 1e-12 * abs(want).max()
+    assert (got == -got[::-1]).all() and (got[1:] > got[:-1]).all()
