@@ -666,6 +666,14 @@ def main():
     b.record()
     torch.cuda.synchronize()
     hot_ms = a.elapsed_time(b) / args.steps
+    # The default deterministic path (no TQ_ACCUMULATE): per-slice partials
+    # in a workspace, then the reduction launch in slice order.
+    wss = [tq.workspace(tq.TQ_OP_GEMV, w, 1) for w in base]
+
+    def det_step(i):
+        for j, w in enumerate(sets[i % copies]):
+            tq.tq_gemv(w, xs[j], 1, ys[j], tq.TQ_FWHT_FUSED, wss[j][0], wss[j][1])
+    det_ms = timed(torch, args.steps, args.warmup, det_step)
     gbs = step_bytes / (ms * 1e-3) / 1e9
     kern_gbs = sum(lin_bytes) / (sum(mean_us) * 1e-6) / 1e9
     traffic = measured_traffic()
@@ -692,6 +700,9 @@ def main():
         "kernel_us": {l.name: round(u, 3) for l, u in zip(lins, mean_us)},
         "kernel_timing": kernel_timing,
         "isolated_launch_us_p10_p50_p90": spread,
+        "deterministic_step": {"ms_per_step": round(det_ms, 5),
+                               "gb_s": round(step_bytes / (det_ms * 1e-3) / 1e9, 1),
+                               "note": "default flags: partials in a workspace + the in-order reduction launch"},
         "mall_hot_single_copy": {"ms_per_step": round(hot_ms, 5),
                                  "gb_s": round(step_bytes / (hot_ms * 1e-3) / 1e9, 1),
                                  "note": "one weight copy, cache-resident; not the metric"},
