@@ -519,8 +519,8 @@ def extra_kv(tq, torch, synth, np):
             "decode_attention_us": round((ms_s + ms_v + ms_sm) * 1e3, 2),
             "quantize_keys": {"ms": round(ms_qk, 3), "vectors_per_s": round(H * n / (ms_qk * 1e-3), 1)},
             "quantize_values": {"ms": round(ms_qv, 3), "vectors_per_s": round(H * n / (ms_qv * 1e-3), 1)},
-            "note": "scores and values each read every record once per query head of a KV head (one "
-                    "workgroup per query); the bytes count them once"}
+            "note": "a workgroup serves the 4 query heads of a KV head, so each record is fetched once per "
+                    "call; the query launch (scores) and the chunk-sum launch (values) are included"}
 
 
 def main():

@@ -182,6 +182,31 @@ __device__ __forceinline__ void lut_fma(const float* tab, const uint32_t (&w)[N]
   (lut_fma_one<C, IB, G>(tab, w, wt, acc), ...);
 }
 
+// acc[32 q + C g + t] += wt[q] * level t of the C-tuple that field g of w
+// selects (32 codes of one record quarter, GQ queries).
+template <int C, int IB, int GQ, int G, int N, int NV>
+__device__ __forceinline__ void kv_values_g_one(const float* tab, const uint32_t (&w)[N], const float (&wt)[GQ],
+                                                float (&acc)[NV]) {
+  const uint32_t idx = field<IB * G, IB>(w);
+  if constexpr (C == 2) {
+    const float2 lv = *reinterpret_cast<const float2*>(&tab[2 * idx]);
+#pragma unroll
+    for (int q = 0; q < GQ; ++q) {
+      acc[32 * q + 2 * G] = fmaf(wt[q], lv.x, acc[32 * q + 2 * G]);
+      acc[32 * q + 2 * G + 1] = fmaf(wt[q], lv.y, acc[32 * q + 2 * G + 1]);
+    }
+  } else {
+    const float lv = tab[idx];
+#pragma unroll
+    for (int q = 0; q < GQ; ++q) acc[32 * q + G] = fmaf(wt[q], lv, acc[32 * q + G]);
+  }
+}
+template <int C, int IB, int N, int GQ, int NV, int... G>
+__device__ __forceinline__ void kv_values_g_decode(const float* tab, const uint32_t (&w)[N], const float (&wt)[GQ],
+                                                   float (&acc)[NV], std::integer_sequence<int, G...>) {
+  (kv_values_g_one<C, IB, GQ, G>(tab, w, wt, acc), ...);
+}
+
 // ------------------------------------------------------------ quantise ---
 // One wavefront per vector, lane l holding coordinates 2l and 2l + 1, all
 // in FP64: radius, sign flip and block-128 transform, direction, nearest
@@ -332,65 +357,124 @@ constexpr int codes_per_lookup() {
 }
 
 // ----------------------------------------------------- score: the keys ---
-// Lane per key.  Tables in LDS, built once per workgroup from the query:
+// Lane per key; a workgroup serves GQ queries of one KV head (the query
+// heads that share its keys), so each key is fetched and split into its
+// fields once for all of them.  Tables in LDS, built once per workgroup:
 // for every group g of C adjacent codes, T_g[i] = sum_t q'_{Cg+t} c[code_t(i)]
-// over the 2^(C mb) concatenations i of C codes, and for every byte of z,
-// Z_g[beta] = sum_t (+-1) (S q')_{8g+t}.  A key's score is then one table
-// read per group plus one per byte of z: r (sum_g T_g + gamma kappa sum_g Z_g)
-// with kappa = sqrt(pi/2)/128.
-template <int MB>
-__global__ __launch_bounds__(256) void kv_scores_kernel(const float* __restrict__ qws, int nq,
-                                                        const uint32_t* __restrict__ keys,
-                                                        const uint16_t* __restrict__ radius,
-                                                        const uint16_t* __restrict__ gamma, long long n,
-                                                        const double* __restrict__ levels, int kpt,
-                                                        float* __restrict__ scores) {
+// over the 2^(C mb) concatenations i of C codes, and for every ZB bits of
+// z, Z_g[beta] = sum_t (+-1) (S q')_{ZB g + t}; each entry holds the GQ
+// queries' values side by side, so one LDS read serves all of them.  A
+// key's score is one table read per group plus one per ZB bits of z:
+// r (sum_g T_g + gamma kappa sum_g Z_g), kappa = sqrt(pi/2)/128.
+template <int GQ>
+struct QVec;
+template <>
+struct QVec<1> {
+  typedef float T;
+};
+template <>
+struct QVec<2> {
+  typedef float T __attribute__((ext_vector_type(2)));
+};
+template <>
+struct QVec<4> {
+  typedef float T __attribute__((ext_vector_type(4)));
+};
+template <typename V>
+__device__ __forceinline__ V vsplat(float x) {
+  return (V)(x);
+}
+template <int GQ>
+__device__ __forceinline__ float vget(const typename QVec<GQ>::T& v, int i) {
+  if constexpr (GQ == 1) {
+    return v;
+  } else {
+    return v[i];
+  }
+}
+template <typename V, int TE, int IB, int O, int N, int... G>
+__device__ __forceinline__ V lut_sum_v(const V* tab, const uint32_t (&w)[N], std::integer_sequence<int, G...>) {
+  return (vsplat<V>(0.0f) + ... + tab[G * TE + field<O + IB * G, IB>(w)]);
+}
+
+// GQ queries per workgroup: the largest of 4, 2, 1 that divides the query
+// heads per KV head and whose tables fit the LDS.
+template <int MB, int GQ>
+constexpr bool kv_scores_fits() {
+  constexpr int C = codes_per_lookup<MB>();
+  constexpr int ZB = GQ == 1 ? 8 : 4;
+  return static_cast<long>((kD / C) * (1 << (C * MB)) + (kD / ZB) * (1 << ZB) + 2 * kD) * GQ * 4 <= 150 * 1024;
+}
+template <int GQ>
+constexpr int kv_scores_threads() {
+  return GQ == 1 ? 256 : 512;
+}
+
+// q' and S q' of each query come from the workspace, formed once per query
+// by kv_query_kernel.  (Forming them inside every workgroup instead, S read
+// from L2 by each, made this kernel 7 us slower than the launch it saved.)
+template <int MB, int GQ>
+__global__ __launch_bounds__(kv_scores_threads<GQ>()) void kv_scores_kernel(
+    const float* __restrict__ qws, int nq, const uint32_t* __restrict__ keys, const uint16_t* __restrict__ radius,
+    const uint16_t* __restrict__ gamma, long long n, const double* __restrict__ levels, int kpt,
+    float* __restrict__ scores) {
+  typedef typename QVec<GQ>::T V;
+  constexpr int BS = kv_scores_threads<GQ>();
   constexpr int C = codes_per_lookup<MB>();
   constexpr int IB = C * MB;
   constexpr int NG = kD / C;
   constexpr int TE = 1 << IB;
+  constexpr int ZB = GQ == 1 ? 8 : 4;  // bits of z per lookup
+  constexpr int NZ = kD / ZB;
   constexpr int RW = 4 * (MB + 1);
   constexpr float kKappa = 0.0097916731f;  // sqrt(pi/2) / 128
-  __shared__ float tab[NG * TE];
-  __shared__ float ztab[16 * 256];
-  __shared__ float qv[2 * kD];
+  static_assert(kv_scores_fits<MB, GQ>(), "tables exceed the LDS");
+  __shared__ V tab[NG * TE];
+  __shared__ V ztab[NZ << ZB];
+  __shared__ V qv[2 * kD];  // [q' | S q'] of the GQ queries, side by side
   __shared__ float lvf[1 << MB];
   const int tid = threadIdx.x;
-  const int qi = blockIdx.y;
-  const int head = qi / nq;
-  qv[tid] = qws[static_cast<size_t>(qi) * 256 + tid];
+  const int groups_per_head = nq / GQ;
+  const int head = blockIdx.y / groups_per_head;
+  const int q0 = head * nq + (blockIdx.y % groups_per_head) * GQ;  // first query of this workgroup
+  for (int e = tid; e < 2 * kD * GQ; e += BS) {
+    const int k = e % (2 * kD), qq = e / (2 * kD);
+    reinterpret_cast<float*>(qv)[k * GQ + qq] = qws[static_cast<size_t>(q0 + qq) * 256 + k];
+  }
   if (tid < (1 << MB)) lvf[tid] = static_cast<float>(levels[tid]);
   __syncthreads();
-  for (int e = tid; e < NG * TE; e += 256) {
+  for (int e = tid; e < NG * TE; e += BS) {
     const int g = e / TE, idx = e % TE;
-    float acc = 0.0f;
+    V acc = vsplat<V>(0.0f);
 #pragma unroll
-    for (int t = 0; t < C; ++t) acc = fmaf(qv[C * g + t], lvf[(idx >> (MB * t)) & ((1 << MB) - 1)], acc);
+    for (int t = 0; t < C; ++t) acc += qv[C * g + t] * lvf[(idx >> (MB * t)) & ((1 << MB) - 1)];
     tab[e] = acc;
   }
-  for (int e = tid; e < 16 * 256; e += 256) {
-    const int g = e >> 8, beta = e & 255;
-    float acc = 0.0f;
+  for (int e = tid; e < (NZ << ZB); e += BS) {
+    const int g = e >> ZB, beta = e & ((1 << ZB) - 1);
+    V acc = vsplat<V>(0.0f);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float s = qv[kD + 8 * g + t];
+    for (int t = 0; t < ZB; ++t) {
+      const V s = qv[kD + ZB * g + t];
       acc += ((beta >> t) & 1) ? s : -s;
     }
     ztab[e] = acc;
   }
   __syncthreads();
   const size_t hn = static_cast<size_t>(head) * static_cast<size_t>(n);
-  const long long k0 = static_cast<long long>(blockIdx.x) * 256 * kpt + tid;
+  const long long k0 = static_cast<long long>(blockIdx.x) * BS * kpt + tid;
   for (int i = 0; i < kpt; ++i) {
-    const long long k = k0 + static_cast<long long>(i) * 256;
+    const long long k = k0 + static_cast<long long>(i) * BS;
     if (k >= n) break;
     uint32_t w[RW];
     load_record(keys + (hn + k) * RW, w);
-    const float mse = lut_sum<TE, IB, 0>(tab, w, std::make_integer_sequence<int, NG>{});
-    const float qjl = lut_sum<256, 8, 128 * MB>(ztab, w, std::make_integer_sequence<int, 16>{});
+    const V mse = lut_sum_v<V, TE, IB, 0>(tab, w, std::make_integer_sequence<int, NG>{});
+    const V qjl = lut_sum_v<V, 1 << ZB, ZB, 128 * MB>(ztab, w, std::make_integer_sequence<int, NZ>{});
     const float r = half_bits_to_f32(radius[hn + k]);
-    const float gm = half_bits_to_f32(gamma[hn + k]);
-    scores[static_cast<size_t>(qi) * static_cast<size_t>(n) + k] = r * fmaf(gm * kKappa, qjl, mse);
+    const float gk = half_bits_to_f32(gamma[hn + k]) * kKappa;
+    const V sc = r * (mse + gk * qjl);
+#pragma unroll
+    for (int qq = 0; qq < GQ; ++qq) scores[static_cast<size_t>(q0 + qq) * static_cast<size_t>(n) + k] = vget<GQ>(sc, qq);
   }
 }
 
@@ -401,8 +485,8 @@ __global__ __launch_bounds__(256) void kv_scores_kernel(const float* __restrict_
 // recursive halving (each exchange hands half of the remaining coordinates
 // to the partner lane, so lane l ends with coordinates 2l, 2l + 1), sums
 // its four wavefronts in LDS and writes one partial vector per key chunk.
-template <int M, int H>
-__device__ __forceinline__ void halve(float (&a)[kD], int lane) {
+template <int M, int H, int N>
+__device__ __forceinline__ void halve(float (&a)[N], int lane) {
   const bool up = (lane & M) != 0;
 #pragma unroll
   for (int i = 0; i < H; ++i) {
@@ -463,36 +547,109 @@ __global__ __launch_bounds__(256) void kv_values_kernel(const float* __restrict_
   }
 }
 
+// GQ queries per workgroup (the query heads of one KV head): four lanes per
+// value, lane part p taking coordinates 32 p .. 32 p + 31 (its m words of
+// the record) for all GQ queries, 32 GQ running sums.  Each value is
+// fetched and split once for all GQ queries.  The wavefront's lanes of one
+// part are reduced by recursive halving over lane strides 32, 16, 8, 4
+// (lane l then holds entries f = (GQ 32 / 16)(l / 4) + i of the flattened
+// [query][coordinate] sums of part l % 4), the four wavefronts in LDS.
+template <int MB, int GQ>
+__global__ __launch_bounds__(256) void kv_values_g_kernel(const float* __restrict__ p, int nq,
+                                                          const uint32_t* __restrict__ vals,
+                                                          const uint16_t* __restrict__ radius, long long n,
+                                                          const double* __restrict__ levels, int kpt,
+                                                          float* __restrict__ partial) {
+  constexpr int C = MB <= 4 ? 2 : 1;
+  constexpr int IB = C * MB;
+  constexpr int TE = 1 << IB;
+  constexpr int RW = 4 * MB;   // record words
+  constexpr int PW = MB;       // words of one quarter (32 codes)
+  constexpr int NV = 32 * GQ;  // running sums per lane
+  constexpr int FIN = NV / 16;  // sums per lane after the halving
+  __shared__ __align__(16) float tab[TE * C];
+  __shared__ float red[4][GQ][kD];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, part = tid & 3;
+  const int groups_per_head = nq / GQ;
+  const int head = blockIdx.y / groups_per_head;
+  const int q0 = head * nq + (blockIdx.y % groups_per_head) * GQ;
+  for (int e = tid; e < TE; e += 256) {
+#pragma unroll
+    for (int t = 0; t < C; ++t) tab[e * C + t] = static_cast<float>(levels[(e >> (MB * t)) & ((1 << MB) - 1)]);
+  }
+  __syncthreads();
+  float acc[NV];
+#pragma unroll
+  for (int f = 0; f < NV; ++f) acc[f] = 0.0f;
+  const size_t hn = static_cast<size_t>(head) * static_cast<size_t>(n);
+  const long long k0 = static_cast<long long>(blockIdx.x) * 64 * kpt + (tid >> 2);
+  for (int i = 0; i < kpt; ++i) {
+    const long long k = k0 + static_cast<long long>(i) * 64;
+    if (k >= n) break;
+    uint32_t w[PW];
+    const uint32_t* rp = vals + (hn + k) * RW + PW * part;
+#pragma unroll
+    for (int x = 0; x < PW; ++x) w[x] = __builtin_nontemporal_load(rp + x);
+    const float r = half_bits_to_f32(radius[hn + k]);
+    float wt[GQ];
+#pragma unroll
+    for (int qq = 0; qq < GQ; ++qq) wt[qq] = p[static_cast<size_t>(q0 + qq) * static_cast<size_t>(n) + k] * r;
+    kv_values_g_decode<C, IB>(tab, w, wt, acc, std::make_integer_sequence<int, 32 / C>{});
+  }
+  halve<32, NV / 2>(acc, lane);
+  halve<16, NV / 4>(acc, lane);
+  halve<8, NV / 8>(acc, lane);
+  halve<4, NV / 16>(acc, lane);
+#pragma unroll
+  for (int x = 0; x < FIN; ++x) {
+    const int f = FIN * (lane >> 2) + x;
+    red[wv][f >> 5][32 * part + (f & 31)] = acc[x];
+  }
+  __syncthreads();
+  for (int o = tid; o < GQ * kD; o += 256) {
+    const int qq = o / kD, c = o % kD;
+    const float v = (red[0][qq][c] + red[1][qq][c]) + (red[2][qq][c] + red[3][qq][c]);
+    partial[(static_cast<size_t>(q0 + qq) * gridDim.x + blockIdx.x) * kD + c] = v;
+  }
+}
+
 // Sum of the chunks' partial vectors, then Pi^T: the block-128 transform
-// (H is symmetric) and the sign flip.  Wavefront w adds chunks w, w + 4,
-// ... into four running sums (four independent loads in flight per step),
-// then wavefront 0 adds the wavefronts' sums: a fixed order, so the result
-// is deterministic.
-__global__ __launch_bounds__(256) void kv_values_finish_kernel(const float* __restrict__ partial, int chunks,
-                                                               const float* __restrict__ signs,
-                                                               float* __restrict__ out) {
-  __shared__ float2 red[4][64];
+// (H is symmetric) and the sign flip.  Wavefront w of 16 adds chunks w,
+// w + 16, ... into four running sums (four independent loads in flight per
+// step), then wavefront 0 adds the wavefronts' sums in order: a fixed order,
+// so the result is deterministic.
+constexpr int kFinishWaves = 16;
+__global__ __launch_bounds__(kFinishWaves * 64) void kv_values_finish_kernel(const float* __restrict__ partial,
+                                                                            int chunks,
+                                                                            const float* __restrict__ signs,
+                                                                            float* __restrict__ out) {
+  __shared__ float2 red[kFinishWaves][64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const size_t qi = blockIdx.x;
   const float2* base = reinterpret_cast<const float2*>(partial + qi * static_cast<size_t>(chunks) * kD) + lane;
+  constexpr int W = kFinishWaves;
   float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f, d0 = 0.f, d1 = 0.f;
   int c = wv;
-  for (; c + 12 < chunks; c += 16) {
+  for (; c + 3 * W < chunks; c += 4 * W) {
     const float2 pa = base[static_cast<size_t>(c) * (kD / 2)];
-    const float2 pb = base[static_cast<size_t>(c + 4) * (kD / 2)];
-    const float2 pc = base[static_cast<size_t>(c + 8) * (kD / 2)];
-    const float2 pd = base[static_cast<size_t>(c + 12) * (kD / 2)];
+    const float2 pb = base[static_cast<size_t>(c + W) * (kD / 2)];
+    const float2 pc = base[static_cast<size_t>(c + 2 * W) * (kD / 2)];
+    const float2 pd = base[static_cast<size_t>(c + 3 * W) * (kD / 2)];
     a0 += pa.x, a1 += pa.y, b0 += pb.x, b1 += pb.y, c0 += pc.x, c1 += pc.y, d0 += pd.x, d1 += pd.y;
   }
-  for (; c < chunks; c += 4) {
+  for (; c < chunks; c += W) {
     const float2 pa = base[static_cast<size_t>(c) * (kD / 2)];
     a0 += pa.x, a1 += pa.y;
   }
   red[wv][lane] = make_float2((a0 + b0) + (c0 + d0), (a1 + b1) + (c1 + d1));
   __syncthreads();
   if (wv == 0) {
-    float v0 = (red[0][lane].x + red[1][lane].x) + (red[2][lane].x + red[3][lane].x);
-    float v1 = (red[0][lane].y + red[1][lane].y) + (red[2][lane].y + red[3][lane].y);
+    float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      v0 += red[w][lane].x;
+      v1 += red[w][lane].y;
+    }
     wave_fwht128<float>(v0, v1, lane, static_cast<float>(kInvSqrtD));
     out[qi * kD + 2 * lane] = signs[2 * lane] * v0;
     out[qi * kD + 2 * lane + 1] = signs[2 * lane + 1] * v1;
@@ -503,10 +660,9 @@ __global__ __launch_bounds__(256) void kv_values_finish_kernel(const float* __re
 // Keys (values) per thread: enough chunks for about 2048 workgroups over
 // all queries, at least 2 (4) keys per thread so that building the tables
 // (reducing the lanes) stays a small part of a workgroup's work.
-int kv_kpt(long long n, long long queries, int lo, int hi) {
-  const long long target = 2048;
-  const long long per_query = (target + queries - 1) / queries;
-  long long kpt = (n + 256 * per_query - 1) / (256 * per_query);
+int kv_kpt(long long n, long long rows, int lo, int hi, int bs = 256, long long target = 2048) {
+  const long long per_row = (target + rows - 1) / rows;
+  long long kpt = (n + bs * per_row - 1) / (bs * per_row);
   if (kpt < lo) kpt = lo;
   if (kpt > hi) kpt = hi;
   return static_cast<int>(kpt);
@@ -514,20 +670,71 @@ int kv_kpt(long long n, long long queries, int lo, int hi) {
 constexpr int kScoreKptLo = 2, kScoreKptHi = 16;
 constexpr int kValueKptLo = 4, kValueKptHi = 32;
 
-long long kv_chunks(long long n, int kpt) { return (n + 256LL * kpt - 1) / (256LL * kpt); }
+long long kv_chunks(long long n, int kpt, int bs = 256) { return (n + static_cast<long long>(bs) * kpt - 1) / (static_cast<long long>(bs) * kpt); }
 
 bool kv_dtype_ok(int d) { return d == TQ_F32 || d == TQ_BF16 || d == TQ_F16; }
 
+// Scores: GQ queries per workgroup (see kv_scores_kernel); the grid is
+// (key chunks, heads * nq / GQ), one workgroup per CU when GQ > 1, so a
+// workgroup then takes at least four keys per thread.
+template <int MB, int GQ>
+int launch_scores_g(long long queries, int nq, hipStream_t s, const float* qws, const uint32_t* keys,
+                    const uint16_t* r, const uint16_t* g, long long n, const double* levels, float* scores) {
+  constexpr int BS = kv_scores_threads<GQ>();
+  const long long rows = queries / GQ;
+  const int kpt = kv_kpt(n, rows, GQ == 1 ? kScoreKptLo : 4, kScoreKptHi, BS, GQ == 1 ? 2048 : 256);
+  const long long chunks = kv_chunks(n, kpt, BS);
+  if (chunks > INT_MAX) return TQ_ESHAPE;
+  hipLaunchKernelGGL((kv_scores_kernel<MB, GQ>), dim3(static_cast<unsigned>(chunks), static_cast<unsigned>(rows)),
+                     dim3(BS), 0, s, qws, nq, keys, r, g, n, levels, kpt, scores);
+  return TQ_OK;
+}
 template <int MB>
-void launch_scores(dim3 grid, hipStream_t s, const float* qws, int nq, const uint32_t* keys, const uint16_t* r,
-                   const uint16_t* g, long long n, const double* levels, int kpt, float* scores) {
-  hipLaunchKernelGGL(kv_scores_kernel<MB>, grid, dim3(256), 0, s, qws, nq, keys, r, g, n, levels, kpt, scores);
+int launch_scores(long long queries, int nq, hipStream_t s, const float* qws, const uint32_t* keys,
+                  const uint16_t* r, const uint16_t* g, long long n, const double* levels, float* scores) {
+  if constexpr (kv_scores_fits<MB, 4>()) {
+    if (nq % 4 == 0) return launch_scores_g<MB, 4>(queries, nq, s, qws, keys, r, g, n, levels, scores);
+  }
+  if (nq % 2 == 0) return launch_scores_g<MB, 2>(queries, nq, s, qws, keys, r, g, n, levels, scores);
+  return launch_scores_g<MB, 1>(queries, nq, s, qws, keys, r, g, n, levels, scores);
+}
+
+// Value sums: GQ queries per workgroup when the query heads per KV head
+// allow (4, 2, else 1); keys per workgroup 64 kpt (GQ > 1, four lanes per
+// value) or 256 kpt (GQ = 1, a lane per value), chosen for about 512 (GQ > 1:
+// two per CU; a sweep over 192..4096 at 128K tokens had its minimum there)
+// or 2048 workgroups.  The workspace holds one partial vector per (query,
+// key chunk).
+struct ValuesPlan {
+  int gq, kpt;
+  long long chunks;
+};
+ValuesPlan kv_values_plan(long long n, long long queries, int nq) {
+  ValuesPlan v;
+  v.gq = nq % 4 == 0 ? 4 : (nq % 2 == 0 ? 2 : 1);
+  if (v.gq == 1) {
+    v.kpt = kv_kpt(n, queries, kValueKptLo, kValueKptHi);
+    v.chunks = kv_chunks(n, v.kpt);
+  } else {
+    v.kpt = kv_kpt(n, queries / v.gq, 8, 256, 64, 512);
+    v.chunks = kv_chunks(n, v.kpt, 64);
+  }
+  return v;
 }
 
 template <int MB>
-void launch_values(dim3 grid, hipStream_t s, const float* p, int nq, const uint32_t* vals, const uint16_t* r,
-                   long long n, const double* levels, int kpt, float* partial) {
-  hipLaunchKernelGGL(kv_values_kernel<MB>, grid, dim3(256), 0, s, p, nq, vals, r, n, levels, kpt, partial);
+void launch_values(const ValuesPlan& v, long long queries, hipStream_t s, const float* p, int nq,
+                   const uint32_t* vals, const uint16_t* r, long long n, const double* levels, float* partial) {
+  const unsigned gx = static_cast<unsigned>(v.chunks);
+  if (v.gq == 4)
+    hipLaunchKernelGGL((kv_values_g_kernel<MB, 4>), dim3(gx, static_cast<unsigned>(queries / 4)), dim3(256), 0, s, p,
+                       nq, vals, r, n, levels, v.kpt, partial);
+  else if (v.gq == 2)
+    hipLaunchKernelGGL((kv_values_g_kernel<MB, 2>), dim3(gx, static_cast<unsigned>(queries / 2)), dim3(256), 0, s, p,
+                       nq, vals, r, n, levels, v.kpt, partial);
+  else
+    hipLaunchKernelGGL(kv_values_kernel<MB>, dim3(gx, static_cast<unsigned>(queries)), dim3(256), 0, s, p, nq, vals,
+                       r, n, levels, v.kpt, partial);
 }
 
 }  // namespace
@@ -581,7 +788,7 @@ size_t tq_kv_workspace(int op, int64_t n, int heads, int nq) {
   const long long queries = static_cast<long long>(heads) * nq;
   if (op == TQ_KV_OP_SCORES) return static_cast<size_t>(queries) * 256 * sizeof(float);
   if (op == TQ_KV_OP_VALUES) {
-    const long long chunks = kv_chunks(n, kv_kpt(n, queries, kValueKptLo, kValueKptHi));
+    const long long chunks = kv_values_plan(n, queries, nq).chunks;
     return static_cast<size_t>(queries) * static_cast<size_t>(chunks > 0 ? chunks : 1) * kD * sizeof(float);
   }
   return SIZE_MAX;
@@ -601,23 +808,24 @@ int tq_kv_scores(const float* q, int heads, int nq, const uint32_t* keys, const 
   if (queries > 65535) return TQ_ESHAPE;
   if (ws_bytes < tq_kv_workspace(TQ_KV_OP_SCORES, n, heads, nq)) return TQ_ENOSPACE;
   if (n == 0) return TQ_OK;
-  const int kpt = kv_kpt(n, queries, kScoreKptLo, kScoreKptHi);
-  const long long chunks = kv_chunks(n, kpt);
-  if (chunks > INT_MAX) return TQ_ESHAPE;
+  if (n > static_cast<long long>(INT_MAX) * 256) return TQ_ESHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* qws = static_cast<float*>(workspace);
   hipLaunchKernelGGL(kv_query_kernel, dim3(static_cast<unsigned>(queries)), dim3(256), 0, s, q, signs, jl, qws);
   TQ_LAUNCH_CHECK();
-  const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(queries));
+  int st;
+#define TQ_KVS(MB) launch_scores<MB>(queries, nq, s, qws, keys, radius, gamma, n, levels, scores)
   switch (bits - 1) {
-    case 1: launch_scores<1>(grid, s, qws, nq, keys, radius, gamma, n, levels, kpt, scores); break;
-    case 2: launch_scores<2>(grid, s, qws, nq, keys, radius, gamma, n, levels, kpt, scores); break;
-    case 3: launch_scores<3>(grid, s, qws, nq, keys, radius, gamma, n, levels, kpt, scores); break;
-    case 4: launch_scores<4>(grid, s, qws, nq, keys, radius, gamma, n, levels, kpt, scores); break;
-    case 5: launch_scores<5>(grid, s, qws, nq, keys, radius, gamma, n, levels, kpt, scores); break;
-    case 6: launch_scores<6>(grid, s, qws, nq, keys, radius, gamma, n, levels, kpt, scores); break;
-    default: launch_scores<7>(grid, s, qws, nq, keys, radius, gamma, n, levels, kpt, scores); break;
+    case 1: st = TQ_KVS(1); break;
+    case 2: st = TQ_KVS(2); break;
+    case 3: st = TQ_KVS(3); break;
+    case 4: st = TQ_KVS(4); break;
+    case 5: st = TQ_KVS(5); break;
+    case 6: st = TQ_KVS(6); break;
+    default: st = TQ_KVS(7); break;
   }
+#undef TQ_KVS
+  if (st != TQ_OK) return st;
   TQ_LAUNCH_CHECK();
   return TQ_OK;
 }
@@ -635,25 +843,25 @@ int tq_kv_values(const float* p, int heads, int nq, const uint32_t* values, cons
   if (queries > 65535) return TQ_ESHAPE;
   if (ws_bytes < tq_kv_workspace(TQ_KV_OP_VALUES, n, heads, nq)) return TQ_ENOSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int kpt = kv_kpt(n, queries, kValueKptLo, kValueKptHi);
-  const long long chunks = kv_chunks(n, kpt);
+  const ValuesPlan v = kv_values_plan(n, queries, nq);
+  const long long chunks = v.chunks;
   if (chunks > INT_MAX) return TQ_ESHAPE;
   float* partial = static_cast<float*>(workspace);
   if (chunks > 0) {
-    const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(queries));
     switch (bits) {
-      case 1: launch_values<1>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
-      case 2: launch_values<2>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
-      case 3: launch_values<3>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
-      case 4: launch_values<4>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
-      case 5: launch_values<5>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
-      case 6: launch_values<6>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
-      case 7: launch_values<7>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
-      default: launch_values<8>(grid, s, p, nq, values, radius, n, levels, kpt, partial); break;
+      case 1: launch_values<1>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
+      case 2: launch_values<2>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
+      case 3: launch_values<3>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
+      case 4: launch_values<4>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
+      case 5: launch_values<5>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
+      case 6: launch_values<6>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
+      case 7: launch_values<7>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
+      default: launch_values<8>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
     }
     TQ_LAUNCH_CHECK();
   }
-  hipLaunchKernelGGL(kv_values_finish_kernel, dim3(static_cast<unsigned>(queries)), dim3(256), 0, s, partial,
+  hipLaunchKernelGGL(kv_values_finish_kernel, dim3(static_cast<unsigned>(queries)), dim3(kFinishWaves * 64), 0, s,
+                     partial,
                      static_cast<int>(chunks), signs, out);
   TQ_LAUNCH_CHECK();
   return TQ_OK;

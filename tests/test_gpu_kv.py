@@ -148,10 +148,10 @@ def _run_values(p, heads, nq, rec, r, n, bits, sd, lv):
 
 
 @pytest.mark.parametrize("bits", range(2, 9))
-@pytest.mark.parametrize("n", [1, 700])
-def test_scores_parity(bits, n):
-    """Keys quantised by the oracle; scores of 2 heads x 3 queries."""
-    heads, nq = 2, 3
+@pytest.mark.parametrize("heads,nq,n", [(2, 3, 1), (2, 3, 700), (2, 4, 700), (1, 2, 700), (3, 8, 1500), (1, 4, 3)])
+def test_scores_parity(bits, heads, nq, n):
+    """Keys quantised by the oracle; scores of `heads` KV heads x `nq`
+    queries each (query groups of 1, 2 and 4 per workgroup)."""
     signs, jl, sd, jd = _setup()
     stores, kqs = [], []
     for h in range(heads):
@@ -168,10 +168,10 @@ def test_scores_parity(bits, n):
 
 
 @pytest.mark.parametrize("bits", range(1, 9))
-@pytest.mark.parametrize("n", [1, 3000])
-def test_values_parity(bits, n):
-    """Values quantised by the oracle; softmax-like weights, 2 heads x 3 queries."""
-    heads, nq = 2, 3
+@pytest.mark.parametrize("heads,nq,n", [(2, 3, 1), (2, 3, 3000), (2, 4, 3000), (1, 2, 3000), (3, 8, 5000), (1, 4, 3)])
+def test_values_parity(bits, heads, nq, n):
+    """Values quantised by the oracle; softmax-like weights, `heads` KV heads
+    x `nq` queries each (query groups of 1, 2 and 4 per workgroup)."""
     signs, jl, sd, jd = _setup()
     stores, vqs = [], []
     for h in range(heads):
@@ -189,15 +189,16 @@ def test_values_parity(bits, n):
     assert_parity(got.reshape(heads * nq, K.D), want.reshape(heads * nq, K.D), VALUE_REL_L2, VALUE_ROW_MAX)
 
 
-def test_values_of_no_tokens_are_zero():
+@pytest.mark.parametrize("nq", [3, 4])
+def test_values_of_no_tokens_are_zero(nq):
     t = torch()
     signs, jl, sd, jd = _setup()
-    out = t.full((2, 3, K.D), 7.0, dtype=t.float32, device="cuda")
-    ws, nb = tq.kv_workspace(tq.TQ_KV_OP_VALUES, 0, 2, 3)
+    out = t.full((2, nq, K.D), 7.0, dtype=t.float32, device="cuda")
+    ws, nb = tq.kv_workspace(tq.TQ_KV_OP_VALUES, 0, 2, nq)
     rec = t.zeros((1, 12), dtype=t.int32, device="cuda")
     r = t.zeros(1, dtype=t.int16, device="cuda")
     p = t.zeros(1, dtype=t.float32, device="cuda")
-    tq.tq_kv_values(p, 2, 3, rec, r, 0, 3, sd, _levels(3, False), out, ws, nb)
+    tq.tq_kv_values(p, 2, nq, rec, r, 0, 3, sd, _levels(3, False), out, ws, nb)
     t.cuda.synchronize()
     assert not out.cpu().numpy().any()
 
