@@ -49,6 +49,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+VALU_F32_PEAK_TFLOPS = 157.3
 ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_m1_dense27b_traffic.md")
 GEMV_SOURCES = ["ternary_weight_quantized_tq_amd/csrc/tq_gemv.hip", "ternary_weight_quantized_tq_amd/csrc/tq_decode.h",
@@ -331,6 +332,15 @@ def extra_block(tq, torch, synth, np, wl):
     out["separate_linears"] = separate
     out["compute"] = ("LDS partial-sum table, FP32" if m == 1 else
                       "v_mfma_f32_16x16x32_f16 (x' as two fp16 parts in the A rows, fp16 trit codes, FP32 accumulate)")
+    # The block's three floors beside its measured step: HBM (packed bytes at
+    # the peak), the matrix cores (2 M N K flops; M >= 2 issues them twice,
+    # for the hi and lo parts of x', at the dense fp16 peak) and the FP32
+    # vector ALU (the same flops at its peak), in microseconds.
+    flops = 2.0 * m * sum(l.n * l.k for l in wl.linears)
+    out["floors_us"] = {"hbm": round(nbytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+                        "mfma_fp16": round((flops * (2 if m > 1 else 1)) / (MFMA_F16_PEAK_TFLOPS * 1e12) * 1e6, 2),
+                        "valu_fp32": round(flops / (VALU_F32_PEAK_TFLOPS * 1e12) * 1e6, 2),
+                        "measured": round(fused["ms_per_step"] * 1e3, 2)}
     return out
 
 

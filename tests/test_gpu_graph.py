@@ -96,3 +96,39 @@ def test_gemm_in_graph():
     y = th.empty((m, w.n), dtype=th.float32, device="cuda")
     ws, nb = tq.workspace(tq.TQ_OP_GEMM, w, m)
     _replays_match(lambda: tq.tq_gemm(w, x, m, y, tq.TQ_FWHT_FUSED, ws, nb), y)
+
+
+@pytest.mark.parametrize("nq", [3, 4])
+def test_kv_cache_in_graph(nq):
+    """KV quantise, scores and value sums (query groups of 1 and 4 per
+    workgroup), each captured and replayed; all deterministic."""
+    th = torch()
+    heads, n, bits = 2, 3000, 3
+    sd, jd = dev(synth.kv_signs(91)), dev(synth.kv_jl(92))
+    lk, lv = dev(tq.tq_kv_codebook(bits - 1)), dev(tq.tq_kv_codebook(bits))
+    x = act_tensor(synth.kv_vectors(93, heads * n, 128, "bf16"))
+    rec = th.zeros((heads * n, 4 * bits), dtype=th.int32, device="cuda")
+    r = th.zeros(heads * n, dtype=th.int16, device="cuda")
+    g = th.zeros(heads * n, dtype=th.int16, device="cuda")
+    quant = lambda: tq.tq_kv_quantize(x, heads * n, sd, jd, lk, bits, True, rec, r, g)
+    quant()
+    th.cuda.synchronize()
+    ref = (rec.clone(), r.clone(), g.clone())
+    gq = th.cuda.CUDAGraph()
+    with th.cuda.graph(gq):
+        quant()
+    for rep in range(3):
+        for t_ in (rec, r, g):
+            t_.fill_(-1)
+        th.cuda.synchronize()
+        gq.replay()
+        th.cuda.synchronize()
+        assert all(th.equal(a, b) for a, b in zip((rec, r, g), ref)), f"quantise replay {rep}"
+    q = dev(synth.kv_vectors(94, heads * nq, 128, "f32").raw.astype(np.float32))
+    scores = th.empty((heads, nq, n), dtype=th.float32, device="cuda")
+    ws, nb = tq.kv_workspace(tq.TQ_KV_OP_SCORES, n, heads, nq)
+    _replays_match(lambda: tq.tq_kv_scores(q, heads, nq, rec, r, g, n, bits, sd, jd, lk, scores, ws, nb), scores)
+    p = th.softmax(scores, dim=-1).contiguous()
+    out = th.empty((heads, nq, 128), dtype=th.float32, device="cuda")
+    wv, nbv = tq.kv_workspace(tq.TQ_KV_OP_VALUES, n, heads, nq)
+    _replays_match(lambda: tq.tq_kv_values(p, heads, nq, rec, r, n, bits, sd, lv, out, wv, nbv), out)
