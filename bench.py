@@ -277,6 +277,53 @@ def cpu_gemm_rows(O, synth, rows=64):
             "note": "extrapolated linearly from the row subset (the dequantised matrix is rebuilt per call)"}
 
 
+def cpu_moe_t1(O, synth):
+    """The oracle on the single-token MoE layer: route the T = 1 logits,
+    quantise and pack the eight routed experts (untimed), then one timed
+    expert-MLP call, in layer tok/s."""
+    wl = synth.MOE_T1
+    ids, rw = O.route(synth.logits(wl.logit_seed, wl.tokens, wl.experts), wl.topk)
+    gu_w, gu_s, dn_w, dn_s = {}, {}, {}, {}
+    for e in sorted(set(int(v) for v in ids.ravel())):
+        gu64, dn64 = synth.expert_weights(e, wl.hidden, wl.inter)
+        t, s_, _ = O.quantize(gu64)
+        gu_w[e], gu_s[e] = O.pack(t), s_
+        t, s_, _ = O.quantize(dn64)
+        dn_w[e], dn_s[e] = O.pack(t), s_
+    x = synth.activations(wl.x_seed, wl.tokens, wl.hidden, "bf16").values
+    t0 = time.perf_counter()
+    O.moe(x, ids, rw, gu_w, gu_s, dn_w, dn_s, wl.hidden, wl.inter)
+    dt = time.perf_counter() - t0
+    return {"workload": wl.name, "seconds": round(dt, 3), "us_per_layer": round(dt * 1e6, 1),
+            "tok_s": round(wl.tokens / dt, 2)}
+
+
+def cpu_kv_sample(K, synth, tokens=65536):
+    """The KV oracle on a sample of the 128K decode workload: one KV head's
+    first `tokens` keys and values (quantised untimed), its 4 queries'
+    scores and one weighted value sum per query, timed; in (key, query)
+    pairs per second, with the full step (8 heads x 131,072 tokens)
+    extrapolated linearly and flagged."""
+    import numpy as np
+    wl = synth.KV_DECODE_128K
+    signs, jl = synth.kv_signs(wl.sign_seed), synth.kv_jl(wl.jl_seed)
+    kq = K.kv_quantize(synth.kv_vectors(wl.key_seed, tokens, 128, "bf16").values, signs, wl.bits, True, jl)
+    vq = K.kv_quantize(synth.kv_vectors(wl.value_seed, tokens, 128, "bf16").values, signs, wl.bits, False)
+    q = synth.kv_vectors(wl.query_seed, wl.queries, 128, "f32").values
+    t0 = time.perf_counter()
+    for j in range(wl.queries):
+        sc = K.kv_scores(q[j], kq, signs, jl)
+        p = np.exp(sc / np.sqrt(128.0) - (sc / np.sqrt(128.0)).max())
+        K.kv_values(p / p.sum(), vq, signs)
+    dt = time.perf_counter() - t0
+    pairs = tokens * wl.queries
+    return {"workload": wl.name, "tokens_sampled": tokens, "heads_sampled": 1, "seconds": round(dt, 3),
+            "pairs_per_s": round(pairs / dt, 1),
+            "extrapolated_ms_full_step": round(dt * (wl.tokens / tokens) * wl.heads * 1e3, 1),
+            "note": "scores, softmax and value sum of one head's 4 queries; extrapolated linearly to 8 heads "
+                    "x 131,072 tokens"}
+
+
 # --------------------------------------------------------------- extras ---
 def extra_block(tq, torch, synth, np, wl):
     """One dense block's seven linears at wl.m activation rows (1: single
@@ -749,6 +796,16 @@ def main():
                 result["cpu_baseline"]["prefill_gemm_rows"] = cpu_gemm_rows(O, synth)
             except Exception as e:  # report, never hide
                 result["cpu_baseline"]["prefill_gemm_rows"] = {"error": f"{type(e).__name__}: {e}"}
+            log("timing the CPU oracle on the MoE layer (T = 1) and a KV sample ...")
+            try:
+                result["cpu_baseline"]["moe_t1"] = cpu_moe_t1(O, synth)
+            except Exception as e:  # report, never hide
+                result["cpu_baseline"]["moe_t1"] = {"error": f"{type(e).__name__}: {e}"}
+            try:
+                from oracle import kv_oracle as K
+                result["cpu_baseline"]["kv_sample"] = cpu_kv_sample(K, synth)
+            except Exception as e:  # report, never hide
+                result["cpu_baseline"]["kv_sample"] = {"error": f"{type(e).__name__}: {e}"}
     print(json.dumps(result), flush=True)
 
 
