@@ -555,7 +555,7 @@ __global__ __launch_bounds__(256) void kv_values_kernel(const float* __restrict_
 // (lane l then holds entries f = (GQ 32 / 16)(l / 4) + i of the flattened
 // [query][coordinate] sums of part l % 4), the four wavefronts in LDS.
 template <int MB, int GQ>
-__global__ __launch_bounds__(256) void kv_values_g_kernel(const float* __restrict__ p, int nq,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void kv_values_g_kernel(const float* __restrict__ p, int nq,
                                                           const uint32_t* __restrict__ vals,
                                                           const uint16_t* __restrict__ radius, long long n,
                                                           const double* __restrict__ levels, int kpt,
@@ -701,10 +701,10 @@ int launch_scores(long long queries, int nq, hipStream_t s, const float* qws, co
 
 // Value sums: GQ queries per workgroup when the query heads per KV head
 // allow (4, 2, else 1); keys per workgroup 64 kpt (GQ > 1, four lanes per
-// value) or 256 kpt (GQ = 1, a lane per value), chosen for about 512 (GQ > 1:
-// two per CU; a sweep over 192..4096 at 128K tokens had its minimum there)
-// or 2048 workgroups.  The workspace holds one partial vector per (query,
-// key chunk).
+// value) or 256 kpt (GQ = 1, a lane per value), chosen for about 768 (GQ > 1:
+// three per CU of the 256, one round; sweeps over 192..4096 at 128K tokens
+// had their minimum there) or 2048 workgroups.  The workspace holds one
+// partial vector per (query, key chunk).
 struct ValuesPlan {
   int gq, kpt;
   long long chunks;
@@ -716,7 +716,7 @@ ValuesPlan kv_values_plan(long long n, long long queries, int nq) {
     v.kpt = kv_kpt(n, queries, kValueKptLo, kValueKptHi);
     v.chunks = kv_chunks(n, v.kpt);
   } else {
-    v.kpt = kv_kpt(n, queries / v.gq, 8, 256, 64, 512);
+    v.kpt = kv_kpt(n, queries / v.gq, 8, 256, 64, 768);
     v.chunks = kv_chunks(n, v.kpt, 64);
   }
   return v;
