@@ -242,6 +242,14 @@ def kv_values(p, vq, signs) -> np.ndarray:
     return unrotate(acc, signs)[0]
 
 
+def kv_attend(scores, scale: float, vq, signs) -> np.ndarray:
+    """Attention output for one query: p = softmax(scale * scores) over the
+    keys (max subtracted, FP64), then sum_i p_i v^_i (kv_values)."""
+    z = float(scale) * np.asarray(scores, dtype=np.float64).reshape(-1)
+    p = np.exp(z - z.max())
+    return kv_values(p / p.sum(), vq, signs)
+
+
 def kv_dequantize_values(vq, signs) -> np.ndarray:
     d = vq["codes"].shape[1]
     return vq["r"].astype(np.float64)[:, None] * unrotate(codebook(vq["bits"], d)[vq["codes"]], signs)

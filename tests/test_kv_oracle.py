@@ -156,6 +156,24 @@ def test_values_weighted_sum_matches_dequantised():
     assert np.allclose(K.kv_values(p, vq, s), p @ K.kv_dequantize_values(vq, s), atol=1e-12)
 
 
+def test_attend_special_cases():
+    """Equal scores average the dequantised values; one score far above the
+    rest selects its value; the result matches scipy's softmax weights."""
+    import scipy.special
+    rng = np.random.default_rng(14)
+    s = synth.kv_signs(15, K.D)
+    v = rng.normal(size=(50, K.D))
+    vq = K.kv_quantize(v, s, 3, False)
+    vhat = K.kv_dequantize_values(vq, s)
+    assert np.allclose(K.kv_attend(np.full(50, 3.7), 0.1, vq, s), vhat.mean(axis=0), atol=1e-12)
+    sc = rng.normal(size=50)
+    sc[17] = 1e4
+    assert np.allclose(K.kv_attend(sc, 1.0, vq, s), vhat[17], atol=1e-12)
+    sc = rng.normal(size=50) * 30
+    want = scipy.special.softmax(0.25 * sc) @ vhat
+    assert np.allclose(K.kv_attend(sc, 0.25, vq, s), want, atol=1e-12)
+
+
 def test_zero_vector():
     s = synth.kv_signs(12, K.D)
     jl = synth.kv_jl(13, K.D)
