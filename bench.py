@@ -521,7 +521,9 @@ def extra_kv(tq, torch, synth, np):
     3 bits: quantisation of the whole cache (prefill rate), then one decode
     step's scores and value sums over copies of the cache rotated past the
     caches (>= 1 GiB).  Algorithmic bytes: every record, radius and gamma
-    once, plus the scores written (scores) or the weights read (values)."""
+    once, plus the scores written (scores) or the weights read (values);
+    the fused attend (softmax folded into the value sums) reads the scores
+    in place of the weights, the same bytes."""
     wl = synth.KV_DECODE_128K
     n, H, G, bits = wl.tokens, wl.heads, wl.queries, wl.bits
     signs = torch.from_numpy(synth.kv_signs(wl.sign_seed)).cuda()
@@ -563,6 +565,13 @@ def extra_kv(tq, torch, synth, np):
         tq.tq_kv_values(p, H, G, v[0], v[1], n, bits, signs, lv, out, ws_v, nb_v)
     ms_v = timed(torch, copies, 2, values)
     ms_sm = timed(torch, 10, 2, lambda i: torch.softmax(scores, dim=-1))
+    ws_a, nb_a = tq.kv_workspace(tq.TQ_KV_OP_ATTEND, n, H, G)
+    scale = 1.0 / float(np.sqrt(128.0))
+
+    def attend(i):
+        v = sets[i % copies][1]
+        tq.tq_kv_attend(scores, scale, H, G, v[0], v[1], n, bits, signs, lv, out, ws_a, nb_a)
+    ms_a = timed(torch, copies, 2, attend)
     b_s = H * n * (rb + 4) + H * G * n * 4
     b_v = H * n * (rb + 2) + H * G * n * 4
     row = lambda ms, b: {"us": round(ms * 1e3, 2), "bytes": b, "gb_s": round(b / (ms * 1e-3) / 1e9, 1),
@@ -571,13 +580,16 @@ def extra_kv(tq, torch, synth, np):
     return {"workload": wl.name, "tokens": n, "kv_heads": H, "queries_per_head": G, "bits": bits,
             "cache_bytes": cache_bytes, "fp16_cache_bytes": fp16_bytes,
             "compression_vs_fp16": round(fp16_bytes / cache_bytes, 3), "cache_copies_rotated": copies,
-            "scores": row(ms_s, b_s), "values": row(ms_v, b_v),
+            "scores": row(ms_s, b_s), "values": row(ms_v, b_v), "attend": row(ms_a, b_v),
             "softmax_torch_us": round(ms_sm * 1e3, 2),
             "decode_attention_us": round((ms_s + ms_v + ms_sm) * 1e3, 2),
+            "decode_attention_fused_us": round((ms_s + ms_a) * 1e3, 2),
             "quantize_keys": {"ms": round(ms_qk, 3), "vectors_per_s": round(H * n / (ms_qk * 1e-3), 1)},
             "quantize_values": {"ms": round(ms_qv, 3), "vectors_per_s": round(H * n / (ms_qv * 1e-3), 1)},
             "note": "a workgroup serves the 4 query heads of a KV head, so each record is fetched once per "
-                    "call; the query launch (scores) and the chunk-sum launch (values) are included"}
+                    "call; the query launch (scores) and the chunk-sum launch (values, attend) are included; "
+                    "decode_attention_us = scores + torch softmax + values, decode_attention_fused_us = scores + "
+                    "attend"}
 
 
 def main():

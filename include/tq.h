@@ -377,7 +377,7 @@ int tq_read_bytes(const void *src, size_t bytes, uint32_t *sink, void *stream);
  * evaluation gives); scores and value sums in FP32. */
 #define TQ_KV_DIM 128
 #define TQ_KV_MAX_BITS 8
-enum { TQ_KV_OP_SCORES = 0, TQ_KV_OP_VALUES = 1 };
+enum { TQ_KV_OP_SCORES = 0, TQ_KV_OP_VALUES = 1, TQ_KV_OP_ATTEND = 2 };
 
 /* The 2^bits levels, ascending, of the Lloyd-Max quantiser of N(0, 1/128)
  * (the distribution of one coordinate of a random unit vector in R^128):
@@ -403,9 +403,10 @@ int tq_kv_quantize(const void *x, int x_dtype, int64_t n, const float *signs,
                    int64_t stride, uint32_t *records, uint16_t *radius,
                    uint16_t *gamma, void *stream);
 
-/* Workspace bytes of tq_kv_scores (op TQ_KV_OP_SCORES) or tq_kv_values
- * (TQ_KV_OP_VALUES) for n cached vectors per head, `heads` heads and nq
- * queries per head; SIZE_MAX for an invalid request. */
+/* Workspace bytes of tq_kv_scores (op TQ_KV_OP_SCORES), tq_kv_values
+ * (TQ_KV_OP_VALUES) or tq_kv_attend (TQ_KV_OP_ATTEND) for n cached vectors
+ * per head, `heads` heads and nq queries per head; SIZE_MAX for an invalid
+ * request. */
 size_t tq_kv_workspace(int op, int64_t n, int heads, int nq);
 
 /* Scores of queries against quantised keys: for head h and query j,
@@ -433,6 +434,24 @@ int tq_kv_values(const float *p, int heads, int nq, const uint32_t *values,
                  const uint16_t *radius, int64_t n, int bits,
                  const float *signs, const double *levels, float *out,
                  void *workspace, size_t ws_bytes, void *stream);
+
+/* Decode attention over quantised values with the softmax folded in
+ * ("Mac users can use TurboQuant in oMLX, with Gemma-4-31B", the section on
+ * enabling TurboQuant in oMLX: its fused decode kernel; the softmax is the
+ * attention the cache serves, not a step of the quantiser): for head h and
+ * query j, out[h][j] = sum_i w_i v^_i / sum_i w_i with
+ * w_i = exp(scale * scores[h][j][i] - max_i scale * scores[h][j][i]),
+ * v^ as for tq_kv_values.  Equal to tq_kv_values with p the softmax of
+ * scale * scores, without writing p: each key chunk keeps its own maximum
+ * and weight sum and the finishing launch rescales the chunks to the
+ * common maximum (the online-softmax merge).  scores fp32
+ * [heads][nq][n], finite or -inf (masked); scale finite; a query whose
+ * scores are all -inf, and n = 0, give zeros.  Other arguments, layout
+ * and limits as for tq_kv_values; deterministic. */
+int tq_kv_attend(const float *scores, float scale, int heads, int nq,
+                 const uint32_t *values, const uint16_t *radius, int64_t n,
+                 int bits, const float *signs, const double *levels,
+                 float *out, void *workspace, size_t ws_bytes, void *stream);
 
 /* Static message for a tq_status value. */
 const char *tq_strerror(int status);

@@ -32,7 +32,7 @@ TQ_FAST_F16 = 8
 TQ_OP_GEMV, TQ_OP_MOE, TQ_OP_GEMM = 0, 1, 2
 TQ_KV_DIM = 128
 TQ_KV_MAX_BITS = 8
-TQ_KV_OP_SCORES, TQ_KV_OP_VALUES = 0, 1
+TQ_KV_OP_SCORES, TQ_KV_OP_VALUES, TQ_KV_OP_ATTEND = 0, 1, 2
 SIZE_MAX = 2 ** 64 - 1
 
 
@@ -80,6 +80,7 @@ _SIGNATURES = {
     "tq_kv_workspace": (_SZ, [_I, _I64, _I, _I]),
     "tq_kv_scores": (_I, [_P, _I, _I, _P, _P, _P, _I64, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "tq_kv_values": (_I, [_P, _I, _I, _P, _P, _I64, _I, _P, _P, _P, _P, _SZ, _P]),
+    "tq_kv_attend": (_I, [_P, ctypes.c_float, _I, _I, _P, _P, _I64, _I, _P, _P, _P, _P, _SZ, _P]),
     "tq_strerror": (ctypes.c_char_p, [_I]),
     "tq_last_error": (ctypes.c_char_p, []),
 }
@@ -287,8 +288,15 @@ def tq_kv_values(p, heads, nq, values, radius, n, bits, signs, levels, out, work
         _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def tq_kv_attend(scores, scale, heads, nq, values, radius, n, bits, signs, levels, out, workspace, ws_bytes,
+                 stream=None):
+    return _check("tq_kv_attend", lib().tq_kv_attend(
+        _ptr(scores), float(scale), heads, nq, _ptr(values), _ptr(radius), n, bits, _ptr(signs), _ptr(levels),
+        _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def kv_workspace(op, n, heads, nq, device="cuda"):
-    """Workspace of the size tq_kv_scores / tq_kv_values needs."""
+    """Workspace of the size tq_kv_scores / tq_kv_values / tq_kv_attend needs."""
     import torch
     nbytes = tq_kv_workspace(op, n, heads, nq)
     if nbytes == SIZE_MAX:

@@ -496,12 +496,159 @@ __device__ __forceinline__ void halve(float (&a)[N], int lane) {
   }
 }
 
-template <int MB>
+// Softmax form (SM, tq_kv_attend): p holds the scores z = scale * s, and
+// value i is weighed by exp(z_i - o) r_i with a running offset o, one per
+// wavefront and query (a uniform value).  o starts at -inf; whenever a lane
+// meets z > o + kOffsetSlack, o moves up to that z and the wavefront's
+// running sums of the query are scaled by exp(o_old - o_new).  Weights so
+// stay below e^kOffsetSlack (chunk sums far inside FP32 range) and the
+// rescaling is rare: never again once o is within kOffsetSlack of the
+// chunk's maximum.  Each lane also sums its weights (l).  At the end the
+// workgroup scales every wavefront to the largest offset m of its four,
+// and (m, l) per (query, chunk) go beside the partial vectors; the
+// finishing launch rescales the chunks to their common maximum.  The loop
+// ends for a whole wavefront at once, so every lane takes part in the
+// rescaling.
+constexpr float kOffsetSlack = 16.0f;
+
+// The offset the exponentials take: o itself, or 0 while o is -inf (every
+// score so far masked), so that they come out 0 rather than NaN.
+__device__ __forceinline__ float exp_offset(float o) { return o == -INFINITY ? 0.0f : o; }
+
+// Raise the wavefront's offset o until no lane has z > o + kOffsetSlack;
+// returns the factor exp(o_before - o_after) for the running sums (1 when
+// o is unchanged, 0 when it was -inf: nothing has been summed yet).
+// Only lanes with `mine` set take part (the lanes whose z is a score of
+// this query).
+__device__ __forceinline__ float raise_offset(float z, float& o, bool mine = true) {
+  float f = 1.0f;
+  uint64_t need = __builtin_amdgcn_ballot_w64(mine && z > o + kOffsetSlack);
+  while (need) {
+    const float zn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), __builtin_ctzll(need)));
+    f = o == -INFINITY ? 0.0f : f * expf(o - zn);
+    o = zn;
+    need = __builtin_amdgcn_ballot_w64(mine && z > o + kOffsetSlack);
+  }
+  return f;
+}
+
+// The softmax form's weights of one value for GQ queries: x holds the
+// scores s on entry and exp(scale s - o) on return (0 for a lane whose
+// value is past the end, valid false).  The common path has one uniform
+// branch; the rescaling path (rare) raises each query's offset and scales
+// its NA running sums acc[NA qq ..] and weight sum.
+template <int GQ, int NA, int NV>
+__device__ __forceinline__ void softmax_weights(float (&x)[GQ], bool valid, float scale, float (&off)[GQ],
+                                                float (&acc)[NV], float (&l)[GQ]) {
+  bool need = false;
+#pragma unroll
+  for (int qq = 0; qq < GQ; ++qq) {
+    x[qq] = valid ? scale * x[qq] : -INFINITY;
+    need = need || x[qq] > off[qq] + kOffsetSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+    for (int qq = 0; qq < GQ; ++qq) {
+      const float f = raise_offset(x[qq], off[qq]);
+      if (f != 1.0f) {
+#pragma unroll
+        for (int j = 0; j < NA; ++j) acc[NA * qq + j] *= f;
+        l[qq] *= f;
+      }
+    }
+  }
+#pragma unroll
+  for (int qq = 0; qq < GQ; ++qq) {
+    x[qq] = expf(x[qq] - exp_offset(off[qq]));
+    l[qq] += x[qq];
+  }
+}
+
+// The grouped kernel's softmax weights of one value, the work split over
+// the value's four lanes: lane part p loads the score of query p % GQ and
+// takes its exponential (one load and one exponential per lane), then the
+// GQ weights are broadcast across the four lanes.  l is the lane's weight
+// sum of its own query.  The common path has one uniform branch.
+template <int GQ, int NV>
+__device__ __forceinline__ void softmax_weights_quad(float z, bool valid, int part, float scale, float (&off)[GQ],
+                                                     float (&acc)[NV], float& l, float (&wt)[GQ]) {
+  static_assert(GQ == 2 || GQ == 4, "four lanes per value serve 2 or 4 queries");
+  const int mq = part & (GQ - 1);
+  z = valid ? scale * z : -INFINITY;
+  float om = off[0];
+#pragma unroll
+  for (int qq = 1; qq < GQ; ++qq) om = mq == qq ? off[qq] : om;
+  if (__builtin_amdgcn_ballot_w64(z > om + kOffsetSlack)) {
+#pragma unroll
+    for (int qq = 0; qq < GQ; ++qq) {
+      const float f = raise_offset(z, off[qq], mq == qq);
+      if (f != 1.0f) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) acc[32 * qq + j] *= f;
+        l = mq == qq ? l * f : l;
+      }
+    }
+    om = off[0];
+#pragma unroll
+    for (int qq = 1; qq < GQ; ++qq) om = mq == qq ? off[qq] : om;
+  }
+  const float w = expf(z - exp_offset(om));
+  l += w;
+  wt[0] = dpp_f32<0x00>(w);  // quad_perm(0,0,0,0): part 0's weight
+  wt[1] = dpp_f32<0x55>(w);  // quad_perm(1,1,1,1)
+  if constexpr (GQ == 4) {
+    wt[2] = dpp_f32<0xAA>(w);
+    wt[3] = dpp_f32<0xFF>(w);
+  }
+}
+
+// End of the softmax form: the workgroup's offset m = max over its four
+// wavefronts, every wavefront's sums scaled to it, and the weight sums l
+// (lane's l belongs to query lq) added per query over the workgroup into
+// lout.  Lanes S0 apart hold different values (1: one value per lane; 4:
+// the four lanes of a value, whose parts p and p + GQ repeat a query), so
+// the lane sums run over strides S0 .. 32 and lane q < GQ then holds
+// query q's wavefront sum.
+template <int GQ, int NV, int S0>
+__device__ __forceinline__ void softmax_merge(float (&off)[GQ], float (&acc)[NV], float l, int lq, float (&lout)[GQ],
+                                              float (*sbuf)[GQ]) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  constexpr int NA = NV / GQ;
+  if (lane == 0)
+#pragma unroll
+    for (int qq = 0; qq < GQ; ++qq) sbuf[wv][qq] = off[qq];
+  __syncthreads();
+#pragma unroll
+  for (int qq = 0; qq < GQ; ++qq) {
+    const float m = fmaxf(fmaxf(sbuf[0][qq], sbuf[1][qq]), fmaxf(sbuf[2][qq], sbuf[3][qq]));
+    const float f = off[qq] == -INFINITY ? 0.0f : expf(off[qq] - m);
+    if (f != 1.0f) {
+#pragma unroll
+      for (int j = 0; j < NA; ++j) acc[NA * qq + j] *= f;
+      l = lq == qq ? l * f : l;
+    }
+    off[qq] = m;
+  }
+  if constexpr (S0 <= 1) l += lane_xor_f32<1>(l, lane);
+  if constexpr (S0 <= 2) l += lane_xor_f32<2>(l, lane);
+  l += lane_xor_f32<4>(l, lane);
+  l += lane_xor_f32<8>(l, lane);
+  l += lane_xor_f32<16>(l, lane);
+  l += lane_xor_f32<32>(l, lane);
+  __syncthreads();  // every wavefront has read the offsets
+  if (lane < GQ) sbuf[wv][lane] = l;
+  __syncthreads();
+#pragma unroll
+  for (int qq = 0; qq < GQ; ++qq) lout[qq] = (sbuf[0][qq] + sbuf[1][qq]) + (sbuf[2][qq] + sbuf[3][qq]);
+}
+
+template <int MB, bool SM>
 __global__ __launch_bounds__(256) void kv_values_kernel(const float* __restrict__ p, int nq,
                                                         const uint32_t* __restrict__ vals,
                                                         const uint16_t* __restrict__ radius, long long n,
                                                         const double* __restrict__ levels, int kpt,
-                                                        float* __restrict__ partial) {
+                                                        float* __restrict__ partial, float scale,
+                                                        float2* __restrict__ ml) {
   constexpr int C = MB <= 4 ? 2 : 1;
   constexpr int IB = C * MB;
   constexpr int NG = kD / C;
@@ -517,18 +664,34 @@ __global__ __launch_bounds__(256) void kv_values_kernel(const float* __restrict_
     for (int t = 0; t < C; ++t) tab[e * C + t] = static_cast<float>(levels[(e >> (MB * t)) & ((1 << MB) - 1)]);
   }
   __syncthreads();
+  float off[1] = {-INFINITY}, lsum[1] = {0.0f};
   float acc[kD];
 #pragma unroll
   for (int j = 0; j < kD; ++j) acc[j] = 0.0f;
   const size_t hn = static_cast<size_t>(head) * static_cast<size_t>(n);
-  const long long k0 = static_cast<long long>(blockIdx.x) * 256 * kpt + tid;
+  const long long kbeg = static_cast<long long>(blockIdx.x) * 256 * kpt;
+  const long long k0 = kbeg + tid;
   for (int i = 0; i < kpt; ++i) {
-    const long long k = k0 + static_cast<long long>(i) * 256;
-    if (k >= n) break;
+    long long k = k0 + static_cast<long long>(i) * 256;
+    bool valid = true;
+    if constexpr (SM) {
+      if (kbeg + 64 * wv + static_cast<long long>(i) * 256 >= n) break;  // whole wavefront past n
+      valid = k < n;
+      k = valid ? k : n - 1;  // an in-bounds stand-in, weighed 0
+    } else {
+      if (k >= n) break;
+    }
     uint32_t w[RW];
     load_record(vals + (hn + k) * RW, w);
-    const float wt = p[static_cast<size_t>(qi) * static_cast<size_t>(n) + k] * half_bits_to_f32(radius[hn + k]);
-    lut_fma<C, IB>(tab, w, wt, acc, std::make_integer_sequence<int, NG>{});
+    const float r = half_bits_to_f32(radius[hn + k]);
+    float pk[1] = {p[static_cast<size_t>(qi) * static_cast<size_t>(n) + k]};
+    if constexpr (SM) softmax_weights<1, kD>(pk, valid, scale, off, acc, lsum);
+    lut_fma<C, IB>(tab, w, pk[0] * r, acc, std::make_integer_sequence<int, NG>{});
+  }
+  if constexpr (SM) {
+    __shared__ float sml[4][1];
+    softmax_merge<1, kD, 1>(off, acc, lsum[0], 0, lsum, sml);
+    if (tid == 0) ml[static_cast<size_t>(qi) * gridDim.x + blockIdx.x] = make_float2(off[0], lsum[0]);
   }
   halve<32, 64>(acc, lane);
   halve<16, 32>(acc, lane);
@@ -554,12 +717,11 @@ __global__ __launch_bounds__(256) void kv_values_kernel(const float* __restrict_
 // part are reduced by recursive halving over lane strides 32, 16, 8, 4
 // (lane l then holds entries f = (GQ 32 / 16)(l / 4) + i of the flattened
 // [query][coordinate] sums of part l % 4), the four wavefronts in LDS.
-template <int MB, int GQ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void kv_values_g_kernel(const float* __restrict__ p, int nq,
-                                                          const uint32_t* __restrict__ vals,
-                                                          const uint16_t* __restrict__ radius, long long n,
-                                                          const double* __restrict__ levels, int kpt,
-                                                          float* __restrict__ partial) {
+template <int MB, int GQ, bool SM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void kv_values_g_kernel(
+    const float* __restrict__ p, int nq, const uint32_t* __restrict__ vals, const uint16_t* __restrict__ radius,
+    long long n, const double* __restrict__ levels, int kpt, float* __restrict__ partial, float scale,
+    float2* __restrict__ ml) {
   constexpr int C = MB <= 4 ? 2 : 1;
   constexpr int IB = C * MB;
   constexpr int TE = 1 << IB;
@@ -578,23 +740,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     for (int t = 0; t < C; ++t) tab[e * C + t] = static_cast<float>(levels[(e >> (MB * t)) & ((1 << MB) - 1)]);
   }
   __syncthreads();
+  float off[GQ], lsum = 0.0f;
+#pragma unroll
+  for (int qq = 0; qq < GQ; ++qq) off[qq] = -INFINITY;
   float acc[NV];
 #pragma unroll
   for (int f = 0; f < NV; ++f) acc[f] = 0.0f;
   const size_t hn = static_cast<size_t>(head) * static_cast<size_t>(n);
-  const long long k0 = static_cast<long long>(blockIdx.x) * 64 * kpt + (tid >> 2);
+  const long long kbeg = static_cast<long long>(blockIdx.x) * 64 * kpt;
+  const long long k0 = kbeg + (tid >> 2);
   for (int i = 0; i < kpt; ++i) {
-    const long long k = k0 + static_cast<long long>(i) * 64;
-    if (k >= n) break;
+    long long k = k0 + static_cast<long long>(i) * 64;
+    bool valid = true;
+    if constexpr (SM) {
+      if (kbeg + 16 * wv + static_cast<long long>(i) * 64 >= n) break;  // whole wavefront past n
+      valid = k < n;
+      k = valid ? k : n - 1;  // an in-bounds stand-in, weighed 0
+    } else {
+      if (k >= n) break;
+    }
     uint32_t w[PW];
     const uint32_t* rp = vals + (hn + k) * RW + PW * part;
 #pragma unroll
     for (int x = 0; x < PW; ++x) w[x] = __builtin_nontemporal_load(rp + x);
     const float r = half_bits_to_f32(radius[hn + k]);
     float wt[GQ];
+    if constexpr (SM) {
+      const float z = p[static_cast<size_t>(q0 + (part & (GQ - 1))) * static_cast<size_t>(n) + k];
+      softmax_weights_quad<GQ>(z, valid, part, scale, off, acc, lsum, wt);
+    } else {
 #pragma unroll
-    for (int qq = 0; qq < GQ; ++qq) wt[qq] = p[static_cast<size_t>(q0 + qq) * static_cast<size_t>(n) + k] * r;
+      for (int qq = 0; qq < GQ; ++qq) wt[qq] = p[static_cast<size_t>(q0 + qq) * static_cast<size_t>(n) + k];
+    }
+#pragma unroll
+    for (int qq = 0; qq < GQ; ++qq) wt[qq] *= r;
     kv_values_g_decode<C, IB>(tab, w, wt, acc, std::make_integer_sequence<int, 32 / C>{});
+  }
+  if constexpr (SM) {
+    __shared__ float sml[4][GQ];
+    float lq[GQ];
+    softmax_merge<GQ, NV, 4>(off, acc, lsum, part & (GQ - 1), lq, sml);
+    if (tid == 0) {
+#pragma unroll
+      for (int qq = 0; qq < GQ; ++qq)
+        ml[static_cast<size_t>(q0 + qq) * gridDim.x + blockIdx.x] = make_float2(off[qq], lq[qq]);
+    }
   }
   halve<32, NV / 2>(acc, lane);
   halve<16, NV / 4>(acc, lane);
@@ -618,37 +808,77 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 // w + 16, ... into four running sums (four independent loads in flight per
 // step), then wavefront 0 adds the wavefronts' sums in order: a fixed order,
 // so the result is deterministic.
+// With SM, chunk c's partial vector and its l_c are first scaled by
+// exp(m_c - M), M the largest m_c of the query, and the sum divided by the
+// scaled l's sum; no chunks (n = 0) give zeros.
+// exp(m_c - M); a chunk whose scores are all -inf has nothing to add.
+__device__ __forceinline__ float chunk_weight(float mc, float mx) { return mc == -INFINITY ? 0.0f : expf(mc - mx); }
 constexpr int kFinishWaves = 16;
+template <bool SM>
 __global__ __launch_bounds__(kFinishWaves * 64) void kv_values_finish_kernel(const float* __restrict__ partial,
                                                                             int chunks,
                                                                             const float* __restrict__ signs,
-                                                                            float* __restrict__ out) {
-  __shared__ float2 red[kFinishWaves][64];
+                                                                            float* __restrict__ out,
+                                                                            const float2* __restrict__ ml) {
+  constexpr int W = kFinishWaves;
+  __shared__ float2 red[W][64];
+  __shared__ float sm[W];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const size_t qi = blockIdx.x;
   const float2* base = reinterpret_cast<const float2*>(partial + qi * static_cast<size_t>(chunks) * kD) + lane;
-  constexpr int W = kFinishWaves;
-  float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f, d0 = 0.f, d1 = 0.f;
+  const float2* mq = ml + qi * static_cast<size_t>(chunks);
+  float mx = 0.0f;
+  if constexpr (SM) {
+    float v = -INFINITY;
+    for (int c = tid; c < chunks; c += W * 64) v = fmaxf(v, mq[c].x);
+    v = wave_max(v, lane);
+    if (lane == 0) sm[wv] = v;
+    __syncthreads();
+    mx = sm[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) mx = fmaxf(mx, sm[w]);
+  }
+  float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f, l = 0.f;
   int c = wv;
-  for (; c + 3 * W < chunks; c += 4 * W) {
+  for (; c + W < chunks; c += 2 * W) {
     const float2 pa = base[static_cast<size_t>(c) * (kD / 2)];
     const float2 pb = base[static_cast<size_t>(c + W) * (kD / 2)];
-    const float2 pc = base[static_cast<size_t>(c + 2 * W) * (kD / 2)];
-    const float2 pd = base[static_cast<size_t>(c + 3 * W) * (kD / 2)];
-    a0 += pa.x, a1 += pa.y, b0 += pb.x, b1 += pb.y, c0 += pc.x, c1 += pc.y, d0 += pd.x, d1 += pd.y;
+    if constexpr (SM) {
+      const float2 ma = mq[c], mb = mq[c + W];
+      const float ea = chunk_weight(ma.x, mx), eb = chunk_weight(mb.x, mx);
+      a0 = fmaf(ea, pa.x, a0), a1 = fmaf(ea, pa.y, a1), b0 = fmaf(eb, pb.x, b0), b1 = fmaf(eb, pb.y, b1);
+      l = fmaf(ea, ma.y, fmaf(eb, mb.y, l));
+    } else {
+      a0 += pa.x, a1 += pa.y, b0 += pb.x, b1 += pb.y;
+    }
   }
   for (; c < chunks; c += W) {
     const float2 pa = base[static_cast<size_t>(c) * (kD / 2)];
-    a0 += pa.x, a1 += pa.y;
+    if constexpr (SM) {
+      const float2 ma = mq[c];
+      const float ea = chunk_weight(ma.x, mx);
+      a0 = fmaf(ea, pa.x, a0), a1 = fmaf(ea, pa.y, a1);
+      l = fmaf(ea, ma.y, l);
+    } else {
+      a0 += pa.x, a1 += pa.y;
+    }
   }
-  red[wv][lane] = make_float2((a0 + b0) + (c0 + d0), (a1 + b1) + (c1 + d1));
+  if constexpr (SM) __syncthreads();  // sm is reused for the l sums
+  red[wv][lane] = make_float2(a0 + b0, a1 + b1);
+  if (SM && lane == 0) sm[wv] = l;  // every lane of a wavefront holds the same l
   __syncthreads();
   if (wv == 0) {
-    float v0 = 0.0f, v1 = 0.0f;
+    float v0 = 0.0f, v1 = 0.0f, lt = 0.0f;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       v0 += red[w][lane].x;
       v1 += red[w][lane].y;
+      if constexpr (SM) lt += sm[w];
+    }
+    if constexpr (SM) {
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+      v0 *= inv;
+      v1 *= inv;
     }
     wave_fwht128<float>(v0, v1, lane, static_cast<float>(kInvSqrtD));
     out[qi * kD + 2 * lane] = signs[2 * lane] * v0;
@@ -722,19 +952,20 @@ ValuesPlan kv_values_plan(long long n, long long queries, int nq) {
   return v;
 }
 
-template <int MB>
+template <int MB, bool SM>
 void launch_values(const ValuesPlan& v, long long queries, hipStream_t s, const float* p, int nq,
-                   const uint32_t* vals, const uint16_t* r, long long n, const double* levels, float* partial) {
+                   const uint32_t* vals, const uint16_t* r, long long n, const double* levels, float* partial,
+                   float scale, float2* ml) {
   const unsigned gx = static_cast<unsigned>(v.chunks);
   if (v.gq == 4)
-    hipLaunchKernelGGL((kv_values_g_kernel<MB, 4>), dim3(gx, static_cast<unsigned>(queries / 4)), dim3(256), 0, s, p,
-                       nq, vals, r, n, levels, v.kpt, partial);
+    hipLaunchKernelGGL((kv_values_g_kernel<MB, 4, SM>), dim3(gx, static_cast<unsigned>(queries / 4)), dim3(256), 0, s,
+                       p, nq, vals, r, n, levels, v.kpt, partial, scale, ml);
   else if (v.gq == 2)
-    hipLaunchKernelGGL((kv_values_g_kernel<MB, 2>), dim3(gx, static_cast<unsigned>(queries / 2)), dim3(256), 0, s, p,
-                       nq, vals, r, n, levels, v.kpt, partial);
+    hipLaunchKernelGGL((kv_values_g_kernel<MB, 2, SM>), dim3(gx, static_cast<unsigned>(queries / 2)), dim3(256), 0, s,
+                       p, nq, vals, r, n, levels, v.kpt, partial, scale, ml);
   else
-    hipLaunchKernelGGL(kv_values_kernel<MB>, dim3(gx, static_cast<unsigned>(queries)), dim3(256), 0, s, p, nq, vals,
-                       r, n, levels, v.kpt, partial);
+    hipLaunchKernelGGL((kv_values_kernel<MB, SM>), dim3(gx, static_cast<unsigned>(queries)), dim3(256), 0, s, p, nq,
+                       vals, r, n, levels, v.kpt, partial, scale, ml);
 }
 
 }  // namespace
@@ -787,9 +1018,10 @@ size_t tq_kv_workspace(int op, int64_t n, int heads, int nq) {
   if (n < 0 || heads < 1 || nq < 1) return SIZE_MAX;
   const long long queries = static_cast<long long>(heads) * nq;
   if (op == TQ_KV_OP_SCORES) return static_cast<size_t>(queries) * 256 * sizeof(float);
-  if (op == TQ_KV_OP_VALUES) {
+  if (op == TQ_KV_OP_VALUES || op == TQ_KV_OP_ATTEND) {
     const long long chunks = kv_values_plan(n, queries, nq).chunks;
-    return static_cast<size_t>(queries) * static_cast<size_t>(chunks > 0 ? chunks : 1) * kD * sizeof(float);
+    const size_t vecs = static_cast<size_t>(queries) * static_cast<size_t>(chunks > 0 ? chunks : 1);
+    return vecs * kD * sizeof(float) + (op == TQ_KV_OP_ATTEND ? vecs * sizeof(float2) : 0);
   }
   return SIZE_MAX;
 }
@@ -830,41 +1062,66 @@ int tq_kv_scores(const float* q, int heads, int nq, const uint32_t* keys, const 
   return TQ_OK;
 }
 
-int tq_kv_values(const float* p, int heads, int nq, const uint32_t* values, const uint16_t* radius, int64_t n,
-                 int bits, const float* signs, const double* levels, float* out, void* workspace, size_t ws_bytes,
-                 void* stream) {
+namespace {
+int kv_values_impl(bool attend, const float* p, float scale, int heads, int nq, const uint32_t* values,
+                   const uint16_t* radius, int64_t n, int bits, const float* signs, const double* levels, float* out,
+                   void* workspace, size_t ws_bytes, void* stream) {
   if (!p || !values || !radius || !signs || !levels || !out || !workspace) return TQ_EINVAL;
   if (bits < 1 || bits > TQ_KV_MAX_BITS) return TQ_EINVAL;
+  if (attend && !std::isfinite(scale)) return TQ_EINVAL;
   if (!tq_aligned(p, 4) || !tq_aligned(values, 16) || !tq_aligned(radius, 2) || !tq_aligned(signs, 4) ||
       !tq_aligned(levels, 8) || !tq_aligned(out, 8) || !tq_aligned(workspace, 16))
     return TQ_EINVAL;
   if (heads < 1 || nq < 1 || n < 0) return TQ_ESHAPE;
   const long long queries = static_cast<long long>(heads) * nq;
   if (queries > 65535) return TQ_ESHAPE;
-  if (ws_bytes < tq_kv_workspace(TQ_KV_OP_VALUES, n, heads, nq)) return TQ_ENOSPACE;
+  if (ws_bytes < tq_kv_workspace(attend ? TQ_KV_OP_ATTEND : TQ_KV_OP_VALUES, n, heads, nq)) return TQ_ENOSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ValuesPlan v = kv_values_plan(n, queries, nq);
   const long long chunks = v.chunks;
   if (chunks > INT_MAX) return TQ_ESHAPE;
   float* partial = static_cast<float*>(workspace);
+  float2* ml = reinterpret_cast<float2*>(partial + static_cast<size_t>(queries) * static_cast<size_t>(chunks) * kD);
   if (chunks > 0) {
+#define TQ_KVV(MB)                                                                                        \
+  (attend ? launch_values<MB, true>(v, queries, s, p, nq, values, radius, n, levels, partial, scale, ml) \
+          : launch_values<MB, false>(v, queries, s, p, nq, values, radius, n, levels, partial, 0.0f, ml))
     switch (bits) {
-      case 1: launch_values<1>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
-      case 2: launch_values<2>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
-      case 3: launch_values<3>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
-      case 4: launch_values<4>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
-      case 5: launch_values<5>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
-      case 6: launch_values<6>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
-      case 7: launch_values<7>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
-      default: launch_values<8>(v, queries, s, p, nq, values, radius, n, levels, partial); break;
+      case 1: TQ_KVV(1); break;
+      case 2: TQ_KVV(2); break;
+      case 3: TQ_KVV(3); break;
+      case 4: TQ_KVV(4); break;
+      case 5: TQ_KVV(5); break;
+      case 6: TQ_KVV(6); break;
+      case 7: TQ_KVV(7); break;
+      default: TQ_KVV(8); break;
     }
+#undef TQ_KVV
     TQ_LAUNCH_CHECK();
   }
-  hipLaunchKernelGGL(kv_values_finish_kernel, dim3(static_cast<unsigned>(queries)), dim3(kFinishWaves * 64), 0, s,
-                     partial,
-                     static_cast<int>(chunks), signs, out);
+  if (attend)
+    hipLaunchKernelGGL(kv_values_finish_kernel<true>, dim3(static_cast<unsigned>(queries)), dim3(kFinishWaves * 64),
+                       0, s, partial, static_cast<int>(chunks), signs, out, ml);
+  else
+    hipLaunchKernelGGL(kv_values_finish_kernel<false>, dim3(static_cast<unsigned>(queries)), dim3(kFinishWaves * 64),
+                       0, s, partial, static_cast<int>(chunks), signs, out, ml);
   TQ_LAUNCH_CHECK();
   return TQ_OK;
+}
+}  // namespace
+
+int tq_kv_values(const float* p, int heads, int nq, const uint32_t* values, const uint16_t* radius, int64_t n,
+                 int bits, const float* signs, const double* levels, float* out, void* workspace, size_t ws_bytes,
+                 void* stream) {
+  return kv_values_impl(false, p, 0.0f, heads, nq, values, radius, n, bits, signs, levels, out, workspace, ws_bytes,
+                        stream);
+}
+
+int tq_kv_attend(const float* scores, float scale, int heads, int nq, const uint32_t* values,
+                 const uint16_t* radius, int64_t n, int bits, const float* signs, const double* levels, float* out,
+                 void* workspace, size_t ws_bytes, void* stream) {
+  return kv_values_impl(true, scores, scale, heads, nq, values, radius, n, bits, signs, levels, out, workspace,
+                        ws_bytes, stream);
 }
 
 }  // extern "C"

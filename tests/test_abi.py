@@ -230,6 +230,15 @@ def test_kv_calls_reject_bad_arguments():
         ("levels", A), ("out", A), ("ws", A), ("wsb", 1 << 20), ("s", None))])
     assert va(vals=None) == tq.TQ_EINVAL and va(bits=0) == tq.TQ_EINVAL and va(out=A + 4) == tq.TQ_EINVAL
     assert va(wsb=tq.tq_kv_workspace(tq.TQ_KV_OP_VALUES, 100, 2, 2) - 1) == tq.TQ_ENOSPACE
+    at = lambda **kw: lib.tq_kv_attend(*[kw.get(k, v) for k, v in (
+        ("s", A), ("scale", 0.125), ("h", 2), ("nq", 2), ("vals", A), ("r", A), ("n", 100), ("bits", 3),
+        ("signs", A), ("levels", A), ("out", A), ("ws", A), ("wsb", 1 << 20), ("st", None))])
+    assert at(s=None) == tq.TQ_EINVAL and at(bits=9) == tq.TQ_EINVAL and at(vals=A + 4) == tq.TQ_EINVAL
+    assert at(scale=float("nan")) == tq.TQ_EINVAL and at(scale=float("inf")) == tq.TQ_EINVAL
+    assert at(h=0) == tq.TQ_ESHAPE and at(n=-1) == tq.TQ_ESHAPE and at(h=300, nq=300) == tq.TQ_ESHAPE
+    # the attend workspace also holds a (maximum, sum) pair per partial vector
+    vb, ab = (tq.tq_kv_workspace(op, 100, 2, 2) for op in (tq.TQ_KV_OP_VALUES, tq.TQ_KV_OP_ATTEND))
+    assert ab > vb and at(wsb=ab - 1) == tq.TQ_ENOSPACE
     assert lib.tq_kv_workspace(tq.TQ_KV_OP_SCORES, 10, 0, 1) == tq.SIZE_MAX
     assert lib.tq_kv_workspace(7, 10, 1, 1) == tq.SIZE_MAX
     assert [tq.tq_kv_record_bytes(b) for b in (0, 1, 3, 8, 9)] == [0, 16, 48, 128, 0]

@@ -12,6 +12,10 @@ ABI against the FP64 oracle (oracle/kv_oracle.py).
   to rel-L2 2e-5 and its largest error to 1e-4 of its largest score.  A
   value sum adds n FP32 products per coordinate (chunked, then the chunks
   in order): rel-L2 1e-5.
+* The fused attend (softmax of scale * scores, then the value sum) takes
+  scale * s and its exponential in FP32: each weight is off by a relative
+  few times 2^-24 |scale s|, under 1e-6 for the logits used here, and the
+  normalising sum of the same weights cancels most of it: rel-L2 2e-5.
 """
 import numpy as np
 import pytest
@@ -26,6 +30,8 @@ pytestmark = pytest.mark.gpu
 
 SCORE_REL_L2, SCORE_ROW_MAX, SCORE_ABS = 2e-5, 1e-4, 2e-5
 VALUE_REL_L2, VALUE_ROW_MAX = 1e-5, 1e-4
+ATTEND_REL_L2, ATTEND_ROW_MAX = 2e-5, 1e-4
+SCALE = 1.0 / np.sqrt(128.0)
 
 
 def _setup(sign_seed=21, jl_seed=22):
@@ -147,6 +153,25 @@ def _run_values(p, heads, nq, rec, r, n, bits, sd, lv):
     return out.cpu().numpy().astype(np.float64)
 
 
+def _run_attend(s, scale, heads, nq, rec, r, n, bits, sd, lv):
+    t = torch()
+    out = t.full((heads, nq, K.D), 7.0, dtype=t.float32, device="cuda")
+    ws, nb = tq.kv_workspace(tq.TQ_KV_OP_ATTEND, n, heads, nq)
+    tq.tq_kv_attend(s, scale, heads, nq, rec, r, n, bits, sd, lv, out, ws, nb)
+    t.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _value_store(heads, n, bits, signs, seed=70):
+    stores, vqs = [], []
+    for h in range(heads):
+        vq = K.kv_quantize(synth.kv_vectors(seed + h, n, K.D, "bf16").values, signs, bits, False)
+        vqs.append(vq)
+        stores.append(_oracle_store(vq))
+    rec, r, _ = _upload_store(stores)
+    return rec, r, vqs
+
+
 @pytest.mark.parametrize("bits", range(2, 9))
 @pytest.mark.parametrize("heads,nq,n", [(2, 3, 1), (2, 3, 700), (2, 4, 700), (1, 2, 700), (3, 8, 1500), (1, 4, 3)])
 def test_scores_parity(bits, heads, nq, n):
@@ -203,6 +228,81 @@ def test_values_of_no_tokens_are_zero(nq):
     assert not out.cpu().numpy().any()
 
 
+@pytest.mark.parametrize("bits", range(1, 9))
+@pytest.mark.parametrize("heads,nq,n", [(2, 3, 1), (2, 3, 3000), (2, 4, 3000), (1, 2, 3000), (3, 8, 5000), (1, 4, 3)])
+def test_attend_parity(bits, heads, nq, n):
+    """Fused softmax + value sum against the oracle's softmax of scale *
+    scores and value sum; scores of attention size (|scale s| up to ~12)."""
+    signs, _, sd, _ = _setup()
+    rec, r, vqs = _value_store(heads, n, bits, signs)
+    rng = np.random.default_rng(90 + bits)
+    s = (rng.normal(size=(heads, nq, n)) * 30.0).astype(np.float32)
+    got = _run_attend(dev(s), SCALE, heads, nq, rec, r, n, bits, sd, _levels(bits, False))
+    want = np.stack([np.stack([K.kv_attend(s[h, j], SCALE, vqs[h], signs) for j in range(nq)])
+                     for h in range(heads)])
+    assert_parity(got.reshape(heads * nq, K.D), want.reshape(heads * nq, K.D), ATTEND_REL_L2, ATTEND_ROW_MAX)
+
+
+@pytest.mark.parametrize("nq", [1, 2, 4])
+def test_attend_rescales_chunks(nq):
+    """The key chunks' maxima differ by far more than FP32's exponent range
+    once exponentiated: a ramp of scores (rising or falling) with one narrow
+    peak in the middle, or a sawtooth whose teeth rise steeply enough that
+    the running offset inside a chunk moves every few keys; masked (-inf)
+    tokens including whole chunks.  The merge must rescale each chunk to the
+    common maximum.  A query whose scores are all -inf gives zeros."""
+    signs, _, sd, _ = _setup()
+    heads, n, bits = 2, 40000, 3
+    rec, r, vqs = _value_store(heads, n, bits, signs, seed=75)
+    s = np.empty((heads, nq, n), np.float32)
+    ramps = [np.linspace(-4000.0, 400.0, n, dtype=np.float32), np.linspace(400.0, -4000.0, n, dtype=np.float32),
+             (450.0 / 256.0 * (np.arange(n) % 256)).astype(np.float32)]
+    for h in range(heads):
+        for j in range(nq):
+            row = ramps[(h + j) % 3].copy()
+            if (h + j) % 3 != 2:
+                row[n // 2 - 3:n // 2 + 3] = 600.0 + np.arange(6, dtype=np.float32)
+            row[1000:9000] = -np.inf
+            row[::7] = -np.inf
+            s[h, j] = row
+    s[1, nq - 1] = -np.inf
+    got = _run_attend(dev(s), SCALE, heads, nq, rec, r, n, bits, sd, _levels(bits, False))
+    for h in range(heads):
+        for j in range(nq):
+            if h == 1 and j == nq - 1:
+                assert not got[h, j].any()
+                continue
+            want = K.kv_attend(s[h, j], SCALE, vqs[h], signs)
+            assert_parity(got[h, j][None], want[None], ATTEND_REL_L2, ATTEND_ROW_MAX, f"h{h} q{j}")
+
+
+@pytest.mark.parametrize("nq", [3, 4])
+def test_attend_of_no_tokens_is_zero(nq):
+    t = torch()
+    signs, jl, sd, jd = _setup()
+    rec = t.zeros((1, 12), dtype=t.int32, device="cuda")
+    r = t.zeros(1, dtype=t.int16, device="cuda")
+    s = t.zeros(1, dtype=t.float32, device="cuda")
+    got = _run_attend(s, SCALE, 2, nq, rec, r, 0, 3, sd, _levels(3, False))
+    assert not got.any()
+
+
+def test_attend_matches_values_of_softmax():
+    """tq_kv_attend against tq_kv_values fed torch's FP32 softmax of the same
+    scores: the two GPU paths agree to FP32 rounding."""
+    t = torch()
+    signs, _, sd, _ = _setup()
+    heads, nq, n, bits = 2, 4, 20000, 3
+    rec, r, _ = _value_store(heads, n, bits, signs)
+    rng = np.random.default_rng(95)
+    s = dev((rng.normal(size=(heads, nq, n)) * 30.0).astype(np.float32))
+    lv = _levels(bits, False)
+    p = t.softmax(s * SCALE, dim=-1).contiguous()
+    a = _run_attend(s, SCALE, heads, nq, rec, r, n, bits, sd, lv)
+    b = _run_values(p, heads, nq, rec, r, n, bits, sd, lv)
+    assert_parity(a.reshape(-1, K.D), b.reshape(-1, K.D), ATTEND_REL_L2, ATTEND_ROW_MAX)
+
+
 def test_attention_pipeline_small():
     """Quantise keys and values on the GPU, score, softmax (torch, FP32),
     weighted value sum; against the oracle doing the same from x."""
@@ -217,8 +317,10 @@ def test_attention_pipeline_small():
     krec, kr, kg = _gpu_quantize(act_tensor(kx), heads * n, bits, True, sd, jd)
     vrec, vr, _ = _gpu_quantize(act_tensor(vx), heads * n, bits, False, sd, jd)
     s = _run_scores(dev(q.raw.astype(np.float32)), heads, nq, krec, kr, kg, n, bits, sd, jd, _levels(bits, True))
-    p = t.softmax(t.from_numpy(s).float().cuda() / np.sqrt(K.D), dim=-1).contiguous()
+    sdev = t.from_numpy(s).float().cuda()
+    p = t.softmax(sdev / np.sqrt(K.D), dim=-1).contiguous()
     got = _run_values(p, heads, nq, vrec, vr, n, bits, sd, _levels(bits, False))
+    fused = _run_attend(sdev, SCALE, heads, nq, vrec, vr, n, bits, sd, _levels(bits, False))
     for h in range(heads):
         kq = K.kv_quantize(kx.values[h * n:(h + 1) * n], signs, bits, True, jl)
         vq = K.kv_quantize(vx.values[h * n:(h + 1) * n], signs, bits, False)
@@ -230,6 +332,7 @@ def test_attention_pipeline_small():
             pr /= pr.sum()
             want = K.kv_values(pr, vq, signs)
             assert_parity(got[h, j][None], want[None], 1e-4, 1e-4, f"out h{h} q{j}")
+            assert_parity(fused[h, j][None], want[None], 1e-4, 1e-4, f"fused h{h} q{j}")
 
 
 @pytest.mark.slow
@@ -266,9 +369,14 @@ def test_full_size_sampled():
             _assert_scores(s[h, j, idx], want, kq["r"], q.values[h * nq + j], f"h{h} q{j}")
             p[h, j, idx] = rng.random(64).astype(np.float32)
     got = _run_values(dev(p), heads, nq, vrec, vr, n, bits, sd, _levels(bits, False))
+    # Fused attend on the same sample: every other score masked to -inf.
+    sm = np.where(p > 0, s.astype(np.float32), -np.inf).astype(np.float32)
+    fused = _run_attend(dev(sm), SCALE, heads, nq, vrec, vr, n, bits, sd, _levels(bits, False))
     for h in range(heads):
         nz = np.nonzero(p[h, 0])[0]
         vq = K.kv_quantize(vx.values[h * n + nz], signs, bits, False)
         for j in range(nq):
             want = K.kv_values(p[h, j, nz].astype(np.float64), vq, signs)
             assert_parity(got[h, j][None], want[None], VALUE_REL_L2, VALUE_ROW_MAX, f"values h{h} q{j}")
+            want = K.kv_attend(sm[h, j, nz], SCALE, vq, signs)
+            assert_parity(fused[h, j][None], want[None], ATTEND_REL_L2, ATTEND_ROW_MAX, f"attend h{h} q{j}")
