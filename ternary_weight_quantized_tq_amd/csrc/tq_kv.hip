@@ -496,27 +496,29 @@ __device__ __forceinline__ void halve(float (&a)[N], int lane) {
   }
 }
 
-// Softmax form (SM, tq_kv_attend): p holds the scores z = scale * s, and
-// value i is weighed by exp(z_i - o) r_i with a running offset o, one per
-// wavefront and query (a uniform value).  o starts at -inf; whenever a lane
-// meets z > o + kOffsetSlack, o moves up to that z and the wavefront's
-// running sums of the query are scaled by exp(o_old - o_new).  Weights so
-// stay below e^kOffsetSlack (chunk sums far inside FP32 range) and the
-// rescaling is rare: never again once o is within kOffsetSlack of the
-// chunk's maximum.  Each lane also sums its weights (l).  At the end the
-// workgroup scales every wavefront to the largest offset m of its four,
-// and (m, l) per (query, chunk) go beside the partial vectors; the
-// finishing launch rescales the chunks to their common maximum.  The loop
-// ends for a whole wavefront at once, so every lane takes part in the
-// rescaling.
-constexpr float kOffsetSlack = 16.0f;
+// Softmax form (SM, tq_kv_attend): p holds the scores s, and the kernels
+// work in base 2: z = scale2 * s with scale2 = scale log2(e), so that
+// exp(scale s) = 2^z and each weight is one hardware exp2.  Value i is
+// weighed by 2^(z_i - o) r_i with a running offset o, one per wavefront and
+// query (a uniform value).  o starts at -inf; whenever a lane meets
+// z > o + kOffsetSlack, o moves up to that z and the wavefront's running
+// sums of the query are scaled by 2^(o_old - o_new).  Weights so stay below
+// 2^kOffsetSlack (chunk sums far inside FP32 range) and the rescaling is
+// rare: never again once o is within kOffsetSlack of the chunk's maximum.
+// Each lane also sums its weights (l).  At the end the workgroup scales
+// every wavefront to the largest offset m of its four, and (m, l) per
+// (query, chunk) go beside the partial vectors; the finishing launch
+// rescales the chunks to their common maximum.  The loop ends for a whole
+// wavefront at once, so every lane takes part in the rescaling.
+constexpr float kOffsetSlack = 24.0f;
+constexpr double kLog2E = 1.4426950408889634;
 
 // The offset the exponentials take: o itself, or 0 while o is -inf (every
 // score so far masked), so that they come out 0 rather than NaN.
 __device__ __forceinline__ float exp_offset(float o) { return o == -INFINITY ? 0.0f : o; }
 
 // Raise the wavefront's offset o until no lane has z > o + kOffsetSlack;
-// returns the factor exp(o_before - o_after) for the running sums (1 when
+// returns the factor 2^(o_before - o_after) for the running sums (1 when
 // o is unchanged, 0 when it was -inf: nothing has been summed yet).
 // Only lanes with `mine` set take part (the lanes whose z is a score of
 // this query).
@@ -525,7 +527,7 @@ __device__ __forceinline__ float raise_offset(float z, float& o, bool mine = tru
   uint64_t need = __builtin_amdgcn_ballot_w64(mine && z > o + kOffsetSlack);
   while (need) {
     const float zn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), __builtin_ctzll(need)));
-    f = o == -INFINITY ? 0.0f : f * expf(o - zn);
+    f = o == -INFINITY ? 0.0f : f * exp2f(o - zn);
     o = zn;
     need = __builtin_amdgcn_ballot_w64(mine && z > o + kOffsetSlack);
   }
@@ -533,7 +535,7 @@ __device__ __forceinline__ float raise_offset(float z, float& o, bool mine = tru
 }
 
 // The softmax form's weights of one value for GQ queries: x holds the
-// scores s on entry and exp(scale s - o) on return (0 for a lane whose
+// scores s on entry and 2^(scale2 s - o) on return (0 for a lane whose
 // value is past the end, valid false).  The common path has one uniform
 // branch; the rescaling path (rare) raises each query's offset and scales
 // its NA running sums acc[NA qq ..] and weight sum.
@@ -559,8 +561,21 @@ __device__ __forceinline__ void softmax_weights(float (&x)[GQ], bool valid, floa
   }
 #pragma unroll
   for (int qq = 0; qq < GQ; ++qq) {
-    x[qq] = expf(x[qq] - exp_offset(off[qq]));
+    x[qq] = __builtin_amdgcn_exp2f(x[qq] - exp_offset(off[qq]));
     l[qq] += x[qq];
+  }
+}
+
+// wt[q] = x of part q of the lane's four-lane group (DPP quad permutations;
+// the four lanes of a value are active or inactive together).
+template <int GQ>
+__device__ __forceinline__ void quad_spread(float x, float (&wt)[GQ]) {
+  static_assert(GQ == 2 || GQ == 4, "four lanes per value serve 2 or 4 queries");
+  wt[0] = dpp_f32<0x00>(x);  // quad_perm(0,0,0,0)
+  wt[1] = dpp_f32<0x55>(x);  // quad_perm(1,1,1,1)
+  if constexpr (GQ == 4) {
+    wt[2] = dpp_f32<0xAA>(x);
+    wt[3] = dpp_f32<0xFF>(x);
   }
 }
 
@@ -572,7 +587,6 @@ __device__ __forceinline__ void softmax_weights(float (&x)[GQ], bool valid, floa
 template <int GQ, int NV>
 __device__ __forceinline__ void softmax_weights_quad(float z, bool valid, int part, float scale, float (&off)[GQ],
                                                      float (&acc)[NV], float& l, float (&wt)[GQ]) {
-  static_assert(GQ == 2 || GQ == 4, "four lanes per value serve 2 or 4 queries");
   const int mq = part & (GQ - 1);
   z = valid ? scale * z : -INFINITY;
   float om = off[0];
@@ -592,14 +606,9 @@ __device__ __forceinline__ void softmax_weights_quad(float z, bool valid, int pa
 #pragma unroll
     for (int qq = 1; qq < GQ; ++qq) om = mq == qq ? off[qq] : om;
   }
-  const float w = expf(z - exp_offset(om));
+  const float w = __builtin_amdgcn_exp2f(z - exp_offset(om));
   l += w;
-  wt[0] = dpp_f32<0x00>(w);  // quad_perm(0,0,0,0): part 0's weight
-  wt[1] = dpp_f32<0x55>(w);  // quad_perm(1,1,1,1)
-  if constexpr (GQ == 4) {
-    wt[2] = dpp_f32<0xAA>(w);
-    wt[3] = dpp_f32<0xFF>(w);
-  }
+  quad_spread<GQ>(w, wt);
 }
 
 // End of the softmax form: the workgroup's offset m = max over its four
@@ -621,7 +630,7 @@ __device__ __forceinline__ void softmax_merge(float (&off)[GQ], float (&acc)[NV]
 #pragma unroll
   for (int qq = 0; qq < GQ; ++qq) {
     const float m = fmaxf(fmaxf(sbuf[0][qq], sbuf[1][qq]), fmaxf(sbuf[2][qq], sbuf[3][qq]));
-    const float f = off[qq] == -INFINITY ? 0.0f : expf(off[qq] - m);
+    const float f = off[qq] == -INFINITY ? 0.0f : exp2f(off[qq] - m);
     if (f != 1.0f) {
 #pragma unroll
       for (int j = 0; j < NA; ++j) acc[NA * qq + j] *= f;
@@ -764,14 +773,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
     for (int x = 0; x < PW; ++x) w[x] = __builtin_nontemporal_load(rp + x);
     const float r = half_bits_to_f32(radius[hn + k]);
+    // Lane part q loads the weight (or score) of query q % GQ; the quad
+    // shares them.
     float wt[GQ];
-    if constexpr (SM) {
-      const float z = p[static_cast<size_t>(q0 + (part & (GQ - 1))) * static_cast<size_t>(n) + k];
-      softmax_weights_quad<GQ>(z, valid, part, scale, off, acc, lsum, wt);
-    } else {
-#pragma unroll
-      for (int qq = 0; qq < GQ; ++qq) wt[qq] = p[static_cast<size_t>(q0 + qq) * static_cast<size_t>(n) + k];
-    }
+    const float pq = p[static_cast<size_t>(q0 + (part & (GQ - 1))) * static_cast<size_t>(n) + k];
+    if constexpr (SM)
+      softmax_weights_quad<GQ>(pq, valid, part, scale, off, acc, lsum, wt);
+    else
+      quad_spread<GQ>(pq, wt);
 #pragma unroll
     for (int qq = 0; qq < GQ; ++qq) wt[qq] *= r;
     kv_values_g_decode<C, IB>(tab, w, wt, acc, std::make_integer_sequence<int, 32 / C>{});
@@ -809,10 +818,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 // step), then wavefront 0 adds the wavefronts' sums in order: a fixed order,
 // so the result is deterministic.
 // With SM, chunk c's partial vector and its l_c are first scaled by
-// exp(m_c - M), M the largest m_c of the query, and the sum divided by the
-// scaled l's sum; no chunks (n = 0) give zeros.
-// exp(m_c - M); a chunk whose scores are all -inf has nothing to add.
-__device__ __forceinline__ float chunk_weight(float mc, float mx) { return mc == -INFINITY ? 0.0f : expf(mc - mx); }
+// 2^(m_c - M) (offsets in base 2), M the largest m_c of the query, and the
+// sum divided by the scaled l's sum; no chunks (n = 0) give zeros.
+// 2^(m_c - M); a chunk whose scores are all -inf has nothing to add.
+__device__ __forceinline__ float chunk_weight(float mc, float mx) { return mc == -INFINITY ? 0.0f : exp2f(mc - mx); }
 constexpr int kFinishWaves = 16;
 template <bool SM>
 __global__ __launch_bounds__(kFinishWaves * 64) void kv_values_finish_kernel(const float* __restrict__ partial,
@@ -1082,9 +1091,10 @@ int kv_values_impl(bool attend, const float* p, float scale, int heads, int nq, 
   if (chunks > INT_MAX) return TQ_ESHAPE;
   float* partial = static_cast<float*>(workspace);
   float2* ml = reinterpret_cast<float2*>(partial + static_cast<size_t>(queries) * static_cast<size_t>(chunks) * kD);
+  const float scale2 = static_cast<float>(static_cast<double>(scale) * kLog2E);
   if (chunks > 0) {
 #define TQ_KVV(MB)                                                                                        \
-  (attend ? launch_values<MB, true>(v, queries, s, p, nq, values, radius, n, levels, partial, scale, ml) \
+  (attend ? launch_values<MB, true>(v, queries, s, p, nq, values, radius, n, levels, partial, scale2, ml) \
           : launch_values<MB, false>(v, queries, s, p, nq, values, radius, n, levels, partial, 0.0f, ml))
     switch (bits) {
       case 1: TQ_KVV(1); break;
