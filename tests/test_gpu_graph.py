@@ -100,8 +100,8 @@ def test_gemm_in_graph():
 
 @pytest.mark.parametrize("nq", [3, 4])
 def test_kv_cache_in_graph(nq):
-    """KV quantise, scores and value sums (query groups of 1 and 4 per
-    workgroup), each captured and replayed; all deterministic."""
+    """KV quantise, scores, value sums and attend (query groups of 1 and 4
+    per workgroup), each captured and replayed; all deterministic."""
     th = torch()
     heads, n, bits = 2, 3000, 3
     sd, jd = dev(synth.kv_signs(91)), dev(synth.kv_jl(92))
@@ -132,3 +132,6 @@ def test_kv_cache_in_graph(nq):
     out = th.empty((heads, nq, 128), dtype=th.float32, device="cuda")
     wv, nbv = tq.kv_workspace(tq.TQ_KV_OP_VALUES, n, heads, nq)
     _replays_match(lambda: tq.tq_kv_values(p, heads, nq, rec, r, n, bits, sd, lv, out, wv, nbv), out)
+    wa, nba = tq.kv_workspace(tq.TQ_KV_OP_ATTEND, n, heads, nq)
+    att = th.empty((heads, nq, 128), dtype=th.float32, device="cuda")
+    _replays_match(lambda: tq.tq_kv_attend(scores, 0.125, heads, nq, rec, r, n, bits, sd, lv, att, wa, nba), att)
