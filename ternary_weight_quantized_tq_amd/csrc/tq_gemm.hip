@@ -29,6 +29,11 @@ constexpr int BM = 64;          // rows of Y per workgroup with x' in two fp16 p
 constexpr int BN = 256;         // columns of Y per workgroup (4 wavefronts x 64)
 constexpr int BK = 160;         // trits per K step = 2 quads = 8 words
 constexpr int kThreads = 256;
+// Wavefronts per row block in gemm_kernel: with x' in two fp16 parts one
+// (the in-wavefront software pipeline; two measured 0.864 against 0.854
+// ms), with one part (TQ_FAST_F16) two (0.481 against 0.506 ms).
+template <int P>
+constexpr int gemm_ts() { return P == 2 ? 1 : 2; }
 
 #define TQ_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
@@ -135,35 +140,42 @@ __device__ __forceinline__ void a_row_of(int idx, int& t, int& part, int& c) {
 
 __device__ __forceinline__ uint2 load_pair_cached(const uint32_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
-// G: scale groups per slice (5 at group 128, 10 at group 64).
-template <int G, int P>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
+// G: scale groups per slice (5 at group 128, 10 at group 64).  TS: wavefronts
+// per row block (1: one wavefront takes all eight A tiles; 2: wavefronts w
+// and w + 4 share row block w % 4, A tiles 0-3 and 4-7, and both decode its
+// words, so that two wavefronts per SIMD hide each other's latencies).
+template <int G, int P, int TS>
+__global__ __launch_bounds__(kThreads * TS) void gemm_kernel(GemmArgs a) {
+  constexpr int kT = kThreads * TS;        // threads per workgroup
+  constexpr int kTiles = kATiles / TS;     // A tiles per wavefront
+  constexpr int kAV = kARows * BK / 8 / kT;  // uint4 of the activation tile per thread per unit
   constexpr int kTok = kARows / P;  // tokens per workgroup
   constexpr int kGroup = kSliceTrits / G;
   constexpr int kScaleVecs = G * 64 / 8;  // 16-byte vectors of one block's slice scales
   constexpr int kScaleLoads = (kScaleVecs + 63) / 64;
   __shared__ __attribute__((aligned(16))) _Float16 As[2][kARows * kAStride];   // 86,016 B
   __shared__ __attribute__((aligned(16))) uint2 codes[81];
-  __shared__ __attribute__((aligned(16))) uint16_t ssc[kThreads / 64][G * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[kT / 64][G * 64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 15, kb = lane >> 4;
+  const int t0 = (wave / 4) * kTiles;  // this wavefront's first A tile
   int mt, nt;
   tile_of(a, mt, nt);
-  const int rb = nt * (BN / 64) + wave;
+  const int rb = nt * (BN / 64) + wave % 4;
   const bool active = rb < a.nb;
   const int rbc = active ? rb : a.nb - 1;
   const int nsl = slices_per_row(a.k);
-  build_code_table(codes, tid, kThreads);
+  build_code_table(codes, tid, kT);
 
   // Loaders.  Unit u: slice u / 4, unit u % 4 of the slice.
   auto a_src = [&](int u, int i) {  // i-th uint4 of this thread in unit u
-    const int idx = tid + i * kThreads;               // 0 .. 2559
+    const int idx = tid + i * kT;                     // 0 .. 2559
     int t, part, c;
     a_row_of<P>(idx, t, part, c);
     const _Float16* src = part ? a.xl : a.xh;
     return reinterpret_cast<const uint4*>(src + static_cast<size_t>(mt * kTok + t) * a.kpad + u * BK + 8 * c);
   };
   auto a_dst = [&](int buf, int i) {
-    const int idx = tid + i * kThreads;
+    const int idx = tid + i * kT;
     int t, part, c;
     a_row_of<P>(idx, t, part, c);
     return reinterpret_cast<uint4*>(&As[buf][(P * t + part) * kAStride + 8 * c]);
@@ -184,26 +196,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
   };
 
   // Unit 0 into buffer 0, slice 0's scales.
-  uint4 av[kAVecs];
+  uint4 av[kAV];
   uint2 wq[4], wn[4];
 #pragma unroll
-  for (int i = 0; i < kAVecs; ++i) av[i] = *a_src(0, i);
+  for (int i = 0; i < kAV; ++i) av[i] = *a_src(0, i);
 #pragma unroll
   for (int h = 0; h < 4; ++h) wq[h] = load_pair_cached(pair_ptr(0, h));
   uint4 scq = *scale_ptr(0, sl), scq2 = scq;
   if constexpr (kScaleLoads > 1) scq2 = *scale_ptr(0, sl2);
 #pragma unroll
-  for (int i = 0; i < kAVecs; ++i) *a_dst(0, i) = av[i];
+  for (int i = 0; i < kAV; ++i) *a_dst(0, i) = av[i];
   if (lane < kScaleVecs) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
   if constexpr (kScaleLoads > 1)
     if (lane + 64 < kScaleVecs) *reinterpret_cast<uint4*>(&ssc[wave][8 * (lane + 64)]) = scq2;
   TQ_LDS_BARRIER();
 
-  float4_t acc[4][kATiles];
+  float4_t acc[4][kTiles];
 #pragma unroll
   for (int h = 0; h < 4; ++h)
 #pragma unroll
-    for (int t = 0; t < kATiles; ++t) acc[h][t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < kTiles; ++t) acc[h][t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const char* cbase = reinterpret_cast<const char*>(codes);
   // Code-table reads of row quarter h of a unit from its word pair.
   auto decode = [&](uint2 w, uint2 (&cv)[10]) {
@@ -214,15 +226,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
     for (int c = 0; c < 10; ++c) cv[c] = *reinterpret_cast<const uint2*>(cbase + o[c]);
   };
 
-  // Software pipeline: while unit u's MFMAs run, row quarter st of unit
-  // u + 1 is decoded (its words were loaded during unit u - 1), unit u + 1's
-  // activations are loaded for the other LDS buffer and unit u + 2's words
-  // are requested.
+  // Software pipeline (TS = 1): while unit u's MFMAs run, row quarter st of
+  // unit u + 1 is decoded (its words were loaded during unit u - 1), unit
+  // u + 1's activations are loaded for the other LDS buffer and unit u + 2's
+  // words are requested.  With TS = 2 the registers do not hold two units'
+  // codes: a wavefront decodes its unit at the unit's start and requests
+  // the next unit's words, and the other wavefront on its SIMD covers the
+  // wait.
   uint2 cv[4][10];
+  if constexpr (TS == 1) {
 #pragma unroll
-  for (int h = 0; h < 4; ++h) decode(wq[h], cv[h]);
+    for (int h = 0; h < 4; ++h) decode(wq[h], cv[h]);
 #pragma unroll
-  for (int h = 0; h < 4; ++h) wq[h] = load_pair_cached(pair_ptr(min(1, a.steps - 1), h));  // unit 1
+    for (int h = 0; h < 4; ++h) wq[h] = load_pair_cached(pair_ptr(min(1, a.steps - 1), h));  // unit 1
+  }
   for (int s = 0; s < nsl; ++s) {
     _Float16 sc[4][G];  // this lane's rows 16 h + j, the slice's G groups
 #pragma unroll
@@ -238,49 +255,59 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
       const bool more = u + 1 < a.steps;
       const int un = more ? u + 1 : u;  // clamped to this unit on the last one
 #pragma unroll
-      for (int i = 0; i < kAVecs; ++i) av[i] = *a_src(un, i);
+      for (int i = 0; i < kAV; ++i) av[i] = *a_src(un, i);
       if (uu == 3) {
         scq = *scale_ptr(min(s + 1, nsl - 1), sl);
         if constexpr (kScaleLoads > 1) scq2 = *scale_ptr(min(s + 1, nsl - 1), sl2);
       }
       uint2 cvn[4][10];
+      if constexpr (TS == 2) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) decode(wq[h], cv[h]);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) wq[h] = load_pair_cached(pair_ptr(un, h));
+      }
       const _Float16* abase = &As[buf][j * kAStride + 8 * kb];
 #pragma unroll
       for (int st = 0; st < 5; ++st) {
         const int g = (160 * uu + 32 * st) / kGroup;  // compile-time: one scale group per step
-        half8_t af[kATiles];
+        half8_t af[kTiles];
 #pragma unroll
-        for (int t = 0; t < kATiles; ++t)
-          af[t] = *reinterpret_cast<const half8_t*>(abase + 16 * t * kAStride + 32 * st);
-        if (st < 4) {
-          decode(wq[st], cvn[st]);
-        } else {
+        for (int t = 0; t < kTiles; ++t)
+          af[t] = *reinterpret_cast<const half8_t*>(abase + 16 * (t0 + t) * kAStride + 32 * st);
+        if constexpr (TS == 1) {
+          if (st < 4) {
+            decode(wq[st], cvn[st]);
+          } else {
 #pragma unroll
-          for (int h = 0; h < 4; ++h) wn[h] = load_pair_cached(pair_ptr(min(u + 2, a.steps - 1), h));
+            for (int h = 0; h < 4; ++h) wn[h] = load_pair_cached(pair_ptr(min(u + 2, a.steps - 1), h));
+          }
         }
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
           const uint4 bq = make_uint4(cv[h][2 * st].x, cv[h][2 * st].y, cv[h][2 * st + 1].x, cv[h][2 * st + 1].y);
           const half8_t b = __builtin_bit_cast(half8_t, bq) * sc[h][g];
 #pragma unroll
-          for (int t = 0; t < kATiles; ++t)
+          for (int t = 0; t < kTiles; ++t)
             acc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t], b, acc[h][t], 0, 0, 0);
         }
       }
       if (more) {
 #pragma unroll
-        for (int i = 0; i < kAVecs; ++i) *a_dst(buf ^ 1, i) = av[i];
+        for (int i = 0; i < kAV; ++i) *a_dst(buf ^ 1, i) = av[i];
       }
       if (uu == 3) {
         if (lane < kScaleVecs) *reinterpret_cast<uint4*>(&ssc[wave][8 * lane]) = scq;
         if constexpr (kScaleLoads > 1)
           if (lane + 64 < kScaleVecs) *reinterpret_cast<uint4*>(&ssc[wave][8 * (lane + 64)]) = scq2;
       }
+      if constexpr (TS == 1) {
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        wq[h] = wn[h];
+        for (int h = 0; h < 4; ++h) {
+          wq[h] = wn[h];
 #pragma unroll
-        for (int c = 0; c < 10; ++c) cv[h][c] = cvn[h][c];
+          for (int c = 0; c < 10; ++c) cv[h][c] = cvn[h][c];
+        }
       }
       TQ_LDS_BARRIER();
     }
@@ -294,12 +321,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
     const int col = rb * 64 + 16 * h + j;
     if (col >= a.n) continue;
 #pragma unroll
-    for (int t = 0; t < kATiles; ++t)
+    for (int t = 0; t < kTiles; ++t)
 #pragma unroll
       for (int q = 0; q < 4 / P; ++q) {
-        // D row 4 kb + v of A tile t: P = 2, token 8 t + 2 kb + q from v = 2q (hi)
-        // and 2q + 1 (lo); P = 1, token 16 t + 4 kb + q.
-        const int row = mt * kTok + (16 / P) * t + (4 / P) * kb + q;
+        // D row 4 kb + v of A tile t0 + t: P = 2, token 8 (t0 + t) + 2 kb + q
+        // from v = 2q (hi) and 2q + 1 (lo); P = 1, token 16 (t0 + t) + 4 kb + q.
+        const int row = mt * kTok + (16 / P) * (t0 + t) + (4 / P) * kb + q;
         if (row < a.m) {
           float* yp = a.y + static_cast<size_t>(row) * a.n + col;
           const float sum = P == 2 ? acc[h][t][2 * q] + acc[h][t][2 * q + 1] : acc[h][t][q];
@@ -526,11 +553,13 @@ extern "C" int tq_gemm(const tq_weights* w, const void* x, int x_dtype, int m, f
     }
   } else {
     if (parts == 2) {
-      if (g5) hipLaunchKernelGGL((gemm_kernel<5, 2>), grid, blk, 0, s, a);
-      else hipLaunchKernelGGL((gemm_kernel<10, 2>), grid, blk, 0, s, a);
+      const dim3 b2(kThreads * gemm_ts<2>());
+      if (g5) hipLaunchKernelGGL((gemm_kernel<5, 2, gemm_ts<2>()>), grid, b2, 0, s, a);
+      else hipLaunchKernelGGL((gemm_kernel<10, 2, gemm_ts<2>()>), grid, b2, 0, s, a);
     } else {
-      if (g5) hipLaunchKernelGGL((gemm_kernel<5, 1>), grid, blk, 0, s, a);
-      else hipLaunchKernelGGL((gemm_kernel<10, 1>), grid, blk, 0, s, a);
+      const dim3 b1(kThreads * gemm_ts<1>());
+      if (g5) hipLaunchKernelGGL((gemm_kernel<5, 1, gemm_ts<1>()>), grid, b1, 0, s, a);
+      else hipLaunchKernelGGL((gemm_kernel<10, 1, gemm_ts<1>()>), grid, b1, 0, s, a);
     }
   }
   TQ_LAUNCH_CHECK();
