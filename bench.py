@@ -64,7 +64,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-extras", action="store_true", help="only the main metric")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--only-extra", choices=["block_m1", "block_m8", "moe", "prefill_gemm", "variants", "kv_cache"],
+    p.add_argument("--only-extra", choices=["block_m1", "block_m8", "moe", "prefill_gemm", "variants", "kv_cache",
+                                            "format"],
                    help="run one extra workload alone and print its JSON (for profiling)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy (for scaling rocprofv3 byte counters)")
@@ -592,6 +593,45 @@ def extra_kv(tq, torch, synth, np):
                     "attend"}
 
 
+def extra_format(tq, torch, synth, np):
+    """The format kernels at the up projection's size (17408 x 5120), HBM
+    bytes each moves over its time: quantise (FP32 weights in; trits and
+    fp16 scales out), pack and unpack in the ROW64 layout, the scale
+    re-layout; and the standalone block-128 transform of a prefill batch
+    (2048 x 5120 bf16 in, FP32 out).  Offline conversion except the
+    transform."""
+    lin = synth.DENSE_DECODE_27B.linears[0]
+    n, k = lin.n, lin.k
+    w = torch.from_numpy(synth.weights(lin.w_seed, n, k).astype(np.float32)).cuda()
+    t = torch.empty((n, k), dtype=torch.int8, device="cuda")
+    sc = torch.empty((n, k // 128), dtype=torch.int16, device="cuda")
+    wts = tq.empty_weights(n, k)
+    t2 = torch.empty_like(t)
+    rows = {}
+
+    def row(name, ms, nbytes):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        rows[name] = {"us": round(ms * 1e3, 2), "bytes": nbytes, "gb_s": round(gbs, 1),
+                      "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    row("quantize_f32", timed(torch, 5, 1, lambda i: tq.tq_quantize(w, n, k, 128, 3, t, sc)),
+        n * k * 4 + n * k + n * (k // 128) * 2)
+    wb = tq.tq_packed_bytes(n, k) - tq.tq_layout_scales(n, k, tq.TQ_LAYOUT_ROW64, 128) * 2
+    row("pack_row64", timed(torch, 10, 1, lambda i: tq.tq_pack(t, n, k, tq.TQ_LAYOUT_ROW64, 3, wts.words)),
+        n * k + wb)
+    row("pack_scales_row64", timed(torch, 10, 1, lambda i: tq.tq_pack_scales(sc, n, k, tq.TQ_LAYOUT_ROW64, 128,
+                                                                              wts.scales)),
+        2 * n * (k // 128) * 2)
+    row("unpack_row64", timed(torch, 10, 1, lambda i: tq.tq_unpack(wts.words, n, k, tq.TQ_LAYOUT_ROW64, 3, t2)),
+        wb + n * k)
+    del w
+    m = 2048
+    x = bf16(torch, synth.activations(5002, m, k, "bf16"))
+    xr = torch.empty((m, k), dtype=torch.float32, device="cuda")
+    row("fwht_bf16_to_f32", timed(torch, 20, 2, lambda i: tq.tq_fwht(x, m, k, xr)), m * k * 2 + m * k * 4)
+    return {"workload": f"format-{n}x{k}", "rows": n, "cols": k, "fwht_rows": m, "kernels": rows,
+            "note": "one launch each, timed in a graph of back-to-back launches on the same buffers"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -609,7 +649,8 @@ def main():
 
     if args.only_extra:
         fn = {"block_m1": extra_block_m1, "block_m8": extra_block_m8, "moe": extra_moe,
-              "prefill_gemm": extra_gemm, "variants": extra_variants, "kv_cache": extra_kv}[args.only_extra]
+              "prefill_gemm": extra_gemm, "variants": extra_variants, "kv_cache": extra_kv,
+              "format": extra_format}[args.only_extra]
         print(json.dumps({args.only_extra: fn(tq, torch, synth, np)}), flush=True)
         return
 
@@ -791,7 +832,8 @@ def main():
     if not args.no_extras:
         extras = {}
         for name, fn in (("block_m1", extra_block_m1), ("block_m8", extra_block_m8), ("moe", extra_moe),
-                         ("prefill_gemm", extra_gemm), ("variants", extra_variants), ("kv_cache", extra_kv)):
+                         ("prefill_gemm", extra_gemm), ("variants", extra_variants), ("kv_cache", extra_kv),
+                         ("format", extra_format)):
             log(f"extra: {name} ...")
             try:
                 extras[name] = fn(tq, torch, synth, np)

@@ -136,6 +136,102 @@ __global__ __launch_bounds__(256) void pack_row64_kernel(const int8_t* __restric
   words[idx] = row < n ? pack_word_row64(trits + static_cast<size_t>(row) * k, k, s, qi, j) : kZeroWord;
 }
 
+// ROW64 pack through LDS: one workgroup per (slice, row block).  The
+// block's 64 rows x 640 trits are staged with 16-byte loads (rows 16-byte
+// aligned: k is a multiple of 128 and the caller's pointer is checked), zero
+// trits past n and k, and each thread then forms 8 of the block's 2048
+// words from 4-trit chunks read back as 32-bit LDS words (a chunk never
+// straddles: 4 divides every chunk offset); the words leave in layout
+// order, one coalesced store per thread and word.
+constexpr int kTileStride = kSliceTrits + 16;  // bytes per staged row (16-byte pad against bank conflicts)
+
+__device__ __forceinline__ uint32_t chunk_value(uint32_t four) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int d = 3; d >= 0; --d) c = c * 3u + digit_of(static_cast<int8_t>((four >> (8 * d)) & 0xffu));
+  return c;
+}
+
+__global__ __launch_bounds__(256) void pack_row64_tile_kernel(const int8_t* __restrict__ trits, int n, int k,
+                                                              int nb, uint32_t* __restrict__ words) {
+  __shared__ __attribute__((aligned(16))) int8_t tile[64 * kTileStride];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x % nb, s = blockIdx.x / nb;
+  const int cols = min(kSliceTrits, k - s * kSliceTrits);  // a multiple of 128
+  for (int i = tid; i < 64 * (kSliceTrits / 16); i += 256) {
+    const int r = i / (kSliceTrits / 16), c16 = i % (kSliceTrits / 16);
+    const int row = b * 64 + r;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < n && 16 * c16 < cols)
+      v = *reinterpret_cast<const uint4*>(trits + static_cast<size_t>(row) * k + s * kSliceTrits + 16 * c16);
+    *reinterpret_cast<uint4*>(&tile[r * kTileStride + 16 * c16]) = v;
+  }
+  __syncthreads();
+  uint32_t* out = words + row64_quad_base(s, b, nb) * 4;
+#pragma unroll
+  for (int i = 0; i < kSliceQuads; ++i) {
+    const int idx = tid + 256 * i;  // layout order within the block: (quad, row, word)
+    const int j = idx & 3, r = (idx >> 2) & 63, qi = idx >> 8;
+    const int wl = 4 * (qi & 1) + j;
+    const int8_t* trow = tile + r * kTileStride + (qi >> 1) * 160;
+    uint32_t acc = 0;
+#pragma unroll
+    for (int c = 4; c >= 0; --c)
+      acc = acc * 81u + chunk_value(*reinterpret_cast<const uint32_t*>(trow + 4 * row64_chunk(wl, c)));
+    out[idx] = acc;
+  }
+}
+
+// ROW64 unpack through LDS, the inverse: each thread decodes 8 words of the
+// block (coalesced loads) into 4-trit chunks, each written as one 32-bit
+// LDS word of int8 trits (an 81-entry table maps a chunk to its four
+// trits), then the staged rows leave with 16-byte stores (rows < n, columns
+// < k).
+__global__ __launch_bounds__(256) void unpack_row64_tile_kernel(const uint32_t* __restrict__ words, int n, int k,
+                                                                int nb, int8_t* __restrict__ trits) {
+  __shared__ __attribute__((aligned(16))) int8_t tile[64 * kTileStride];
+  __shared__ uint32_t four[81];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x % nb, s = blockIdx.x / nb;
+  const int cols = min(kSliceTrits, k - s * kSliceTrits);
+  if (tid < 81) {
+    uint32_t v = 0, c = tid;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      v |= (static_cast<uint32_t>(static_cast<int>(c % 3u) - 1) & 0xffu) << (8 * d);
+      c /= 3u;
+    }
+    four[tid] = v;
+  }
+  const uint32_t* in = words + row64_quad_base(s, b, nb) * 4;
+  uint32_t wv[kSliceQuads];
+#pragma unroll
+  for (int i = 0; i < kSliceQuads; ++i) wv[i] = in[tid + 256 * i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kSliceQuads; ++i) {
+    const int idx = tid + 256 * i;
+    const int j = idx & 3, r = (idx >> 2) & 63, qi = idx >> 8;
+    const int wl = 4 * (qi & 1) + j;
+    int8_t* trow = tile + r * kTileStride + (qi >> 1) * 160;
+    uint32_t v = wv[i];
+#pragma unroll
+    for (int c = 0; c < 5; ++c) {
+      const uint32_t q = v / 81u;
+      *reinterpret_cast<uint32_t*>(trow + 4 * row64_chunk(wl, c)) = four[min(v - 81u * q, 80u)];  // < 81 unless the word is >= 3^20
+      v = q;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < 64 * (kSliceTrits / 16); i += 256) {
+    const int r = i / (kSliceTrits / 16), c16 = i % (kSliceTrits / 16);
+    const int row = b * 64 + r;
+    if (row < n && 16 * c16 < cols)
+      *reinterpret_cast<uint4*>(trits + static_cast<size_t>(row) * k + s * kSliceTrits + 16 * c16) =
+          *reinterpret_cast<const uint4*>(&tile[r * kTileStride + 16 * c16]);
+  }
+}
+
 // Binary words (levels 2): bit i of word w is weight 32w + i, 1 for +1; any
 // value other than -1 packs as 1 (the sign rule's side for 0); bits past k
 // are 0.
@@ -342,8 +438,12 @@ int tq_pack(const int8_t* trits, int n, int k, int layout, int levels, uint32_t*
                        trits, n, k, wpr, words);
   } else {
     const int nsl = slices_per_row(k), nb = row_blocks(n);
-    hipLaunchKernelGGL(pack_row64_kernel, dim3(grid_for(static_cast<size_t>(nsl) * nb * kSliceQuads * 256)),
-                       dim3(256), 0, s, trits, n, k, nsl, nb, words);
+    if (tq_aligned(trits, 16) && static_cast<size_t>(nsl) * nb <= UINT_MAX)
+      hipLaunchKernelGGL(pack_row64_tile_kernel, dim3(static_cast<unsigned>(static_cast<size_t>(nsl) * nb)),
+                         dim3(256), 0, s, trits, n, k, nb, words);
+    else
+      hipLaunchKernelGGL(pack_row64_kernel, dim3(grid_for(static_cast<size_t>(nsl) * nb * kSliceQuads * 256)),
+                         dim3(256), 0, s, trits, n, k, nsl, nb, words);
   }
   TQ_LAUNCH_CHECK();
   return TQ_OK;
@@ -404,8 +504,13 @@ int tq_unpack(const uint32_t* words, int n, int k, int layout, int levels, int8_
     return TQ_OK;
   }
   const int wpr = layout == TQ_LAYOUT_ROW64 ? slices_per_row(k) * kSliceWords : words_per_row(k);
-  hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(static_cast<size_t>(n) * wpr)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), words, n, k, layout, wpr, row_blocks(n), trits);
+  const size_t tiles = static_cast<size_t>(slices_per_row(k)) * row_blocks(n);
+  if (layout == TQ_LAYOUT_ROW64 && tq_aligned(trits, 16) && tiles <= UINT_MAX)
+    hipLaunchKernelGGL(unpack_row64_tile_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), words, n, k, row_blocks(n), trits);
+  else
+    hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(static_cast<size_t>(n) * wpr)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), words, n, k, layout, wpr, row_blocks(n), trits);
   TQ_LAUNCH_CHECK();
   return TQ_OK;
 }

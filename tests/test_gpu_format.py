@@ -50,6 +50,28 @@ def test_pack_row64_layout(n, k):
     assert np.array_equal(back.cpu().numpy(), t)
 
 
+@pytest.mark.parametrize("n,k", [(65, 768), (3, 17408)])
+def test_pack_row64_unaligned_trits(n, k):
+    """Trits at an address that is not 16-byte aligned take the per-word
+    kernels (the staged ones need aligned rows); same words, same trits
+    back."""
+    th = torch()
+    t = synth.trits(40 + n + k, n, k)
+    buf = th.zeros(n * k + 16, dtype=th.int8, device="cuda")
+    src = buf[3:3 + n * k]
+    src.copy_(th.from_numpy(t.ravel()).cuda())
+    words = th.empty(tq.tq_layout_words(n, k, tq.TQ_LAYOUT_ROW64, 3), dtype=th.int32, device="cuda")
+    tq.tq_pack(src, n, k, tq.TQ_LAYOUT_ROW64, 3, words)
+    full = row64_to_rowmajor(host_u32(words), n, k)
+    assert np.array_equal(full[:n], O.pack(row64_word_order(t)))
+    assert np.all(full[n:] == ZERO_WORD)
+    out = th.zeros(n * k + 16, dtype=th.int8, device="cuda")
+    tq.tq_unpack(words, n, k, tq.TQ_LAYOUT_ROW64, 3, out[5:5 + n * k])
+    got = out.cpu().numpy()
+    assert np.array_equal(got[5:5 + n * k].reshape(n, k), t)
+    assert not got[:5].any() and not got[5 + n * k:].any()
+
+
 def _near_tie(w_rot, gamma, rel=1e-12):
     n, k = w_rot.shape
     g = np.repeat(gamma, 128, axis=1)
