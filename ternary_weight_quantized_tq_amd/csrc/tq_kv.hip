@@ -214,96 +214,142 @@ __device__ __forceinline__ void kv_values_g_decode(const float* tab, const uint3
 // the lower level), and for keys the residual, its norm and z = sign(S e)
 // with S^T staged in LDS.  The workgroup's four wavefronts walk the vectors
 // together so that the barriers around the shared staging are uniform.
+// Orders a wavefront's LDS stores before its later LDS loads of other
+// lanes' values (and those loads before the next stores): the wavefront's
+// LDS operations are waited for and the compiler keeps them on their side.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+}
+
+constexpr int kQWaves = 8;  // wavefronts per quantise workgroup (one copy of S^T in LDS for all)
+constexpr int kQVecs = 4;   // vectors per wavefront and pass
+
+// Each wavefront quantises kQVecs vectors per pass: their loads first, then
+// per vector the radius, sign flip and block-128 butterfly, the nearest
+// levels (binary search over the cell boundaries) and, for keys, the
+// residual e, its norm and S e.  The projection reads S^T from LDS once per
+// pass for all kQVecs vectors (row lane and lane + 64 per lane), so its LDS
+// traffic per vector is a quarter of one vector at a time.  Everything a
+// wavefront exchanges through LDS is its own: no workgroup barrier in the
+// loop.
 template <bool KEYS>
-__global__ __launch_bounds__(256) void kv_quantize_kernel(const void* __restrict__ x, int x_dtype, long long n,
-                                                          const float* __restrict__ signs,
-                                                          const float* __restrict__ jl,
-                                                          const double* __restrict__ levels, int mb, long long stride,
-                                                          int rec_words, uint32_t* __restrict__ rec,
-                                                          uint16_t* __restrict__ radius,
-                                                          uint16_t* __restrict__ gamma) {
+__global__ __launch_bounds__(kQWaves * 64) void kv_quantize_kernel(const void* __restrict__ x, int x_dtype, long long n,
+                                                                 const float* __restrict__ signs,
+                                                                 const float* __restrict__ jl,
+                                                                 const double* __restrict__ levels, int mb,
+                                                                 long long stride, int rec_words,
+                                                                 uint32_t* __restrict__ rec,
+                                                                 uint16_t* __restrict__ radius,
+                                                                 uint16_t* __restrict__ gamma) {
   __shared__ float st[KEYS ? kD * kD : 1];  // st[k][row] = S[row][k]
   __shared__ double lv[256];
   __shared__ double mids[256];
-  __shared__ double ebuf[4][KEYS ? kD : 1];
-  __shared__ uint32_t chunk[4][64];
+  __shared__ __attribute__((aligned(16))) double ebuf[KEYS ? kQWaves : 1][kQVecs][KEYS ? kD : 2];
+  __shared__ uint32_t chunk[kQWaves][kQVecs][64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nl = 1 << mb;
-  for (int i = tid; i < nl; i += 256) lv[i] = levels[i];
-  for (int i = tid; i < nl - 1; i += 256) mids[i] = (levels[i] + levels[i + 1]) / 2.0;
+  for (int i = tid; i < nl; i += kQWaves * 64) lv[i] = levels[i];
+  for (int i = tid; i < nl - 1; i += kQWaves * 64) mids[i] = (levels[i] + levels[i + 1]) / 2.0;
   if constexpr (KEYS) {
-    for (int i = tid; i < kD * kD; i += 256) st[(i % kD) * kD + i / kD] = jl[i];
+    for (int i = tid; i < kD * kD; i += kQWaves * 64) st[(i % kD) * kD + i / kD] = jl[i];
   }
   __syncthreads();
   const double sg0 = signs[2 * lane], sg1 = signs[2 * lane + 1];
   const int code_words = 4 * mb;
-  for (long long base = static_cast<long long>(blockIdx.x) * 4; base < n; base += static_cast<long long>(gridDim.x) * 4) {
-    const long long v = base + wv;
-    const bool ok = v < n;
-    double x0 = 0.0, x1 = 0.0;
-    if (ok) {
-      x0 = static_cast<double>(load_act(x, x_dtype, static_cast<size_t>(v) * kD + 2 * lane));
-      x1 = static_cast<double>(load_act(x, x_dtype, static_cast<size_t>(v) * kD + 2 * lane + 1));
-    }
-    double ss = x0 * x0 + x1 * x1;
+  constexpr long long kPass = kQWaves * kQVecs;
+  for (long long base = static_cast<long long>(blockIdx.x) * kPass; base < n;
+       base += static_cast<long long>(gridDim.x) * kPass) {
+    const long long v0 = base + static_cast<long long>(wv) * kQVecs;
+    double xa[kQVecs], xb[kQVecs];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-    const double r = sqrt(ss);
-    double y0 = sg0 * x0, y1 = sg1 * x1;
-    wave_fwht128<double>(y0, y1, lane, kInvSqrtD);
-    const double u0 = r > 0.0 ? y0 / r : 0.0;
-    const double u1 = r > 0.0 ? y1 / r : 0.0;
-    int c0 = 0, c1 = 0;
-    for (int s = nl >> 1; s >= 1; s >>= 1) {
-      if (mids[c0 + s - 1] < u0) c0 += s;
-      if (mids[c1 + s - 1] < u1) c1 += s;
+    for (int q = 0; q < kQVecs; ++q) {
+      xa[q] = 0.0;
+      xb[q] = 0.0;
+      if (v0 + q < n) {
+        xa[q] = static_cast<double>(load_act(x, x_dtype, static_cast<size_t>(v0 + q) * kD + 2 * lane));
+        xb[q] = static_cast<double>(load_act(x, x_dtype, static_cast<size_t>(v0 + q) * kD + 2 * lane + 1));
+      }
     }
-    chunk[wv][lane] = static_cast<uint32_t>(c0) | (static_cast<uint32_t>(c1) << mb);
-    double gam = 0.0;
-    if constexpr (KEYS) {
-      const double e0 = u0 - lv[c0], e1 = u1 - lv[c1];
-      ebuf[wv][2 * lane] = e0;
-      ebuf[wv][2 * lane + 1] = e1;
-      double g2 = e0 * e0 + e1 * e1;
+    double rq[kQVecs], gq[kQVecs];
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) g2 += __shfl_xor(g2, off);
-      gam = sqrt(g2);
+    for (int q = 0; q < kQVecs; ++q) {
+      double ss = xa[q] * xa[q] + xb[q] * xb[q];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+      const double r = sqrt(ss);
+      double y0 = sg0 * xa[q], y1 = sg1 * xb[q];
+      wave_fwht128<double>(y0, y1, lane, kInvSqrtD);
+      const double u0 = r > 0.0 ? y0 / r : 0.0;
+      const double u1 = r > 0.0 ? y1 / r : 0.0;
+      int c0 = 0, c1 = 0;
+      for (int s = nl >> 1; s >= 1; s >>= 1) {
+        if (mids[c0 + s - 1] < u0) c0 += s;
+        if (mids[c1 + s - 1] < u1) c1 += s;
+      }
+      chunk[wv][q][lane] = static_cast<uint32_t>(c0) | (static_cast<uint32_t>(c1) << mb);
+      double gam = 0.0;
+      if constexpr (KEYS) {
+        const double e0 = u0 - lv[c0], e1 = u1 - lv[c1];
+        *reinterpret_cast<double2*>(&ebuf[wv][q][2 * lane]) = make_double2(e0, e1);
+        double g2 = e0 * e0 + e1 * e1;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) g2 += __shfl_xor(g2, off);
+        gam = sqrt(g2);
+      }
+      rq[q] = r;
+      gq[q] = gam;
     }
-    __syncthreads();
-    const size_t rbase = static_cast<size_t>(v) * static_cast<size_t>(stride);
+    wave_lds_sync();
     if constexpr (KEYS) {
-      double sa = 0.0, sb = 0.0;
-      for (int k = 0; k < kD; ++k) {
-        const double e = ebuf[wv][k];
-        sa = fma(static_cast<double>(st[k * kD + lane]), e, sa);
-        sb = fma(static_cast<double>(st[k * kD + lane + 64]), e, sb);
+      double sa[kQVecs], sb[kQVecs];
+#pragma unroll
+      for (int q = 0; q < kQVecs; ++q) sa[q] = sb[q] = 0.0;
+      for (int k = 0; k < kD; k += 2) {
+        const double s0 = st[k * kD + lane], s1 = st[k * kD + lane + 64];
+        const double t0 = st[(k + 1) * kD + lane], t1 = st[(k + 1) * kD + lane + 64];
+#pragma unroll
+        for (int q = 0; q < kQVecs; ++q) {
+          const double2 e = *reinterpret_cast<const double2*>(&ebuf[wv][q][k]);
+          sa[q] = fma(t0, e.y, fma(s0, e.x, sa[q]));
+          sb[q] = fma(t1, e.y, fma(s1, e.x, sb[q]));
+        }
       }
-      const unsigned long long za = __ballot(sa >= 0.0);
-      const unsigned long long zb = __ballot(sb >= 0.0);
-      const int zi = lane - code_words;
-      if (ok && zi >= 0 && zi < 4) {
-        const unsigned long long zm = zi < 2 ? za : zb;
-        rec[rbase * rec_words + code_words + zi] = static_cast<uint32_t>((zi & 1) ? (zm >> 32) : zm);
+#pragma unroll
+      for (int q = 0; q < kQVecs; ++q) {
+        const unsigned long long za = __ballot(sa[q] >= 0.0);
+        const unsigned long long zb = __ballot(sb[q] >= 0.0);
+        const int zi = lane - code_words;
+        if (v0 + q < n && zi >= 0 && zi < 4) {
+          const unsigned long long zm = zi < 2 ? za : zb;
+          rec[static_cast<size_t>(v0 + q) * static_cast<size_t>(stride) * rec_words + code_words + zi] =
+              static_cast<uint32_t>((zi & 1) ? (zm >> 32) : zm);
+        }
       }
     }
-    if (ok && lane < code_words) {
-      // Word `lane` of the code fields: bits 32 lane .. 32 lane + 31, from
-      // the 2 mb-bit chunks of the lanes that overlap them.
-      const int cw = 2 * mb;
-      const int l0 = (32 * lane) / cw, l1 = (32 * lane + 31) / cw;
-      uint32_t word = 0;
-      for (int l = l0; l <= l1; ++l) {
-        const uint32_t c = chunk[wv][l];
-        const int off = l * cw - 32 * lane;
-        word |= off >= 0 ? (c << off) : (c >> (-off));
+#pragma unroll
+    for (int q = 0; q < kQVecs; ++q) {
+      if (v0 + q >= n) break;
+      const size_t rbase = static_cast<size_t>(v0 + q) * static_cast<size_t>(stride);
+      if (lane < code_words) {
+        // Word `lane` of the code fields: bits 32 lane .. 32 lane + 31, from
+        // the 2 mb-bit chunks of the lanes that overlap them.
+        const int cw = 2 * mb;
+        const int l0 = (32 * lane) / cw, l1 = (32 * lane + 31) / cw;
+        uint32_t word = 0;
+        for (int l = l0; l <= l1; ++l) {
+          const uint32_t c = chunk[wv][q][l];
+          const int off = l * cw - 32 * lane;
+          word |= off >= 0 ? (c << off) : (c >> (-off));
+        }
+        rec[rbase * rec_words + lane] = word;
       }
-      rec[rbase * rec_words + lane] = word;
+      if (lane == 0) {
+        radius[rbase] = f64_to_f16_rne(rq[q]);
+        if constexpr (KEYS) gamma[rbase] = f64_to_f16_rne(gq[q]);
+      }
     }
-    if (ok && lane == 0) {
-      radius[rbase] = f64_to_f16_rne(r);
-      if constexpr (KEYS) gamma[rbase] = f64_to_f16_rne(gam);
-    }
-    __syncthreads();
+    wave_lds_sync();  // this pass's reads are done before the next pass's stores
   }
 }
 
@@ -1009,15 +1055,15 @@ int tq_kv_quantize(const void* x, int x_dtype, int64_t n, const float* signs, co
   if (n < 0 || stride < 1) return TQ_ESHAPE;
   if (n == 0) return TQ_OK;
   const int mb = keys ? bits - 1 : bits;
-  const long long groups = (n + 3) / 4;
-  const unsigned grid = static_cast<unsigned>(groups < 4096 ? groups : 4096);
+  const long long groups = (n + kQWaves * kQVecs - 1) / (kQWaves * kQVecs);
+  const unsigned grid = static_cast<unsigned>(groups < 2048 ? groups : 2048);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int rw = 4 * bits;
-if (keys)
-    hipLaunchKernelGGL(kv_quantize_kernel<true>, dim3(grid), dim3(256), 0, s, x, x_dtype, n, signs, jl, levels, mb,
+  if (keys)
+    hipLaunchKernelGGL(kv_quantize_kernel<true>, dim3(grid), dim3(kQWaves * 64), 0, s, x, x_dtype, n, signs, jl, levels, mb,
                        stride, rw, records, radius, gamma);
   else
-    hipLaunchKernelGGL(kv_quantize_kernel<false>, dim3(grid), dim3(256), 0, s, x, x_dtype, n, signs, jl, levels, mb,
+    hipLaunchKernelGGL(kv_quantize_kernel<false>, dim3(grid), dim3(kQWaves * 64), 0, s, x, x_dtype, n, signs, jl, levels, mb,
                        stride, rw, records, radius, gamma);
   TQ_LAUNCH_CHECK();
   return TQ_OK;
