@@ -94,6 +94,14 @@ TQ_HD void word_offsets_s(uint32_t w, uint32_t o[5]) {
 // o[j] = 4 * chunk j (digits 4j..4j+3) of the word.
 TQ_HD void word_offsets(uint32_t w, uint32_t o[5]) { word_offsets_s<2>(w, o); }
 
+// True when all four bytes of `four` (int8 trits of a chunk, lowest digit in
+// the low byte) are -1, 0 or 1: each byte plus 1 without carries between
+// bytes must be 0, 1 or 2 (no bit above the low two, and not 3).
+TQ_HD bool chunk_trits_valid(uint32_t four) {
+  const uint32_t y = ((four & 0x7f7f7f7fu) + 0x01010101u) ^ (four & 0x80808080u);
+  return ((y & 0xfcfcfcfcu) | (y & (y >> 1) & 0x01010101u)) == 0u;
+}
+
 // Chunk order of the ROW64 layout.  A unit is 160 trits of a row = 8 words
 // = 40 chunks of 4 trits; its words hold its own trits only, but chunk j of
 // unit word wl (0..7) is unit chunk row64_chunk(wl, j), i.e. unit trits

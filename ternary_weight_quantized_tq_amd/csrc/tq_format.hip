@@ -145,7 +145,13 @@ __global__ __launch_bounds__(256) void pack_row64_kernel(const int8_t* __restric
 // order, one coalesced store per thread and word.
 constexpr int kTileStride = kSliceTrits + 16;  // bytes per staged row (16-byte pad against bank conflicts)
 
+// Chunk value sum_d (t_d + 1) 3^d of four int8 trits in one 32-bit word:
+// one 4-way int8 dot product with (1, 3, 9, 27) plus 40 when all four are in
+// {-1, 0, 1} (chunk_trits_valid); a chunk holding another value takes the
+// per-digit rule (packed as a zero trit).
 __device__ __forceinline__ uint32_t chunk_value(uint32_t four) {
+  if (chunk_trits_valid(four))
+    return static_cast<uint32_t>(__builtin_amdgcn_sdot4(static_cast<int>(four), 0x1b090301, 40, false));
   uint32_t c = 0;
 #pragma unroll
   for (int d = 3; d >= 0; --d) c = c * 3u + digit_of(static_cast<int8_t>((four >> (8 * d)) & 0xffu));

@@ -100,3 +100,55 @@ def test_row64_chunk_order():
     for kb in range(4):
         digits = [row64_chunk(2 * kb + h, j) for h in range(2) for j in range(5)]
         assert digits == [8 * s + 2 * kb + e for s in range(5) for e in range(2)]
+
+
+VALID_PROG = r'''
+#include <stdio.h>
+#include <stdint.h>
+#include "tq_decode.h"
+using namespace tq;
+int main() {
+  long bad = 0;
+  /* every byte value at every position, the other bytes each of -1, 0, 1 */
+  const uint32_t ok3[3] = {0xffu, 0x00u, 0x01u};
+  for (int pos = 0; pos < 4; ++pos)
+    for (uint32_t b = 0; b < 256u; ++b)
+      for (int f = 0; f < 81; ++f) {
+        uint32_t four = 0;
+        int g = f;
+        for (int i = 0; i < 4; ++i) {
+          uint32_t byte = ok3[g % 3];
+          g /= 3;
+          if (i == pos) byte = b;
+          four |= byte << (8 * i);
+        }
+        const int8_t sb = (int8_t)b;
+        const bool want = sb >= -1 && sb <= 1;
+        bad += chunk_trits_valid(four) != want;
+      }
+  /* two invalid bytes at once */
+  for (uint32_t a = 0; a < 256u; ++a)
+    for (uint32_t b = 0; b < 256u; ++b) {
+      const uint32_t four = a | (b << 16);
+      const bool want = ((int8_t)a >= -1 && (int8_t)a <= 1) && ((int8_t)b >= -1 && (int8_t)b <= 1);
+      bad += chunk_trits_valid(four) != want;
+    }
+  printf("%ld\n", bad);
+  return bad != 0;
+}
+'''
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_chunk_trits_valid_exhaustive():
+    """The pack kernel's test that a chunk's four int8 values are trits (its
+    fast path then takes one int8 dot product): every byte value at every
+    position beside every valid combination of the others, and every pair of
+    bytes at two positions, against the plain range test."""
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "v.cpp")
+        exe = os.path.join(d, "v")
+        open(src, "w").write(VALID_PROG)
+        subprocess.run(["g++", "-O2", "-std=c++17", f"-I{CSRC}", src, "-o", exe], check=True)
+        p = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+        assert p.returncode == 0 and p.stdout.strip() == "0", p.stdout + p.stderr
