@@ -9,47 +9,68 @@ using namespace tq;
 namespace {
 
 // ------------------------------------------------------------ quantize ---
-// One wavefront per (row, block of 128): load the block in FP64, transform
-// it (27B ternary page, section 2 (1)), then per scale group (the whole
-// block at group 128; lanes 0..31 and 32..63 at group 64, since lane l holds
-// elements 2l, 2l + 1) take gamma = mean |w'| with an fp16 scale (section
-// 2 (2)) and ternarise with the absmean threshold (the TurboQuant-MLX
-// page's {-c, 0, +c}) or take signs (levels 2, its pure 1-bit variant).
+// A wavefront takes kQuantBlocks consecutive (row, block of 128) jobs: the
+// blocks' loads are all issued first (so that enough bytes are in flight),
+// then each block is transformed in FP64 (27B ternary page, section 2 (1))
+// and, per scale group (the whole block at group 128; lanes 0..31 and
+// 32..63 at group 64, since lane l holds elements 2l, 2l + 1), gets
+// gamma = mean |w'| with an fp16 scale (section 2 (2)) and is ternarised
+// with the absmean threshold (the TurboQuant-MLX page's {-c, 0, +c}) or
+// takes signs (levels 2, its pure 1-bit variant).
+constexpr int kQuantBlocks = 8;
+
 template <typename T>
 __global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ w, int n, int k, int group, int levels,
                                                        int8_t* __restrict__ trits,
                                                        uint16_t* __restrict__ scales) {
   const int blocks = k / 128, groups = k / group;
-  const long long job = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (job >= static_cast<long long>(n) * blocks) return;
+  const long long jobs = static_cast<long long>(n) * blocks;
+  const long long job0 = (static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kQuantBlocks;
+  if (job0 >= jobs) return;
   const int lane = threadIdx.x & 63;
-  const int row = static_cast<int>(job / blocks);
-  const int blk = static_cast<int>(job % blocks);
-  const size_t base = static_cast<size_t>(row) * k + static_cast<size_t>(blk) * 128 + 2 * lane;
-  double v0 = static_cast<double>(w[base]);
-  double v1 = static_cast<double>(w[base + 1]);
-  wave_fwht128<double>(v0, v1, lane, 0.08838834764831845 /* 1/sqrt(128) */);
-  double s = fabs(v0) + fabs(v1);
-  // Sum over the lanes of one group: all 64 lanes at group 128, 32 at 64.
+  double v[kQuantBlocks][2];
 #pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  const double s_other_half = __shfl_xor(s, 32);
-  if (group == 128) s += s_other_half;
-  const double gamma = s / static_cast<double>(group);
-  int8_t t0, t1;
-  if (levels == 2) {
-    t0 = v0 >= 0.0 ? 1 : -1;
-    t1 = v1 >= 0.0 ? 1 : -1;
-  } else {
-    const double thr = gamma * 0.5;
-    t0 = v0 > thr ? 1 : (v0 < -thr ? -1 : 0);
-    t1 = v1 > thr ? 1 : (v1 < -thr ? -1 : 0);
+  for (int jb = 0; jb < kQuantBlocks; ++jb) {
+    const long long job = min(job0 + jb, jobs - 1);  // past the end: a repeat, not stored
+    const size_t base = static_cast<size_t>(job) * 128 + 2 * lane;  // rows are whole blocks: job * 128
+    v[jb][0] = static_cast<double>(w[base]);
+    v[jb][1] = static_cast<double>(w[base + 1]);
   }
-  const uint16_t pair = static_cast<uint16_t>(static_cast<uint8_t>(t0)) |
-                        static_cast<uint16_t>(static_cast<uint16_t>(static_cast<uint8_t>(t1)) << 8);
-  reinterpret_cast<uint16_t*>(trits + base)[0] = pair;
-  const int g = group == 128 ? blk : 2 * blk + (lane >> 5);
-  if ((lane & (group == 128 ? 63 : 31)) == 0) scales[static_cast<size_t>(row) * groups + g] = f64_to_f16_rne(gamma);
+#pragma unroll
+  for (int jb = 0; jb < kQuantBlocks; ++jb) {
+    const long long job = job0 + jb;
+    if (job >= jobs) break;
+    const int row = static_cast<int>(job / blocks);
+    const int blk = static_cast<int>(job % blocks);
+    const size_t base = static_cast<size_t>(job) * 128 + 2 * lane;
+    double v0 = v[jb][0], v1 = v[jb][1];
+    wave_fwht128<double>(v0, v1, lane, 0.08838834764831845 /* 1/sqrt(128) */);
+    double s = fabs(v0) + fabs(v1);
+    // Sum over the lanes of one group: all 64 lanes at group 128, 32 at 64.
+    s += lane_xor_f64<16>(s, lane);
+    s += lane_xor_f64<8>(s, lane);
+    s += lane_xor_f64<4>(s, lane);
+    s += lane_xor_f64<2>(s, lane);
+    s += lane_xor_f64<1>(s, lane);
+    const double s_other_half = lane_xor_f64<32>(s, lane);
+    if (group == 128) s += s_other_half;
+    const double gamma = s / static_cast<double>(group);
+    int8_t t0, t1;
+    if (levels == 2) {
+      t0 = v0 >= 0.0 ? 1 : -1;
+      t1 = v1 >= 0.0 ? 1 : -1;
+    } else {
+      const double thr = gamma * 0.5;
+      t0 = v0 > thr ? 1 : (v0 < -thr ? -1 : 0);
+      t1 = v1 > thr ? 1 : (v1 < -thr ? -1 : 0);
+    }
+    const uint16_t pair = static_cast<uint16_t>(static_cast<uint8_t>(t0)) |
+                          static_cast<uint16_t>(static_cast<uint16_t>(static_cast<uint8_t>(t1)) << 8);
+    reinterpret_cast<uint16_t*>(trits + base)[0] = pair;
+    const int g = group == 128 ? blk : 2 * blk + (lane >> 5);
+    if ((lane & (group == 128 ? 63 : 31)) == 0)
+      scales[static_cast<size_t>(row) * groups + g] = f64_to_f16_rne(gamma);
+  }
 }
 
 // ---------------------------------------------------------------- pack ---
@@ -404,8 +425,9 @@ int tq_quantize(const void* w, int w_dtype, int n, int k, int group, int levels,
   if (!tq_aligned(w, w_dtype == TQ_F64 ? 8 : 4) || !tq_aligned(trits, 2) || !tq_aligned(scales, 2)) return TQ_EINVAL;
   if (n <= 0 || k <= 0 || k % TQ_GROUP) return TQ_ESHAPE;
   const size_t jobs = static_cast<size_t>(n) * (k / 128);
-  if (jobs > (static_cast<size_t>(UINT_MAX) / 4)) return TQ_ESHAPE;
-  const unsigned grid = static_cast<unsigned>((jobs + 3) / 4);
+  const size_t waves = (jobs + kQuantBlocks - 1) / kQuantBlocks;
+  if (waves > (static_cast<size_t>(UINT_MAX) / 4)) return TQ_ESHAPE;
+  const unsigned grid = static_cast<unsigned>((waves + 3) / 4);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w_dtype == TQ_F64)
     hipLaunchKernelGGL(quantize_kernel<double>, dim3(grid), dim3(256), 0, s, static_cast<const double*>(w), n, k,

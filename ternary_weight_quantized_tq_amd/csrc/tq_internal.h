@@ -1,5 +1,6 @@
 // Internal helpers shared by the HIP kernels and the C-ABI host layer.
 #pragma once
+#include <type_traits>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -136,6 +137,27 @@ __device__ __forceinline__ float lane_xor_f32(float v, int lane) {
   }
 }
 
+// The same exchange for a double: its two 32-bit halves moved by the
+// 32-bit exchange (bit moves and selects only, so the value is exact).
+template <int S>
+__device__ __forceinline__ double lane_xor_f64(double v, int lane) {
+  const unsigned long long b = static_cast<unsigned long long>(__double_as_longlong(v));
+  const uint32_t lo = __float_as_uint(lane_xor_f32<S>(__uint_as_float(static_cast<uint32_t>(b)), lane));
+  const uint32_t hi = __float_as_uint(lane_xor_f32<S>(__uint_as_float(static_cast<uint32_t>(b >> 32)), lane));
+  return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+// Sum of v over the wavefront, lane strides 32, 16, .., 1 in that order
+// (every lane gets it).
+__device__ __forceinline__ double wave_sum_f64(double v, int lane) {
+  v += lane_xor_f64<32>(v, lane);
+  v += lane_xor_f64<16>(v, lane);
+  v += lane_xor_f64<8>(v, lane);
+  v += lane_xor_f64<4>(v, lane);
+  v += lane_xor_f64<2>(v, lane);
+  v += lane_xor_f64<1>(v, lane);
+  return v;
+}
+
 // Walsh-Hadamard transform of B independent blocks of 128 (one per v[r]),
 // each held by the wavefront with lane l owning elements 2l and 2l+1.
 // Stage stride 1 is inside the lane; strides 2..64 pair lane l with lane
@@ -189,14 +211,21 @@ __device__ __forceinline__ void wave_fwht128(T& v0, T& v1, int lane, T scale) {
     v1 = v[0][1];
   } else {
     T a = v0 + v1, b = v0 - v1;
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-      const T pa = __shfl_xor(a, s);
-      const T pb = __shfl_xor(b, s);
-      const T sgn = (lane & s) ? T(-1) : T(1);  // lower lane a + p, upper lane p - a
+    // Stage of stride S: the lower lane of a pair keeps a + p, the upper p - a.
+    auto stage = [&](auto tag) {
+      constexpr int S = decltype(tag)::value;
+      const T pa = lane_xor_f64<S>(a, lane);
+      const T pb = lane_xor_f64<S>(b, lane);
+      const T sgn = (lane & S) ? T(-1) : T(1);
       a = sgn * a + pa;
       b = sgn * b + pb;
-    }
+    };
+    stage(std::integral_constant<int, 1>{});
+    stage(std::integral_constant<int, 2>{});
+    stage(std::integral_constant<int, 4>{});
+    stage(std::integral_constant<int, 8>{});
+    stage(std::integral_constant<int, 16>{});
+    stage(std::integral_constant<int, 32>{});
     v0 = a * scale;
     v1 = b * scale;
   }

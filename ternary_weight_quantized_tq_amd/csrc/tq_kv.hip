@@ -274,10 +274,7 @@ __global__ __launch_bounds__(kQWaves * 64) void kv_quantize_kernel(const void* _
     double rq[kQVecs], gq[kQVecs];
 #pragma unroll
     for (int q = 0; q < kQVecs; ++q) {
-      double ss = xa[q] * xa[q] + xb[q] * xb[q];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-      const double r = sqrt(ss);
+      const double r = sqrt(wave_sum_f64(xa[q] * xa[q] + xb[q] * xb[q], lane));
       double y0 = sg0 * xa[q], y1 = sg1 * xb[q];
       wave_fwht128<double>(y0, y1, lane, kInvSqrtD);
       const double u0 = r > 0.0 ? y0 / r : 0.0;
@@ -292,10 +289,7 @@ __global__ __launch_bounds__(kQWaves * 64) void kv_quantize_kernel(const void* _
       if constexpr (KEYS) {
         const double e0 = u0 - lv[c0], e1 = u1 - lv[c1];
         *reinterpret_cast<double2*>(&ebuf[wv][q][2 * lane]) = make_double2(e0, e1);
-        double g2 = e0 * e0 + e1 * e1;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) g2 += __shfl_xor(g2, off);
-        gam = sqrt(g2);
+        gam = sqrt(wave_sum_f64(e0 * e0 + e1 * e1, lane));
       }
       rq[q] = r;
       gq[q] = gam;
