@@ -300,6 +300,29 @@ __global__ __launch_bounds__(256) void pack_bin_row64_kernel(const int8_t* __res
   words[idx] = row < n ? pack_bits(trits + static_cast<size_t>(row) * k, k, w * TQ_BITS_PER_WORD) : 0u;
 }
 
+// ROW64 scale re-layout through LDS, one workgroup per row block: its 64
+// rows' scales (groups contiguous per row) are read once, coalesced, and
+// every slice's [group][64 rows] piece is written contiguously.  For
+// blocks whose scales fit kScaleTileBytes of LDS; larger ones take
+// scales_row64_kernel.
+constexpr int kScaleTileBytes = 32 * 1024;
+__global__ __launch_bounds__(256) void scales_row64_tile_kernel(const uint16_t* __restrict__ s, int n, int groups,
+                                                                int nsl, int nb, int G, uint16_t* __restrict__ out) {
+  __shared__ uint16_t tile[kScaleTileBytes / 2];  // [row][group]
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int rows = min(64, n - b * 64);
+  const uint16_t* src = s + static_cast<size_t>(b) * 64 * groups;
+  for (int i = tid; i < rows * groups; i += 256) tile[i] = src[i];  // contiguous: the block's rows are adjacent
+  __syncthreads();
+  for (int sl = 0; sl < nsl; ++sl) {
+    uint16_t* dst = out + (static_cast<size_t>(sl) * nb + b) * G * 64;
+    for (int i = tid; i < G * 64; i += 256) {
+      const int gi = i >> 6, r = i & 63, g = sl * G + gi;
+      dst[i] = (r < rows && g < groups) ? tile[r * groups + g] : static_cast<uint16_t>(0);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void scales_row64_kernel(const uint16_t* __restrict__ s, int n, int groups,
                                                            int nsl, int nb, int G, uint16_t* __restrict__ out) {
   const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -511,8 +534,12 @@ int tq_pack_scales(const uint16_t* scales, int n, int k, int layout, int group, 
     return TQ_OK;
   }
   const int nb = row_blocks(n), nsl = slices_per_row(k);
-  hipLaunchKernelGGL(scales_row64_kernel, dim3(grid_for(static_cast<size_t>(nsl) * nb * G * 64)), dim3(256), 0, s,
-                     scales, n, groups, nsl, nb, G, scales_out);
+  if (static_cast<size_t>(64) * groups * 2 <= kScaleTileBytes)
+    hipLaunchKernelGGL(scales_row64_tile_kernel, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, scales, n, groups,
+                       nsl, nb, G, scales_out);
+  else
+    hipLaunchKernelGGL(scales_row64_kernel, dim3(grid_for(static_cast<size_t>(nsl) * nb * G * 64)), dim3(256), 0, s,
+                       scales, n, groups, nsl, nb, G, scales_out);
   TQ_LAUNCH_CHECK();
   return TQ_OK;
 }
