@@ -67,11 +67,16 @@ extern "C" {
 #define TQ_TRITS_PER_WORD 20
 #define TQ_GROUP 128      /* default weights per scale; 64 is the other group size */
 #define TQ_BITS_PER_WORD 32 /* binary variant: one sign bit per weight */
+/* Largest n, k or activation row count m that any call takes (2^30): every
+ * row, slice and word index the kernels form then fits an int.  Larger
+ * sizes are TQ_ESHAPE, and the size queries return 0 for them. */
+#define TQ_MAX_DIM (1 << 30)
 
 typedef enum {
   TQ_OK = 0,
   TQ_EINVAL = -1,       /* null pointer, bad enum, bad flag                    */
-  TQ_ESHAPE = -2,       /* size out of range or K not a multiple of 128        */
+  TQ_ESHAPE = -2,       /* size out of range (above TQ_MAX_DIM, or not
+                           positive) or K not a multiple of 128              */
   TQ_EFORMAT = -3,      /* descriptor magic/version/layout/expert count wrong  */
   TQ_ENOSPACE = -4,     /* workspace too small                                 */
   TQ_EHIP = -5,         /* a HIP launch failed                                 */

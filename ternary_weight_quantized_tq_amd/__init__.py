@@ -22,6 +22,7 @@ TQ_VERSION = 2
 TQ_TRITS_PER_WORD = 20
 TQ_GROUP = 128
 TQ_BITS_PER_WORD = 32
+TQ_MAX_DIM = 1 << 30
 TQ_OK, TQ_EINVAL, TQ_ESHAPE, TQ_EFORMAT, TQ_ENOSPACE, TQ_EHIP, TQ_EUNSUPPORTED, TQ_EDATA = 0, -1, -2, -3, -4, -5, -6, -7
 TQ_F32, TQ_BF16, TQ_F16, TQ_F64 = 0, 1, 2, 3
 TQ_LAYOUT_ROWMAJOR, TQ_LAYOUT_ROW64 = 0, 1

@@ -1,6 +1,7 @@
 // Workspace sizing and error reporting for the C entry points.
 #include "tq_internal.h"
 
+#include <limits.h>
 #include <stdio.h>
 
 namespace {
@@ -14,13 +15,13 @@ void tq_set_hip_error(hipError_t e, const char* where) {
 extern "C" const char* tq_last_error(void) { return g_last_error; }
 
 extern "C" size_t tq_workspace_bytes(int op, const tq_weights* w, int m_or_t, int topk) {
-  if (tq_check_weights(w, 0) != TQ_OK || m_or_t < 1) return SIZE_MAX;
+  if (tq_check_weights(w, 0) != TQ_OK || !tq::tq_dim_ok(m_or_t)) return SIZE_MAX;
   switch (op) {
     case TQ_OP_GEMV:
       if (w->num_experts != 1 || m_or_t > 8) return SIZE_MAX;
       return tq_gemv_workspace(w->n, w->k, m_or_t);
     case TQ_OP_MOE:
-      if (topk < 1 || topk > 32) return SIZE_MAX;
+      if (topk < 1 || topk > 32 || static_cast<long long>(m_or_t) * topk > INT_MAX / 4) return SIZE_MAX;
       return tq_moe_workspace(w, m_or_t, topk);
     case TQ_OP_GEMM:
       if (w->num_experts != 1) return SIZE_MAX;

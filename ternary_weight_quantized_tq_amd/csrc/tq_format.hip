@@ -398,21 +398,21 @@ inline unsigned grid_for(size_t threads) { return static_cast<unsigned>((threads
 
 extern "C" {
 
-size_t tq_words_per_row(int k) { return k > 0 ? static_cast<size_t>(words_per_row(k)) : 0; }
+size_t tq_words_per_row(int k) { return tq_dim_ok(k) ? static_cast<size_t>(words_per_row(k)) : 0; }
 
 size_t tq_packed_bytes(int n, int k) {
-  if (n <= 0 || k <= 0) return 0;
+  if (!tq_dim_ok(n) || !tq_dim_ok(k)) return 0;
   return 4ull * n * words_per_row(k) + 2ull * n * (k / TQ_GROUP);
 }
 
 size_t tq_format_bytes(int n, int k, int group, int levels) {
-  if (n <= 0 || k <= 0 || !tq_group_ok(group) || !tq_levels_ok(levels) || k % group) return 0;
+  if (!tq_dim_ok(n) || !tq_dim_ok(k) || !tq_group_ok(group) || !tq_levels_ok(levels) || k % group) return 0;
   const size_t wpr = levels == 3 ? words_per_row(k) : words_per_row_bin(k);
   return 4ull * n * wpr + 2ull * n * (k / group);
 }
 
 size_t tq_layout_words(int n, int k, int layout, int levels) {
-  if (n <= 0 || k <= 0 || !tq_levels_ok(levels)) return 0;
+  if (!tq_dim_ok(n) || !tq_dim_ok(k) || !tq_levels_ok(levels)) return 0;
   if (layout == TQ_LAYOUT_ROWMAJOR)
     return static_cast<size_t>(n) * (levels == 3 ? words_per_row(k) : words_per_row_bin(k));
   if (layout == TQ_LAYOUT_ROW64) return tq_row64_words(n, k, levels);
@@ -420,7 +420,7 @@ size_t tq_layout_words(int n, int k, int layout, int levels) {
 }
 
 size_t tq_layout_scales(int n, int k, int layout, int group) {
-  if (n <= 0 || k <= 0 || !tq_group_ok(group) || k % TQ_GROUP) return 0;
+  if (!tq_dim_ok(n) || !tq_dim_ok(k) || !tq_group_ok(group) || k % TQ_GROUP) return 0;
   if (layout == TQ_LAYOUT_ROWMAJOR) return static_cast<size_t>(n) * (k / group);
   if (layout == TQ_LAYOUT_ROW64) return tq_row64_scales(n, k, group);
   return 0;
@@ -446,7 +446,7 @@ int tq_quantize(const void* w, int w_dtype, int n, int k, int group, int levels,
   if (w_dtype != TQ_F64 && w_dtype != TQ_F32) return TQ_EINVAL;
   if (!tq_group_ok(group) || !tq_levels_ok(levels)) return TQ_EINVAL;
   if (!tq_aligned(w, w_dtype == TQ_F64 ? 8 : 4) || !tq_aligned(trits, 2) || !tq_aligned(scales, 2)) return TQ_EINVAL;
-  if (n <= 0 || k <= 0 || k % TQ_GROUP) return TQ_ESHAPE;
+  if (!tq_dim_ok(n) || !tq_dim_ok(k) || k % TQ_GROUP) return TQ_ESHAPE;
   const size_t jobs = static_cast<size_t>(n) * (k / 128);
   const size_t waves = (jobs + kQuantBlocks - 1) / kQuantBlocks;
   if (waves > (static_cast<size_t>(UINT_MAX) / 4)) return TQ_ESHAPE;
@@ -467,7 +467,7 @@ int tq_pack(const int8_t* trits, int n, int k, int layout, int levels, uint32_t*
   if (layout != TQ_LAYOUT_ROWMAJOR && layout != TQ_LAYOUT_ROW64) return TQ_EINVAL;
   if (!tq_levels_ok(levels)) return TQ_EINVAL;
   if (!tq_aligned(words, 4)) return TQ_EINVAL;
-  if (n <= 0 || k <= 0) return TQ_ESHAPE;
+  if (!tq_dim_ok(n) || !tq_dim_ok(k)) return TQ_ESHAPE;
   if (layout == TQ_LAYOUT_ROW64 && k % TQ_GROUP) return TQ_ESHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (levels == 2) {
@@ -521,7 +521,7 @@ int tq_pack_scales(const uint16_t* scales, int n, int k, int layout, int group, 
   if (layout != TQ_LAYOUT_ROWMAJOR && layout != TQ_LAYOUT_ROW64) return TQ_EINVAL;
   if (!tq_group_ok(group)) return TQ_EINVAL;
   if (!tq_aligned(scales, 2) || !tq_aligned(scales_out, 2)) return TQ_EINVAL;
-  if (n <= 0 || k <= 0 || k % TQ_GROUP) return TQ_ESHAPE;
+  if (!tq_dim_ok(n) || !tq_dim_ok(k) || k % TQ_GROUP) return TQ_ESHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int groups = k / group, G = slice_groups(group);
   if (layout == TQ_LAYOUT_ROWMAJOR) {
@@ -549,7 +549,7 @@ int tq_unpack(const uint32_t* words, int n, int k, int layout, int levels, int8_
   if (layout != TQ_LAYOUT_ROWMAJOR && layout != TQ_LAYOUT_ROW64) return TQ_EINVAL;
   if (!tq_levels_ok(levels)) return TQ_EINVAL;
   if (!tq_aligned(words, 4)) return TQ_EINVAL;
-  if (n <= 0 || k <= 0) return TQ_ESHAPE;
+  if (!tq_dim_ok(n) || !tq_dim_ok(k)) return TQ_ESHAPE;
   if (layout == TQ_LAYOUT_ROW64 && k % TQ_GROUP) return TQ_ESHAPE;
   if (levels == 2) {
     const int wpr = layout == TQ_LAYOUT_ROW64 ? slices_per_row(k) * kSliceWordsBin : words_per_row_bin(k);
@@ -574,7 +574,7 @@ int tq_fwht(const void* x, int x_dtype, int m, int k, float* x_rot, void* stream
   if (!x || !x_rot) return TQ_EINVAL;
   if (bad_dtype(x_dtype)) return TQ_EINVAL;
   if (!tq_aligned(x, tq_act_align(x_dtype)) || !tq_aligned(x_rot, 8)) return TQ_EINVAL;
-  if (m <= 0 || k <= 0 || k % TQ_GROUP) return TQ_ESHAPE;
+  if (!tq_dim_ok(m) || !tq_dim_ok(k) || k % TQ_GROUP) return TQ_ESHAPE;
   const size_t jobs = static_cast<size_t>(m) * (k / 128);
   if (jobs > (static_cast<size_t>(UINT_MAX) / 4)) return TQ_ESHAPE;
   hipLaunchKernelGGL(fwht_kernel, dim3(static_cast<unsigned>((jobs + 3) / 4)), dim3(256), 0,

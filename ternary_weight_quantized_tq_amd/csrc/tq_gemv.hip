@@ -854,7 +854,7 @@ int tq_check_weights(const tq_weights* w, int experts_expected) {
   if (w->layout != TQ_LAYOUT_ROW64) return w->layout == TQ_LAYOUT_ROWMAJOR ? TQ_EUNSUPPORTED : TQ_EFORMAT;
   if (experts_expected > 0 && w->num_experts != experts_expected) return TQ_EFORMAT;
   if (w->num_experts < 1) return TQ_EFORMAT;
-  if (w->n <= 0 || w->k <= 0 || w->k % TQ_GROUP) return TQ_ESHAPE;
+  if (!tq_dim_ok(w->n) || !tq_dim_ok(w->k) || w->k % TQ_GROUP) return TQ_ESHAPE;
   if (!w->words || !w->scales) return TQ_EINVAL;
   if (!tq_aligned(w->words, 16) || !tq_aligned(w->scales, 16)) return TQ_EINVAL;
   return TQ_OK;

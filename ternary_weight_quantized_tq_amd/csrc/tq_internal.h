@@ -28,6 +28,8 @@ constexpr int kSliceQuadsBin = 5;
 __host__ __device__ constexpr int slice_groups(int group) { return kSliceTrits / group; }
 inline bool tq_group_ok(int group) { return group == 64 || group == 128; }
 inline bool tq_levels_ok(int levels) { return levels == 2 || levels == 3; }
+// A matrix or activation dimension the library takes: 1 .. TQ_MAX_DIM.
+inline bool tq_dim_ok(int v) { return v > 0 && v <= TQ_MAX_DIM; }
 
 // Pointer alignment checks of the entry points: p is a multiple of a bytes
 // (a a power of two); activations are read two elements at a time.

@@ -165,6 +165,36 @@ def test_moe_and_gemm_check_alignment():
     assert gemm(ws=0x5008) == tq.TQ_EINVAL
 
 
+def test_dimensions_above_the_limit_are_rejected():
+    """n, k and m up to TQ_MAX_DIM pass the shape checks (the size queries
+    return finite sizes), one step beyond is TQ_ESHAPE or a zero / SIZE_MAX
+    size, before any device work."""
+    lib = tq.lib()
+    top, big = tq.TQ_MAX_DIM, tq.TQ_MAX_DIM + 128
+    assert 0 < tq.tq_packed_bytes(top, top) < tq.SIZE_MAX
+    assert tq.tq_packed_bytes(big, 128) == 0 and tq.tq_packed_bytes(128, big) == 0
+    assert tq.tq_format_bytes(big, 128, 64, 2) == 0
+    assert tq.tq_layout_words(top, top, tq.TQ_LAYOUT_ROW64, 3) > 0
+    assert tq.tq_layout_words(big, 128, tq.TQ_LAYOUT_ROW64, 3) == 0
+    assert tq.tq_layout_scales(128, big, tq.TQ_LAYOUT_ROWMAJOR, 128) == 0
+    assert lib.tq_words_per_row(big) == 0
+    for kw in (dict(n=big), dict(k=big)):
+        w = _desc(**kw)
+        assert lib.tq_gemv(ctypes.byref(w), 0x3000, tq.TQ_BF16, 1, 0x4000, 0, 0x5000, 1 << 20, None) == tq.TQ_ESHAPE
+        assert lib.tq_workspace_bytes(tq.TQ_OP_GEMV, ctypes.byref(w), 1, 0) == tq.SIZE_MAX
+    w = _desc()
+    assert lib.tq_workspace_bytes(tq.TQ_OP_GEMM, ctypes.byref(w), big, 0) == tq.SIZE_MAX
+    assert lib.tq_workspace_bytes(tq.TQ_OP_MOE, ctypes.byref(_desc(num_experts=4)), 1 << 28, 8) == tq.SIZE_MAX
+    assert lib.tq_gemm(ctypes.byref(w), 0x3000, tq.TQ_F32, big, 0x4000, 0, 0x5000, 1 << 24, None) == tq.TQ_ESHAPE
+    assert lib.tq_pack(0x10, big, 20, tq.TQ_LAYOUT_ROWMAJOR, 3, 0x10, None) == tq.TQ_ESHAPE
+    assert lib.tq_pack(0x10, 4, big, tq.TQ_LAYOUT_ROW64, 3, 0x10, None) == tq.TQ_ESHAPE
+    assert lib.tq_unpack(0x10, big, 128, tq.TQ_LAYOUT_ROW64, 3, 0x10, None) == tq.TQ_ESHAPE
+    assert lib.tq_pack_scales(0x10, big, 128, tq.TQ_LAYOUT_ROW64, 128, 0x10, None) == tq.TQ_ESHAPE
+    assert lib.tq_quantize(0x10, tq.TQ_F64, big, 128, 128, 3, 0x10, 0x10, None) == tq.TQ_ESHAPE
+    assert lib.tq_fwht(0x10, tq.TQ_F32, big, 128, 0x10, None) == tq.TQ_ESHAPE
+    assert lib.tq_fwht(0x10, tq.TQ_F32, 2, big, 0x10, None) == tq.TQ_ESHAPE
+
+
 def test_offline_calls_check_alignment():
     lib = tq.lib()
     assert lib.tq_pack(0x10, 4, 20, 0, 3, 0x12, None) == tq.TQ_EINVAL             # words 4 bytes
